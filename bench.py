@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the channelwise gated delta rule on one MI355X.
+
+Prints ONE JSON line.  ``value`` is prefill throughput in tokens/s on the single-sequence
+prefill workload (B=1, T=4097 with a ragged final chunk, HK=16, HV=32, dk=dv=128,
+chunk 64, bf16 q/k/v, fp32 g/beta/state/outputs).  A "step" is one full prefill call
+(both kernels: the chunk-parallel stage and the sequential carry).  The same line
+carries the decode half of the metric (state GB/s over 1000 carried decode steps at
+B=32, HK=16, HV=32, dk=dv=128), the roofline of the dominant kernel, the fp64 CPU
+oracle's throughput on the same workload, and the parity error of this run's outputs
+against that oracle.  All inputs are seeded synthetic data resident in HBM before timing.
+
+    python bench.py [--steps K] [--warmup W] [--decode-steps N] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s (HV=32,dk=dv=128) + decode state GB/s, % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak, published
+
+
+def prefill_bytes(B, T, HK, HV, dk, dv, elt, h0):
+    """Algorithmic HBM bytes of one prefill, split by the kernel that must move them.
+
+    prep  : q, k (once per key head), g, beta
+    carry : v, o, the initial state (if any) and the final state
+    """
+    prep = B * T * (2 * HK * dk * elt + HV * (dk * 4 + 4))
+    carry = B * T * HV * (dv * elt + dv * 4) + B * HV * dk * dv * 4 * (2 if h0 else 1)
+    return prep, carry
+
+
+def prefill_flops(B, T, HV, dk, dv, C):
+    """Algorithmic flops of the chunked form, per chunk of L tokens and value head:
+    gram + causal terms 2K L^2, solve (K+V) L(L-1), state products 6 L K V, P U V L(L+1).
+    Returns (prep, carry) with the gram and the pseudo-key solve in prep."""
+    prep = carry = 0
+    t = T
+    while t > 0:
+        L = min(C, t)
+        prep += 2 * dk * L * L + dk * L * (L - 1)
+        carry += dv * L * (L - 1) + 6 * L * dk * dv + dv * L * (L + 1)
+        t -= L
+    return prep * B * HV, carry * B * HV
+
+
+def decode_bytes(B, HK, HV, dk, dv, elt):
+    return 2 * B * HV * dk * dv * 4 + B * (2 * HK * dk * elt + HV * (dv * elt + dk * 4 + 4 + dv * 4))
+
+
+def _mean(xs):
+    return sum(xs) / len(xs)
+
+
+def bench_prefill(w, steps, warmup):
+    import torch
+
+    import gated_delta_rule_70_amd as gdr
+    from gdr_synth import workload_inputs
+
+    x = workload_inputs(w)
+    d = {k: (None if v is None else v.cuda()) for k, v in x.items()}
+    B, T, HK, HV, dk, dv, C = w.B, w.T, w.HK, w.HV, w.dk, w.dv, w.chunk
+    ws = torch.empty(gdr.workspace_bytes(B, T, HK, HV, dk, dv, C), dtype=torch.uint8, device="cuda")
+    o = torch.empty(B, T, HV, dv, device="cuda")
+    ht = torch.empty(B, HV, dk, dv, device="cuda")
+
+    def call(stage):
+        gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], chunk=C, o=o, ht=ht,
+                          workspace=ws, stage=stage)
+
+    for _ in range(warmup):
+        call("prep")
+        call("carry")
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        call("prep")
+        e[1].record()
+        call("carry")
+        e[2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prep_ms = _mean([e[0].elapsed_time(e[1]) for e in ev])
+    carry_ms = _mean([e[1].elapsed_time(e[2]) for e in ev])
+    return x, o, ht, wall, prep_ms, carry_ms
+
+
+def bench_decode(w, steps, warmup):
+    """Carried decode steps on one state (the workload as defined), then the same number of
+    steps cycling over 8 independent states (512 MiB) so the state stream cannot be
+    served from the 256 MB last-level cache."""
+    import torch
+
+    import gated_delta_rule_70_amd as gdr
+    from gdr_synth import make_inputs
+
+    B, HK, HV, dk, dv = w.B, w.HK, w.HV, w.dk, w.dv
+    nstep = min(steps, w.steps)
+    x = make_inputs(B, nstep, HK, HV, dk, dv, dtype=w.dtype, seed=w.seed, h0=True)
+    # per-step contiguous views [B,1,H,d]
+    tm = {n: x[n].transpose(0, 1).contiguous().cuda() for n in ("q", "k", "v", "g", "beta")}
+    h0 = x["h0"].cuda()
+    L = gdr.lib()
+    dims = gdr.Dims(B, 1, HK, HV, dk, dv, 0, gdr.BF16)
+    obuf = torch.empty(nstep, B, HV, dv, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = [(ptr(tm["q"][t]), ptr(tm["k"][t]), ptr(tm["v"][t]), ptr(tm["g"][t]), ptr(tm["beta"][t]),
+             ptr(obuf[t])) for t in range(nstep)]
+
+    def run(states, timed):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(nstep)] if timed else None
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(nstep):
+            s = ptr(states[t % len(states)])
+            q, k, v, g, b, o = args[t]
+            if timed:
+                ev[t][0].record()
+            st = L.gdr_decode_step(ctypes.byref(dims), q, k, v, g, b, s, o, s, stream)
+            if st != 0:
+                raise RuntimeError(f"gdr_decode_step failed: {st}")
+            if timed:
+                ev[t][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = [a.elapsed_time(b) for a, b in ev] if timed else []
+        return wall, per
+
+    scratch = [h0.clone()]
+    for _ in range(max(1, warmup)):
+        run(scratch, False)
+    state = h0.clone()
+    wall_c, per_c = run([state], True)
+    rot = [h0.clone() for _ in range(8)]
+    wall_r, per_r = run(rot, True)
+    per_c.sort()
+    per_r.sort()
+    return {
+        "nstep": nstep,
+        "carried": {"wall_s": wall_c, "mean_ms": _mean(per_c), "median_ms": per_c[len(per_c) // 2]},
+        "rotating8": {"wall_s": wall_r, "mean_ms": _mean(per_r), "median_ms": per_r[len(per_r) // 2]},
+        "inputs": x, "obuf": obuf, "state": state,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--workload", default="prefill_b1_t4097")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the recurrence's (batch, head) pairs are independent, "
+              "so a multi-GPU run is N independent copies of this one; run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_70_amd as gdr  # noqa: F401  (fails loudly if libgdr.so is missing)
+    from gdr_synth import DECODE, WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    elt = 2 if w.dtype == torch.bfloat16 else 4
+    x, o, ht, wall, prep_ms, carry_ms = bench_prefill(w, args.steps, args.warmup)
+    ntok = w.B * w.T
+    ms_per_step = wall / args.steps * 1e3
+    value = ntok / (wall / args.steps)
+    b_prep, b_carry = prefill_bytes(w.B, w.T, w.HK, w.HV, w.dk, w.dv, elt, w.h0)
+    f_prep, f_carry = prefill_flops(w.B, w.T, w.HV, w.dk, w.dv, w.chunk)
+    kern_ms = prep_ms + carry_ms
+    dom = "chunk_carry" if carry_ms >= prep_ms else "chunk_prep"
+    dom_ms = max(prep_ms, carry_ms)
+    dom_bytes = b_carry if dom == "chunk_carry" else b_prep
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "alg_bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 5)}
+    path_gbs = (b_prep + b_carry) / (kern_ms * 1e-3) / 1e9
+    path_tflops = (f_prep + f_carry) / (kern_ms * 1e-3) / 1e12
+    prefill = {
+        "kernels_ms": {"chunk_prep": round(prep_ms, 5), "chunk_carry": round(carry_ms, 5)},
+        "path_alg_bytes": b_prep + b_carry, "path_alg_flops": f_prep + f_carry,
+        "path_hbm_GBps": round(path_gbs, 1), "path_hbm_frac": round(path_gbs / HBM_PEAK_GBS, 4),
+        "path_mfma_TFLOPs": round(path_tflops, 2),
+        "path_frac_of_bf16_mfma_peak": round(path_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "tokens_per_s_kernel_time": round(ntok / (kern_ms * 1e-3), 1),
+    }
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16 mfma operands, f32 accumulate/state", "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} T={w.T} HK={w.HK} HV={w.HV} dk={w.dk} dv={w.dv} "
+                               f"chunk={w.chunk} bf16 q/k/v, fp32 g/beta/state/o, h0={'yes' if w.h0 else 'no'}",
+                   "global_batch": w.B, "seq_len": w.T, "parallelism": "single GPU"},
+        "roofline": roofline, "prefill": prefill,
+    }
+
+    if not args.no_decode:
+        dres = bench_decode(DECODE, args.decode_steps, 10)
+        dbytes = decode_bytes(DECODE.B, DECODE.HK, DECODE.HV, DECODE.dk, DECODE.dv, 2)
+        sbytes = 2 * DECODE.B * DECODE.HV * DECODE.dk * DECODE.dv * 4
+        dec = {"workload": f"decode_b32: B={DECODE.B} HK={DECODE.HK} HV={DECODE.HV} dk=dv={DECODE.dk} "
+                           f"bf16 q/k/v, {dres['nstep']} carried steps",
+               "alg_bytes_per_step": dbytes, "state_bytes_per_step": sbytes}
+        for mode in ("carried", "rotating8"):
+            r = dres[mode]
+            gbs = dbytes / (r["mean_ms"] * 1e-3) / 1e9
+            dec[mode] = {"avg_launch_ms": round(r["mean_ms"], 5), "median_launch_ms": round(r["median_ms"], 5),
+                         "wall_ms_per_step": round(r["wall_s"] / dres["nstep"] * 1e3, 5),
+                         "state_GBps": round(sbytes / (r["mean_ms"] * 1e-3) / 1e9, 1),
+                         "total_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        line["decode"] = dec
+
+    if not args.no_cpu_baseline:
+        import numpy as np
+
+        import oracle
+
+        t0 = time.perf_counter()
+        o_ref, ht_ref = oracle.sequential(**x)
+        cpu_s = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(ntok / cpu_s, 1), "unit": "tokens/s",
+                                "cores": oracle.num_threads(), "kind": "oracle",
+                                "sample": f"the full {w.name} workload ({ntok} tokens x {w.HV} value heads), "
+                                          f"fp64 sequential recurrence, {cpu_s:.2f} s"}
+        line["parity_vs_oracle"] = {
+            "o": float(oracle.rel_err(o.double().cpu().numpy(), o_ref)),
+            "state": float(oracle.rel_err(ht.double().cpu().numpy(), ht_ref)),
+            "tolerance": 2e-3}
+        del np
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

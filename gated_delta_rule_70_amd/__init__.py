@@ -1,0 +1,181 @@
+"""Channelwise gated delta rule on AMD Instinct MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libgdr.so`` (C ABI declared in ``include/gdr.h``).  It only
+marshals arguments: PyTorch supplies device memory and the current HIP stream, and every
+step of the computation runs in the library's HIP kernels.  There is no CPU fallback:
+if the library is missing, the calls raise.
+
+    import torch, gated_delta_rule_70_amd as gdr
+    o, ht = gdr.chunk_prefill(q, k, v, g, beta, h0=None, chunk=64)   # prefill, any T >= 1
+    o = gdr.decode_step(q1, k1, v1, g1, beta1, state)                  # T == 1, state in place
+
+Layouts (dense, row-major, on the GPU): q, k ``[B,T,HK,dk]`` and v ``[B,T,HV,dv]`` in
+bf16 or fp32; g ``[B,T,HV,dk]`` and beta ``[B,T,HV]`` in fp32; states ``[B,HV,dk,dv]``
+fp32; o ``[B,T,HV,dv]`` fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["decode_step", "chunk_prefill", "workspace_bytes", "GdrError", "lib", "Dims",
+           "LIB_PATH", "ABI_VERSION"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so")
+ABI_VERSION = 1
+BF16, F32 = 0, 1
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("HK", ctypes.c_int32),
+                ("HV", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("qkv_dtype", ctypes.c_int32)]
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"gdr status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+_VP = ctypes.c_void_p
+
+
+def lib():
+    """Load libgdr.so (after torch, so both share one HIP runtime) and bind its symbols."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m gated_delta_rule_70_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    L.gdr_abi_version.restype = ctypes.c_int
+    L.gdr_abi_version.argtypes = []
+    L.gdr_status_str.restype = ctypes.c_char_p
+    L.gdr_status_str.argtypes = [ctypes.c_int]
+    L.gdr_decode_step.restype = ctypes.c_int
+    L.gdr_decode_step.argtypes = [ctypes.POINTER(Dims)] + [_VP] * 9
+    L.gdr_chunk_prefill_workspace_bytes.restype = ctypes.c_size_t
+    L.gdr_chunk_prefill_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
+    L.gdr_chunk_prefill.restype = ctypes.c_int
+    L.gdr_chunk_prefill.argtypes = [ctypes.POINTER(Dims)] + [_VP] * 9 + [ctypes.c_size_t, _VP]
+    for name in ("gdr_chunk_prep", "gdr_chunk_carry"):
+        fn = getattr(L, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = L.gdr_chunk_prefill.argtypes
+    if L.gdr_abi_version() != ABI_VERSION:
+        raise RuntimeError("libgdr.so ABI version mismatch; rebuild it")
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise GdrError(status, lib().gdr_status_str(status).decode())
+
+
+def _qkv_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else _VP(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _dims(q, v, chunk) -> Dims:
+    B, T, HK, dk = q.shape
+    HV, dv = v.shape[2], v.shape[3]
+    return Dims(B, T, HK, HV, dk, dv, int(chunk), _qkv_dtype(q))
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _VP(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check_inputs(q, k, v, g, beta):
+    dt = q.dtype
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dt)
+    _need(g, "g", torch.float32)
+    _need(beta, "beta", torch.float32)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4:
+        raise ValueError("q, k must be [B,T,HK,dk] and v [B,T,HV,dv]")
+
+
+def workspace_bytes(B, T, HK, HV, dk, dv, chunk=64, dtype=torch.bfloat16) -> int:
+    d = Dims(B, T, HK, HV, dk, dv, chunk, BF16 if dtype == torch.bfloat16 else F32)
+    return int(lib().gdr_chunk_prefill_workspace_bytes(ctypes.byref(d)))
+
+
+def decode_step(q, k, v, g, beta, state, o=None, out_state=None, stream=None):
+    """One decode step (T == 1).  Updates ``state`` in place unless ``out_state`` is given.
+
+    ``state`` may be None (zero initial state; then ``out_state`` receives the new state if
+    given).  Returns ``o`` ``[B,1,HV,dv]`` fp32.
+    """
+    _check_inputs(q, k, v, g, beta)
+    B, T, HK, dk = q.shape
+    HV, dv = v.shape[2], v.shape[3]
+    if state is not None:
+        _need(state, "state", torch.float32)
+    if o is None:
+        o = torch.empty(B, T, HV, dv, device=q.device, dtype=torch.float32)
+    _need(o, "o", torch.float32)
+    ht = state if out_state is None else out_state
+    if ht is not None:
+        _need(ht, "out_state", torch.float32)
+    d = _dims(q, v, 0)
+    _check(lib().gdr_decode_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(state), _ptr(o), _ptr(ht), _stream(stream)))
+    return o
+
+
+def chunk_prefill(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
+                  workspace=None, want_state: bool = True, stream=None, stage: str = "both"):
+    """Chunkwise WY/UT prefill over all T tokens.  Returns ``(o, ht)`` (``ht`` None if not wanted).
+
+    ``workspace`` (optional) is a uint8 GPU tensor of at least ``workspace_bytes(...)``
+    bytes; one is allocated if omitted.  ``ht`` may be ``h0`` itself (in-place carry).
+    ``stage`` selects "both" (gdr_chunk_prefill), "prep" (gdr_chunk_prep) or "carry"
+    (gdr_chunk_carry, which needs a workspace filled by "prep" for the same inputs).
+    """
+    entry = {"both": "gdr_chunk_prefill", "prep": "gdr_chunk_prep", "carry": "gdr_chunk_carry"}[stage]
+    _check_inputs(q, k, v, g, beta)
+    B, T, HK, dk = q.shape
+    HV, dv = v.shape[2], v.shape[3]
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    if o is None:
+        o = torch.empty(B, T, HV, dv, device=q.device, dtype=torch.float32)
+    _need(o, "o", torch.float32)
+    if ht is None and want_state:
+        ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
+    if ht is not None:
+        _need(ht, "ht", torch.float32)
+    d = _dims(q, v, chunk)
+    need = int(lib().gdr_chunk_prefill_workspace_bytes(ctypes.byref(d)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    _need(workspace, "workspace", torch.uint8)
+    _check(getattr(lib(), entry)(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                   _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht), _ptr(workspace),
+                                   ctypes.c_size_t(workspace.numel()), _stream(stream)))
+    return o, ht

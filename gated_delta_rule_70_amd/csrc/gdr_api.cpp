@@ -1,0 +1,208 @@
+// Host entry points of libgdr.so: argument validation, workspace sizing and kernel
+// launches on the caller's stream.  Every check runs before the first HIP call, so a call
+// that fails validation enqueues nothing and writes nothing.
+#include "gdr.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "gdr_launch.h"
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+    bool empty() const { return hi <= lo; }
+};
+
+Range range_of(const void* p, size_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, p ? lo + bytes : lo};
+}
+
+bool overlap(Range a, Range b) { return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_head_dim(int d) { return d == 32 || d == 64 || d == 128; }
+
+// Sizes in bytes of every tensor, computed in 64-bit with overflow checks.
+struct Sizes {
+    size_t q, v, g, beta, state, o;
+};
+
+// Multiply non-negative factors, failing on overflow past 2^62.
+bool mul_ok(size_t a, size_t b, size_t* out) {
+    if (a != 0 && b > (size_t(1) << 62) / a) return false;
+    *out = a * b;
+    return true;
+}
+
+bool tensor_sizes(const gdr_dims& d, size_t elt, Sizes* s) {
+    size_t bt, bth, btv, x;
+    if (!mul_ok((size_t)d.B, (size_t)d.T, &bt)) return false;
+    if (!mul_ok(bt, (size_t)d.HK, &bth) || !mul_ok(bt, (size_t)d.HV, &btv)) return false;
+    if (!mul_ok(bth, (size_t)d.dk, &x) || !mul_ok(x, elt, &s->q)) return false;
+    if (!mul_ok(btv, (size_t)d.dv, &x) || !mul_ok(x, elt, &s->v)) return false;
+    if (!mul_ok(btv, (size_t)d.dk, &x) || !mul_ok(x, 4, &s->g)) return false;
+    if (!mul_ok(btv, 4, &s->beta)) return false;
+    if (!mul_ok(btv, (size_t)d.dv, &x) || !mul_ok(x, 4, &s->o)) return false;
+    size_t bh;
+    if (!mul_ok((size_t)d.B, (size_t)d.HV, &bh) || !mul_ok(bh, (size_t)d.dk, &x) ||
+        !mul_ok(x, (size_t)d.dv, &x) || !mul_ok(x, 4, &s->state))
+        return false;
+    return true;
+}
+
+// Shared validation of dims, pointers, alignment and aliasing.
+int validate(const gdr_dims* d, bool decode, const void* q, const void* k, const void* v,
+             const float* g, const float* beta, const float* h0, const float* o,
+             const float* ht, Sizes* sizes) {
+    if (!d || !q || !k || !v || !g || !beta || !o) return GDR_ERR_NULL;
+    if (d->B < 1 || d->T < 1 || d->HK < 1 || d->HV < 1 || d->HV % d->HK != 0) return GDR_ERR_SHAPE;
+    if (decode && d->T != 1) return GDR_ERR_SHAPE;
+    if (!supported_head_dim(d->dk) || !supported_head_dim(d->dv)) return GDR_ERR_UNSUPPORTED;
+    if (d->qkv_dtype != GDR_BF16 && d->qkv_dtype != GDR_F32) return GDR_ERR_UNSUPPORTED;
+    if (!decode && d->chunk != 16 && d->chunk != 32 && d->chunk != 64) return GDR_ERR_UNSUPPORTED;
+    const size_t elt = d->qkv_dtype == GDR_F32 ? 4 : 2;
+    if (!tensor_sizes(*d, elt, sizes)) return GDR_ERR_SHAPE;
+    // Grid sizes must fit the launch limits: (B*HV) heads times chunks or column tiles.
+    const long long heads = (long long)d->B * d->HV;
+    const long long nchunk = decode ? 1 : (d->T + d->chunk - 1) / d->chunk;
+    if (heads * nchunk >= (1LL << 31) || heads * (d->dv / 16) >= (1LL << 31)) return GDR_ERR_SHAPE;
+
+    const void* ptrs[] = {q, k, v, g, beta, h0, o, ht};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDR_ERR_ALIGN;
+
+    const Range rq = range_of(q, sizes->q), rk = range_of(k, sizes->q), rv = range_of(v, sizes->v),
+                rg = range_of(g, sizes->g), rb = range_of(beta, sizes->beta),
+                rh0 = range_of(h0, sizes->state), ro = range_of(o, sizes->o),
+                rht = range_of(ht, sizes->state);
+    const Range inputs[] = {rq, rk, rv, rg, rb};
+    for (const Range& r : inputs) {
+        if (overlap(ro, r) || overlap(rht, r)) return GDR_ERR_ALIAS;
+    }
+    if (overlap(ro, rh0) || overlap(ro, rht)) return GDR_ERR_ALIAS;
+    if (overlap(rht, rh0) && rht.lo != rh0.lo) return GDR_ERR_ALIAS;
+    return GDR_OK;
+}
+
+gdr::LaunchArgs make_args(const gdr_dims* d, const void* q, const void* k, const void* v,
+                          const float* g, const float* beta, const float* h0, float* o, float* ht,
+                          void* workspace, void* stream) {
+    gdr::LaunchArgs a;
+    a.B = d->B;
+    a.T = d->T;
+    a.HK = d->HK;
+    a.HV = d->HV;
+    a.dk = d->dk;
+    a.dv = d->dv;
+    a.chunk = d->chunk;
+    a.qkv_f32 = d->qkv_dtype == GDR_F32;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.h0 = h0;
+    a.o = o;
+    a.ht = ht;
+    a.workspace = workspace;
+    a.stream = stream;
+    return a;
+}
+
+size_t workspace_bytes_unchecked(const gdr_dims* d) {
+    const gdr::ChunkRecord rec = gdr::ChunkRecord::make(d->chunk, d->dk);
+    const size_t nchunk = (size_t)((d->T + d->chunk - 1) / d->chunk);
+    size_t x;
+    if (!mul_ok((size_t)d->B * (size_t)d->HV, nchunk, &x) || !mul_ok(x, rec.bytes, &x)) return 0;
+    return x;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+const char* gdr_status_str(int status) {
+    switch (status) {
+        case GDR_OK: return "ok";
+        case GDR_ERR_NULL: return "a required pointer is NULL";
+        case GDR_ERR_SHAPE: return "invalid shape (B/T/HK/HV, HV % HK, decode T != 1, or size overflow)";
+        case GDR_ERR_UNSUPPORTED: return "unsupported head dim, chunk size or dtype";
+        case GDR_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case GDR_ERR_ALIAS: return "output buffers overlap inputs, or ht partially overlaps h0";
+        case GDR_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case GDR_ERR_HIP: return "HIP runtime error or kernel launch failure";
+        default: return "unknown status";
+    }
+}
+
+int gdr_decode_step(const gdr_dims* dims, const void* q, const void* k, const void* v,
+                    const float* g, const float* beta, const float* h0, float* o, float* ht,
+                    void* stream) {
+    Sizes s;
+    const int st = validate(dims, true, q, k, v, g, beta, h0, o, ht, &s);
+    if (st != GDR_OK) return st;
+    const gdr::LaunchArgs a = make_args(dims, q, k, v, g, beta, h0, o, ht, nullptr, stream);
+    return gdr::launch_decode(a) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+size_t gdr_chunk_prefill_workspace_bytes(const gdr_dims* dims) {
+    if (!dims || dims->B < 1 || dims->T < 1 || dims->HK < 1 || dims->HV < 1 ||
+        dims->HV % dims->HK != 0 || !supported_head_dim(dims->dk) ||
+        !supported_head_dim(dims->dv) ||
+        (dims->chunk != 16 && dims->chunk != 32 && dims->chunk != 64))
+        return 0;
+    return workspace_bytes_unchecked(dims);
+}
+
+static int prefill_stages(const gdr_dims* dims, const void* q, const void* k, const void* v,
+                          const float* g, const float* beta, const float* h0, float* o, float* ht,
+                          void* workspace, size_t workspace_bytes, void* stream, bool prep,
+                          bool carry) {
+    Sizes s;
+    const int st = validate(dims, false, q, k, v, g, beta, h0, o, ht, &s);
+    if (st != GDR_OK) return st;
+    const size_t need = workspace_bytes_unchecked(dims);
+    if (need == 0) return GDR_ERR_SHAPE;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
+        return GDR_ERR_WORKSPACE;
+    const Range rw = range_of(workspace, need);
+    const Range others[] = {range_of(q, s.q), range_of(k, s.q), range_of(v, s.v), range_of(g, s.g),
+                            range_of(beta, s.beta), range_of(h0, s.state), range_of(o, s.o),
+                            range_of(ht, s.state)};
+    for (const Range& r : others)
+        if (overlap(rw, r)) return GDR_ERR_ALIAS;
+    const gdr::LaunchArgs a = make_args(dims, q, k, v, g, beta, h0, o, ht, workspace, stream);
+    if (prep && gdr::launch_chunk_prep(a) != hipSuccess) return GDR_ERR_HIP;
+    if (carry && gdr::launch_chunk_carry(a) != hipSuccess) return GDR_ERR_HIP;
+    return GDR_OK;
+}
+
+int gdr_chunk_prefill(const gdr_dims* dims, const void* q, const void* k, const void* v,
+                      const float* g, const float* beta, const float* h0, float* o, float* ht,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_stages(dims, q, k, v, g, beta, h0, o, ht, workspace, workspace_bytes, stream,
+                          true, true);
+}
+
+int gdr_chunk_prep(const gdr_dims* dims, const void* q, const void* k, const void* v,
+                   const float* g, const float* beta, const float* h0, float* o, float* ht,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_stages(dims, q, k, v, g, beta, h0, o, ht, workspace, workspace_bytes, stream,
+                          true, false);
+}
+
+int gdr_chunk_carry(const gdr_dims* dims, const void* q, const void* k, const void* v,
+                    const float* g, const float* beta, const float* h0, float* o, float* ht,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_stages(dims, q, k, v, g, beta, h0, o, ht, workspace, workspace_bytes, stream,
+                          false, true);
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Internal interface between the host entry points (gdr_api.cpp) and the kernel launchers
+// (one .hip file per kernel family).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdr {
+
+struct LaunchArgs {
+    int B, T, HK, HV, dk, dv, chunk;
+    bool qkv_f32;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const float* h0;
+    float* o;
+    float* ht;
+    void* workspace;
+    void* stream;
+};
+
+// Per-(batch, head, chunk) record that the chunk-parallel kernel writes and the
+// sequential carry kernel reads: fp16 MFMA operand fragments (1 KiB each: 64 lanes x 8
+// halves) followed by the chunk's total decay exp(gamma_last) in fp32.
+struct ChunkRecord {
+    int nb;        // 16-row blocks per chunk (C / 16)
+    int nqs;       // 32-wide token reduction steps (ceil(C / 32))
+    int kc;        // 32-wide key-channel reduction steps (dk / 32)
+    int dkt;       // 16-row key-channel tiles (dk / 16)
+    int off_qt;    // fragment offsets (in fragments) of each operand
+    int off_w;
+    int off_kb;
+    int off_tb;
+    int off_p;
+    int nfrag;
+    size_t bytes;  // record stride, 256-byte aligned
+
+    __host__ __device__ static ChunkRecord make(int C, int dk) {
+        ChunkRecord r{};
+        r.nb = C / 16;
+        r.nqs = (C + 31) / 32;
+        r.kc = dk / 32;
+        r.dkt = dk / 16;
+        r.off_qt = 0;                          // decayed queries   [nb][kc]
+        r.off_w = r.off_qt + r.nb * r.kc;      // -W pseudo-keys    [nb][kc]
+        r.off_kb = r.off_w + r.nb * r.kc;      // K-bar transposed  [dkt][nqs]
+        r.off_tb = r.off_kb + r.dkt * r.nqs;   // T diag(beta)      [nb][nqs]
+        r.off_p = r.off_tb + r.nb * r.nqs;     // causal q.k terms  [nb][nqs]
+        r.nfrag = r.off_p + r.nb * r.nqs;
+        const size_t raw = (size_t)r.nfrag * 1024 + (size_t)dk * 4;
+        r.bytes = (raw + 255) / 256 * 256;
+        return r;
+    }
+};
+
+hipError_t launch_decode(const LaunchArgs& a);
+hipError_t launch_chunk_prep(const LaunchArgs& a);
+hipError_t launch_chunk_carry(const LaunchArgs& a);
+
+}  // namespace gdr

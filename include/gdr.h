@@ -1,0 +1,134 @@
+/*
+ * gdr.h -- C ABI of libgdr.so: the channelwise gated delta rule on AMD Instinct MI355X
+ * (gfx950), as hand-written HIP kernels.
+ *
+ * The operation.  For every batch b and value head h (key head kh = h / (HV/HK)) the
+ * library carries an fp32 state S[dk][dv] and, for every token t,
+ *     S   <- diag(exp(g_t)) S                              per-channel decay, g_t in R^dk
+ *     S   <- S + beta_t k_t (v_t - S^T k_t)^T              rank-one delta update
+ *     o_t  = S^T q_t                                       output from the updated state
+ * This is the recurrence whose decode step ExecuTorch PR #21021 ("Reorder channelwise
+ * gated delta rule chunked hot loops for autovectorization") restructures into two
+ * state traversals (first commit summary) and whose prefill it evaluates in chunkwise
+ * WY/UT form, routed by sequence length (second commit summary).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers to dense row-major arrays, 16-byte aligned:
+ *       q, k  [B][T][HK][dk]   (qkv_dtype)      v     [B][T][HV][dv]  (qkv_dtype)
+ *       g     [B][T][HV][dk]   fp32 log-decay   beta  [B][T][HV]      fp32
+ *       h0,ht [B][HV][dk][dv]  fp32 state       o     [B][T][HV][dv]  fp32
+ *     value head h reads key head h / (HV/HK) (contiguous GQA groups).
+ *   - h0 == NULL means a zero initial state; ht == NULL means the final state is not
+ *     written.  ht may equal h0 exactly (in-place carry) but must not partially overlap
+ *     it.  o must not overlap any input, h0 or ht.
+ *   - The caller owns every buffer.  The library never allocates or frees device memory
+ *     and keeps no per-call state.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *     returns without waiting; buffers must stay valid until the stream reaches it.
+ *   - Every argument check runs on the host before any HIP call: a call that returns an
+ *     error has enqueued nothing and written nothing.  Launch failures return
+ *     GDR_ERR_HIP.  The library never aborts or prints.  NaN/Inf inputs are not checked
+ *     and propagate.
+ *   - Supported: dk, dv in {32, 64, 128}; chunk in {16, 32, 64}; HV % HK == 0; B, T >= 1;
+ *     q/k/v in bf16 or fp32.  Decay values are expected to satisfy g <= 0 with the total
+ *     decay over any 8 consecutive tokens below 80 in every channel (exp(g) >= ~5e-5 per
+ *     token); outside that range the prefill path's intra-chunk decay factors can
+ *     overflow fp32.  The decode path has no such limit.
+ *   - Results are bitwise reproducible for identical inputs and dims (no atomics).
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDR_ABI_VERSION 1
+
+typedef enum {
+    GDR_OK = 0,
+    GDR_ERR_NULL = 1,        /* a required pointer (dims, q, k, v, g, beta, o) is NULL     */
+    GDR_ERR_SHAPE = 2,       /* B/T/HK/HV < 1, HV % HK != 0, decode with T != 1, overflow */
+    GDR_ERR_UNSUPPORTED = 3, /* dk/dv/chunk/dtype outside the supported set               */
+    GDR_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned                   */
+    GDR_ERR_ALIAS = 5,       /* o overlaps an input/h0/ht, or ht partially overlaps h0    */
+    GDR_ERR_WORKSPACE = 6,   /* workspace NULL, misaligned or smaller than required       */
+    GDR_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed                 */
+} gdr_status;
+
+typedef enum { GDR_BF16 = 0, GDR_F32 = 1 } gdr_dtype;
+
+typedef struct {
+    int32_t B, T, HK, HV, dk, dv;
+    int32_t chunk;      /* prefill chunk length C (ignored by the decode step)             */
+    int32_t qkv_dtype;  /* gdr_dtype of q, k and v                                         */
+} gdr_dims;
+
+/*
+ * One autoregressive decode step (T must be 1): the two-pass token recurrence of
+ * ExecuTorch PR #21021, first commit summary -- pass 1 forms the prediction S^T k with
+ * the decay folded in, pass 2 applies decay and the rank-one update and accumulates the
+ * output.  On the GPU each state element is read from HBM once and written once.
+ * Normally called in place (ht == h0).  Uses no workspace.
+ */
+int gdr_decode_step(const gdr_dims* dims, const void* q, const void* k, const void* v,
+                    const float* g, const float* beta, const float* h0, float* o, float* ht,
+                    void* stream);
+
+/*
+ * Bytes of device workspace gdr_chunk_prefill needs for these dims (0 if dims are
+ * invalid).  The workspace holds per-chunk operands that the chunk-parallel kernel hands
+ * to the sequential state-carry kernel -- the per-worker scratch arena of ExecuTorch PR
+ * #21021 (second commit summary), carved per (batch, head, chunk).
+ */
+size_t gdr_chunk_prefill_workspace_bytes(const gdr_dims* dims);
+
+/*
+ * Chunkwise WY/UT prefill for any T >= 1 (ExecuTorch PR #21021, second commit summary):
+ * per-channel log-decay prefixes, the beta-folded strictly-lower gram A, an exact
+ * 16x16-block forward-substitution solve of (I + A), WY pseudo-keys and pseudo-values,
+ * causal intra-chunk query/key terms, and the inter-chunk state carry; the ragged last
+ * chunk is handled by the same code (zero-padded rows).  The block solve follows the
+ * exact block forward substitution of uzu PR #576 ("Support TreeUpdateSolve kernel").
+ * `workspace` must be a 256-byte-aligned device buffer of at least
+ * gdr_chunk_prefill_workspace_bytes(dims) bytes; its contents on entry are ignored.
+ */
+int gdr_chunk_prefill(const gdr_dims* dims, const void* q, const void* k, const void* v,
+                      const float* g, const float* beta, const float* h0, float* o, float* ht,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two stages of gdr_chunk_prefill as separate calls, with the same arguments and
+ * checks.  gdr_chunk_prefill(...) is exactly gdr_chunk_prep(...) followed by
+ * gdr_chunk_carry(...) on the same stream and workspace.
+ *   gdr_chunk_prep  -- chunk-parallel stage (one workgroup per batch, value head, chunk):
+ *                      decay prefixes, gram A and causal terms P on the matrix cores, the
+ *                      16x16-block solve of (I + A), WY pseudo-keys; writes the workspace.
+ *                      Reads q, k, g, beta; never touches v, h0, o or ht.
+ *   gdr_chunk_carry -- sequential stage (chunks in order, value dimension split across
+ *                      workgroups): pseudo-values, outputs and the state carry.  Reads
+ *                      the workspace written by gdr_chunk_prep for the same inputs, v
+ *                      and h0; writes o and ht.
+ * Splitting them lets a caller time or overlap the stages.
+ */
+int gdr_chunk_prep(const gdr_dims* dims, const void* q, const void* k, const void* v,
+                   const float* g, const float* beta, const float* h0, float* o, float* ht,
+                   void* workspace, size_t workspace_bytes, void* stream);
+int gdr_chunk_carry(const gdr_dims* dims, const void* q, const void* k, const void* v,
+                    const float* g, const float* beta, const float* h0, float* o, float* ht,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static English text for a status code (never NULL). */
+const char* gdr_status_str(int status);
+
+/* GDR_ABI_VERSION of the loaded library. */
+int gdr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

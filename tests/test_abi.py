@@ -1,0 +1,171 @@
+"""The C ABI of libgdr.so on the host: it loads, exports every declared symbol, sizes the
+workspace, and rejects bad arguments before touching any GPU.
+
+No test here launches a kernel.  Fake device addresses are used only on paths whose
+validation fails on the host (the library runs every check before its first HIP call).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_70_amd as gdr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EALIAS, EWS, EHIP = range(8)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gdr.LIB_PATH):
+        from gated_delta_rule_70_amd import build
+
+        build.build(verbose=False)
+    return gdr.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(gdr_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "gdr_abi_version", "gdr_chunk_carry", "gdr_chunk_prefill", "gdr_chunk_prefill_workspace_bytes",
+        "gdr_chunk_prep", "gdr_decode_step", "gdr_status_str"])
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", gdr.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_version_and_status_strings(L):
+    assert L.gdr_abi_version() == gdr.ABI_VERSION
+    texts = {L.gdr_status_str(s).decode() for s in range(8)}
+    assert len(texts) == 8
+    assert L.gdr_status_str(99).decode() == "unknown status"
+
+
+# fake, well-separated, 256-byte-aligned device addresses (never dereferenced)
+BASE = 1 << 40
+SLOT = 1 << 32
+
+
+def addr(i, off=0):
+    return ctypes.c_void_p(BASE + i * SLOT + off)
+
+
+def dims(**kw):
+    d = dict(B=2, T=5, HK=2, HV=4, dk=64, dv=32, chunk=16, qkv_dtype=0)
+    d.update(kw)
+    return gdr.Dims(**d)
+
+
+def prefill(L, d, ws_bytes=None, entry="gdr_chunk_prefill", **ptrs):
+    p = {n: addr(i) for i, n in enumerate(["q", "k", "v", "g", "beta", "h0", "o", "ht", "ws"])}
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = L.gdr_chunk_prefill_workspace_bytes(ctypes.byref(d)) if d is not None else 0
+    return getattr(L, entry)(None if d is None else ctypes.byref(d), p["q"], p["k"], p["v"], p["g"],
+                               p["beta"], p["h0"], p["o"], p["ht"], p["ws"], ctypes.c_size_t(ws_bytes),
+                               None)
+
+
+def decode(L, d, **ptrs):
+    p = {n: addr(i) for i, n in enumerate(["q", "k", "v", "g", "beta", "h0", "o", "ht"])}
+    p.update(ptrs)
+    return L.gdr_decode_step(None if d is None else ctypes.byref(d), p["q"], p["k"], p["v"], p["g"],
+                             p["beta"], p["h0"], p["o"], p["ht"], None)
+
+
+def test_null_arguments(L):
+    assert prefill(L, None) == ENULL
+    assert decode(L, None) == ENULL
+    for name in ("q", "k", "v", "g", "beta", "o"):
+        assert prefill(L, dims(), **{name: None}) == ENULL, name
+        assert decode(L, dims(T=1), **{name: None}) == ENULL, name
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(T=0), dict(HK=0), dict(HV=0), dict(HK=3, HV=4),
+                                dict(B=-1), dict(T=1 << 30, B=1 << 10)])
+def test_bad_shapes(L, kw):
+    assert prefill(L, dims(**kw)) == ESHAPE
+
+
+def test_decode_requires_one_token(L):
+    assert decode(L, dims(T=2)) == ESHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(dk=48), dict(dv=256), dict(dk=16), dict(chunk=8),
+                                dict(chunk=128), dict(qkv_dtype=2)])
+def test_unsupported(L, kw):
+    assert prefill(L, dims(**kw)) == EUNSUP
+
+
+def test_misaligned_pointers(L):
+    for name in ("q", "k", "v", "g", "beta", "h0", "o", "ht"):
+        assert prefill(L, dims(), **{name: addr(9, 4)}) == EALIGN, name
+
+
+def test_aliasing(L):
+    d = dims()
+    assert prefill(L, d, o=addr(0, 256)) == EALIAS           # o inside q
+    assert prefill(L, d, ht=addr(3, 0)) == EALIAS            # ht over g
+    assert prefill(L, d, ht=addr(5, 256)) == EALIAS          # ht partially over h0
+    assert prefill(L, d, o=addr(7, 0)) == EALIAS             # o over ht
+    assert prefill(L, d, ws=addr(6, 0)) == EALIAS            # workspace over o
+
+
+@pytest.mark.parametrize("entry", ["gdr_chunk_prep", "gdr_chunk_carry"])
+def test_stage_entries_validate_like_prefill(L, entry):
+    assert prefill(L, None, entry=entry) == ENULL
+    assert prefill(L, dims(B=0), entry=entry) == ESHAPE
+    assert prefill(L, dims(dk=48), entry=entry) == EUNSUP
+    assert prefill(L, dims(), entry=entry, q=addr(0, 8)) == EALIGN
+    assert prefill(L, dims(), entry=entry, o=addr(0, 256)) == EALIAS
+    assert prefill(L, dims(), entry=entry, ws_bytes=1) == EWS
+
+
+def test_workspace_checks(L):
+    d = dims()
+    need = L.gdr_chunk_prefill_workspace_bytes(ctypes.byref(d))
+    assert need > 0 and need % 256 == 0
+    assert prefill(L, d, ws_bytes=need - 1) == EWS
+    assert prefill(L, d, ws=None) == EWS
+    assert prefill(L, d, ws=addr(8, 16)) == EWS
+
+
+def test_workspace_size_formula(L):
+    # one record per (batch, value head, chunk): fp16 operand fragments of 1 KiB each and
+    # dk fp32 decay totals, rounded up to 256 bytes
+    for (dk, C) in [(32, 16), (64, 32), (128, 64), (128, 16)]:
+        d = dims(dk=dk, chunk=C, T=100)
+        nb, nqs, kc, dkt = C // 16, (C + 31) // 32, dk // 32, dk // 16
+        nfrag = 2 * nb * kc + dkt * nqs + 2 * nb * nqs
+        rec = -(-(nfrag * 1024 + 4 * dk) // 256) * 256
+        nchunk = -(-100 // C)
+        assert L.gdr_chunk_prefill_workspace_bytes(ctypes.byref(d)) == 2 * 4 * nchunk * rec
+    assert L.gdr_chunk_prefill_workspace_bytes(ctypes.byref(dims(dk=48))) == 0
+    assert L.gdr_chunk_prefill_workspace_bytes(None) == 0
+
+
+def _gpu_visible():
+    import torch
+
+    return torch.cuda.device_count() > 0
+
+
+@pytest.mark.skipif("_gpu_visible()", reason="valid fake pointers would reach a real GPU")
+def test_valid_arguments_reach_the_runtime_without_a_gpu(L):
+    # with no GPU, a call that passes validation fails at the first HIP call, cleanly
+    assert prefill(L, dims(), ht=addr(5, 0)) == EHIP        # in-place ht == h0 is allowed
+    assert decode(L, dims(T=1), ht=addr(5, 0)) == EHIP

@@ -1,0 +1,160 @@
+"""Chunked prefill on the GPU against the fp64 oracle: small shapes that span several
+16-row blocks and chunks with ragged tails, the five measured workloads (sampled head
+groups at full size), and the structural invariants of the method."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_70_amd as gdr
+import oracle
+from gdr_synth import PREFILL_1x4097, PREFILL_1x32768, PREFILL_8x97, PREFILL_8x512, TINY, workload_inputs
+from gpu_util import TOL, bf16_exact_unit_keys, dev, err, note, oracle_on_groups, sampled_groups, small_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(d, chunk, h0=True, **kw):
+    return gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                             h0=d["h0"] if h0 else None, chunk=chunk, **kw)
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("T", [1, 15, 17, 33, 64, 97, 130])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_prefill_small_128(C, T, dtype):
+    x = small_inputs(2, T, 2, 4, 128, 128, dtype=dtype, seed=T + C)
+    o_ref, ht_ref = oracle.sequential(**x)
+    note(f"prefill dk=dv=128 C={C} T={T} {dtype}")
+    o, ht = run_prefill(dev(x), C)
+    torch.cuda.synchronize()
+    eo, es = err(o, o_ref), err(ht, ht_ref)
+    assert eo < TOL and es < TOL, f"o {eo:.2e} state {es:.2e}"
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 32), (32, 128), (64, 64), (64, 32), (128, 32), (128, 64)])
+@pytest.mark.parametrize("C", [16, 64])
+@pytest.mark.parametrize("G", [1, 2])
+@pytest.mark.parametrize("h0", [True, False])
+def test_prefill_head_dims(dk, dv, C, G, h0):
+    x = small_inputs(2, 77, 2, 2 * G, dk, dv, seed=dk * 3 + dv + C + G, h0=h0)
+    o_ref, ht_ref = oracle.sequential(**x)
+    note(f"prefill dk={dk} dv={dv} C={C} G={G} h0={h0}")
+    o, ht = run_prefill(dev(x), C, h0=h0)
+    torch.cuda.synchronize()
+    eo, es = err(o, o_ref), err(ht, ht_ref)
+    assert eo < TOL and es < TOL, f"o {eo:.2e} state {es:.2e}"
+
+
+def test_tiny_workload_full():
+    """Tiny prefill, all fp32: B=1, HK=1, HV=2, T=64, dk=dv=32, chunk 16, h0 = 0."""
+    w = TINY
+    x = workload_inputs(w)
+    o_ref, ht_ref = oracle.sequential(**x)
+    note("tiny workload")
+    o, ht = run_prefill(dev(x), w.chunk, h0=False)
+    torch.cuda.synchronize()
+    assert err(o, o_ref) < TOL and err(ht, ht_ref) < TOL
+
+
+@pytest.mark.parametrize("w", [PREFILL_1x4097, PREFILL_8x512, PREFILL_8x97, PREFILL_1x32768],
+                         ids=lambda w: w.name)
+def test_measured_workloads_sampled(w):
+    """Full-size runs in the benchmark's launch configuration; sampled (batch, key-head)
+    groups are compared with the oracle on every output and on the final state."""
+    x = workload_inputs(w)
+    d = dev(x)
+    note(f"workload {w.name}")
+    o, ht = run_prefill(d, w.chunk, h0=w.h0)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(ht).all()
+    G = w.HV // w.HK
+    n = 2 if w.T > 10000 else 4
+    groups = sampled_groups(w.B, w.HK, n, seed=w.seed)
+    ref = oracle_on_groups(x, groups, G)
+    oc, hc = o.cpu(), ht.cpu()
+    for (b, kh), (o_r, ht_r) in ref.items():
+        hv = slice(kh * G, (kh + 1) * G)
+        eo, es = err(oc[b, :, hv], o_r), err(hc[b, hv], ht_r)
+        print(f"{w.name} group {(b, kh)}: o {eo:.2e} state {es:.2e}")
+        assert eo < TOL and es < TOL, f"group {(b, kh)}: o {eo:.2e} state {es:.2e}"
+
+
+def test_split_sequence_carry():
+    x = small_inputs(2, 200, 2, 4, 128, 128, seed=21)
+    d = dev(x)
+    note("split sequence")
+    o, ht = run_prefill(d, 64)
+    first = {n: (t[:, :83].contiguous() if n != "h0" else t) for n, t in d.items()}
+    o1, ht1 = run_prefill(first, 64)
+    second = {n: (t[:, 83:].contiguous() if n != "h0" else ht1) for n, t in d.items()}
+    o2, ht2 = run_prefill(second, 64)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = oracle.sequential(**x)
+    assert err(torch.cat([o1, o2], 1), o_ref) < TOL and err(ht2, ht_ref) < TOL
+    assert err(o, o_ref) < TOL and err(ht, ht_ref) < TOL
+
+
+def test_prefill_then_decode_matches_concatenation():
+    x = small_inputs(2, 70, 2, 4, 128, 128, seed=23)
+    d = dev(x)
+    note("prefill + decode")
+    pre = {n: (t[:, :66].contiguous() if n != "h0" else t) for n, t in d.items()}
+    o_p, state = run_prefill(pre, 64)
+    outs = [o_p]
+    for t in range(66, 70):
+        outs.append(gdr.decode_step(*(d[n][:, t:t + 1].contiguous() for n in ("q", "k", "v", "g", "beta")),
+                                    state))
+    torch.cuda.synchronize()
+    o_ref, ht_ref = oracle.sequential(**x)
+    assert err(torch.cat(outs, 1), o_ref) < TOL and err(state, ht_ref) < TOL
+
+
+def test_in_place_state_and_canaries():
+    x = small_inputs(2, 97, 2, 4, 128, 128, seed=25)
+    d = dev(x)
+    o_ref, ht_ref = oracle.sequential(**x)
+    need = gdr.workspace_bytes(2, 97, 2, 4, 128, 128, chunk=64)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda").fill_(0xFF)   # NaN-pattern halves
+    o = torch.full((2, 97, 4, 128), float("nan"), device="cuda")
+    state = d["h0"].clone()
+    note("in-place state + canaries")
+    gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=state, ht=state, o=o,
+                      workspace=ws, chunk=64)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    assert err(o, o_ref) < TOL and err(state, ht_ref) < TOL
+
+
+def test_prefill_deterministic():
+    x = small_inputs(2, 150, 2, 4, 128, 128, seed=27)
+    d = dev(x)
+    note("prefill determinism")
+    o1, h1 = run_prefill(d, 64)
+    o2, h2 = run_prefill(d, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+def test_prefill_exact_write_real_shape():
+    # beta = 1, unit keys exact in bf16/fp16, q = k: every output equals its v exactly in
+    # exact arithmetic, whatever the decay and initial state
+    B, T, HK, HV = 1, 130, 2, 4
+    x = small_inputs(B, T, HK, HV, 128, 128, seed=29)
+    k = bf16_exact_unit_keys(B, T, HK, 128, seed=4).to(torch.bfloat16)
+    x["k"], x["q"] = k, k.clone()
+    x["beta"] = torch.ones_like(x["beta"])
+    note("prefill exact write")
+    o, _ = run_prefill(dev(x), 64)
+    torch.cuda.synchronize()
+    assert err(o, x["v"].double().numpy()) < TOL
+
+
+def test_chunk_size_invariance():
+    x = small_inputs(1, 160, 2, 4, 64, 64, seed=31)
+    d = dev(x)
+    note("chunk size invariance")
+    res = [run_prefill(d, C) for C in (16, 32, 64)]
+    torch.cuda.synchronize()
+    o_ref, ht_ref = oracle.sequential(**x)
+    for o, ht in res:
+        assert err(o, o_ref) < TOL and err(ht, ht_ref) < TOL
