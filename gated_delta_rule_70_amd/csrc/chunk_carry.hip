@@ -9,186 +9,338 @@
 // (ExecuTorch PR #21021 "Reorder channelwise gated delta rule chunked hot loops for
 // autovectorization", second commit summary: WY pseudo-keys/values and inter-chunk state
 // carry).  Columns of S evolve independently, so the value dimension is split across
-// workgroups: one 64-lane wave owns NT 16-column tiles of one (batch, value head) and
-// walks its chunks in order with the S tile resident in MFMA accumulators the whole time.
+// workgroups: a workgroup owns NT 16-column tiles of one (batch, value head) and walks
+// the chunks in order.
 //
-// Every product is a 16x16x32 fp16 MFMA with fp32 accumulation.  The accumulator tiles of
-// S and U feed the B operand of the next product directly (the reduction slots follow
-// perm_slot, which matches the rows an accumulator lane holds), so the carry needs no LDS
-// and no cross-lane shuffles; the A operands arrive pre-permuted from the workspace.
+// Inside a workgroup the chunk's rows are split across NW = C/16 waves: wave w computes
+// row tile w of U and O and owns the state row tiles ct = w, w + NW, ...  Per chunk the
+// waves exchange two small fp16 operand sets through LDS (the state's B fragments, then
+// U's), one barrier each, so the chain U -> S' that bounds the recurrence runs on all
+// SIMDs of a CU and each wave loads only the share of the chunk's operands it uses.
+// Every product is a 16x16x32 fp16 MFMA with fp32 accumulation; accumulator tiles map
+// to B fragments without shuffles (reduction slots follow perm_slot).
 //
-// Launch: blocks = (B*HV) x (dv / (16*NT)), block index = colgroup * (B*HV) + head, so all
-// column groups of a head share the same XCD (blocks are dealt round-robin to the 8 XCDs)
-// and read the head's chunk operands from one L2.
+// Memory pipeline: each wave keeps its operand fragments and the raw v rows in two
+// register sets and refills a set with the operands of the chunk two ahead right after
+// their last use (buffer loads, fragment index in an SGPR), so every load has two chunks
+// of work to land; outputs are stored one chunk late.
+//
+// Launch: blocks = (B*HV) x (dv / (16*NT)), block index = colgroup * (B*HV) + head, so
+// all column groups of a head share one XCD (blocks are dealt round-robin to the 8 XCDs)
+// and read the head's records through one L2.
 #include "gdr_device.h"
 #include "gdr_launch.h"
 
 namespace gdr {
 
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ half4 to_half4(f32x4 x) {
+    return half4{static_cast<_Float16>(x[0]), static_cast<_Float16>(x[1]), static_cast<_Float16>(x[2]),
+                 static_cast<_Float16>(x[3])};
+}
+
 template <typename TIn, int DK, int DV, int C, int NT>
-__global__ __launch_bounds__(64) void chunk_carry_kernel(const TIn* __restrict__ v,
-                                                         const float* h0, float* __restrict__ o,
-                                                         float* ht,
-                                                         const unsigned char* __restrict__ ws,
-                                                         int B, int T, int HV, int NC) {
+__global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
+    const TIn* __restrict__ v, const float* h0, float* __restrict__ o, float* ht,
+    const unsigned char* __restrict__ ws, int B, int T, int HV, int NC) {
     constexpr int NB = C / 16;
+    constexpr int NW = NB;                    // one wave per 16-row tile of the chunk
     constexpr int NQS = (C + 31) / 32;
     constexpr int KC = DK / 32;
     constexpr int DKT = DK / 16;
+    constexpr int OWN = (DKT + NW - 1) / NW;  // state row tiles per wave (at most)
+    constexpr ChunkRecord R = ChunkRecord::make(C, DK);
+    constexpr int ELT = sizeof(TIn);
 
-    const ChunkRecord R = ChunkRecord::make(C, DK);
+    // exchange buffers, lane-major: state B fragments [KC][NT], U B fragments [NQS][NT]
+    __shared__ half8 sSB[KC * NT * 64];
+    __shared__ half8 sUB[NQS * NT * 64];
+    __shared__ __attribute__((aligned(16))) _Float16 sV[NT * 16 * C];  // v tile, [nt][col][row]
+
     const int NH = B * HV;
     const int blk = blockIdx.x;
     const int bh = blk % NH;
     const int cg = blk / NH;
     const int h = bh % HV;
     const int b = bh / HV;
-    const int lane = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // row tile of this wave
+    const int lane = threadIdx.x & 63;
     const int li = lane & 15;
     const int gq = lane >> 4;
+    const int nq_w = w / 2 + 1;  // token steps that row tile w's lower-triangular rows touch
 
     int jcol[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) jcol[nt] = 16 * (cg * NT + nt) + li;
 
-    // state tile in accumulator layout: S[ct][nt][i] = S[16ct + 4gq + i][jcol[nt]]
-    f32x4 S[DKT][NT];
+    // owned state tiles in accumulator layout: S[j][nt][i] = S[16 ct_j + 4gq + i][jcol[nt]]
+    f32x4 S[OWN][NT];
     const size_t sb = (size_t)bh * DK * DV;
 #pragma unroll
-    for (int ct = 0; ct < DKT; ++ct)
+    for (int j = 0; j < OWN; ++j) {
+        const int ct = w + NW * j;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (h0 != nullptr && ct < DKT) {  // uniform
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = h0[sb + (size_t)(16 * ct + 4 * gq + i) * DV + jcol[nt]];
+            }
+            S[j][nt] = x;
+        }
+    }
+
+    // Buffer resources: this head's records, and this batch element's v and o rows (the
+    // host guarantees each fits a 31-bit byte offset).  Wave-uniform offsets (fragment
+    // index, row within a chunk) go to SGPRs; one per-lane offset is built per chunk.
+    const unsigned char* rec0 = ws + (size_t)bh * NC * R.bytes;
+    const int rowv = HV * DV * ELT;  // bytes between consecutive tokens of v
+    const int rowo = HV * DV * 4;    // ... of o
+    const rsrc_t rs_rec = make_rsrc(rec0, (uint32_t)NC * R.bytes);
+    const rsrc_t rs_v = make_rsrc(v + (size_t)b * T * HV * DV, (uint32_t)T * rowv);
+    const rsrc_t rs_o = make_rsrc(o + (size_t)b * T * HV * DV, (uint32_t)T * rowo);
+
+    // v rows of a chunk.  Wave w loads rows 16w .. 16w+15 of its workgroup's 16*NT columns
+    // with one vector load per 16-column tile (lane l: row l/4, four columns 4(l%4)..),
+    // keeping the raw bits in registers until the chunk starts; rows past T sit beyond the
+    // buffer's range (the row is part of the per-lane offset) and read as zero.  At the
+    // start of the chunk the rows go to a column-major fp16 tile in LDS, from which every
+    // wave reads the B fragments of Tb V (reduction slots follow perm_slot).
+    typedef uint32_t VRaw[NT][ELT];  // 4 elements of one row per lane and column tile
+    auto load_v = [&](int n, VRaw& V) {
+        const int row = n * C + 16 * w + (lane >> 2);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int off = (row * HV + h) * DV * ELT + (16 * (cg * NT + nt) + 4 * (lane & 3)) * ELT;
+            if constexpr (ELT == 2) {
+                const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs_v, off, 0, 0);
+                V[nt][0] = x[0];
+                V[nt][1] = x[1];
+            } else {
+                const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs_v, off, 0, 0);
+                V[nt][0] = x[0];
+                V[nt][1] = x[1];
+                V[nt][2] = x[2];
+                V[nt][3] = x[3];
+            }
+        }
+    };
+    auto publish_v = [&](const VRaw& V) {  // -> sV[nt][col][row], fp16
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[ct][nt][i] = h0 ? h0[sb + (size_t)(16 * ct + 4 * gq + i) * DV + jcol[nt]] : 0.f;
-
-    for (int n = 0; n < NC; ++n) {
-        const unsigned char* rec = ws + (size_t)((size_t)bh * NC + n) * R.bytes;
-        const half8* fr = reinterpret_cast<const half8*>(rec) + lane;
-        const float* egl = reinterpret_cast<const float*>(rec + (size_t)R.nfrag * 1024);
+            for (int e = 0; e < 4; ++e) {
+                float x;
+                if constexpr (ELT == 2) x = __uint_as_float((e & 1) ? (V[nt][e >> 1] & 0xFFFF0000u) : (V[nt][e >> 1] << 16));
+                else x = __uint_as_float(V[nt][e]);
+                sV[(nt * 16 + 4 * (lane & 3) + e) * C + 16 * w + (lane >> 2)] = static_cast<_Float16>(x);
+            }
+    };
+    auto read_v = [&](half8 (&V)[NQS][NT]) {
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs)
+            if (qs < nq_w) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const _Float16* col = &sV[(nt * 16 + li) * C + 32 * qs + 4 * gq];
+                    const half4 lo = *reinterpret_cast<const half4*>(col);
+                    half4 hi = {static_cast<_Float16>(0.f), static_cast<_Float16>(0.f),
+                                static_cast<_Float16>(0.f), static_cast<_Float16>(0.f)};
+                    if (32 * qs + 16 < C) hi = *reinterpret_cast<const half4*>(col + 16);  // compile-time
+                    V[qs][nt] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+            }
+    };
+    // outputs of row tile w of chunk n
+    auto store_o = [&](int n, const f32x4 (&O)[NT]) {
         const int t0 = n * C;
+        const int obase = ((t0 + 16 * w + 4 * gq) * HV + h) * DV * 4;
+        if (t0 + C <= T) {  // uniform: the whole chunk exists
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) buf_store_f32(O[nt][i], rs_o, obase + jcol[nt] * 4, i * rowo);
+        } else {  // ragged last chunk: rows past T fall outside the buffer and are dropped
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) buf_store_f32(O[nt][i], rs_o, obase + jcol[nt] * 4 + i * rowo, 0);
+        }
+    };
 
-        // B operands from the state accumulators
+    // This wave's operand fragments, in registers, double-buffered across chunks: the set
+    // used by chunk n is refilled with chunk n+2's fragments right after each one's last
+    // use, so every load has two chunks of work to land (the empty asm keeps a load where
+    // it is written; the compiler would otherwise sink it to its next use and stall).  The
+    // chunk loop is unrolled by two so each set has fixed registers.
+    struct Frags {
+        half8 tb[NQS], w[KC], q[KC], p[NQS], kb[OWN][NQS];
+        f32x4 e[OWN];
+        uint32_t v[NT][ELT];     // raw bits of this wave's v rows of the chunk
+    };
+    auto ld = [&](half8& dst, int vrec, int f) {
+        dst = buf_load_half8(rs_rec, vrec, f * 1024);
+        asm volatile("" ::: "memory");
+    };
+    auto ld_egl = [&](int vrec, int ct) {  // exp(gam_last) for rows 16ct + 4gq .. +3
+        return buf_load_f32x4(rs_rec, vrec - lane * 16 + gq * 16, R.nfrag * 1024 + ct * 64);
+    };
+    auto load_all = [&](Frags& F, int n) {
+        const int vrec = n * R.bytes + lane * 16;
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs)
+            if (qs < nq_w) {
+                ld(F.tb[qs], vrec, R.off_tb + ChunkRecord::tri_base(w) + qs);
+                ld(F.p[qs], vrec, R.off_p + ChunkRecord::tri_base(w) + qs);
+            }
+#pragma unroll
+        for (int p = 0; p < KC; ++p) {
+            ld(F.w[p], vrec, R.off_w + w * KC + p);
+            ld(F.q[p], vrec, R.off_qt + w * KC + p);
+        }
+#pragma unroll
+        for (int j = 0; j < OWN; ++j) {
+            const int ct = w + NW * j;
+            if (ct < DKT) {
+#pragma unroll
+                for (int qs = 0; qs < NQS; ++qs) ld(F.kb[j][qs], vrec, R.off_kb + ct * NQS + qs);
+                F.e[j] = ld_egl(vrec, ct);
+            }
+        }
+        load_v(n, F.v);
+    };
+
+    f32x4 Op[NT];
+    // One chunk: consume set F (chunk n) and refill it with chunk nn's operands.
+    auto step = [&](Frags& F, int n, int nn) {
+        const int vrec = nn * R.bytes + lane * 16;
+        publish_v(F.v);
+        load_v(nn, F.v);
+
+        // 1. publish this wave's state tiles as halves of the state B fragments
+#pragma unroll
+        for (int j = 0; j < OWN; ++j) {
+            const int ct = w + NW * j;
+            if (ct < DKT) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    *(reinterpret_cast<half4*>(&sSB[((ct >> 1) * NT + nt) * 64 + lane]) + (ct & 1)) =
+                        to_half4(S[j][nt]);
+            }
+        }
+        lds_barrier();
         half8 SB[KC][NT];
 #pragma unroll
         for (int p = 0; p < KC; ++p)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj)
-                    SB[p][nt][jj] = static_cast<_Float16>(S[2 * p + (jj >> 2)][nt][jj & 3]);
+            for (int nt = 0; nt < NT; ++nt) SB[p][nt] = sSB[(p * NT + nt) * 64 + lane];
+        half8 Vc[NQS][NT];
+        read_v(Vc);
 
-        // B operands from the chunk's values (rows past T are zero)
-        half8 VB[NQS][NT];
+        if (n > 0) store_o(n - 1, Op);
+
+        // 2. U_w = Tb V - W S for row tile w
+        f32x4 U[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) U[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int qs = 0; qs < NQS; ++qs)
+            if (qs < nq_w) {
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const int r = 32 * qs + perm_slot(gq, jj);
-                const int t = t0 + r;
-                const bool live = r < C && t < T;
-                const size_t vrow = (((size_t)b * T + (live ? t : 0)) * HV + h) * DV;
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    VB[qs][nt][jj] = live ? static_cast<_Float16>(to_f32(v[vrow + jcol[nt]]))
-                                          : static_cast<_Float16>(0.f);
-            }
-
-        // U = Tb V - W S
-        f32x4 U[NB][NT];
-#pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) U[rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int qs = 0; qs < NQS; ++qs) {
-                if (2 * qs > rt) break;
-                const half8 a = fr[(size_t)(R.off_tb + rt * NQS + qs) * 64];
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) U[rt][nt] = mfma_f16(a, VB[qs][nt], U[rt][nt]);
+                for (int nt = 0; nt < NT; ++nt) U[nt] = mfma_f16(F.tb[qs], Vc[qs][nt], U[nt]);
+                ld(F.tb[qs], vrec, R.off_tb + ChunkRecord::tri_base(w) + qs);
             }
 #pragma unroll
-            for (int p = 0; p < KC; ++p) {
-                const half8 a = fr[(size_t)(R.off_w + rt * KC + p) * 64];
+        for (int p = 0; p < KC; ++p) {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) U[rt][nt] = mfma_f16(a, SB[p][nt], U[rt][nt]);
-            }
+            for (int nt = 0; nt < NT; ++nt) U[nt] = mfma_f16(F.w[p], SB[p][nt], U[nt]);
+            ld(F.w[p], vrec, R.off_w + w * KC + p);
         }
-
-        // O = Qt S  (+ P U below)
-        f32x4 O[NB][NT];
+        // 3. publish U_w as half of a U B fragment
 #pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
+        for (int nt = 0; nt < NT; ++nt)
+            *(reinterpret_cast<half4*>(&sUB[((w >> 1) * NT + nt) * 64 + lane]) + (w & 1)) = to_half4(U[nt]);
+        // 4. O_w = Qt S (independent of U; overlaps the exchange)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) O[rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < NT; ++nt) Op[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int p = 0; p < KC; ++p) {
-                const half8 a = fr[(size_t)(R.off_qt + rt * KC + p) * 64];
+        for (int p = 0; p < KC; ++p) {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) O[rt][nt] = mfma_f16(a, SB[p][nt], O[rt][nt]);
-            }
+            for (int nt = 0; nt < NT; ++nt) Op[nt] = mfma_f16(F.q[p], SB[p][nt], Op[nt]);
+            ld(F.q[p], vrec, R.off_qt + w * KC + p);
         }
-
-        // B operands from the U accumulators
+        lds_barrier();
         half8 UB[NQS][NT];
 #pragma unroll
         for (int qs = 0; qs < NQS; ++qs)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
+            for (int nt = 0; nt < NT; ++nt) {
+                half8 x = sUB[(qs * NT + nt) * 64 + lane];
+                if (2 * qs + 1 >= NB) {  // compile-time: this step has no second row tile
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int rt = 2 * qs + (jj >> 2);
-                    UB[qs][nt][jj] = rt < NB ? static_cast<_Float16>(U[rt < NB ? rt : 0][nt][jj & 3])
-                                             : static_cast<_Float16>(0.f);
+                    for (int jj = 4; jj < 8; ++jj) x[jj] = static_cast<_Float16>(0.f);
                 }
-
-#pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
-#pragma unroll
-            for (int qs = 0; qs < NQS; ++qs) {
-                if (2 * qs > rt) break;
-                const half8 a = fr[(size_t)(R.off_p + rt * NQS + qs) * 64];
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) O[rt][nt] = mfma_f16(a, UB[qs][nt], O[rt][nt]);
+                UB[qs][nt] = x;
             }
-        }
 
-        // S' = diag(exp(gam_last)) S + Kb^T U
+        // 5. S' = diag(exp(gam_last)) S + Kb^T U for the owned state tiles
 #pragma unroll
-        for (int ct = 0; ct < DKT; ++ct) {
-            const f32x4 e = *reinterpret_cast<const f32x4*>(egl + 16 * ct + 4 * gq);
+        for (int j = 0; j < OWN; ++j) {
+            const int ct = w + NW * j;
+            if (ct < DKT) {
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) S[ct][nt] *= e;
+                for (int nt = 0; nt < NT; ++nt) S[j][nt] *= F.e[j];
+                F.e[j] = ld_egl(vrec, ct);
 #pragma unroll
-            for (int qs = 0; qs < NQS; ++qs) {
-                const half8 a = fr[(size_t)(R.off_kb + ct * NQS + qs) * 64];
+                for (int qs = 0; qs < NQS; ++qs) {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) S[ct][nt] = mfma_f16(a, UB[qs][nt], S[ct][nt]);
-            }
-        }
-
-        // outputs: rows 16rt + 4gq + i of this chunk
-#pragma unroll
-        for (int rt = 0; rt < NB; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = t0 + 16 * rt + 4 * gq + i;
-                if (t < T) {
-                    const size_t orow = (((size_t)b * T + t) * HV + h) * DV;
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) o[orow + jcol[nt]] = O[rt][nt][i];
+                    for (int nt = 0; nt < NT; ++nt) S[j][nt] = mfma_f16(F.kb[j][qs], UB[qs][nt], S[j][nt]);
+                    ld(F.kb[j][qs], vrec, R.off_kb + ct * NQS + qs);
                 }
             }
+        }
+        // 6. O_w += P U
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs)
+            if (qs < nq_w) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) Op[nt] = mfma_f16(F.p[qs], UB[qs][nt], Op[nt]);
+                ld(F.p[qs], vrec, R.off_p + ChunkRecord::tri_base(w) + qs);
+            }
+    };
+
+    Frags FA, FB;
+    load_all(FA, 0);
+    load_all(FB, min(1, NC - 1));
+    // Two copies of the loop (even / odd chunk count) keep each body free of branches, so
+    // the compiler's wait counting sees the steady state of the pipeline.
+    if ((NC & 1) == 0) {
+        for (int n = 0; n < NC; n += 2) {
+            step(FA, n, min(n + 2, NC - 1));
+            step(FB, n + 1, min(n + 3, NC - 1));
+        }
+    } else {
+        step(FA, 0, min(2, NC - 1));
+        for (int n = 1; n < NC; n += 2) {
+            step(FB, n, min(n + 2, NC - 1));
+            step(FA, n + 1, min(n + 3, NC - 1));
+        }
     }
+    store_o(NC - 1, Op);
 
     if (ht) {
 #pragma unroll
-        for (int ct = 0; ct < DKT; ++ct)
+        for (int j = 0; j < OWN; ++j) {
+            const int ct = w + NW * j;
+            if (ct < DKT) {
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
+                for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    ht[sb + (size_t)(16 * ct + 4 * gq + i) * DV + jcol[nt]] = S[ct][nt][i];
+                    for (int i = 0; i < 4; ++i)
+                        ht[sb + (size_t)(16 * ct + 4 * gq + i) * DV + jcol[nt]] = S[j][nt][i];
+            }
+        }
     }
 }
 
@@ -196,17 +348,30 @@ template <typename TIn, int DK, int DV, int C, int NT>
 static hipError_t launch_carry_t(const LaunchArgs& a) {
     const int NC = (a.T + C - 1) / C;
     const long long nblk = (long long)a.B * a.HV * (DV / (16 * NT));
-    hipLaunchKernelGGL((chunk_carry_kernel<TIn, DK, DV, C, NT>), dim3((unsigned)nblk), dim3(64), 0,
-                       (hipStream_t)a.stream, (const TIn*)a.v, a.h0, a.o, a.ht,
-                       (const unsigned char*)a.workspace, a.B, a.T, a.HV, NC);
+    hipLaunchKernelGGL((chunk_carry_kernel<TIn, DK, DV, C, NT>), dim3((unsigned)nblk),
+                       dim3(64 * (C / 16)), 0, (hipStream_t)a.stream, (const TIn*)a.v, a.h0, a.o,
+                       a.ht, (const unsigned char*)a.workspace, a.B, a.T, a.HV, NC);
     return hipGetLastError();
+}
+
+// Column split: with few heads every 16-column tile gets its own workgroup (the most
+// parallel carry, for B*HV too small to fill 256 CUs otherwise); with many heads a
+// workgroup covers several tiles so each head's records are read from L2 fewer times.
+template <typename TIn, int DK, int DV, int C>
+static hipError_t dispatch_split(const LaunchArgs& a) {
+    constexpr int CT = DV / 16;
+    const long long tiles = (long long)a.B * a.HV * CT;
+    if constexpr (CT >= 2) {
+        if (tiles > 1024) return launch_carry_t<TIn, DK, DV, C, 2>(a);
+    }
+    return launch_carry_t<TIn, DK, DV, C, 1>(a);
 }
 
 template <typename TIn, int DK, int DV>
 static hipError_t dispatch_chunk(const LaunchArgs& a) {
-    if (a.chunk == 16) return launch_carry_t<TIn, DK, DV, 16, 1>(a);
-    if (a.chunk == 32) return launch_carry_t<TIn, DK, DV, 32, 1>(a);
-    if (a.chunk == 64) return launch_carry_t<TIn, DK, DV, 64, 1>(a);
+    if (a.chunk == 16) return dispatch_split<TIn, DK, DV, 16>(a);
+    if (a.chunk == 32) return dispatch_split<TIn, DK, DV, 32>(a);
+    if (a.chunk == 64) return dispatch_split<TIn, DK, DV, 64>(a);
     return hipErrorInvalidValue;
 }
 

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const TIn* __restrict__
     __shared__ float sSeg[NSEG * DK];
     __shared__ float sY[(NB > 1 ? NB - 1 : 1) * 256];
 
-    const ChunkRecord R = ChunkRecord::make(C, DK);
+    constexpr ChunkRecord R = ChunkRecord::make(C, DK);
     const int blk = blockIdx.x;
     const int n = blk % NC;
     const int bh = blk / NC;
@@ -92,10 +92,14 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const TIn* __restrict__
         float loc[RPS];
         float acc = 0.f;
 #pragma unroll
-        for (int m = 0; m < RPS; ++m) {
+        for (int m = 0; m < RPS; ++m) {  // unconditional loads from clamped rows, then mask
             const int r = seg * RPS + m;
-            const float gv = r < L ? g[(((size_t)b * T + t0 + r) * HV + h) * DK + c] : 0.f;
-            acc += gv;
+            const float gv = g[(((size_t)b * T + t0 + min(r, L - 1)) * HV + h) * DK + c];
+            loc[m] = r < L ? gv : 0.f;
+        }
+#pragma unroll
+        for (int m = 0; m < RPS; ++m) {
+            acc += loc[m];
             loc[m] = acc;
         }
         sSeg[seg * DK + c] = acc;
@@ -111,16 +115,17 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const TIn* __restrict__
         for (int idx = tid; idx < C * VPR; idx += 256) {
             const int r = idx / VPR;
             const int cv = idx % VPR;
-            uint4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
-            if (r < L) {
-                const size_t off = (((size_t)b * T + t0 + r) * HK + kh) * DK + (size_t)cv * VN;
-                kv = *reinterpret_cast<const uint4*>(k + off);
-                qv = *reinterpret_cast<const uint4*>(q + off);
-            }
+            const size_t off = (((size_t)b * T + t0 + min(r, L - 1)) * HK + kh) * DK + (size_t)cv * VN;
+            uint4 kv = *reinterpret_cast<const uint4*>(k + off);
+            uint4 qv = *reinterpret_cast<const uint4*>(q + off);
+            if (r >= L) kv = qv = uint4{0u, 0u, 0u, 0u};
             *reinterpret_cast<uint4*>(&sK[r * XP + cv * VN]) = kv;
             *reinterpret_cast<uint4*>(&sQ[r * XP + cv * VN]) = qv;
         }
-        if (tid < C) sBeta[tid] = tid < L ? beta[((size_t)b * T + t0 + tid) * HV + h] : 0.f;
+        if (tid < C) {
+            const float bv = beta[((size_t)b * T + t0 + min(tid, L - 1)) * HV + h];
+            sBeta[tid] = tid < L ? bv : 0.f;
+        }
         for (int idx = tid; idx < C * AP; idx += 256) sT[idx] = 0.f;
     }
     __syncthreads();
@@ -227,8 +232,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const TIn* __restrict__
             Pt[J] = (J <= I) ? pv : f32x4{0.f, 0.f, 0.f, 0.f};
         }
         // P fragments for row block I: slot jj <- tile J = 2qs + jj/4, row i = jj % 4
+        // (token steps qs <= I/2 only; the rest of the block row is zero)
 #pragma unroll
         for (int qs = 0; qs < NQS; ++qs) {
+            if (2 * qs > I) break;
             half8 x;
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
@@ -236,7 +243,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const TIn* __restrict__
                 x[jj] = J < NB ? static_cast<_Float16>(Pt[J < NB ? J : 0][jj & 3])
                                : static_cast<_Float16>(0.f);
             }
-            frags[(size_t)(R.off_p + I * NQS + qs) * 64 + lane] = x;
+            frags[(size_t)(R.off_p + ChunkRecord::tri_base(I) + qs) * 64 + lane] = x;
         }
     } else {
         // rows of A above the computed blocks are never read; nothing to do
@@ -288,6 +295,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const TIn* __restrict__
     // ---- Tb = Tinv diag(beta) fragments ------------------------------------------------
     for (int f = wave; f < NB * NQS; f += 4) {
         const int rt = f / NQS, qs = f % NQS;
+        if (2 * qs > rt) continue;
         const int r = 16 * rt + li;
         half8 x;
 #pragma unroll
@@ -296,7 +304,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const TIn* __restrict__
             x[jj] = s < C ? static_cast<_Float16>(sT[r * AP + s] * sBeta[s])
                           : static_cast<_Float16>(0.f);
         }
-        frags[(size_t)(R.off_tb + f) * 64 + lane] = x;
+        frags[(size_t)(R.off_tb + ChunkRecord::tri_base(rt) + qs) * 64 + lane] = x;
     }
 
     // ---- pseudo-keys: W^T = (exp(gam) * K)^T Tb^T on the matrix cores; store -W --------

@@ -39,6 +39,46 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Buffer resource over `nbytes` bytes at `base` (raw, stride 0).  Buffer loads and stores
+// take a 32-bit per-lane offset plus a wave-uniform offset held in an SGPR, which keeps
+// address arithmetic off the vector ALU; a load whose per-lane offset is past `nbytes`
+// returns zero and such a store is dropped.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ half8 buf_load_half8(rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ f32x4 buf_load_f32x4(rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+// Raw bits of one q/k/v element (fp32 bits, or bf16 bits zero-extended); converted by
+// raw_to_f32 only where the value is used, so the load stays in flight until then.
+__device__ __forceinline__ uint32_t buf_load_raw(rsrc_t r, int voff, int soff, float) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t buf_load_raw(rsrc_t r, int voff, int soff, bf16_t) {
+    return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
+}
+__device__ __forceinline__ float raw_to_f32(uint32_t x, float) { return __uint_as_float(x); }
+__device__ __forceinline__ float raw_to_f32(uint32_t x, bf16_t) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ void buf_store_f32(float x, rsrc_t r, int voff, int soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
+// (lgkmcnt(0)), then s_barrier.  Unlike __syncthreads() it does not wait for outstanding
+// global/buffer loads (vmcnt), so prefetches stay in flight across it.  The empty asm
+// statements stop the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt(63) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Reduction-slot permutation used for every fragment that meets an accumulator tile.
 // Slot jj (0..7) of lane group g inside a 32-wide reduction step maps to index
 //   16 * (jj / 4) + 4 * g + (jj % 4)

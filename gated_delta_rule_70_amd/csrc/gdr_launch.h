@@ -25,34 +25,48 @@ struct LaunchArgs {
 
 // Per-(batch, head, chunk) record that the chunk-parallel kernel writes and the
 // sequential carry kernel reads: fp16 MFMA operand fragments (1 KiB each: 64 lanes x 8
-// halves) followed by the chunk's total decay exp(gamma_last) in fp32.
+// halves, lane-major) followed by one 1 KiB block whose first dk floats hold the chunk's
+// total decay exp(gam_last).  Records are a whole number of KiB so the carry kernel can
+// stream one into LDS with 1 KiB wave-wide copies.
+//   Qt  [nb][kc]    decayed queries exp(gam) * q           (rows r, reduction over dk)
+//   -W  [nb][kc]    negated WY pseudo-keys                  (rows r, reduction over dk)
+//   Kb  [dkt][nqs]  decay-to-end keys, transposed           (rows c, reduction over tokens)
+//   Tb  [tri]       Tinv diag(beta), lower block triangle   (rows r, reduction over tokens)
+//   P   [tri]       causal q.k terms, lower block triangle  (rows r, reduction over tokens)
+// "tri" holds, for row tile rt, the token steps qs <= rt / 2 only (the others are zero).
 struct ChunkRecord {
     int nb;        // 16-row blocks per chunk (C / 16)
     int nqs;       // 32-wide token reduction steps (ceil(C / 32))
     int kc;        // 32-wide key-channel reduction steps (dk / 32)
     int dkt;       // 16-row key-channel tiles (dk / 16)
+    int ntri;      // fragments of a block-lower-triangular token operand
     int off_qt;    // fragment offsets (in fragments) of each operand
     int off_w;
     int off_kb;
     int off_tb;
     int off_p;
-    int nfrag;
-    size_t bytes;  // record stride, 256-byte aligned
+    int nfrag;     // operand fragments; the decay block follows them
+    int bytes;     // record stride: (nfrag + 1) KiB
 
-    __host__ __device__ static ChunkRecord make(int C, int dk) {
+    __host__ __device__ static constexpr int tri_base(int rt) {
+        int b = 0;
+        for (int r = 0; r < rt; ++r) b += r / 2 + 1;
+        return b;
+    }
+    __host__ __device__ static constexpr ChunkRecord make(int C, int dk) {
         ChunkRecord r{};
         r.nb = C / 16;
         r.nqs = (C + 31) / 32;
         r.kc = dk / 32;
         r.dkt = dk / 16;
-        r.off_qt = 0;                          // decayed queries   [nb][kc]
-        r.off_w = r.off_qt + r.nb * r.kc;      // -W pseudo-keys    [nb][kc]
-        r.off_kb = r.off_w + r.nb * r.kc;      // K-bar transposed  [dkt][nqs]
-        r.off_tb = r.off_kb + r.dkt * r.nqs;   // T diag(beta)      [nb][nqs]
-        r.off_p = r.off_tb + r.nb * r.nqs;     // causal q.k terms  [nb][nqs]
-        r.nfrag = r.off_p + r.nb * r.nqs;
-        const size_t raw = (size_t)r.nfrag * 1024 + (size_t)dk * 4;
-        r.bytes = (raw + 255) / 256 * 256;
+        r.ntri = tri_base(r.nb);
+        r.off_qt = 0;
+        r.off_w = r.off_qt + r.nb * r.kc;
+        r.off_kb = r.off_w + r.nb * r.kc;
+        r.off_tb = r.off_kb + r.dkt * r.nqs;
+        r.off_p = r.off_tb + r.ntri;
+        r.nfrag = r.off_p + r.ntri;
+        r.bytes = (r.nfrag + 1) * 1024;
         return r;
     }
 };
