@@ -5,7 +5,7 @@
 // log-decay prefixes, the beta-folded triangular transform, WY pseudo-keys and
 // pseudo-values, causal query/key terms, then the inter-chunk state carry.  Everything
 // except the carry depends on one chunk only, so this kernel runs it for all
-// (batch, value head, chunk) triples at once -- one 256-thread workgroup each -- and hands
+// (batch, value head, chunk) triples at once -- one 512-thread workgroup each -- and hands
 // the results to the sequential carry kernel as fp16 MFMA operand fragments.
 //
 // For a chunk of C tokens (rows r, s; gam = inclusive prefix of g inside the chunk):
@@ -17,11 +17,19 @@
 //   carry    Qt = exp(gam) * Q;  Kb = exp(gam_last - gam) * K;  exp(gam_last)
 // Outputs per chunk (see ChunkRecord): Qt, -W, Kb^T, Tb, P as fragments, exp(gam_last).
 //
-// Decay factors inside the MFMA operands are split around a per-16-row-block reference
-// row so no operand exceeds its format's range: for blocks J < I the reference is the
-// last row of J, making both factors <= 1 (fp16 operands); for the diagonal blocks it is
-// the block's 8th row, and operands are split into bf16 hi + lo parts (three products),
-// which keeps ~16 significant bits with fp32's exponent range.
+// Decay factors.  Every factor is built from two per-element exponentials around the
+// middle row m_I = 16I + 7 of the element's 16-row block I,
+//   Z_rc = exp(gam_rc - gam_{m_I,c}),   Zi_rc = exp(gam_{m_I,c} - gam_rc),
+// and per-(block, channel) constants, so no operand leaves its format's range:
+//   blocks J < I (fp16):  exp(gam_r - gam_s) = [Z_r a_I] [Zi_s b_J] E_IJ, where
+//       a_I = exp(gam_m - gam_{16I-1}), b_J = exp(gam_{16J+15} - gam_m),
+//       E_IJ = exp(gam_{16I-1} - gam_{16J+15}); both bracketed factors are <= 1;
+//   diagonal blocks (bf16 hi + lo split, three products, fp32 range, ~16 bits):
+//       exp(gam_r - gam_s) = Z_r Zi_s;
+//   Qt = q Z G_I, Kb = k Zi L_I, exp(gam) k = k Z G_I with G_I = exp(gam_m),
+//       L_I = exp(gam_last - gam_m).
+// Z and Zi stay finite while the decay over 8 consecutive tokens of a block is below ~88
+// (mean g above about -11 per token), the range documented in gdr.h.
 #include "gdr_device.h"
 #include "gdr_launch.h"
 
@@ -39,34 +47,43 @@ struct VecLoad<bf16_t> {
 };
 
 template <typename TIn, int DK, int C>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(const TIn* __restrict__ q,
+__global__ __launch_bounds__(512) void chunk_prep_kernel(const TIn* __restrict__ q,
                                                          const TIn* __restrict__ k,
                                                          const float* __restrict__ g,
                                                          const float* __restrict__ beta,
                                                          unsigned char* __restrict__ ws, int T,
                                                          int HK, int HV, int NC) {
+    constexpr int NTH = 512;
     constexpr int NB = C / 16;
     constexpr int NQS = (C + 31) / 32;
     constexpr int KC = DK / 32;
     constexpr int DKT = DK / 16;
-    constexpr int GP = DK + 4;               // padded fp32 row (gam)
+    constexpr int ZP = DK + 4;        // padded fp32 row (Z, Zi)
     constexpr int VN = VecLoad<TIn>::N;
-    constexpr int XP = DK + VN;              // padded input row (k, q)
-    constexpr int AP = C + 4;                // padded fp32 row (A, Tinv)
-    constexpr int NSEG = 256 / DK;           // scan segments per channel
-    constexpr int RPS = C / NSEG;            // rows per segment
+    constexpr int XP = DK + VN;       // padded input row (k)
+    constexpr int AP = C + 4;         // padded fp32 row (A, Tinv)
+    constexpr int NSEG = NTH / DK;    // scan segments per channel
+    constexpr int RPS = C / NSEG;     // rows per segment
+    constexpr int NOFF = NB * (NB - 1) / 2;
     static_assert(RPS >= 1 && C % NSEG == 0, "chunk too short for this key dim");
-
-    __shared__ float sGam[C * GP];
-    __shared__ TIn sK[C * XP];
-    __shared__ TIn sQ[C * XP];
-    __shared__ float sA[C * AP];
-    __shared__ float sT[C * AP];
-    __shared__ float sBeta[C];
-    __shared__ float sSeg[NSEG * DK];
-    __shared__ float sY[(NB > 1 ? NB - 1 : 1) * 256];
-
     constexpr ChunkRecord R = ChunkRecord::make(C, DK);
+
+    // LDS.  Z/Zi are dead once the gram and the carry operands are formed; Tinv reuses them.
+    constexpr int NZZ = (2 * C * ZP > C * AP) ? 2 * C * ZP : C * AP;
+    __shared__ float sZZ[NZZ];
+    __shared__ TIn sK[C * XP];
+    __shared__ float sA[C * AP];
+    __shared__ _Float16 sP[C * C];
+    __shared__ float sRef[NB * 3 * DK];      // gam at rows 16I-1, 16I+7, 16I+15
+    __shared__ float sCa[NB * DK], sCb[NB * DK], sCg[NB * DK], sCl[NB * DK];
+    __shared__ float sCe[(NOFF > 0 ? NOFF : 1) * DK];
+    __shared__ float sSeg[NSEG * DK];
+    __shared__ float sBeta[C];
+    __shared__ float sY[(NB > 1 ? NB - 1 : 1) * 256];
+    float* sZ = sZZ;
+    float* sZi = sZZ + C * ZP;
+    float* sT = sZZ;  // Tinv reuses the Z/Zi area once the gram is done
+
     const int blk = blockIdx.x;
     const int n = blk % NC;
     const int bh = blk / NC;
@@ -77,184 +94,282 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const TIn* __restrict__
     const int L = min(C, T - t0);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15;
     const int gq = lane >> 4;
 
     unsigned char* rec = ws + (size_t)((size_t)bh * NC + n) * R.bytes;
     half8* frags = reinterpret_cast<half8*>(rec);
     float* egl_out = reinterpret_cast<float*>(rec + (size_t)R.nfrag * 1024);
+    const size_t qk_row0 = (((size_t)b * T + t0) * HK + kh) * DK;  // row r at qk_row0 + r*HK*DK
+    const size_t qk_rstride = (size_t)HK * DK;
 
-    // ---- load g and form the inclusive per-channel prefix (two-level scan) -------------
+    // ---- 1. g -> per-channel inclusive prefix (two-level scan); k rows and beta -> LDS ----
+    float gam_loc[RPS];
+    const int sc = tid % DK;     // channel of this thread in the scan
+    const int sseg = tid / DK;   // segment of this thread
     {
-        const int c = tid % DK;
-        const int seg = tid / DK;
-        float loc[RPS];
-        float acc = 0.f;
 #pragma unroll
         for (int m = 0; m < RPS; ++m) {  // unconditional loads from clamped rows, then mask
-            const int r = seg * RPS + m;
-            const float gv = g[(((size_t)b * T + t0 + min(r, L - 1)) * HV + h) * DK + c];
-            loc[m] = r < L ? gv : 0.f;
+            const int r = sseg * RPS + m;
+            const float gv = g[(((size_t)b * T + t0 + min(r, L - 1)) * HV + h) * DK + sc];
+            gam_loc[m] = r < L ? gv : 0.f;
         }
+        float acc = 0.f;
 #pragma unroll
         for (int m = 0; m < RPS; ++m) {
-            acc += loc[m];
-            loc[m] = acc;
+            acc += gam_loc[m];
+            gam_loc[m] = acc;
         }
-        sSeg[seg * DK + c] = acc;
-        __syncthreads();
-        float off = 0.f;
-        for (int s2 = 0; s2 < seg; ++s2) off += sSeg[s2 * DK + c];
-#pragma unroll
-        for (int m = 0; m < RPS; ++m) sGam[(seg * RPS + m) * GP + c] = loc[m] + off;
-    }
-    // ---- load k, q rows (zero past the chunk end) and beta ------------------------------
-    {
+        sSeg[sseg * DK + sc] = acc;
+
         constexpr int VPR = DK / VN;  // vectors per row
-        for (int idx = tid; idx < C * VPR; idx += 256) {
+        for (int idx = tid; idx < C * VPR; idx += NTH) {
             const int r = idx / VPR;
             const int cv = idx % VPR;
-            const size_t off = (((size_t)b * T + t0 + min(r, L - 1)) * HK + kh) * DK + (size_t)cv * VN;
-            uint4 kv = *reinterpret_cast<const uint4*>(k + off);
-            uint4 qv = *reinterpret_cast<const uint4*>(q + off);
-            if (r >= L) kv = qv = uint4{0u, 0u, 0u, 0u};
+            uint4 kv = *reinterpret_cast<const uint4*>(k + qk_row0 + min(r, L - 1) * qk_rstride + cv * VN);
+            if (r >= L) kv = uint4{0u, 0u, 0u, 0u};
             *reinterpret_cast<uint4*>(&sK[r * XP + cv * VN]) = kv;
-            *reinterpret_cast<uint4*>(&sQ[r * XP + cv * VN]) = qv;
         }
         if (tid < C) {
             const float bv = beta[((size_t)b * T + t0 + min(tid, L - 1)) * HV + h];
             sBeta[tid] = tid < L ? bv : 0.f;
         }
-        for (int idx = tid; idx < C * AP; idx += 256) sT[idx] = 0.f;
+    }
+    __syncthreads();
+    {
+        float off = 0.f;
+        for (int s2 = 0; s2 < sseg; ++s2) off += sSeg[s2 * DK + sc];
+#pragma unroll
+        for (int m = 0; m < RPS; ++m) {
+            const int r = sseg * RPS + m;
+            const float gv = gam_loc[m] + off;
+            gam_loc[m] = gv;
+            const int I = r >> 4, rr = r & 15;
+            if (rr == 7) sRef[(I * 3 + 1) * DK + sc] = gv;
+            if (rr == 15) {
+                sRef[(I * 3 + 2) * DK + sc] = gv;
+                if (I + 1 < NB) sRef[((I + 1) * 3 + 0) * DK + sc] = gv;
+            }
+        }
+        if (sseg == 0) sRef[0 * DK + sc] = 0.f;  // the row before the chunk: gam = 0
+    }
+    __syncthreads();
+    // ---- 2. per-element factors Z, Zi and per-(block, channel) constants ----------------
+    {
+#pragma unroll
+        for (int m = 0; m < RPS; ++m) {
+            const int r = sseg * RPS + m;
+            const int I = r >> 4;
+            const float gm = sRef[(I * 3 + 1) * DK + sc];
+            sZ[r * ZP + sc] = __expf(gam_loc[m] - gm);
+            sZi[r * ZP + sc] = __expf(gm - gam_loc[m]);
+        }
+        const float gl = sRef[((NB - 1) * 3 + 2) * DK + sc];  // gam at the last row
+        for (int I = sseg; I < NB; I += NSEG) {
+            const float gp = sRef[(I * 3 + 0) * DK + sc];
+            const float gm = sRef[(I * 3 + 1) * DK + sc];
+            const float ge = sRef[(I * 3 + 2) * DK + sc];
+            sCa[I * DK + sc] = __expf(gm - gp);
+            sCb[I * DK + sc] = __expf(ge - gm);
+            sCg[I * DK + sc] = __expf(gm);
+            sCl[I * DK + sc] = __expf(gl - gm);
+        }
+        for (int pr = sseg; pr < NOFF; pr += NSEG) {
+            int I = 1, base = 0;
+            while (base + I <= pr) base += I++;
+            const int J = pr - base;
+            sCe[pr * DK + sc] = __expf(sRef[(I * 3 + 0) * DK + sc] - sRef[(J * 3 + 2) * DK + sc]);
+        }
+        if (sseg == 0) egl_out[sc] = __expf(gl);
     }
     __syncthreads();
 
     auto kval = [&](int r, int c) { return to_f32(sK[r * XP + c]); };
-    auto qval = [&](int r, int c) { return to_f32(sQ[r * XP + c]); };
-    auto gam = [&](int r, int c) { return sGam[r * GP + c]; };
+    auto qrow = [&](int r) { return q + qk_row0 + min(r, L - 1) * qk_rstride; };
+    // 4 consecutive q values of row r from channel c0 (zero past the chunk end)
+    auto q4 = [&](int r, int c0, float (&x)[4]) {
+        const TIn* p = qrow(r) + c0;
+        if constexpr (VN == 8) {
+            const uint2 u = *reinterpret_cast<const uint2*>(p);
+            x[0] = __uint_as_float(u.x << 16);
+            x[1] = __uint_as_float(u.x & 0xFFFF0000u);
+            x[2] = __uint_as_float(u.y << 16);
+            x[3] = __uint_as_float(u.y & 0xFFFF0000u);
+        } else {
+            const float4 u = *reinterpret_cast<const float4*>(p);
+            x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+        }
+        if (r >= L) x[0] = x[1] = x[2] = x[3] = 0.f;
+    };
+    // 8 consecutive q values of row r from channel c0 (zero past the chunk end)
+    auto q8 = [&](int r, int c0, float (&x)[8]) {
+        const TIn* p = qrow(r) + c0;
+        if constexpr (VN == 8) {
+            const uint4 u = *reinterpret_cast<const uint4*>(p);
+            const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x[2 * j] = __uint_as_float(w4[j] << 16);
+                x[2 * j + 1] = __uint_as_float(w4[j] & 0xFFFF0000u);
+            }
+        } else {
+            const float4 u0 = *reinterpret_cast<const float4*>(p);
+            const float4 u1 = *reinterpret_cast<const float4*>(p + 4);
+            x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+            x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+        }
+        if (r >= L) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] = 0.f;
+        }
+    };
 
-    // ---- carry operands: decayed queries, decay-to-end keys (transposed), exp(gam_last) --
-    for (int f = wave; f < NB * KC; f += 4) {
+    // ---- 3. carry operands: Qt and Kb^T fragments; exp(gam) k fragments for W ------------
+    for (int f = wave; f < NB * KC; f += NTH / 64) {
         const int rt = f / KC, p = f % KC;
+        const int r = 16 * rt + li;
+        float x[4], y[4];
+        q4(r, 32 * p + 4 * gq, x);       // slots 0..3 <- channels 32p + 4gq + 0..3
+        q4(r, 32 * p + 16 + 4 * gq, y);  // slots 4..7 <- channels 32p + 16 + 4gq + 0..3
+        half8 o8;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const int c = 32 * p + perm_slot(gq, jj);
+            const float qv = jj < 4 ? x[jj] : y[jj - 4];
+            o8[jj] = static_cast<_Float16>(qv * sZ[r * ZP + c] * sCg[rt * DK + c]);
+        }
+        frags[(size_t)(R.off_qt + f) * 64 + lane] = o8;
+    }
+    for (int f = wave; f < DKT * NQS; f += NTH / 64) {
+        const int ct = f / NQS, qs = f % NQS;
+        const int c = 16 * ct + li;
+        half8 o8;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const int r = 32 * qs + perm_slot(gq, jj);
+            o8[jj] = r < C ? static_cast<_Float16>(kval(r, c) * sZi[r * ZP + c] * sCl[(r >> 4) * DK + c])
+                           : static_cast<_Float16>(0.f);
+        }
+        frags[(size_t)(R.off_kb + f) * 64 + lane] = o8;
+    }
+    // W^T = (exp(gam) K)^T Tb^T is computed by wave w for key-channel step p = w % KC and
+    // row tiles rt = w / KC, w / KC + 8 / KC, ...; its A operand (exp(gam) k, transposed)
+    // is formed now, while Z is still live.
+    constexpr int WW = (NTH / 64) / KC;  // waves per key-channel step (2, 4 or 8)
+    const int wp = wave % KC;
+    half8 ka[2][NQS];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+        const int c = 16 * (2 * wp + h2) + li;
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const int s = 32 * qs + 8 * gq + jj;
+                ka[h2][qs][jj] = s < C ? static_cast<_Float16>(kval(s, c) * sZ[s * ZP + c] * sCg[(s >> 4) * DK + c])
+                                       : static_cast<_Float16>(0.f);
+            }
+    }
+
+    // ---- 4. gram A (-> sA, fp32, times beta_r) and causal terms P (-> sP, fp16) ---------
+    // Work items: the NB diagonal block pairs first (three bf16 products per step), then the
+    // NB(NB-1)/2 off-diagonal pairs (one fp16 product per step), dealt round-robin to waves.
+    // The accumulator holds the transposed tile [s in block J][r in block I].
+    for (int item = wave; item < NB + NOFF; item += NTH / 64) {
+        int I, J, pr = -1;
+        if (item < NB) {
+            I = J = item;
+        } else {
+            pr = item - NB;
+            I = 1;
+            int base = 0;
+            while (base + I <= pr) base += I++;
+            J = pr - base;
+        }
+        const int s = 16 * J + li;  // A-operand row (key side)
+        const int r = 16 * I + li;  // B-operand row (key / query side)
+        f32x4 accA = {0.f, 0.f, 0.f, 0.f};
+        f32x4 accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < KC; ++p) {
+            const int c0 = 32 * p + 8 * gq;
+            float qv[8];
+            q8(r, c0, qv);
+            if (I == J) {
+                bf16x8 ah, al, kh_, kl, qh, ql;
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int c = c0 + jj;
+                    __bf16 hi, lo;
+                    split_bf16(kval(s, c) * sZi[s * ZP + c], hi, lo);
+                    ah[jj] = hi;
+                    al[jj] = lo;
+                    const float z = sZ[r * ZP + c];
+                    split_bf16(kval(r, c) * z, hi, lo);
+                    kh_[jj] = hi;
+                    kl[jj] = lo;
+                    split_bf16(qv[jj] * z, hi, lo);
+                    qh[jj] = hi;
+                    ql[jj] = lo;
+                }
+                accA = mfma_bf16(ah, kh_, accA);
+                accA = mfma_bf16(al, kh_, accA);
+                accA = mfma_bf16(ah, kl, accA);
+                accP = mfma_bf16(ah, qh, accP);
+                accP = mfma_bf16(al, qh, accP);
+                accP = mfma_bf16(ah, ql, accP);
+            } else {
+                half8 a, bk, bq;
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int c = c0 + jj;
+                    a[jj] = static_cast<_Float16>(kval(s, c) * sZi[s * ZP + c] * sCb[J * DK + c] * sCe[pr * DK + c]);
+                    const float za = sZ[r * ZP + c] * sCa[I * DK + c];
+                    bk[jj] = static_cast<_Float16>(kval(r, c) * za);
+                    bq[jj] = static_cast<_Float16>(qv[jj] * za);
+                }
+                accA = mfma_f16(a, bk, accA);
+                accP = mfma_f16(a, bq, accP);
+            }
+        }
+        const float br = sBeta[r];
+        f32x4 av;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int sl = 4 * gq + i;
+            const bool lowA = J < I || sl < li;
+            const bool lowP = J < I || sl <= li;
+            av[i] = lowA ? accA[i] * br : 0.f;
+            sP[r * C + 16 * J + sl] = static_cast<_Float16>(lowP ? accP[i] : 0.f);
+        }
+        *reinterpret_cast<f32x4*>(&sA[r * AP + 16 * J + 4 * gq]) = av;
+    }
+    __syncthreads();  // gram done; Z, Zi no longer needed
+
+    // ---- 5. P fragments (block lower triangle) and Tinv := 0 ----------------------------
+    for (int f = wave; f < R.ntri; f += NTH / 64) {
+        int rt = 0;
+        while (ChunkRecord::tri_base(rt + 1) <= f) ++rt;
+        const int qs = f - ChunkRecord::tri_base(rt);
         const int r = 16 * rt + li;
         half8 x;
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-            const int c = 32 * p + perm_slot(gq, jj);
-            x[jj] = static_cast<_Float16>(qval(r, c) * __expf(gam(r, c)));
+            const int sx = 32 * qs + perm_slot(gq, jj);
+            x[jj] = (sx < C && sx <= r) ? sP[r * C + sx] : static_cast<_Float16>(0.f);
         }
-        frags[(size_t)(R.off_qt + f) * 64 + lane] = x;
+        frags[(size_t)(R.off_p + f) * 64 + lane] = x;
     }
-    for (int f = wave; f < DKT * NQS; f += 4) {
-        const int ct = f / NQS, qs = f % NQS;
-        const int c = 16 * ct + li;
-        const float gl = gam(C - 1, c);
-        half8 x;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const int r = 32 * qs + perm_slot(gq, jj);
-            x[jj] = r < C ? static_cast<_Float16>(kval(r, c) * __expf(gl - gam(r, c)))
-                          : static_cast<_Float16>(0.f);
-        }
-        frags[(size_t)(R.off_kb + f) * 64 + lane] = x;
-    }
-    if (tid < DK) egl_out[tid] = __expf(gam(C - 1, tid));
-
-    // ---- gram A (-> LDS, fp32) and causal terms P (-> fragments), wave I = row block ----
-    if (wave < NB) {
-        const int I = wave;
-        const int r = 16 * I + li;  // B-operand row (query/key side)
-        f32x4 Pt[NB];
-#pragma unroll
-        for (int J = 0; J < NB; ++J) {
-            f32x4 accA = {0.f, 0.f, 0.f, 0.f};
-            f32x4 accP = {0.f, 0.f, 0.f, 0.f};
-            const int s = 16 * J + li;  // A-operand row (key side)
-            if (J < I) {
-                const int m = 16 * J + 15;
-#pragma unroll
-                for (int p = 0; p < KC; ++p) {
-                    half8 a, bk, bq;
-#pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) {
-                        const int c = 32 * p + 8 * gq + jj;
-                        const float gm = gam(m, c);
-                        a[jj] = static_cast<_Float16>(kval(s, c) * __expf(gm - gam(s, c)));
-                        const float fr = __expf(gam(r, c) - gm);
-                        bk[jj] = static_cast<_Float16>(kval(r, c) * fr);
-                        bq[jj] = static_cast<_Float16>(qval(r, c) * fr);
-                    }
-                    accA = mfma_f16(a, bk, accA);
-                    accP = mfma_f16(a, bq, accP);
-                }
-            } else if (J == I) {
-                const int m = 16 * I + 7;
-#pragma unroll
-                for (int p = 0; p < KC; ++p) {
-                    bf16x8 ah, al, kh_, kl, qh, ql;
-#pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) {
-                        const int c = 32 * p + 8 * gq + jj;
-                        const float gm = gam(m, c);
-                        __bf16 hi, lo;
-                        split_bf16(kval(s, c) * __expf(gm - gam(s, c)), hi, lo);
-                        ah[jj] = hi;
-                        al[jj] = lo;
-                        const float fr = __expf(gam(r, c) - gm);
-                        split_bf16(kval(r, c) * fr, hi, lo);
-                        kh_[jj] = hi;
-                        kl[jj] = lo;
-                        split_bf16(qval(r, c) * fr, hi, lo);
-                        qh[jj] = hi;
-                        ql[jj] = lo;
-                    }
-                    accA = mfma_bf16(ah, kh_, accA);
-                    accA = mfma_bf16(al, kh_, accA);
-                    accA = mfma_bf16(ah, kl, accA);
-                    accP = mfma_bf16(ah, qh, accP);
-                    accP = mfma_bf16(al, qh, accP);
-                    accP = mfma_bf16(ah, ql, accP);
-                }
-            }
-            // accumulator lane holds [s = 16J + 4gq + i][r = 16I + li]
-            const float br = sBeta[r];
-            f32x4 av, pv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int sl = 4 * gq + i;
-                const bool lowA = J < I || (J == I && sl < li);
-                const bool lowP = J < I || (J == I && sl <= li);
-                av[i] = lowA ? accA[i] * br : 0.f;
-                pv[i] = lowP ? accP[i] : 0.f;
-            }
-            if (J <= I) *reinterpret_cast<f32x4*>(&sA[r * AP + 16 * J + 4 * gq]) = av;
-            Pt[J] = (J <= I) ? pv : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        // P fragments for row block I: slot jj <- tile J = 2qs + jj/4, row i = jj % 4
-        // (token steps qs <= I/2 only; the rest of the block row is zero)
-#pragma unroll
-        for (int qs = 0; qs < NQS; ++qs) {
-            if (2 * qs > I) break;
-            half8 x;
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const int J = 2 * qs + (jj >> 2);
-                x[jj] = J < NB ? static_cast<_Float16>(Pt[J < NB ? J : 0][jj & 3])
-                               : static_cast<_Float16>(0.f);
-            }
-            frags[(size_t)(R.off_p + ChunkRecord::tri_base(I) + qs) * 64 + lane] = x;
-        }
-    } else {
-        // rows of A above the computed blocks are never read; nothing to do
-    }
+    for (int idx = tid; idx < C * AP; idx += NTH) sT[idx] = 0.f;
     __syncthreads();
 
-    // ---- block forward substitution: Tinv = (I + A)^-1 ---------------------------------
-    // diagonal 16x16 blocks: lane j of wave w inverts column j of block w
-    if (wave < NB && lane < 16) {
-        const int base = 16 * wave;
-        const int j = lane;
+    // ---- 6. block forward substitution: Tinv = (I + A)^-1 ------------------------------
+    // diagonal 16x16 blocks, all at once: lane 16*blk + j of wave 0 solves column j of
+    // block blk by substitution down its 16 rows.
+    if (wave == 0 && (lane >> 4) < NB) {
+        const int base = 16 * (lane >> 4);
+        const int j = lane & 15;
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -270,18 +385,18 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const TIn* __restrict__
     // off-diagonal blocks by distance d:  Tinv_IJ = -Tinv_II * sum_{M=J}^{I-1} A_IM Tinv_MJ
 #pragma unroll
     for (int d = 1; d < NB; ++d) {
-        const int ii = tid >> 4, jj = tid & 15;
-        for (int I = d; I < NB; ++I) {
+        const int e = tid & 255, ii = e >> 4, jj = e & 15;
+        for (int I = d + (tid >> 8); I < NB; I += NTH / 256) {
             const int J = I - d;
             float y = 0.f;
             for (int M = J; M < I; ++M)
 #pragma unroll
                 for (int kk = 0; kk < 16; ++kk)
                     y += sA[(16 * I + ii) * AP + 16 * M + kk] * sT[(16 * M + kk) * AP + 16 * J + jj];
-            sY[(I - d) * 256 + tid] = y;
+            sY[(I - d) * 256 + e] = y;
         }
         __syncthreads();
-        for (int I = d; I < NB; ++I) {
+        for (int I = d + (tid >> 8); I < NB; I += NTH / 256) {
             const int J = I - d;
             float t = 0.f;
 #pragma unroll
@@ -292,61 +407,42 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const TIn* __restrict__
         __syncthreads();
     }
 
-    // ---- Tb = Tinv diag(beta) fragments ------------------------------------------------
-    for (int f = wave; f < NB * NQS; f += 4) {
-        const int rt = f / NQS, qs = f % NQS;
-        if (2 * qs > rt) continue;
+    // ---- 7. Tb = Tinv diag(beta) fragments ----------------------------------------------
+    for (int f = wave; f < R.ntri; f += NTH / 64) {
+        int rt = 0;
+        while (ChunkRecord::tri_base(rt + 1) <= f) ++rt;
+        const int qs = f - ChunkRecord::tri_base(rt);
         const int r = 16 * rt + li;
         half8 x;
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-            const int s = 32 * qs + perm_slot(gq, jj);
-            x[jj] = s < C ? static_cast<_Float16>(sT[r * AP + s] * sBeta[s])
-                          : static_cast<_Float16>(0.f);
+            const int sx = 32 * qs + perm_slot(gq, jj);
+            x[jj] = sx < C ? static_cast<_Float16>(sT[r * AP + sx] * sBeta[sx]) : static_cast<_Float16>(0.f);
         }
-        frags[(size_t)(R.off_tb + ChunkRecord::tri_base(rt) + qs) * 64 + lane] = x;
+        frags[(size_t)(R.off_tb + f) * 64 + lane] = x;
     }
 
-    // ---- pseudo-keys: W^T = (exp(gam) * K)^T Tb^T on the matrix cores; store -W --------
-    if (wave < KC) {
-        const int p = wave;
-        half8 ka[2][NQS];
+    // ---- 8. pseudo-keys: W^T = (exp(gam) K)^T Tb^T on the matrix cores; store -W --------
+    for (int rt = wave / KC; rt < NB; rt += WW) {
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+        const int r = 16 * rt + li;
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            const int c = 16 * (2 * p + h2) + li;
+        for (int qs = 0; qs < NQS; ++qs) {
+            if (2 * qs > rt) break;
+            half8 bt;
 #pragma unroll
-            for (int qs = 0; qs < NQS; ++qs) {
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int s = 32 * qs + 8 * gq + jj;
-                    ka[h2][qs][jj] = s < C ? static_cast<_Float16>(kval(s, c) * __expf(gam(s, c)))
-                                           : static_cast<_Float16>(0.f);
-                }
+            for (int jj = 0; jj < 8; ++jj) {
+                const int sx = 32 * qs + 8 * gq + jj;
+                bt[jj] = sx < C ? static_cast<_Float16>(sT[r * AP + sx] * sBeta[sx]) : static_cast<_Float16>(0.f);
             }
+            acc0 = mfma_f16(ka[0][qs], bt, acc0);
+            acc1 = mfma_f16(ka[1][qs], bt, acc1);
         }
+        half8 x;
 #pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
-            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-            const int r = 16 * rt + li;
-#pragma unroll
-            for (int qs = 0; qs < NQS; ++qs) {
-                if (2 * qs > rt) break;
-                half8 bt;
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int s = 32 * qs + 8 * gq + jj;
-                    bt[jj] = s < C ? static_cast<_Float16>(sT[r * AP + s] * sBeta[s])
-                                   : static_cast<_Float16>(0.f);
-                }
-                acc0 = mfma_f16(ka[0][qs], bt, acc0);
-                acc1 = mfma_f16(ka[1][qs], bt, acc1);
-            }
-            half8 x;
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
-                x[jj] = static_cast<_Float16>(-((jj >> 2) ? acc1[jj & 3] : acc0[jj & 3]));
-            frags[(size_t)(R.off_w + rt * KC + p) * 64 + lane] = x;
-        }
+        for (int jj = 0; jj < 8; ++jj)
+            x[jj] = static_cast<_Float16>(-((jj >> 2) ? acc1[jj & 3] : acc0[jj & 3]));
+        frags[(size_t)(R.off_w + rt * KC + wp) * 64 + lane] = x;
     }
 }
 
@@ -354,7 +450,7 @@ template <typename TIn, int DK, int C>
 static hipError_t launch_prep_t(const LaunchArgs& a) {
     const int NC = (a.T + C - 1) / C;
     const long long nblk = (long long)a.B * a.HV * NC;
-    hipLaunchKernelGGL((chunk_prep_kernel<TIn, DK, C>), dim3((unsigned)nblk), dim3(256), 0,
+    hipLaunchKernelGGL((chunk_prep_kernel<TIn, DK, C>), dim3((unsigned)nblk), dim3(512), 0,
                        (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g, a.beta,
                        (unsigned char*)a.workspace, a.T, a.HK, a.HV, NC);
     return hipGetLastError();
