@@ -30,7 +30,9 @@
  *     GDR_ERR_HIP.  The library never aborts or prints.  NaN/Inf inputs are not checked
  *     and propagate.
  *   - Supported: dk, dv in {32, 64, 128}; chunk in {16, 32, 64}; HV % HK == 0; B, T >= 1;
- *     q/k/v in bf16 or fp32.  Decay values are expected to satisfy g <= 0 with the total
+ *     q/k/v in bf16 or fp32.  Prefill also needs T*HV*dv*4 < 2^31 (one batch element's
+ *     outputs) and ceil(T/chunk) * (workspace bytes per chunk) < 2^31 (one head's chunk
+ *     records); about 130K tokens at HV = 32, dv = 128.  Decay values are expected to satisfy g <= 0 with the total
  *     decay over any 8 consecutive tokens below 80 in every channel (exp(g) >= ~5e-5 per
  *     token); outside that range the prefill path's intra-chunk decay factors can
  *     overflow fp32.  The decode path has no such limit.
@@ -51,7 +53,8 @@ extern "C" {
 typedef enum {
     GDR_OK = 0,
     GDR_ERR_NULL = 1,        /* a required pointer (dims, q, k, v, g, beta, o) is NULL     */
-    GDR_ERR_SHAPE = 2,       /* B/T/HK/HV < 1, HV % HK != 0, decode with T != 1, overflow */
+    GDR_ERR_SHAPE = 2,       /* B/T/HK/HV < 1, HV % HK != 0, decode with T != 1, a size
+                                past the limits below                                      */
     GDR_ERR_UNSUPPORTED = 3, /* dk/dv/chunk/dtype outside the supported set               */
     GDR_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned                   */
     GDR_ERR_ALIAS = 5,       /* o overlaps an input/h0/ht, or ht partially overlaps h0    */
