@@ -5,8 +5,9 @@
 // log-decay prefixes, the beta-folded triangular transform, WY pseudo-keys and
 // pseudo-values, causal query/key terms, then the inter-chunk state carry.  Everything
 // except the carry depends on one chunk only, so this kernel runs it for all
-// (batch, value head, chunk) triples at once -- one 512-thread workgroup each -- and hands
-// the results to the sequential carry kernel as fp16 MFMA operand fragments.
+// (batch, value head, chunk) triples in parallel -- persistent 512-thread workgroups, one
+// item at a time each -- and hands the results to the sequential carry kernel as fp16 MFMA
+// operand fragments.
 //
 // For a chunk of C tokens (rows r, s; gam = inclusive prefix of g inside the chunk):
 //   gram     A_rs = beta_r sum_c k_rc k_sc exp(gam_rc - gam_sc)   (s < r)
@@ -51,8 +52,8 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(const TIn* __restrict__
                                                          const TIn* __restrict__ k,
                                                          const float* __restrict__ g,
                                                          const float* __restrict__ beta,
-                                                         unsigned char* __restrict__ ws, int T,
-                                                         int HK, int HV, int NC) {
+                                                         unsigned char* __restrict__ ws, int B,
+                                                         int T, int HK, int HV, int NC) {
     constexpr int NTH = 512;
     constexpr int NB = C / 16;
     constexpr int NQS = (C + 31) / 32;
@@ -84,19 +85,57 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(const TIn* __restrict__
     float* sZi = sZZ + C * ZP;
     float* sT = sZZ;  // Tinv reuses the Z/Zi area once the gram is done
 
-    const int blk = blockIdx.x;
-    const int n = blk % NC;
-    const int bh = blk / NC;
+    const int tid0 = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+    const int sc = tid0 % DK;     // channel of this thread in the scan
+    const int sseg = tid0 / DK;   // segment of this thread
+    constexpr int VPR = DK / VN;                       // k vectors per row
+    constexpr int KV = (C * VPR + NTH - 1) / NTH;      // k vectors per thread
+
+    // Persistent workgroups: each walks (batch, head, chunk) items with a stride of the
+    // grid and prefetches the next item's g, k and beta into registers while the current
+    // item computes, so neither a workgroup launch nor the input latency sits between items.
+    const int total = B * HV * NC;
+    float gpre[RPS];
+    uint4 kpre[KV];
+    float bpre = 0.f;
+    auto prefetch = [&](int it) {
+        const int pn = it % NC, pbh = it / NC;
+        const int ph = pbh % HV, pb = pbh / HV, pkh = ph / (HV / HK);
+        const int pt0 = pn * C, pL = min(C, T - pt0);
+#pragma unroll
+        for (int m = 0; m < RPS; ++m) {  // unconditional loads from clamped rows, masked later
+            const int r = sseg * RPS + m;
+            gpre[m] = g[(((size_t)pb * T + pt0 + min(r, pL - 1)) * HV + ph) * DK + sc];
+        }
+        const size_t prow0 = (((size_t)pb * T + pt0) * HK + pkh) * DK;
+#pragma unroll
+        for (int i = 0; i < KV; ++i) {
+            const int idx = tid0 + i * NTH;
+            const int r = idx / VPR, cv = idx % VPR;
+            if (idx < C * VPR)
+                kpre[i] = *reinterpret_cast<const uint4*>(k + prow0 + min(r, pL - 1) * (size_t)HK * DK + cv * VN);
+        }
+        if (tid0 < C) bpre = beta[((size_t)pb * T + pt0 + min(tid0, pL - 1)) * HV + ph];
+    };
+    if (blockIdx.x < total) prefetch(blockIdx.x);
+
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    // Lane indices are laundered through an empty asm each iteration: otherwise the
+    // compiler hoists every per-lane LDS address of the (fully unrolled) body out of the
+    // loop and keeps them all live, which overflows the register file.
+    int tid = tid0;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int li = lane & 15;
+    const int gq = lane >> 4;
+    const int n = item % NC;
+    const int bh = item / NC;
     const int h = bh % HV;
     const int b = bh / HV;
     const int kh = h / (HV / HK);
     const int t0 = n * C;
     const int L = min(C, T - t0);
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int li = lane & 15;
-    const int gq = lane >> 4;
 
     unsigned char* rec = ws + (size_t)((size_t)bh * NC + n) * R.bytes;
     half8* frags = reinterpret_cast<half8*>(rec);
@@ -106,35 +145,25 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(const TIn* __restrict__
 
     // ---- 1. g -> per-channel inclusive prefix (two-level scan); k rows and beta -> LDS ----
     float gam_loc[RPS];
-    const int sc = tid % DK;     // channel of this thread in the scan
-    const int sseg = tid / DK;   // segment of this thread
     {
-#pragma unroll
-        for (int m = 0; m < RPS; ++m) {  // unconditional loads from clamped rows, then mask
-            const int r = sseg * RPS + m;
-            const float gv = g[(((size_t)b * T + t0 + min(r, L - 1)) * HV + h) * DK + sc];
-            gam_loc[m] = r < L ? gv : 0.f;
-        }
         float acc = 0.f;
 #pragma unroll
         for (int m = 0; m < RPS; ++m) {
-            acc += gam_loc[m];
+            const int r = sseg * RPS + m;
+            acc += r < L ? gpre[m] : 0.f;
             gam_loc[m] = acc;
         }
         sSeg[sseg * DK + sc] = acc;
-
-        constexpr int VPR = DK / VN;  // vectors per row
-        for (int idx = tid; idx < C * VPR; idx += NTH) {
-            const int r = idx / VPR;
-            const int cv = idx % VPR;
-            uint4 kv = *reinterpret_cast<const uint4*>(k + qk_row0 + min(r, L - 1) * qk_rstride + cv * VN);
-            if (r >= L) kv = uint4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<uint4*>(&sK[r * XP + cv * VN]) = kv;
+#pragma unroll
+        for (int i = 0; i < KV; ++i) {
+            const int idx = tid + i * NTH;
+            const int r = idx / VPR, cv = idx % VPR;
+            if (idx < C * VPR) {
+                const uint4 kv = r < L ? kpre[i] : uint4{0u, 0u, 0u, 0u};
+                *reinterpret_cast<uint4*>(&sK[r * XP + cv * VN]) = kv;
+            }
         }
-        if (tid < C) {
-            const float bv = beta[((size_t)b * T + t0 + min(tid, L - 1)) * HV + h];
-            sBeta[tid] = tid < L ? bv : 0.f;
-        }
+        if (tid < C) sBeta[tid] = tid < L ? bpre : 0.f;
     }
     __syncthreads();
     {
@@ -226,12 +255,26 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(const TIn* __restrict__
     };
 
     // ---- 3. carry operands: Qt and Kb^T fragments; exp(gam) k fragments for W ------------
-    for (int f = wave; f < NB * KC; f += NTH / 64) {
+    static_assert((NB * KC) % (NTH / 64) == 0 || NB * KC < NTH / 64, "Qt fragments per wave");
+    constexpr int QT_PER_WAVE = (NB * KC + NTH / 64 - 1) / (NTH / 64);
+    float qx[QT_PER_WAVE][4], qy[QT_PER_WAVE][4];  // all q loads issued first
+#pragma unroll
+    for (int i = 0; i < QT_PER_WAVE; ++i) {
+        const int f = wave + i * (NTH / 64);
+        if (f < NB * KC) {
+            const int rt = f / KC, p = f % KC;
+            q4(16 * rt + li, 32 * p + 4 * gq, qx[i]);       // slots 0..3: channels 32p + 4gq + 0..3
+            q4(16 * rt + li, 32 * p + 16 + 4 * gq, qy[i]);  // slots 4..7: channels 32p + 16 + 4gq + ..
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < QT_PER_WAVE; ++i) {
+        const int f = wave + i * (NTH / 64);
+        if (f >= NB * KC) break;
         const int rt = f / KC, p = f % KC;
         const int r = 16 * rt + li;
-        float x[4], y[4];
-        q4(r, 32 * p + 4 * gq, x);       // slots 0..3 <- channels 32p + 4gq + 0..3
-        q4(r, 32 * p + 16 + 4 * gq, y);  // slots 4..7 <- channels 32p + 16 + 4gq + 0..3
+        const float (&x)[4] = qx[i];
+        const float (&y)[4] = qy[i];
         half8 o8;
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
@@ -373,6 +416,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(const TIn* __restrict__
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
+            asm volatile("" ::: "memory");  // load row i just before use (bounds register use)
             float s = (i == j) ? 1.f : 0.f;
 #pragma unroll
             for (int kk = 0; kk < i; ++kk) s -= sA[(base + i) * AP + base + kk] * x[kk];
@@ -406,6 +450,10 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(const TIn* __restrict__
         }
         __syncthreads();
     }
+
+    // the next item's inputs: issued here (register pressure is low from now on) and
+    // landing while this item finishes
+    if (item + (int)gridDim.x < total) prefetch(item + gridDim.x);
 
     // ---- 7. Tb = Tinv diag(beta) fragments ----------------------------------------------
     for (int f = wave; f < R.ntri; f += NTH / 64) {
@@ -444,15 +492,32 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(const TIn* __restrict__
             x[jj] = static_cast<_Float16>(-((jj >> 2) ? acc1[jj & 3] : acc0[jj & 3]));
         frags[(size_t)(R.off_w + rt * KC + wp) * 64 + lane] = x;
     }
+    __syncthreads();  // the next item overwrites this item's LDS
+    }
 }
 
 template <typename TIn, int DK, int C>
 static hipError_t launch_prep_t(const LaunchArgs& a) {
     const int NC = (a.T + C - 1) / C;
-    const long long nblk = (long long)a.B * a.HV * NC;
+    const long long items = (long long)a.B * a.HV * NC;
+    // one persistent workgroup per resident slot (occupancy x CUs of the current device)
+    static thread_local int cached_dev = -1, cached_slots = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (dev != cached_dev) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return hipErrorInvalidDevice;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunk_prep_kernel<TIn, DK, C>, 512, 0) !=
+            hipSuccess)
+            return hipErrorInvalidDevice;
+        cached_slots = cus * (per_cu > 0 ? per_cu : 1);
+        cached_dev = dev;
+    }
+    const long long nblk = items < cached_slots ? items : cached_slots;
     hipLaunchKernelGGL((chunk_prep_kernel<TIn, DK, C>), dim3((unsigned)nblk), dim3(512), 0,
                        (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g, a.beta,
-                       (unsigned char*)a.workspace, a.T, a.HK, a.HV, NC);
+                       (unsigned char*)a.workspace, a.B, a.T, a.HK, a.HV, NC);
     return hipGetLastError();
 }
 
