@@ -5,130 +5,457 @@
 // log-decay prefixes, the beta-folded triangular transform, WY pseudo-keys and
 // pseudo-values, causal query/key terms, then the inter-chunk state carry.  Everything
 // except the carry depends on one chunk only, so this kernel runs it for all
-// (batch, value head, chunk) triples in parallel -- persistent 512-thread workgroups, one
-// item at a time each -- and hands the results to the sequential carry kernel as fp16 MFMA
-// operand fragments.
+// (batch, value head, chunk) triples in parallel and hands the results to the sequential
+// carry kernel as fp16 MFMA operand fragments (see ChunkRecord).
 //
 // For a chunk of C tokens (rows r, s; gam = inclusive prefix of g inside the chunk):
 //   gram     A_rs = beta_r sum_c k_rc k_sc exp(gam_rc - gam_sc)   (s < r)
 //   causal   P_rs =        sum_c q_rc k_sc exp(gam_rc - gam_sc)   (s <= r)
 //   solve    Tinv = (I + A)^-1 by exact 16x16-block forward substitution (the block TRSM
-//            of uzu PR #576, "Support TreeUpdateSolve kernel", done in fp32 in LDS)
+//            of uzu PR #576, "Support TreeUpdateSolve kernel", here on fp32 matrix cores)
 //   WY       Tb = Tinv diag(beta);  W = Tb (exp(gam) * K)           (pseudo-keys)
 //   carry    Qt = exp(gam) * Q;  Kb = exp(gam_last - gam) * K;  exp(gam_last)
-// Outputs per chunk (see ChunkRecord): Qt, -W, Kb^T, Tb, P as fragments, exp(gam_last).
 //
-// Decay factors.  Every factor is built from two per-element exponentials around the
-// middle row m_I = 16I + 7 of the element's 16-row block I,
-//   Z_rc = exp(gam_rc - gam_{m_I,c}),   Zi_rc = exp(gam_{m_I,c} - gam_rc),
-// and per-(block, channel) constants, so no operand leaves its format's range:
-//   blocks J < I (fp16):  exp(gam_r - gam_s) = [Z_r a_I] [Zi_s b_J] E_IJ, where
-//       a_I = exp(gam_m - gam_{16I-1}), b_J = exp(gam_{16J+15} - gam_m),
-//       E_IJ = exp(gam_{16I-1} - gam_{16J+15}); both bracketed factors are <= 1;
-//   diagonal blocks (bf16 hi + lo split, three products, fp32 range, ~16 bits):
-//       exp(gam_r - gam_s) = Z_r Zi_s;
-//   Qt = q Z G_I, Kb = k Zi L_I, exp(gam) k = k Z G_I with G_I = exp(gam_m),
-//       L_I = exp(gam_last - gam_m).
+// Work split.  One workgroup per chunk, one wave per 16-row block I.  Lane (i, g) of wave
+// I (i = lane % 16, g = lane / 16) owns token row 16I + i and, for every 32-channel step
+// p, the eight key channels 32p + perm_slot(g, 0..7): exactly the slots of an MFMA
+// operand fragment.  So the decay prefix is a 16-lane DPP scan, the carry operands Qt
+// are stored straight from registers, and the block's own gram and causal tiles come out
+// of its registers.  Accumulator tiles land in "row layout" (lane (i, g) holds row i,
+// columns 4g..4g+3), which is again the fragment slot order of the token-reduction
+// operands Tb and P.  LDS carries only what crosses waves: block totals of the prefix,
+// the key-side operands of the off-diagonal gram blocks, the transposed key tiles of the
+// token reductions (W and Kb), and the blocks of Tinv during the solve.
+//
+// Decay factors (log2 units; every exponential is a hardware exp2).  Inside block I,
+//   Z_r = exp(gam_r - gam_m), Zi_r = 1 / Z_r   (m = 16I + 7, the block's middle row)
+// for the diagonal tiles (bf16 hi + lo split, three products, fp32 range, ~16 bits);
+// off-diagonal tiles J < I use, in fp16 and with both factors <= 1 while g <= 0,
+//   key side   k_s exp(gam_{16J+15} - gam_s)
+//   row side   k_r exp(gam_r - gam_{16I-1}) * exp(gam_{16I-1} - gam_{16J+15}).
 // Z and Zi stay finite while the decay over 8 consecutive tokens of a block is below ~88
 // (mean g above about -11 per token), the range documented in gdr.h.
 #include "gdr_device.h"
 #include "gdr_launch.h"
 
 namespace gdr {
+namespace {
 
+constexpr float kLog2e = 1.4426950408889634f;
+
+// x from lane (row lane - N) of the same 16-lane DPP row, 0 for the first N lanes.
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 0x110 + N, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// D(16x16) += A(16x4) B(4x16) in fp32.  Lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16]; D as for the fp16 products.
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Four consecutive input elements of one row, widened to fp32 on use.
 template <typename TIn>
-struct VecLoad;
+struct In4;
 template <>
-struct VecLoad<float> {
-    static constexpr int N = 4;
+struct In4<bf16_t> {
+    uint2 u;
+    __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ float operator[](int e) const {
+        const uint32_t w = e < 2 ? u.x : u.y;
+        return (e & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+    }
 };
 template <>
-struct VecLoad<bf16_t> {
-    static constexpr int N = 8;
+struct In4<float> {
+    float4 u;
+    __device__ __forceinline__ void load(const float* p) { u = *reinterpret_cast<const float4*>(p); }
+    __device__ __forceinline__ float operator[](int e) const {
+        return e == 0 ? u.x : e == 1 ? u.y : e == 2 ? u.z : u.w;
+    }
 };
 
-template <typename TIn, int DK, int C>
-__global__ __launch_bounds__(512) void chunk_prep_kernel(const TIn* __restrict__ q,
-                                                         const TIn* __restrict__ k,
-                                                         const float* __restrict__ g,
-                                                         const float* __restrict__ beta,
-                                                         unsigned char* __restrict__ ws, int B,
-                                                         int T, int HK, int HV, int NC) {
-    constexpr int NTH = 512;
+__device__ __forceinline__ float f4(const float4& v, int e) {
+    return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+}
+
+// Eight fp16 values: lo = 4 halves at p, hi = 4 halves at p + 16 (or zero).
+__device__ __forceinline__ half8 lds_pair4(const _Float16* p, bool hi_valid) {
+    const uint2 lo = *reinterpret_cast<const uint2*>(p);
+    const uint2 hi = hi_valid ? *reinterpret_cast<const uint2*>(p + 16) : uint2{0u, 0u};
+    return __builtin_bit_cast(half8, uint4{lo.x, lo.y, hi.x, hi.y});
+}
+
+template <int DK, int C>
+struct PrepLds {
+    static constexpr int NB = C / 16;
+    static constexpr int KC = DK / 32;
+    static constexpr int KTP = C + 8;  // halves per channel row of a transposed key tile
+    static constexpr int TTP = C + 4;  // floats per row of the transposed inverse
+    static constexpr int SZ_KT = DK * KTP * 2;
+    static constexpr int SZ_AS = (NB > 1 ? NB - 1 : 1) * KC * 1024;
+    static constexpr int SZ_TT = C * TTP * 4;
+    static constexpr int SZ_AT = NB * 256 * 4;
+    static constexpr int SZ_U = (SZ_KT + SZ_AS > SZ_TT + SZ_AT) ? SZ_KT + SZ_AS : SZ_TT + SZ_AT;
+};
+
+struct PrepCtx {
+    _Float16* sKT;   // (exp(gam) k)^T          [channel][token]  (gram, W)
+    _Float16* sKbT;  // (exp(gL - gam) k)^T     [channel][token]  (Kb)         } phase 2-3
+    half8* sAs;      // off-diagonal key-side fragments [J][p][lane]           }
+    float* sTT;      // Tinv^T                  [token s][token r]             } solve
+    float* sAT;      // diagonal gram blocks, transposed [I][j][k] = A_II[k][j] }
+    float* sTot;     // per-block prefix totals [I][channel]
+    float* sMid;     // per-block prefix at the middle row [I][channel]
+    float* sBeta;    // beta per row (0 past the chunk end)
+};
+
+// The whole per-chunk computation as seen by wave I (a compile-time block index, so that
+// every per-block register array is indexed statically).  All waves pass the same number
+// of workgroup barriers.
+template <typename TIn, int DK, int C, int I>
+__device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restrict__ q,
+                                          const TIn* __restrict__ k, const float* __restrict__ g,
+                                          const float* __restrict__ beta, unsigned char* rec, int b,
+                                          int T, int HK, int HV, int h, int kh, int t0, int L) {
     constexpr int NB = C / 16;
-    constexpr int NQS = (C + 31) / 32;
     constexpr int KC = DK / 32;
     constexpr int DKT = DK / 16;
-    constexpr int ZP = DK + 4;        // padded fp32 row (Z, Zi)
-    constexpr int VN = VecLoad<TIn>::N;
-    constexpr int XP = DK + VN;       // padded input row (k)
-    constexpr int AP = C + 4;         // padded fp32 row (A, Tinv)
-    constexpr int NSEG = NTH / DK;    // scan segments per channel
-    constexpr int RPS = C / NSEG;     // rows per segment
-    constexpr int NOFF = NB * (NB - 1) / 2;
-    static_assert(RPS >= 1 && C % NSEG == 0, "chunk too short for this key dim");
+    constexpr int NQS = (C + 31) / 32;
+    constexpr int KTP = PrepLds<DK, C>::KTP;
+    constexpr int TTP = PrepLds<DK, C>::TTP;
     constexpr ChunkRecord R = ChunkRecord::make(C, DK);
+    constexpr int NT = I / 2 + 1;  // token reduction steps of row tile I
 
-    // LDS.  Z/Zi are dead once the gram and the carry operands are formed; Tinv reuses them.
-    constexpr int NZZ = (2 * C * ZP > C * AP) ? 2 * C * ZP : C * AP;
-    __shared__ float sZZ[NZZ];
-    __shared__ TIn sK[C * XP];
-    __shared__ float sA[C * AP];
-    __shared__ _Float16 sP[C * C];
-    __shared__ float sRef[NB * 3 * DK];      // gam at rows 16I-1, 16I+7, 16I+15
-    __shared__ float sCa[NB * DK], sCb[NB * DK], sCg[NB * DK], sCl[NB * DK];
-    __shared__ float sCe[(NOFF > 0 ? NOFF : 1) * DK];
-    __shared__ float sSeg[NSEG * DK];
-    __shared__ float sBeta[C];
-    __shared__ float sY[(NB > 1 ? NB - 1 : 1) * 256];
-    float* sZ = sZZ;
-    float* sZi = sZZ + C * ZP;
-    float* sT = sZZ;  // Tinv reuses the Z/Zi area once the gram is done
-
-    const int tid0 = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
-    const int sc = tid0 % DK;     // channel of this thread in the scan
-    const int sseg = tid0 / DK;   // segment of this thread
-    constexpr int VPR = DK / VN;                       // k vectors per row
-    constexpr int KV = (C * VPR + NTH - 1) / NTH;      // k vectors per thread
-
-    // Persistent workgroups: each walks (batch, head, chunk) items with a stride of the
-    // grid and prefetches the next item's g, k and beta into registers while the current
-    // item computes, so neither a workgroup launch nor the input latency sits between items.
-    const int total = B * HV * NC;
-    float gpre[RPS];
-    uint4 kpre[KV];
-    float bpre = 0.f;
-    auto prefetch = [&](int it) {
-        const int pn = it % NC, pbh = it / NC;
-        const int ph = pbh % HV, pb = pbh / HV, pkh = ph / (HV / HK);
-        const int pt0 = pn * C, pL = min(C, T - pt0);
-#pragma unroll
-        for (int m = 0; m < RPS; ++m) {  // unconditional loads from clamped rows, masked later
-            const int r = sseg * RPS + m;
-            gpre[m] = g[(((size_t)pb * T + pt0 + min(r, pL - 1)) * HV + ph) * DK + sc];
-        }
-        const size_t prow0 = (((size_t)pb * T + pt0) * HK + pkh) * DK;
-#pragma unroll
-        for (int i = 0; i < KV; ++i) {
-            const int idx = tid0 + i * NTH;
-            const int r = idx / VPR, cv = idx % VPR;
-            if (idx < C * VPR)
-                kpre[i] = *reinterpret_cast<const uint4*>(k + prow0 + min(r, pL - 1) * (size_t)HK * DK + cv * VN);
-        }
-        if (tid0 < C) bpre = beta[((size_t)pb * T + pt0 + min(tid0, pL - 1)) * HV + ph];
-    };
-    if (blockIdx.x < total) prefetch(blockIdx.x);
-
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    // Lane indices are laundered through an empty asm each iteration: otherwise the
-    // compiler hoists every per-lane LDS address of the (fully unrolled) body out of the
-    // loop and keeps them all live, which overflows the register file.
-    int tid = tid0;
-    asm volatile("" : "+v"(tid));
-    const int lane = tid & 63;
+    const int lane = threadIdx.x & 63;
     const int li = lane & 15;
     const int gq = lane >> 4;
+    const int r = 16 * I + li;
+    const bool rv = r < L;
+    const int rc = rv ? r : L - 1;
+    const size_t tok = (size_t)b * T + t0 + rc;
+    const float* grow = g + (tok * HV + h) * DK;
+    const TIn* krow = k + (tok * HK + kh) * DK;
+    const TIn* qrow = q + (tok * HK + kh) * DK;
+    half8* frags = reinterpret_cast<half8*>(rec);
+
+    // ---- 1. loads (clamped rows, masked), g -> log2 units, 16-row inclusive scan ---------
+    float x[KC][8];
+    In4<TIn> kin[KC][2], qin[KC][2];
+#pragma unroll
+    for (int p = 0; p < KC; ++p)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int cb = 32 * p + 16 * hh + 4 * gq;
+            const float4 gv = *reinterpret_cast<const float4*>(grow + cb);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[p][4 * hh + e] = f4(gv, e);
+            kin[p][hh].load(krow + cb);
+            qin[p][hh].load(qrow + cb);
+        }
+    const float bta = rv ? beta[tok * HV + h] : 0.f;
+#pragma unroll
+    for (int p = 0; p < KC; ++p)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            float v = rv ? x[p][jj] * kLog2e : 0.f;
+            v += row_shr<1>(v);
+            v += row_shr<2>(v);
+            v += row_shr<4>(v);
+            v += row_shr<8>(v);
+            x[p][jj] = v;  // local prefix P_r (log2 units) through row r of the block
+        }
+    if (li == 15 || li == 7) {
+        float* dst = (li == 15 ? s.sTot : s.sMid) + I * DK;
+#pragma unroll
+        for (int p = 0; p < KC; ++p)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                *reinterpret_cast<float4*>(dst + 32 * p + 16 * hh + 4 * gq) =
+                    float4{x[p][4 * hh], x[p][4 * hh + 1], x[p][4 * hh + 2], x[p][4 * hh + 3]};
+    }
+    if (gq == 0) s.sBeta[r] = bta;
+    lds_barrier();  // B1
+
+    // ---- 2. factors; Qt; transposed key tiles; key-side fragments; diagonal gram ---------
+    f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+    half8 bk[KC], bq[KC];  // row-side operands of the off-diagonal tiles (I > 0)
+    float* egl_out = reinterpret_cast<float*>(rec + (size_t)R.nfrag * 1024);
+#pragma unroll
+    for (int p = 0; p < KC; ++p) {
+        asm volatile("" ::: "memory");  // keep this step's LDS reads here (register pressure)
+        float off[8], gl[8], ti[8], md[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int cb = 32 * p + 16 * hh + 4 * gq;
+            const float4 m4 = *reinterpret_cast<const float4*>(s.sMid + I * DK + cb);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                md[4 * hh + e] = f4(m4, e);
+                off[4 * hh + e] = 0.f;
+                gl[4 * hh + e] = 0.f;
+            }
+#pragma unroll
+            for (int J = 0; J < NB; ++J) {
+                const float4 t4 = *reinterpret_cast<const float4*>(s.sTot + J * DK + cb);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = f4(t4, e);
+                    gl[4 * hh + e] += v;
+                    if (J < I) off[4 * hh + e] += v;
+                    if (J == I) ti[4 * hh + e] = v;
+                }
+            }
+        }
+        half8 qt, as;
+        bf16x8 ah, al, kzh, kzl, qzh, qzl;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const int hh = jj >> 2, e = jj & 3;
+            const int c = 32 * p + 16 * hh + 4 * gq + e;
+            const float P = x[p][jj];
+            const float kv = rv ? kin[p][hh][e] : 0.f;
+            const float qv = rv ? qin[p][hh][e] : 0.f;
+            const float z = ex2(P - md[jj]);
+            const float zi = ex2(md[jj] - P);
+            const float eg = ex2(off[jj] + P);
+            const float ek = ex2(gl[jj] - off[jj] - P);
+            qt[jj] = static_cast<_Float16>(qv * eg);
+            s.sKT[c * KTP + r] = static_cast<_Float16>(kv * eg);
+            s.sKbT[c * KTP + r] = static_cast<_Float16>(kv * ek);
+            __bf16 hi, lo;
+            split_bf16(kv * zi, hi, lo);
+            ah[jj] = hi;
+            al[jj] = lo;
+            split_bf16(kv * z, hi, lo);
+            kzh[jj] = hi;
+            kzl[jj] = lo;
+            split_bf16(qv * z, hi, lo);
+            qzh[jj] = hi;
+            qzl[jj] = lo;
+            if constexpr (I > 0) {
+                const float zs = ex2(P);
+                bk[p][jj] = static_cast<_Float16>(kv * zs);
+                bq[p][jj] = static_cast<_Float16>(qv * zs);
+            }
+            if constexpr (I < NB - 1) as[jj] = static_cast<_Float16>(kv * ex2(ti[jj] - P));
+        }
+        frags[(size_t)(R.off_qt + I * KC + p) * 64 + lane] = qt;
+        if constexpr (I < NB - 1) s.sAs[(I * KC + p) * 64 + lane] = as;
+        accA = mfma_bf16(ah, kzh, accA);
+        accA = mfma_bf16(al, kzh, accA);
+        accA = mfma_bf16(ah, kzl, accA);
+        accP = mfma_bf16(ah, qzh, accP);
+        accP = mfma_bf16(al, qzh, accP);
+        accP = mfma_bf16(ah, qzl, accP);
+        if (I == 0 && li == 0) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                *reinterpret_cast<float4*>(egl_out + 32 * p + 16 * hh + 4 * gq) =
+                    float4{ex2(gl[4 * hh]), ex2(gl[4 * hh + 1]), ex2(gl[4 * hh + 2]), ex2(gl[4 * hh + 3])};
+        }
+    }
+    lds_barrier();  // B2
+
+    // ---- 3. off-diagonal gram tiles; Kb and P fragments ---------------------------------
+    // aR[J], pR[J]: rows of block I against the columns of block J, in row layout.
+    f32x4 aR[I + 1], pR[I + 1];
+    aR[I] = accA;
+    pR[I] = accP;
+#pragma unroll
+    for (int J = 0; J < I; ++J) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f}, pc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < KC; ++p) {
+            half8 ok = bk[p], oq = bq[p];
+            if (J < I - 1) {
+                // blocks between J and I: scale by exp(gam_{16I-1} - gam_{16J+15})
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int cb = 32 * p + 16 * hh + 4 * gq;
+                    float ex[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int M = J + 1; M < I; ++M) {
+                        const float4 t4 = *reinterpret_cast<const float4*>(s.sTot + M * DK + cb);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ex[e] += f4(t4, e);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float f = ex2(ex[e]);
+                        ok[4 * hh + e] = static_cast<_Float16>(static_cast<float>(ok[4 * hh + e]) * f);
+                        oq[4 * hh + e] = static_cast<_Float16>(static_cast<float>(oq[4 * hh + e]) * f);
+                    }
+                }
+            }
+            const half8 ak = s.sAs[(J * KC + p) * 64 + lane];
+            a = mfma_f16(ak, ok, a);
+            pc = mfma_f16(ak, oq, pc);
+        }
+        aR[J] = a;
+        pR[J] = pc;
+    }
+#pragma unroll
+    for (int f = I; f < DKT * NQS; f += NB) {
+        const int ct = f / NQS, qs = f % NQS;
+        frags[(size_t)(R.off_kb + f) * 64 + lane] =
+            lds_pair4(s.sKbT + (16 * ct + li) * KTP + 32 * qs + 4 * gq, C > 16);
+    }
+#pragma unroll
+    for (int J = 0; J <= I; ++J)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int sl = 4 * gq + i;
+            aR[J][i] = (J < I || sl < li) ? aR[J][i] * bta : 0.f;
+            pR[J][i] = (J < I || sl <= li) ? pR[J][i] : 0.f;
+        }
+#pragma unroll
+    for (int qs = 0; qs < NT; ++qs) {
+        half8 v;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const int J = 2 * qs + (jj >> 2);
+            v[jj] = J <= I ? static_cast<_Float16>(pR[J <= I ? J : I][jj & 3]) : static_cast<_Float16>(0.f);
+        }
+        frags[(size_t)(R.off_p + ChunkRecord::tri_base(I) + qs) * 64 + lane] = v;
+    }
+    lds_barrier();  // B3: the key-side fragments and the Kb tile are dead; solve area live
+
+    // ---- 4. diagonal block inverse, rows by lane: T_II = (I + A_II)^-1 ----------------------
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s.sAT[I * 256 + (4 * gq + i) * 16 + li] = aR[I][i];
+    asm volatile("" ::: "memory");
+    float t[16];
+#pragma unroll
+    for (int j = 15; j >= 0; --j) {
+        float acc = (j == li) ? 1.f : 0.f;
+        const float* col = s.sAT + I * 256 + j * 16;  // A_II[kk][j] for kk = 0..15
+#pragma unroll
+        for (int kk = j + 1; kk < 16; ++kk) acc -= t[kk] * col[kk];
+        t[j] = acc;
+        asm volatile("" : "+v"(t[j])::"memory");  // finish row j before reading the next column
+    }
+    // publish T_II into Tinv^T (one lane group), then read it back in row layout:
+    // lane (i, g) holds T_II[i][4g .. 4g+3]
+    if (gq == 0) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s.sTT[(16 * I + j) * TTP + 16 * I + li] = t[j];
+    }
+    asm volatile("" ::: "memory");
+    float tR[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tR[i] = s.sTT[(16 * I + 4 * gq + i) * TTP + 16 * I + li];
+    lds_barrier();  // B4
+
+    // ---- 5. off-diagonal inverse blocks, one block row per stage ------------------------
+    //   T_IJ = -T_II sum_{M=J}^{I-1} A_IM T_MJ; stage d finishes block row d.  Products run on
+    //   the fp32 matrix cores: the row-layout A_IM is the A operand and column-layout T_MJ
+    //   (lane (j, g) holds T_MJ[4g .. 4g+3][j], read from Tinv^T) the B operand, with
+    //   reduction index 4g + kk in step kk, so accumulators come out in column layout.
+    f32x4 Y[I > 0 ? I : 1];
+#pragma unroll
+    for (int J = 0; J < I; ++J) Y[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Tb fragments and pseudo-keys of block row I, once that row of Tinv is final
+    auto finish_row = [&]() {
+        half8 tb[NT];
+#pragma unroll
+        for (int qs = 0; qs < NT; ++qs) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int J = 2 * qs + hh;
+                if (J > I) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) tb[qs][4 * hh + i] = static_cast<_Float16>(0.f);
+                } else {
+                    const float4 b4 = *reinterpret_cast<const float4*>(s.sBeta + 16 * J + 4 * gq);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float tv = (J == I) ? tR[i] : s.sTT[(16 * J + 4 * gq + i) * TTP + 16 * I + li];
+                        tb[qs][4 * hh + i] = static_cast<_Float16>(tv * f4(b4, i));
+                    }
+                }
+            }
+            frags[(size_t)(R.off_tb + ChunkRecord::tri_base(I) + qs) * 64 + lane] = tb[qs];
+        }
+        // W^T = (exp(gam) K)^T Tb^T: A operand from the transposed key tile, B operand Tb
+#pragma unroll
+        for (int p = 0; p < KC; ++p) {
+            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int qs = 0; qs < NT; ++qs) {
+                const half8 k0 = lds_pair4(s.sKT + (32 * p + li) * KTP + 32 * qs + 4 * gq, C > 16);
+                const half8 k1 = lds_pair4(s.sKT + (32 * p + 16 + li) * KTP + 32 * qs + 4 * gq, C > 16);
+                a0 = mfma_f16(k0, tb[qs], a0);
+                a1 = mfma_f16(k1, tb[qs], a1);
+            }
+            half8 w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                w[i] = static_cast<_Float16>(-a0[i]);
+                w[4 + i] = static_cast<_Float16>(-a1[i]);
+            }
+            frags[(size_t)(R.off_w + I * KC + p) * 64 + lane] = w;
+        }
+    };
+
+#pragma unroll
+    for (int d = 1; d < NB; ++d) {
+        if (I >= d) {
+            const int M = d - 1;
+#pragma unroll
+            for (int J = 0; J <= M; ++J) {
+                const f32x4 tm = *reinterpret_cast<const f32x4*>(s.sTT + (16 * J + li) * TTP + 16 * M + 4 * gq);
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) Y[J] = mfma_f32(aR[M][kk], tm[kk], Y[J]);
+            }
+            if (I == d) {
+#pragma unroll
+                for (int J = 0; J < I; ++J) {
+                    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) z = mfma_f32(tR[kk], Y[J][kk], z);
+                    *reinterpret_cast<f32x4*>(s.sTT + (16 * J + li) * TTP + 16 * I + 4 * gq) = -z;
+                }
+                asm volatile("" ::: "memory");
+            }
+        }
+        if (I == d - 1) finish_row();
+        if (d < NB - 1) lds_barrier();
+    }
+    if constexpr (I == NB - 1) finish_row();
+}
+
+template <typename TIn, int DK, int C>
+__global__ __launch_bounds__(C * 4, 2) void chunk_prep_kernel(const TIn* __restrict__ q,
+                                                              const TIn* __restrict__ k,
+                                                              const float* __restrict__ g,
+                                                              const float* __restrict__ beta,
+                                                              unsigned char* __restrict__ ws, int B,
+                                                              int T, int HK, int HV, int NC) {
+    using Lds = PrepLds<DK, C>;
+    constexpr int NB = C / 16;
+    constexpr ChunkRecord R = ChunkRecord::make(C, DK);
+    __shared__ __align__(16) _Float16 sKT[DK * Lds::KTP];
+    __shared__ __align__(16) float sTot[NB * DK];
+    __shared__ __align__(16) float sMid[NB * DK];
+    __shared__ __align__(16) float sBeta[C];
+    __shared__ __align__(16) unsigned char sU[Lds::SZ_U];
+    PrepCtx s;
+    s.sKT = sKT;
+    s.sKbT = reinterpret_cast<_Float16*>(sU);
+    s.sAs = reinterpret_cast<half8*>(sU + Lds::SZ_KT);
+    s.sTT = reinterpret_cast<float*>(sU);
+    s.sAT = reinterpret_cast<float*>(sU + Lds::SZ_TT);
+    s.sTot = sTot;
+    s.sMid = sMid;
+    s.sBeta = sBeta;
+
+    const int item = blockIdx.x;
     const int n = item % NC;
     const int bh = item / NC;
     const int h = bh % HV;
@@ -136,393 +463,30 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(const TIn* __restrict__
     const int kh = h / (HV / HK);
     const int t0 = n * C;
     const int L = min(C, T - t0);
-
-    unsigned char* rec = ws + (size_t)((size_t)bh * NC + n) * R.bytes;
-    half8* frags = reinterpret_cast<half8*>(rec);
-    float* egl_out = reinterpret_cast<float*>(rec + (size_t)R.nfrag * 1024);
-    const size_t qk_row0 = (((size_t)b * T + t0) * HK + kh) * DK;  // row r at qk_row0 + r*HK*DK
-    const size_t qk_rstride = (size_t)HK * DK;
-
-    // ---- 1. g -> per-channel inclusive prefix (two-level scan); k rows and beta -> LDS ----
-    float gam_loc[RPS];
-    {
-        float acc = 0.f;
-#pragma unroll
-        for (int m = 0; m < RPS; ++m) {
-            const int r = sseg * RPS + m;
-            acc += r < L ? gpre[m] : 0.f;
-            gam_loc[m] = acc;
-        }
-        sSeg[sseg * DK + sc] = acc;
-#pragma unroll
-        for (int i = 0; i < KV; ++i) {
-            const int idx = tid + i * NTH;
-            const int r = idx / VPR, cv = idx % VPR;
-            if (idx < C * VPR) {
-                const uint4 kv = r < L ? kpre[i] : uint4{0u, 0u, 0u, 0u};
-                *reinterpret_cast<uint4*>(&sK[r * XP + cv * VN]) = kv;
-            }
-        }
-        if (tid < C) sBeta[tid] = tid < L ? bpre : 0.f;
+    unsigned char* rec = ws + ((size_t)bh * NC + n) * R.bytes;
+    const int I = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#define GDR_WAVE(I_)                                                                             \
+    if (I == I_) {                                                                               \
+        if constexpr (I_ < NB)                                                                   \
+            prep_wave<TIn, DK, C, I_>(s, q, k, g, beta, rec, b, T, HK, HV, h, kh, t0, L);        \
+        return;                                                                                  \
     }
-    __syncthreads();
-    {
-        float off = 0.f;
-        for (int s2 = 0; s2 < sseg; ++s2) off += sSeg[s2 * DK + sc];
-#pragma unroll
-        for (int m = 0; m < RPS; ++m) {
-            const int r = sseg * RPS + m;
-            const float gv = gam_loc[m] + off;
-            gam_loc[m] = gv;
-            const int I = r >> 4, rr = r & 15;
-            if (rr == 7) sRef[(I * 3 + 1) * DK + sc] = gv;
-            if (rr == 15) {
-                sRef[(I * 3 + 2) * DK + sc] = gv;
-                if (I + 1 < NB) sRef[((I + 1) * 3 + 0) * DK + sc] = gv;
-            }
-        }
-        if (sseg == 0) sRef[0 * DK + sc] = 0.f;  // the row before the chunk: gam = 0
-    }
-    __syncthreads();
-    // ---- 2. per-element factors Z, Zi and per-(block, channel) constants ----------------
-    {
-#pragma unroll
-        for (int m = 0; m < RPS; ++m) {
-            const int r = sseg * RPS + m;
-            const int I = r >> 4;
-            const float gm = sRef[(I * 3 + 1) * DK + sc];
-            sZ[r * ZP + sc] = __expf(gam_loc[m] - gm);
-            sZi[r * ZP + sc] = __expf(gm - gam_loc[m]);
-        }
-        const float gl = sRef[((NB - 1) * 3 + 2) * DK + sc];  // gam at the last row
-        for (int I = sseg; I < NB; I += NSEG) {
-            const float gp = sRef[(I * 3 + 0) * DK + sc];
-            const float gm = sRef[(I * 3 + 1) * DK + sc];
-            const float ge = sRef[(I * 3 + 2) * DK + sc];
-            sCa[I * DK + sc] = __expf(gm - gp);
-            sCb[I * DK + sc] = __expf(ge - gm);
-            sCg[I * DK + sc] = __expf(gm);
-            sCl[I * DK + sc] = __expf(gl - gm);
-        }
-        for (int pr = sseg; pr < NOFF; pr += NSEG) {
-            int I = 1, base = 0;
-            while (base + I <= pr) base += I++;
-            const int J = pr - base;
-            sCe[pr * DK + sc] = __expf(sRef[(I * 3 + 0) * DK + sc] - sRef[(J * 3 + 2) * DK + sc]);
-        }
-        if (sseg == 0) egl_out[sc] = __expf(gl);
-    }
-    __syncthreads();
-
-    auto kval = [&](int r, int c) { return to_f32(sK[r * XP + c]); };
-    auto qrow = [&](int r) { return q + qk_row0 + min(r, L - 1) * qk_rstride; };
-    // 4 consecutive q values of row r from channel c0 (zero past the chunk end)
-    auto q4 = [&](int r, int c0, float (&x)[4]) {
-        const TIn* p = qrow(r) + c0;
-        if constexpr (VN == 8) {
-            const uint2 u = *reinterpret_cast<const uint2*>(p);
-            x[0] = __uint_as_float(u.x << 16);
-            x[1] = __uint_as_float(u.x & 0xFFFF0000u);
-            x[2] = __uint_as_float(u.y << 16);
-            x[3] = __uint_as_float(u.y & 0xFFFF0000u);
-        } else {
-            const float4 u = *reinterpret_cast<const float4*>(p);
-            x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
-        }
-        if (r >= L) x[0] = x[1] = x[2] = x[3] = 0.f;
-    };
-    // 8 consecutive q values of row r from channel c0 (zero past the chunk end)
-    auto q8 = [&](int r, int c0, float (&x)[8]) {
-        const TIn* p = qrow(r) + c0;
-        if constexpr (VN == 8) {
-            const uint4 u = *reinterpret_cast<const uint4*>(p);
-            const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                x[2 * j] = __uint_as_float(w4[j] << 16);
-                x[2 * j + 1] = __uint_as_float(w4[j] & 0xFFFF0000u);
-            }
-        } else {
-            const float4 u0 = *reinterpret_cast<const float4*>(p);
-            const float4 u1 = *reinterpret_cast<const float4*>(p + 4);
-            x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
-            x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
-        }
-        if (r >= L) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] = 0.f;
-        }
-    };
-
-    // ---- 3. carry operands: Qt and Kb^T fragments; exp(gam) k fragments for W ------------
-    static_assert((NB * KC) % (NTH / 64) == 0 || NB * KC < NTH / 64, "Qt fragments per wave");
-    constexpr int QT_PER_WAVE = (NB * KC + NTH / 64 - 1) / (NTH / 64);
-    float qx[QT_PER_WAVE][4], qy[QT_PER_WAVE][4];  // all q loads issued first
-#pragma unroll
-    for (int i = 0; i < QT_PER_WAVE; ++i) {
-        const int f = wave + i * (NTH / 64);
-        if (f < NB * KC) {
-            const int rt = f / KC, p = f % KC;
-            q4(16 * rt + li, 32 * p + 4 * gq, qx[i]);       // slots 0..3: channels 32p + 4gq + 0..3
-            q4(16 * rt + li, 32 * p + 16 + 4 * gq, qy[i]);  // slots 4..7: channels 32p + 16 + 4gq + ..
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < QT_PER_WAVE; ++i) {
-        const int f = wave + i * (NTH / 64);
-        if (f >= NB * KC) break;
-        const int rt = f / KC, p = f % KC;
-        const int r = 16 * rt + li;
-        const float (&x)[4] = qx[i];
-        const float (&y)[4] = qy[i];
-        half8 o8;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const int c = 32 * p + perm_slot(gq, jj);
-            const float qv = jj < 4 ? x[jj] : y[jj - 4];
-            o8[jj] = static_cast<_Float16>(qv * sZ[r * ZP + c] * sCg[rt * DK + c]);
-        }
-        frags[(size_t)(R.off_qt + f) * 64 + lane] = o8;
-    }
-    for (int f = wave; f < DKT * NQS; f += NTH / 64) {
-        const int ct = f / NQS, qs = f % NQS;
-        const int c = 16 * ct + li;
-        half8 o8;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const int r = 32 * qs + perm_slot(gq, jj);
-            o8[jj] = r < C ? static_cast<_Float16>(kval(r, c) * sZi[r * ZP + c] * sCl[(r >> 4) * DK + c])
-                           : static_cast<_Float16>(0.f);
-        }
-        frags[(size_t)(R.off_kb + f) * 64 + lane] = o8;
-    }
-    // W^T = (exp(gam) K)^T Tb^T is computed by wave w for key-channel step p = w % KC and
-    // row tiles rt = w / KC, w / KC + 8 / KC, ...; its A operand (exp(gam) k, transposed)
-    // is formed now, while Z is still live.
-    constexpr int WW = (NTH / 64) / KC;  // waves per key-channel step (2, 4 or 8)
-    const int wp = wave % KC;
-    half8 ka[2][NQS];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-        const int c = 16 * (2 * wp + h2) + li;
-#pragma unroll
-        for (int qs = 0; qs < NQS; ++qs)
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const int s = 32 * qs + 8 * gq + jj;
-                ka[h2][qs][jj] = s < C ? static_cast<_Float16>(kval(s, c) * sZ[s * ZP + c] * sCg[(s >> 4) * DK + c])
-                                       : static_cast<_Float16>(0.f);
-            }
-    }
-
-    // ---- 4. gram A (-> sA, fp32, times beta_r) and causal terms P (-> sP, fp16) ---------
-    // Work items: the NB diagonal block pairs first (three bf16 products per step), then the
-    // NB(NB-1)/2 off-diagonal pairs (one fp16 product per step), dealt round-robin to waves.
-    // The accumulator holds the transposed tile [s in block J][r in block I].
-    for (int item = wave; item < NB + NOFF; item += NTH / 64) {
-        int I, J, pr = -1;
-        if (item < NB) {
-            I = J = item;
-        } else {
-            pr = item - NB;
-            I = 1;
-            int base = 0;
-            while (base + I <= pr) base += I++;
-            J = pr - base;
-        }
-        const int s = 16 * J + li;  // A-operand row (key side)
-        const int r = 16 * I + li;  // B-operand row (key / query side)
-        f32x4 accA = {0.f, 0.f, 0.f, 0.f};
-        f32x4 accP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int p = 0; p < KC; ++p) {
-            const int c0 = 32 * p + 8 * gq;
-            float qv[8];
-            q8(r, c0, qv);
-            if (I == J) {
-                bf16x8 ah, al, kh_, kl, qh, ql;
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int c = c0 + jj;
-                    __bf16 hi, lo;
-                    split_bf16(kval(s, c) * sZi[s * ZP + c], hi, lo);
-                    ah[jj] = hi;
-                    al[jj] = lo;
-                    const float z = sZ[r * ZP + c];
-                    split_bf16(kval(r, c) * z, hi, lo);
-                    kh_[jj] = hi;
-                    kl[jj] = lo;
-                    split_bf16(qv[jj] * z, hi, lo);
-                    qh[jj] = hi;
-                    ql[jj] = lo;
-                }
-                accA = mfma_bf16(ah, kh_, accA);
-                accA = mfma_bf16(al, kh_, accA);
-                accA = mfma_bf16(ah, kl, accA);
-                accP = mfma_bf16(ah, qh, accP);
-                accP = mfma_bf16(al, qh, accP);
-                accP = mfma_bf16(ah, ql, accP);
-            } else {
-                half8 a, bk, bq;
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int c = c0 + jj;
-                    a[jj] = static_cast<_Float16>(kval(s, c) * sZi[s * ZP + c] * sCb[J * DK + c] * sCe[pr * DK + c]);
-                    const float za = sZ[r * ZP + c] * sCa[I * DK + c];
-                    bk[jj] = static_cast<_Float16>(kval(r, c) * za);
-                    bq[jj] = static_cast<_Float16>(qv[jj] * za);
-                }
-                accA = mfma_f16(a, bk, accA);
-                accP = mfma_f16(a, bq, accP);
-            }
-        }
-        const float br = sBeta[r];
-        f32x4 av;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int sl = 4 * gq + i;
-            const bool lowA = J < I || sl < li;
-            const bool lowP = J < I || sl <= li;
-            av[i] = lowA ? accA[i] * br : 0.f;
-            sP[r * C + 16 * J + sl] = static_cast<_Float16>(lowP ? accP[i] : 0.f);
-        }
-        *reinterpret_cast<f32x4*>(&sA[r * AP + 16 * J + 4 * gq]) = av;
-    }
-    __syncthreads();  // gram done; Z, Zi no longer needed
-
-    // ---- 5. P fragments (block lower triangle) and Tinv := 0 ----------------------------
-    for (int f = wave; f < R.ntri; f += NTH / 64) {
-        int rt = 0;
-        while (ChunkRecord::tri_base(rt + 1) <= f) ++rt;
-        const int qs = f - ChunkRecord::tri_base(rt);
-        const int r = 16 * rt + li;
-        half8 x;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const int sx = 32 * qs + perm_slot(gq, jj);
-            x[jj] = (sx < C && sx <= r) ? sP[r * C + sx] : static_cast<_Float16>(0.f);
-        }
-        frags[(size_t)(R.off_p + f) * 64 + lane] = x;
-    }
-    for (int idx = tid; idx < C * AP; idx += NTH) sT[idx] = 0.f;
-    __syncthreads();
-
-    // ---- 6. block forward substitution: Tinv = (I + A)^-1 ------------------------------
-    // diagonal 16x16 blocks, all at once: lane 16*blk + j of wave 0 solves column j of
-    // block blk by substitution down its 16 rows.
-    if (wave == 0 && (lane >> 4) < NB) {
-        const int base = 16 * (lane >> 4);
-        const int j = lane & 15;
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            asm volatile("" ::: "memory");  // load row i just before use (bounds register use)
-            float s = (i == j) ? 1.f : 0.f;
-#pragma unroll
-            for (int kk = 0; kk < i; ++kk) s -= sA[(base + i) * AP + base + kk] * x[kk];
-            x[i] = s;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sT[(base + i) * AP + base + j] = x[i];
-    }
-    __syncthreads();
-    // off-diagonal blocks by distance d:  Tinv_IJ = -Tinv_II * sum_{M=J}^{I-1} A_IM Tinv_MJ
-#pragma unroll
-    for (int d = 1; d < NB; ++d) {
-        const int e = tid & 255, ii = e >> 4, jj = e & 15;
-        for (int I = d + (tid >> 8); I < NB; I += NTH / 256) {
-            const int J = I - d;
-            float y = 0.f;
-            for (int M = J; M < I; ++M)
-#pragma unroll
-                for (int kk = 0; kk < 16; ++kk)
-                    y += sA[(16 * I + ii) * AP + 16 * M + kk] * sT[(16 * M + kk) * AP + 16 * J + jj];
-            sY[(I - d) * 256 + e] = y;
-        }
-        __syncthreads();
-        for (int I = d + (tid >> 8); I < NB; I += NTH / 256) {
-            const int J = I - d;
-            float t = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk)
-                t -= sT[(16 * I + ii) * AP + 16 * I + kk] * sY[(I - d) * 256 + kk * 16 + jj];
-            sT[(16 * I + ii) * AP + 16 * J + jj] = t;
-        }
-        __syncthreads();
-    }
-
-    // the next item's inputs: issued here (register pressure is low from now on) and
-    // landing while this item finishes
-    if (item + (int)gridDim.x < total) prefetch(item + gridDim.x);
-
-    // ---- 7. Tb = Tinv diag(beta) fragments ----------------------------------------------
-    for (int f = wave; f < R.ntri; f += NTH / 64) {
-        int rt = 0;
-        while (ChunkRecord::tri_base(rt + 1) <= f) ++rt;
-        const int qs = f - ChunkRecord::tri_base(rt);
-        const int r = 16 * rt + li;
-        half8 x;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const int sx = 32 * qs + perm_slot(gq, jj);
-            x[jj] = sx < C ? static_cast<_Float16>(sT[r * AP + sx] * sBeta[sx]) : static_cast<_Float16>(0.f);
-        }
-        frags[(size_t)(R.off_tb + f) * 64 + lane] = x;
-    }
-
-    // ---- 8. pseudo-keys: W^T = (exp(gam) K)^T Tb^T on the matrix cores; store -W --------
-    for (int rt = wave / KC; rt < NB; rt += WW) {
-        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-        const int r = 16 * rt + li;
-#pragma unroll
-        for (int qs = 0; qs < NQS; ++qs) {
-            if (2 * qs > rt) break;
-            half8 bt;
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const int sx = 32 * qs + 8 * gq + jj;
-                bt[jj] = sx < C ? static_cast<_Float16>(sT[r * AP + sx] * sBeta[sx]) : static_cast<_Float16>(0.f);
-            }
-            acc0 = mfma_f16(ka[0][qs], bt, acc0);
-            acc1 = mfma_f16(ka[1][qs], bt, acc1);
-        }
-        half8 x;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-            x[jj] = static_cast<_Float16>(-((jj >> 2) ? acc1[jj & 3] : acc0[jj & 3]));
-        frags[(size_t)(R.off_w + rt * KC + wp) * 64 + lane] = x;
-    }
-    __syncthreads();  // the next item overwrites this item's LDS
-    }
+    GDR_WAVE(0) GDR_WAVE(1) GDR_WAVE(2) GDR_WAVE(3)
+#undef GDR_WAVE
 }
 
 template <typename TIn, int DK, int C>
-static hipError_t launch_prep_t(const LaunchArgs& a) {
+hipError_t launch_prep_t(const LaunchArgs& a) {
     const int NC = (a.T + C - 1) / C;
     const long long items = (long long)a.B * a.HV * NC;
-    // one persistent workgroup per resident slot (occupancy x CUs of the current device)
-    static thread_local int cached_dev = -1, cached_slots = 0;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-    if (dev != cached_dev) {
-        int cus = 0, per_cu = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return hipErrorInvalidDevice;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunk_prep_kernel<TIn, DK, C>, 512, 0) !=
-            hipSuccess)
-            return hipErrorInvalidDevice;
-        cached_slots = cus * (per_cu > 0 ? per_cu : 1);
-        cached_dev = dev;
-    }
-    const long long nblk = items < cached_slots ? items : cached_slots;
-    hipLaunchKernelGGL((chunk_prep_kernel<TIn, DK, C>), dim3((unsigned)nblk), dim3(512), 0,
+    hipLaunchKernelGGL((chunk_prep_kernel<TIn, DK, C>), dim3((unsigned)items), dim3(C * 4), 0,
                        (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g, a.beta,
                        (unsigned char*)a.workspace, a.B, a.T, a.HK, a.HV, NC);
     return hipGetLastError();
 }
 
 template <typename TIn>
-static hipError_t dispatch_prep(const LaunchArgs& a) {
+hipError_t dispatch_prep(const LaunchArgs& a) {
 #define GDR_CASE(DK_, C_) \
     if (a.dk == DK_ && a.chunk == C_) return launch_prep_t<TIn, DK_, C_>(a);
     GDR_CASE(32, 16) GDR_CASE(32, 32) GDR_CASE(32, 64)
@@ -531,6 +495,8 @@ static hipError_t dispatch_prep(const LaunchArgs& a) {
 #undef GDR_CASE
     return hipErrorInvalidValue;
 }
+
+}  // namespace
 
 hipError_t launch_chunk_prep(const LaunchArgs& a) {
     return a.qkv_f32 ? dispatch_prep<float>(a) : dispatch_prep<bf16_t>(a);
