@@ -99,8 +99,7 @@ struct PrepLds {
     static constexpr int SZ_KT = DK * KTP * 2;
     static constexpr int SZ_AS = (NB > 1 ? NB - 1 : 1) * KC * 1024;
     static constexpr int SZ_TT = C * TTP * 4;
-    static constexpr int SZ_AT = NB * 256 * 4;
-    static constexpr int SZ_U = (SZ_KT + SZ_AS > SZ_TT + SZ_AT) ? SZ_KT + SZ_AS : SZ_TT + SZ_AT;
+    static constexpr int SZ_U = (SZ_KT + SZ_AS > SZ_TT) ? SZ_KT + SZ_AS : SZ_TT;
 };
 
 struct PrepCtx {
@@ -108,9 +107,10 @@ struct PrepCtx {
     _Float16* sKbT;  // (exp(gL - gam) k)^T     [channel][token]  (Kb)         } phase 2-3
     half8* sAs;      // off-diagonal key-side fragments [J][p][lane]           }
     float* sTT;      // Tinv^T                  [token s][token r]             } solve
-    float* sAT;      // diagonal gram blocks, transposed [I][j][k] = A_II[k][j] }
+    float* sAT;      // diagonal blocks, transposed: A_II, then Tinv_II  [I][j][k] = X[k][j]
     float* sTot;     // per-block prefix totals [I][channel]
     float* sMid;     // per-block prefix at the middle row [I][channel]
+    float* sCon;     // per-block decay constants [I][4][channel]
     float* sBeta;    // beta per row (0 past the chunk end)
 };
 
@@ -185,80 +185,114 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
     f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
     half8 bk[KC], bq[KC];  // row-side operands of the off-diagonal tiles (I > 0)
     float* egl_out = reinterpret_cast<float*>(rec + (size_t)R.nfrag * 1024);
+    // Per-channel constants of block I (log2 units; m = middle row, e = gam at the block's
+    // last row, o = gam at the row before the block, gL = gam at the chunk's last row):
+    //   exp(P_m), exp(o + P_m), exp(gL - o - P_m), exp(e - o - P_m)
+    // so that every factor is one of the two per-element exponentials Z = exp(P - P_m),
+    // Zi = exp(P_m - P) times a constant.  One lane per channel computes them.
+    float* con = s.sCon + I * 4 * DK;
+#pragma unroll
+    for (int c = lane; c < DK; c += 64) {
+        const float md = s.sMid[I * DK + c];
+        float off = 0.f, gl = 0.f, ti = 0.f;
+#pragma unroll
+        for (int J = 0; J < NB; ++J) {
+            const float v = s.sTot[J * DK + c];
+            gl += v;
+            if (J < I) off += v;
+            if (J == I) ti = v;
+        }
+        con[c] = ex2(md);
+        con[DK + c] = ex2(off + md);
+        con[2 * DK + c] = ex2(gl - off - md);
+        con[3 * DK + c] = ex2(ti - md);
+        if (I == 0) egl_out[c] = ex2(gl);  // exp(gam_last), natural base
+    }
+    asm volatile("" ::: "memory");  // this wave's own LDS writes are read back in order
 #pragma unroll
     for (int p = 0; p < KC; ++p) {
         asm volatile("" ::: "memory");  // keep this step's LDS reads here (register pressure)
-        float off[8], gl[8], ti[8], md[8];
+        float md[8], c1[8], c2[8], c3[8], c4[8];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int cb = 32 * p + 16 * hh + 4 * gq;
             const float4 m4 = *reinterpret_cast<const float4*>(s.sMid + I * DK + cb);
+            const float4 k1 = *reinterpret_cast<const float4*>(con + cb);
+            const float4 k2 = *reinterpret_cast<const float4*>(con + DK + cb);
+            const float4 k3 = *reinterpret_cast<const float4*>(con + 2 * DK + cb);
+            const float4 k4 = *reinterpret_cast<const float4*>(con + 3 * DK + cb);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 md[4 * hh + e] = f4(m4, e);
-                off[4 * hh + e] = 0.f;
-                gl[4 * hh + e] = 0.f;
-            }
-#pragma unroll
-            for (int J = 0; J < NB; ++J) {
-                const float4 t4 = *reinterpret_cast<const float4*>(s.sTot + J * DK + cb);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float v = f4(t4, e);
-                    gl[4 * hh + e] += v;
-                    if (J < I) off[4 * hh + e] += v;
-                    if (J == I) ti[4 * hh + e] = v;
-                }
+                c1[4 * hh + e] = f4(k1, e);
+                c2[4 * hh + e] = f4(k2, e);
+                c3[4 * hh + e] = f4(k3, e);
+                c4[4 * hh + e] = f4(k4, e);
             }
         }
         half8 qt, as;
-        bf16x8 ah, al, kzh, kzl, qzh, qzl;
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
             const int hh = jj >> 2, e = jj & 3;
             const int c = 32 * p + 16 * hh + 4 * gq + e;
-            const float P = x[p][jj];
             const float kv = rv ? kin[p][hh][e] : 0.f;
             const float qv = rv ? qin[p][hh][e] : 0.f;
-            const float z = ex2(P - md[jj]);
-            const float zi = ex2(md[jj] - P);
-            const float eg = ex2(off[jj] + P);
-            const float ek = ex2(gl[jj] - off[jj] - P);
+            const float dz = x[p][jj] - md[jj];
+            const float z = ex2(dz);
+            const float zi = ex2(-dz);
+            const float eg = z * c2[jj];
             qt[jj] = static_cast<_Float16>(qv * eg);
             s.sKT[c * KTP + r] = static_cast<_Float16>(kv * eg);
-            s.sKbT[c * KTP + r] = static_cast<_Float16>(kv * ek);
-            __bf16 hi, lo;
-            split_bf16(kv * zi, hi, lo);
-            ah[jj] = hi;
-            al[jj] = lo;
-            split_bf16(kv * z, hi, lo);
-            kzh[jj] = hi;
-            kzl[jj] = lo;
-            split_bf16(qv * z, hi, lo);
-            qzh[jj] = hi;
-            qzl[jj] = lo;
+            s.sKbT[c * KTP + r] = static_cast<_Float16>(kv * (zi * c3[jj]));
+            // diagonal tiles on the fp32 matrix cores: reduction step = this slot's channel
+            // in each of the four lane groups
+            const float a = kv * zi;
+            accA = mfma_f32(a, kv * z, accA);
+            accP = mfma_f32(a, qv * z, accP);
             if constexpr (I > 0) {
-                const float zs = ex2(P);
+                const float zs = z * c1[jj];
                 bk[p][jj] = static_cast<_Float16>(kv * zs);
                 bq[p][jj] = static_cast<_Float16>(qv * zs);
             }
-            if constexpr (I < NB - 1) as[jj] = static_cast<_Float16>(kv * ex2(ti[jj] - P));
+            if constexpr (I < NB - 1) as[jj] = static_cast<_Float16>(kv * (zi * c4[jj]));
         }
         frags[(size_t)(R.off_qt + I * KC + p) * 64 + lane] = qt;
         if constexpr (I < NB - 1) s.sAs[(I * KC + p) * 64 + lane] = as;
-        accA = mfma_bf16(ah, kzh, accA);
-        accA = mfma_bf16(al, kzh, accA);
-        accA = mfma_bf16(ah, kzl, accA);
-        accP = mfma_bf16(ah, qzh, accP);
-        accP = mfma_bf16(al, qzh, accP);
-        accP = mfma_bf16(ah, qzl, accP);
-        if (I == 0 && li == 0) {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                *reinterpret_cast<float4*>(egl_out + 32 * p + 16 * hh + 4 * gq) =
-                    float4{ex2(gl[4 * hh]), ex2(gl[4 * hh + 1]), ex2(gl[4 * hh + 2]), ex2(gl[4 * hh + 3])};
-        }
     }
+    // diagonal tiles in row layout: gram rows times beta_r, strictly lower; causal lower
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int sl = 4 * gq + i;
+        accA[i] = sl < li ? accA[i] * bta : 0.f;
+        accP[i] = sl <= li ? accP[i] : 0.f;
+    }
+
+    // ---- diagonal block inverse, rows by lane: T_II = (I + A_II)^-1 ----------------------
+    // Only this wave's rows are involved, so it runs while the other waves finish phase 2.
+    float* at = s.sAT + I * 256;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) at[(4 * gq + i) * 16 + li] = accA[i];
+    asm volatile("" ::: "memory");
+    float t[16];
+#pragma unroll
+    for (int j = 15; j >= 0; --j) {
+        float acc = (j == li) ? 1.f : 0.f;
+        const float* col = at + j * 16;  // A_II[kk][j] for kk = 0..15
+#pragma unroll
+        for (int kk = j + 1; kk < 16; ++kk) acc -= t[kk] * col[kk];
+        t[j] = acc;
+        asm volatile("" : "+v"(t[j])::"memory");  // finish row j before reading the next column
+    }
+    // T_II back into the same slot, transposed (lane i writes row i), then row layout:
+    // lane (i, g) holds T_II[i][4g .. 4g+3]
+    if (gq == 0) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) at[j * 16 + li] = t[j];
+    }
+    asm volatile("" ::: "memory");
+    float tR[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tR[i] = at[(4 * gq + i) * 16 + li];
     lds_barrier();  // B2
 
     // ---- 3. off-diagonal gram tiles; Kb and P fragments ---------------------------------
@@ -306,13 +340,9 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
             lds_pair4(s.sKbT + (16 * ct + li) * KTP + 32 * qs + 4 * gq, C > 16);
     }
 #pragma unroll
-    for (int J = 0; J <= I; ++J)
+    for (int J = 0; J < I; ++J)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int sl = 4 * gq + i;
-            aR[J][i] = (J < I || sl < li) ? aR[J][i] * bta : 0.f;
-            pR[J][i] = (J < I || sl <= li) ? pR[J][i] : 0.f;
-        }
+        for (int i = 0; i < 4; ++i) aR[J][i] *= bta;
 #pragma unroll
     for (int qs = 0; qs < NT; ++qs) {
         half8 v;
@@ -325,30 +355,9 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
     }
     lds_barrier();  // B3: the key-side fragments and the Kb tile are dead; solve area live
 
-    // ---- 4. diagonal block inverse, rows by lane: T_II = (I + A_II)^-1 ----------------------
+    // ---- 4. publish T_II into Tinv^T ------------------------------------------------------
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s.sAT[I * 256 + (4 * gq + i) * 16 + li] = aR[I][i];
-    asm volatile("" ::: "memory");
-    float t[16];
-#pragma unroll
-    for (int j = 15; j >= 0; --j) {
-        float acc = (j == li) ? 1.f : 0.f;
-        const float* col = s.sAT + I * 256 + j * 16;  // A_II[kk][j] for kk = 0..15
-#pragma unroll
-        for (int kk = j + 1; kk < 16; ++kk) acc -= t[kk] * col[kk];
-        t[j] = acc;
-        asm volatile("" : "+v"(t[j])::"memory");  // finish row j before reading the next column
-    }
-    // publish T_II into Tinv^T (one lane group), then read it back in row layout:
-    // lane (i, g) holds T_II[i][4g .. 4g+3]
-    if (gq == 0) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) s.sTT[(16 * I + j) * TTP + 16 * I + li] = t[j];
-    }
-    asm volatile("" ::: "memory");
-    float tR[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) tR[i] = s.sTT[(16 * I + 4 * gq + i) * TTP + 16 * I + li];
+    for (int i = 0; i < 4; ++i) s.sTT[(16 * I + 4 * gq + i) * TTP + 16 * I + li] = tR[i];
     lds_barrier();  // B4
 
     // ---- 5. off-diagonal inverse blocks, one block row per stage ------------------------
@@ -443,6 +452,8 @@ __global__ __launch_bounds__(C * 4, 2) void chunk_prep_kernel(const TIn* __restr
     __shared__ __align__(16) _Float16 sKT[DK * Lds::KTP];
     __shared__ __align__(16) float sTot[NB * DK];
     __shared__ __align__(16) float sMid[NB * DK];
+    __shared__ __align__(16) float sCon[NB * 4 * DK];
+    __shared__ __align__(16) float sAT[NB * 256];
     __shared__ __align__(16) float sBeta[C];
     __shared__ __align__(16) unsigned char sU[Lds::SZ_U];
     PrepCtx s;
@@ -450,7 +461,8 @@ __global__ __launch_bounds__(C * 4, 2) void chunk_prep_kernel(const TIn* __restr
     s.sKbT = reinterpret_cast<_Float16*>(sU);
     s.sAs = reinterpret_cast<half8*>(sU + Lds::SZ_KT);
     s.sTT = reinterpret_cast<float*>(sU);
-    s.sAT = reinterpret_cast<float*>(sU + Lds::SZ_TT);
+    s.sAT = sAT;
+    s.sCon = sCon;
     s.sTot = sTot;
     s.sMid = sMid;
     s.sBeta = sBeta;
