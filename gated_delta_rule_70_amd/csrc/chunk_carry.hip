@@ -20,10 +20,12 @@
 // Every product is a 16x16x32 fp16 MFMA with fp32 accumulation; accumulator tiles map
 // to B fragments without shuffles (reduction slots follow perm_slot).
 //
-// Memory pipeline: each wave keeps its operand fragments and the raw v rows in two
-// register sets and refills a set with the operands of the chunk two ahead right after
-// their last use (buffer loads, fragment index in an SGPR), so every load has two chunks
-// of work to land; outputs are stored one chunk late.
+// Memory pipeline: each wave keeps its operand fragments and the raw v rows in a ring of
+// three register sets.  At the start of chunk n it requests chunk n+2's operands into the
+// set chunk n-1 has just released (buffer loads, fragment index in an SGPR), so every
+// load has two whole chunks of work to land; outputs are stored one chunk late.  The
+// chunk step is straight-line code (no per-wave branches), which keeps the compiler's
+// memory-wait counts at the pipeline's real depth.
 //
 // Launch: blocks = (B*HV) x (dv / (16*NT)), block index = colgroup * (B*HV) + head, so
 // all column groups of a head share one XCD (blocks are dealt round-robin to the 8 XCDs)
@@ -53,10 +55,14 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
     constexpr ChunkRecord R = ChunkRecord::make(C, DK);
     constexpr int ELT = sizeof(TIn);
 
-    // exchange buffers, lane-major: state B fragments [KC][NT], U B fragments [NQS][NT]
-    __shared__ half8 sSB[KC * NT * 64];
-    __shared__ half8 sUB[NQS * NT * 64];
-    __shared__ __attribute__((aligned(16))) _Float16 sV[NT * 16 * C];  // v tile, [nt][col][row]
+    // exchange buffers, three copies (chunk index mod 3), lane-major: state B fragments
+    // [KC][NT], U B fragments [NQS][NT]; and the chunk's v tile [nt][col][row] in fp16,
+    // columns padded to VP halves so the 16 columns a fragment read touches fall in
+    // different LDS banks
+    constexpr int VP = C + 4;
+    __shared__ half8 sSB[3][KC * NT * 64];
+    __shared__ half8 sUB[3][NQS * NT * 64];
+    __shared__ __attribute__((aligned(16))) _Float16 sV[3][NT * 16 * VP];
 
     const int NH = B * HV;
     const int blk = blockIdx.x;
@@ -65,10 +71,10 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
     const int h = bh % HV;
     const int b = bh / HV;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // row tile of this wave
+    __builtin_assume(w >= 0 && w < NW);  // lets the compiler drop the per-tile guards
     const int lane = threadIdx.x & 63;
     const int li = lane & 15;
     const int gq = lane >> 4;
-    const int nq_w = w / 2 + 1;  // token steps that row tile w's lower-triangular rows touch
 
     int jcol[NT];
 #pragma unroll
@@ -126,7 +132,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
             }
         }
     };
-    auto publish_v = [&](const VRaw& V) {  // -> sV[nt][col][row], fp16
+    auto publish_v = [&](const VRaw& V, _Float16* dst) {  // -> [nt][col][row], fp16
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -134,46 +140,35 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
                 float x;
                 if constexpr (ELT == 2) x = __uint_as_float((e & 1) ? (V[nt][e >> 1] & 0xFFFF0000u) : (V[nt][e >> 1] << 16));
                 else x = __uint_as_float(V[nt][e]);
-                sV[(nt * 16 + 4 * (lane & 3) + e) * C + 16 * w + (lane >> 2)] = static_cast<_Float16>(x);
+                dst[(nt * 16 + 4 * (lane & 3) + e) * VP + 16 * w + (lane >> 2)] = static_cast<_Float16>(x);
             }
     };
-    auto read_v = [&](half8 (&V)[NQS][NT]) {
+    auto read_v = [&](half8 (&V)[NQS][NT], const _Float16* src) {
 #pragma unroll
         for (int qs = 0; qs < NQS; ++qs)
-            if (qs < nq_w) {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const _Float16* col = &sV[(nt * 16 + li) * C + 32 * qs + 4 * gq];
-                    const half4 lo = *reinterpret_cast<const half4*>(col);
-                    half4 hi = {static_cast<_Float16>(0.f), static_cast<_Float16>(0.f),
-                                static_cast<_Float16>(0.f), static_cast<_Float16>(0.f)};
-                    if (32 * qs + 16 < C) hi = *reinterpret_cast<const half4*>(col + 16);  // compile-time
-                    V[qs][nt] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                }
+            for (int nt = 0; nt < NT; ++nt) {
+                const _Float16* col = &src[(nt * 16 + li) * VP + 32 * qs + 4 * gq];
+                const half4 lo = *reinterpret_cast<const half4*>(col);
+                half4 hi = {static_cast<_Float16>(0.f), static_cast<_Float16>(0.f),
+                            static_cast<_Float16>(0.f), static_cast<_Float16>(0.f)};
+                if (32 * qs + 16 < C) hi = *reinterpret_cast<const half4*>(col + 16);  // compile-time
+                V[qs][nt] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
     };
-    // outputs of row tile w of chunk n
+    // outputs of row tile w of chunk n (rows past T fall outside the buffer and are dropped;
+    // the row stays in the per-lane offset so one form serves every chunk)
     auto store_o = [&](int n, const f32x4 (&O)[NT]) {
-        const int t0 = n * C;
-        const int obase = ((t0 + 16 * w + 4 * gq) * HV + h) * DV * 4;
-        if (t0 + C <= T) {  // uniform: the whole chunk exists
+        const int obase = ((n * C + 16 * w + 4 * gq) * HV + h) * DV * 4;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) buf_store_f32(O[nt][i], rs_o, obase + jcol[nt] * 4, i * rowo);
-        } else {  // ragged last chunk: rows past T fall outside the buffer and are dropped
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) buf_store_f32(O[nt][i], rs_o, obase + jcol[nt] * 4 + i * rowo, 0);
-        }
+            for (int nt = 0; nt < NT; ++nt) buf_store_f32(O[nt][i], rs_o, obase + jcol[nt] * 4 + i * rowo, 0);
     };
 
-    // This wave's operand fragments, in registers, double-buffered across chunks: the set
-    // used by chunk n is refilled with chunk n+2's fragments right after each one's last
-    // use, so every load has two chunks of work to land (the empty asm keeps a load where
-    // it is written; the compiler would otherwise sink it to its next use and stall).  The
-    // chunk loop is unrolled by two so each set has fixed registers.
+    // This wave's operand fragments, in registers, in a ring of three sets (the empty asm
+    // keeps a load where it is written; the compiler would otherwise sink it to its next
+    // use and stall).  The chunk loop is unrolled by three so each set has fixed registers.
     struct Frags {
         half8 tb[NQS], w[KC], q[KC], p[NQS], kb[OWN][NQS];
         f32x4 e[OWN];
@@ -189,11 +184,10 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
     auto load_all = [&](Frags& F, int n) {
         const int vrec = n * R.bytes + lane * 16;
 #pragma unroll
-        for (int qs = 0; qs < NQS; ++qs)
-            if (qs < nq_w) {
-                ld(F.tb[qs], vrec, R.off_tb + ChunkRecord::tri_base(w) + qs);
-                ld(F.p[qs], vrec, R.off_p + ChunkRecord::tri_base(w) + qs);
-            }
+        for (int qs = 0; qs < NQS; ++qs) {
+            ld(F.tb[qs], vrec, R.off_tb + w * NQS + qs);
+            ld(F.p[qs], vrec, R.off_p + w * NQS + qs);
+        }
 #pragma unroll
         for (int p = 0; p < KC; ++p) {
             ld(F.w[p], vrec, R.off_w + w * KC + p);
@@ -212,11 +206,17 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
     };
 
     f32x4 Op[NT];
-    // One chunk: consume set F (chunk n) and refill it with chunk nn's operands.
-    auto step = [&](Frags& F, int n, int nn) {
-        const int vrec = nn * R.bytes + lane * 16;
-        publish_v(F.v);
-        load_v(nn, F.v);
+    // One chunk: request chunk nn's operands into set Fn, consume set F (chunk n), using
+    // exchange-buffer copy `par`.
+    auto step = [&](Frags& F, Frags& Fn, int n, int nn, int par) {
+        load_all(Fn, nn);
+        // The empty asm fixes where the raw v bits are consumed: the compiler would otherwise
+        // convert them a step early, while their load may still be in flight.
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int e = 0; e < ELT; ++e) asm volatile("" : "+v"(F.v[nt][e]));
+        publish_v(F.v, sV[par]);
 
         // 1. publish this wave's state tiles as halves of the state B fragments
 #pragma unroll
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
             if (ct < DKT) {
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
-                    *(reinterpret_cast<half4*>(&sSB[((ct >> 1) * NT + nt) * 64 + lane]) + (ct & 1)) =
+                    *(reinterpret_cast<half4*>(&sSB[par][((ct >> 1) * NT + nt) * 64 + lane]) + (ct & 1)) =
                         to_half4(S[j][nt]);
             }
         }
@@ -234,9 +234,9 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
 #pragma unroll
         for (int p = 0; p < KC; ++p)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) SB[p][nt] = sSB[(p * NT + nt) * 64 + lane];
+            for (int nt = 0; nt < NT; ++nt) SB[p][nt] = sSB[par][(p * NT + nt) * 64 + lane];
         half8 Vc[NQS][NT];
-        read_v(Vc);
+        read_v(Vc, sV[par]);
 
         if (n > 0) store_o(n - 1, Op);
 
@@ -246,37 +246,30 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
         for (int nt = 0; nt < NT; ++nt) U[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int qs = 0; qs < NQS; ++qs)
-            if (qs < nq_w) {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) U[nt] = mfma_f16(F.tb[qs], Vc[qs][nt], U[nt]);
-                ld(F.tb[qs], vrec, R.off_tb + ChunkRecord::tri_base(w) + qs);
-            }
+            for (int nt = 0; nt < NT; ++nt) U[nt] = mfma_f16(F.tb[qs], Vc[qs][nt], U[nt]);
 #pragma unroll
-        for (int p = 0; p < KC; ++p) {
+        for (int p = 0; p < KC; ++p)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) U[nt] = mfma_f16(F.w[p], SB[p][nt], U[nt]);
-            ld(F.w[p], vrec, R.off_w + w * KC + p);
-        }
         // 3. publish U_w as half of a U B fragment
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-            *(reinterpret_cast<half4*>(&sUB[((w >> 1) * NT + nt) * 64 + lane]) + (w & 1)) = to_half4(U[nt]);
+            *(reinterpret_cast<half4*>(&sUB[par][((w >> 1) * NT + nt) * 64 + lane]) + (w & 1)) = to_half4(U[nt]);
         // 4. O_w = Qt S (independent of U; overlaps the exchange)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) Op[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int p = 0; p < KC; ++p) {
+        for (int p = 0; p < KC; ++p)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) Op[nt] = mfma_f16(F.q[p], SB[p][nt], Op[nt]);
-            ld(F.q[p], vrec, R.off_qt + w * KC + p);
-        }
         lds_barrier();
         half8 UB[NQS][NT];
 #pragma unroll
         for (int qs = 0; qs < NQS; ++qs)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                half8 x = sUB[(qs * NT + nt) * 64 + lane];
+                half8 x = sUB[par][(qs * NT + nt) * 64 + lane];
                 if (2 * qs + 1 >= NB) {  // compile-time: this step has no second row tile
 #pragma unroll
                     for (int jj = 4; jj < 8; ++jj) x[jj] = static_cast<_Float16>(0.f);
@@ -291,42 +284,33 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
             if (ct < DKT) {
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) S[j][nt] *= F.e[j];
-                F.e[j] = ld_egl(vrec, ct);
 #pragma unroll
-                for (int qs = 0; qs < NQS; ++qs) {
+                for (int qs = 0; qs < NQS; ++qs)
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) S[j][nt] = mfma_f16(F.kb[j][qs], UB[qs][nt], S[j][nt]);
-                    ld(F.kb[j][qs], vrec, R.off_kb + ct * NQS + qs);
-                }
             }
         }
         // 6. O_w += P U
 #pragma unroll
         for (int qs = 0; qs < NQS; ++qs)
-            if (qs < nq_w) {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) Op[nt] = mfma_f16(F.p[qs], UB[qs][nt], Op[nt]);
-                ld(F.p[qs], vrec, R.off_p + ChunkRecord::tri_base(w) + qs);
-            }
+            for (int nt = 0; nt < NT; ++nt) Op[nt] = mfma_f16(F.p[qs], UB[qs][nt], Op[nt]);
     };
 
-    Frags FA, FB;
+    Frags FA, FB, FC;
     load_all(FA, 0);
     load_all(FB, min(1, NC - 1));
-    // Two copies of the loop (even / odd chunk count) keep each body free of branches, so
-    // the compiler's wait counting sees the steady state of the pipeline.
-    if ((NC & 1) == 0) {
-        for (int n = 0; n < NC; n += 2) {
-            step(FA, n, min(n + 2, NC - 1));
-            step(FB, n + 1, min(n + 3, NC - 1));
-        }
-    } else {
-        step(FA, 0, min(2, NC - 1));
-        for (int n = 1; n < NC; n += 2) {
-            step(FB, n, min(n + 2, NC - 1));
-            step(FA, n + 1, min(n + 3, NC - 1));
-        }
+    // Three steps per iteration (register set and exchange copy fixed per position), then
+    // up to two more; the requested chunk is clamped to the last one, whose operands then
+    // simply arrive twice.
+    int n = 0;
+    for (; n + 3 <= NC; n += 3) {
+        step(FA, FC, n, min(n + 2, NC - 1), 0);
+        step(FB, FA, n + 1, min(n + 3, NC - 1), 1);
+        step(FC, FB, n + 2, min(n + 4, NC - 1), 2);
     }
+    if (n < NC) step(FA, FC, n, min(n + 2, NC - 1), 0);
+    if (n + 1 < NC) step(FB, FA, n + 1, min(n + 3, NC - 1), 1);
     store_o(NC - 1, Op);
 
     if (ht) {

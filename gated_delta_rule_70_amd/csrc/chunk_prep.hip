@@ -344,14 +344,14 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
 #pragma unroll
         for (int i = 0; i < 4; ++i) aR[J][i] *= bta;
 #pragma unroll
-    for (int qs = 0; qs < NT; ++qs) {
+    for (int qs = 0; qs < NQS; ++qs) {
         half8 v;
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
             const int J = 2 * qs + (jj >> 2);
             v[jj] = J <= I ? static_cast<_Float16>(pR[J <= I ? J : I][jj & 3]) : static_cast<_Float16>(0.f);
         }
-        frags[(size_t)(R.off_p + ChunkRecord::tri_base(I) + qs) * 64 + lane] = v;
+        frags[(size_t)(R.off_p + I * NQS + qs) * 64 + lane] = v;
     }
     lds_barrier();  // B3: the key-side fragments and the Kb tile are dead; solve area live
 
@@ -389,8 +389,11 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
                     }
                 }
             }
-            frags[(size_t)(R.off_tb + ChunkRecord::tri_base(I) + qs) * 64 + lane] = tb[qs];
+            frags[(size_t)(R.off_tb + I * NQS + qs) * 64 + lane] = tb[qs];
         }
+#pragma unroll
+        for (int qs = NT; qs < NQS; ++qs)
+            frags[(size_t)(R.off_tb + I * NQS + qs) * 64 + lane] = half8{};
         // W^T = (exp(gam) K)^T Tb^T: A operand from the transposed key tile, B operand Tb
 #pragma unroll
         for (int p = 0; p < KC; ++p) {

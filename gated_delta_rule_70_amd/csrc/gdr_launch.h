@@ -31,15 +31,15 @@ struct LaunchArgs {
 //   Qt  [nb][kc]    decayed queries exp(gam) * q           (rows r, reduction over dk)
 //   -W  [nb][kc]    negated WY pseudo-keys                  (rows r, reduction over dk)
 //   Kb  [dkt][nqs]  decay-to-end keys, transposed           (rows c, reduction over tokens)
-//   Tb  [tri]       Tinv diag(beta), lower block triangle   (rows r, reduction over tokens)
-//   P   [tri]       causal q.k terms, lower block triangle  (rows r, reduction over tokens)
-// "tri" holds, for row tile rt, the token steps qs <= rt / 2 only (the others are zero).
+//   Tb  [nb][nqs]   Tinv diag(beta)                         (rows r, reduction over tokens)
+//   P   [nb][nqs]   causal q.k terms                        (rows r, reduction over tokens)
+// Tb and P are lower triangular; their all-zero fragments are stored too, so every row
+// tile reads the same operand count.
 struct ChunkRecord {
     int nb;        // 16-row blocks per chunk (C / 16)
     int nqs;       // 32-wide token reduction steps (ceil(C / 32))
     int kc;        // 32-wide key-channel reduction steps (dk / 32)
     int dkt;       // 16-row key-channel tiles (dk / 16)
-    int ntri;      // fragments of a block-lower-triangular token operand
     int off_qt;    // fragment offsets (in fragments) of each operand
     int off_w;
     int off_kb;
@@ -48,24 +48,18 @@ struct ChunkRecord {
     int nfrag;     // operand fragments; the decay block follows them
     int bytes;     // record stride: (nfrag + 1) KiB
 
-    __host__ __device__ static constexpr int tri_base(int rt) {
-        int b = 0;
-        for (int r = 0; r < rt; ++r) b += r / 2 + 1;
-        return b;
-    }
     __host__ __device__ static constexpr ChunkRecord make(int C, int dk) {
         ChunkRecord r{};
         r.nb = C / 16;
         r.nqs = (C + 31) / 32;
         r.kc = dk / 32;
         r.dkt = dk / 16;
-        r.ntri = tri_base(r.nb);
         r.off_qt = 0;
         r.off_w = r.off_qt + r.nb * r.kc;
         r.off_kb = r.off_w + r.nb * r.kc;
         r.off_tb = r.off_kb + r.dkt * r.nqs;
-        r.off_p = r.off_tb + r.ntri;
-        r.nfrag = r.off_p + r.ntri;
+        r.off_p = r.off_tb + r.nb * r.nqs;
+        r.nfrag = r.off_p + r.nb * r.nqs;
         r.bytes = (r.nfrag + 1) * 1024;
         return r;
     }

@@ -145,14 +145,12 @@ def test_workspace_checks(L):
 
 
 def test_workspace_size_formula(L):
-    # one record per (batch, value head, chunk): fp16 operand fragments of 1 KiB each
-    # (two block-lower-triangular token operands keep only token steps qs <= rt/2), plus
-    # one 1 KiB block for the dk fp32 decay totals
+    # one record per (batch, value head, chunk): fp16 operand fragments of 1 KiB each,
+    # plus one 1 KiB block for the dk fp32 decay totals
     for (dk, C) in [(32, 16), (64, 32), (128, 64), (128, 16)]:
         d = dims(dk=dk, chunk=C, T=100)
         nb, nqs, kc, dkt = C // 16, (C + 31) // 32, dk // 32, dk // 16
-        ntri = sum(rt // 2 + 1 for rt in range(nb))
-        nfrag = 2 * nb * kc + dkt * nqs + 2 * ntri
+        nfrag = 2 * nb * kc + dkt * nqs + 2 * nb * nqs  # Qt, -W, Kb, Tb, P
         rec = (nfrag + 1) * 1024
         nchunk = -(-100 // C)
         assert L.gdr_chunk_prefill_workspace_bytes(ctypes.byref(d)) == 2 * 4 * nchunk * rec
