@@ -11,11 +11,27 @@ oracle's throughput on the same workload, and the parity error of this run's out
 against that oracle.  All inputs are seeded synthetic data resident in HBM before timing.
 
     python bench.py [--steps K] [--warmup W] [--decode-steps N] [--no-cpu-baseline]
+
+The roofline's ``traffic`` (HBM bytes per launch of the dominant kernel) comes from the
+committed summary of two rocprofv3 counter runs, used only while the kernel sources still
+match the digest recorded with it:
+
+    rocprofv3 --pmc FETCH_SIZE -d <dirF> -o run -f csv -- python3 bench.py --profile-run
+    rocprofv3 --pmc WRITE_SIZE -d <dirW> -o run -f csv -- python3 bench.py --profile-run
+    python3 bench.py --summarize-pmc <dirF> <dirW>      # -> profiles/hbm_traffic_...md
+
+``--profile-run`` is a short run that also launches one calibration kernel of known
+traffic (a 256 MiB fp32 negation: 256 MiB read, 256 MiB written); the counters of every
+kernel are scaled by what they read for it.  ``--summarize-stats <dir>`` turns a
+``rocprofv3 --kernel-trace --stats`` run into the kernel-time summary under profiles/.
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +44,136 @@ if ROOT not in sys.path:
 METRIC = "prefill tokens/s (HV=32,dk=dv=128) + decode state GB/s, % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak, published
+
+CSRC = os.path.join(ROOT, "gated_delta_rule_70_amd", "csrc")
+KERNEL_SOURCES = {  # kernel -> the sources its machine code is built from
+    "chunk_prep": ["chunk_prep.hip", "gdr_device.h", "gdr_launch.h"],
+    "chunk_carry": ["chunk_carry.hip", "gdr_device.h", "gdr_launch.h"],
+    "decode": ["decode.hip", "gdr_device.h", "gdr_launch.h"],
+}
+KERNEL_SYMBOL = {"chunk_prep": "chunk_prep_kernel", "chunk_carry": "chunk_carry_kernel",
+                 "decode": "decode_kernel"}
+CALIB_BYTES = 256 << 20           # calibration kernel: reads and writes this many bytes
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_b1_t4097_decode_b32.md")
+
+
+def source_digest(kernel):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_rows(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch_kib(rows, counter):
+    """kernel name -> mean per-dispatch value of `counter` (KiB), summed over the rows of a
+    dispatch (one per agent dimension)."""
+    disp = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Kernel_Name"], r["Dispatch_Id"])
+        disp[key] = disp.get(key, 0.0) + float(r["Counter_Value"])
+    by_kernel = {}
+    for (name, _), v in disp.items():
+        by_kernel.setdefault(name, []).append(v)
+    return {k: sum(v) / len(v) for k, v in by_kernel.items()}
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    fetch = _per_dispatch_kib(_counter_rows(fetch_dir), "FETCH_SIZE")
+    write = _per_dispatch_kib(_counter_rows(write_dir), "WRITE_SIZE")
+    calib = [k for k in fetch if "neg" in k.lower()]
+    if len(calib) != 1 or calib[0] not in write:
+        raise SystemExit(f"calibration kernel not found uniquely: {calib}")
+    f_fac = CALIB_BYTES / (fetch[calib[0]] * 1024.0)
+    w_fac = CALIB_BYTES / (write[calib[0]] * 1024.0)
+    out = {"calibration": {"kernel": calib[0], "bytes_read": CALIB_BYTES, "bytes_written": CALIB_BYTES,
+                           "fetch_kib": fetch[calib[0]], "write_kib": write[calib[0]],
+                           "fetch_factor": f_fac, "write_factor": w_fac},
+           "kernels": {}}
+    for kern, sym in KERNEL_SYMBOL.items():
+        names = [k for k in fetch if sym in k]
+        if not names:
+            continue
+        nm = max(names, key=lambda k: fetch[k])  # the instantiation the workload launches
+        fb = fetch[nm] * 1024.0 * f_fac
+        wb = write.get(nm, 0.0) * 1024.0 * w_fac
+        out["kernels"][kern] = {"symbol": nm, "fetch_kib": fetch[nm], "write_kib": write.get(nm, 0.0),
+                                "fetch_bytes": round(fb), "write_bytes": round(wb),
+                                "traffic_bytes": round(fb + wb), "source_digest": source_digest(kern)}
+    lines = ["# HBM traffic per launch: prefill B=1 T=4097 HV=32 dk=dv=128 and decode B=32",
+             "",
+             "Two counter runs of the same short benchmark (FETCH_SIZE, then WRITE_SIZE, KiB per",
+             "dispatch), each scaled by what the counter reads for a calibration kernel of known",
+             "traffic (a 256 MiB fp32 negation).  `source_digest` identifies the kernel sources the",
+             "numbers belong to; bench.py reports them only while the sources still match.",
+             "",
+             "Commands (repository root, one MI355X):",
+             "",
+             "```",
+             "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run -f csv -- python3 bench.py --profile-run",
+             "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run -f csv -- python3 bench.py --profile-run",
+             "python3 bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write",
+             "```",
+             "",
+             "| kernel | fetch MB | write MB | traffic MB |",
+             "|---|---|---|---|"]
+    for kern, v in out["kernels"].items():
+        lines.append(f"| `{kern}` | {v['fetch_bytes'] / 1e6:.2f} | {v['write_bytes'] / 1e6:.2f} | "
+                     f"{v['traffic_bytes'] / 1e6:.2f} |")
+    lines += ["", f"Calibration factors: fetch {f_fac:.4f}, write {w_fac:.4f} (bytes per counted byte).",
+              "", "```json", json.dumps(out, indent=1), "```", ""]
+    with open(TRAFFIC_SUMMARY, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {TRAFFIC_SUMMARY}")
+
+
+def read_traffic(kernel):
+    """Calibrated HBM bytes per launch of `kernel`, or None if there is no summary for the
+    current sources."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+        blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        k = blob["kernels"][kernel]
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
+    if k.get("source_digest") != source_digest(kernel):
+        return None
+    return k["traffic_bytes"]
+
+
+def summarize_stats(d, out_name, command):
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    tot = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = [f"# Kernel trace: {out_name}", "", "Command (repository root, one MI355X):", "", "```", command, "```", "",
+             "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{100 * float(r['TotalDurationNs']) / tot:.1f}% |")
+    path = os.path.join(ROOT, "profiles", out_name.replace(" ", "_") + ".md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {path}")
 
 
 def prefill_bytes(B, T, HK, HV, dk, dv, elt, h0):
@@ -168,7 +314,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--workload", default="prefill_b1_t4097")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="short run for counter collection, plus the calibration kernel")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("DIR", "NAME", "COMMAND"))
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return
+    if args.profile_run:
+        args.steps, args.warmup, args.decode_steps, args.no_cpu_baseline = 3, 1, 50, True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the recurrence's (batch, head) pairs are independent, "
               "so a multi-GPU run is N independent copies of this one; run with --gpus 1.",
@@ -185,6 +343,12 @@ def main():
         sys.exit(1)
     w = WORKLOADS[args.workload]
     elt = 2 if w.dtype == torch.bfloat16 else 4
+    if args.profile_run:  # calibration kernel of known traffic for the counter runs
+        xc = torch.ones(CALIB_BYTES // 4, device="cuda")
+        yc = torch.empty_like(xc)
+        torch.neg(xc, out=yc)
+        torch.cuda.synchronize()
+        del xc, yc
     x, o, ht, wall, prep_ms, carry_ms = bench_prefill(w, args.steps, args.warmup)
     ntok = w.B * w.T
     ms_per_step = wall / args.steps * 1e3
@@ -197,7 +361,7 @@ def main():
     dom_bytes = b_carry if dom == "chunk_carry" else b_prep
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(dom),
                 "alg_bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 5)}
     path_gbs = (b_prep + b_carry) / (kern_ms * 1e-3) / 1e9
     path_tflops = (f_prep + f_carry) / (kern_ms * 1e-3) / 1e12
@@ -242,13 +406,18 @@ def main():
 
         import oracle
 
-        t0 = time.perf_counter()
-        o_ref, ht_ref = oracle.sequential(**x)
-        cpu_s = time.perf_counter() - t0
-        line["cpu_baseline"] = {"value": round(ntok / cpu_s, 1), "unit": "tokens/s",
+        # the full workload, repeated until about 10 s of CPU time have been spent (<= 30 runs)
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            o_ref, ht_ref = oracle.sequential(**x)
+            runs += 1
+            cpu_s = time.perf_counter() - t0
+            if cpu_s >= 10.0 or runs >= 30:
+                break
+        line["cpu_baseline"] = {"value": round(runs * ntok / cpu_s, 1), "unit": "tokens/s",
                                 "cores": oracle.num_threads(), "kind": "oracle",
                                 "sample": f"the full {w.name} workload ({ntok} tokens x {w.HV} value heads), "
-                                          f"fp64 sequential recurrence, {cpu_s:.2f} s"}
+                                          f"fp64 sequential recurrence, {runs} runs in {cpu_s:.1f} s"}
         line["parity_vs_oracle"] = {
             "o": float(oracle.rel_err(o.double().cpu().numpy(), o_ref)),
             "state": float(oracle.rel_err(ht.double().cpu().numpy(), ht_ref)),
