@@ -64,7 +64,10 @@ struct In4;
 template <>
 struct In4<bf16_t> {
     uint2 u;
-    __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ void load(rsrc_t r, int voff) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+        u = uint2{x[0], x[1]};
+    }
     __device__ __forceinline__ float operator[](int e) const {
         const uint32_t w = e < 2 ? u.x : u.y;
         return (e & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
@@ -73,7 +76,10 @@ struct In4<bf16_t> {
 template <>
 struct In4<float> {
     float4 u;
-    __device__ __forceinline__ void load(const float* p) { u = *reinterpret_cast<const float4*>(p); }
+    __device__ __forceinline__ void load(rsrc_t r, int voff) {
+        const f32x4 x = buf_load_f32x4(r, voff, 0);
+        u = float4{x[0], x[1], x[2], x[3]};
+    }
     __device__ __forceinline__ float operator[](int e) const {
         return e == 0 ? u.x : e == 1 ? u.y : e == 2 ? u.z : u.w;
     }
@@ -100,6 +106,7 @@ struct PrepLds {
     static constexpr int SZ_AS = (NB > 1 ? NB - 1 : 1) * KC * 1024;
     static constexpr int SZ_TT = C * TTP * 4;
     static constexpr int SZ_U = (SZ_KT + SZ_AS > SZ_TT) ? SZ_KT + SZ_AS : SZ_TT;
+    static constexpr int NCON = 4 + (NB > 2 ? NB - 2 : 0);  // decay constants per (block, channel)
 };
 
 struct PrepCtx {
@@ -110,7 +117,7 @@ struct PrepCtx {
     float* sAT;      // diagonal blocks, transposed: A_II, then Tinv_II  [I][j][k] = X[k][j]
     float* sTot;     // per-block prefix totals [I][channel]
     float* sMid;     // per-block prefix at the middle row [I][channel]
-    float* sCon;     // per-block decay constants [I][4][channel]
+    float* sCon;     // per-block decay constants [I][NCON][channel]
     float* sBeta;    // beta per row (0 past the chunk end)
 };
 
@@ -131,38 +138,48 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
     constexpr ChunkRecord R = ChunkRecord::make(C, DK);
     constexpr int NT = I / 2 + 1;  // token reduction steps of row tile I
 
+    constexpr int NCON = PrepLds<DK, C>::NCON;
+    constexpr int ELT = sizeof(TIn);
     const int lane = threadIdx.x & 63;
     const int li = lane & 15;
     const int gq = lane >> 4;
     const int r = 16 * I + li;
-    const bool rv = r < L;
-    const int rc = rv ? r : L - 1;
-    const size_t tok = (size_t)b * T + t0 + rc;
-    const float* grow = g + (tok * HV + h) * DK;
-    const TIn* krow = k + (tok * HK + kh) * DK;
-    const TIn* qrow = q + (tok * HK + kh) * DK;
     half8* frags = reinterpret_cast<half8*>(rec);
 
-    // ---- 1. loads (clamped rows, masked), g -> log2 units, 16-row inclusive scan ---------
+    // ---- 1. loads, g -> log2 units, 16-row inclusive scan ---------------------------------
+    // Buffer resources over this batch element's rows: a row past the sequence end lies
+    // beyond the range and reads as zero, which is exactly the zero padding of the ragged
+    // last chunk (g = 0, k = q = 0, beta = 0).  The host keeps every offset below 2^31.
+    const rsrc_t rs_g = make_rsrc(g + (size_t)b * T * HV * DK, (uint32_t)T * HV * DK * 4);
+    const rsrc_t rs_k = make_rsrc(k + (size_t)b * T * HK * DK, (uint32_t)T * HK * DK * ELT);
+    const rsrc_t rs_q = make_rsrc(q + (size_t)b * T * HK * DK, (uint32_t)T * HK * DK * ELT);
+    const rsrc_t rs_b = make_rsrc(beta + (size_t)b * T * HV, (uint32_t)T * HV * 4);
+    const int tr = t0 + r;  // token row within this batch element
     float x[KC][8];
     In4<TIn> kin[KC][2], qin[KC][2];
+    const float bta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_b, (tr * HV + h) * 4, 0, 0));
 #pragma unroll
     for (int p = 0; p < KC; ++p)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int cb = 32 * p + 16 * hh + 4 * gq;
-            const float4 gv = *reinterpret_cast<const float4*>(grow + cb);
+            const f32x4 gv = buf_load_f32x4(rs_g, ((tr * HV + h) * DK + cb) * 4, 0);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[p][4 * hh + e] = f4(gv, e);
-            kin[p][hh].load(krow + cb);
-            qin[p][hh].load(qrow + cb);
+            for (int e = 0; e < 4; ++e) x[p][4 * hh + e] = gv[e];
         }
-    const float bta = rv ? beta[tok * HV + h] : 0.f;
+#pragma unroll
+    for (int p = 0; p < KC; ++p)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int cb = 32 * p + 16 * hh + 4 * gq;
+            kin[p][hh].load(rs_k, ((tr * HK + kh) * DK + cb) * ELT);
+            qin[p][hh].load(rs_q, ((tr * HK + kh) * DK + cb) * ELT);
+        }
 #pragma unroll
     for (int p = 0; p < KC; ++p)
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-            float v = rv ? x[p][jj] * kLog2e : 0.f;
+            float v = x[p][jj] * kLog2e;
             v += row_shr<1>(v);
             v += row_shr<2>(v);
             v += row_shr<4>(v);
@@ -190,7 +207,7 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
     //   exp(P_m), exp(o + P_m), exp(gL - o - P_m), exp(e - o - P_m)
     // so that every factor is one of the two per-element exponentials Z = exp(P - P_m),
     // Zi = exp(P_m - P) times a constant.  One lane per channel computes them.
-    float* con = s.sCon + I * 4 * DK;
+    float* con = s.sCon + I * NCON * DK;
 #pragma unroll
     for (int c = lane; c < DK; c += 64) {
         const float md = s.sMid[I * DK + c];
@@ -206,6 +223,14 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
         con[DK + c] = ex2(off + md);
         con[2 * DK + c] = ex2(gl - off - md);
         con[3 * DK + c] = ex2(ti - md);
+        // exp(gam_{16I-1} - gam_{16J+15}) for the off-diagonal tiles J <= I - 2 (the decay over
+        // the blocks strictly between J and I), slot 4 + (I - 2 - J)
+        float between = 0.f;
+#pragma unroll
+        for (int J = I - 2; J >= 0; --J) {
+            between += s.sTot[(J + 1) * DK + c];
+            con[(4 + I - 2 - J) * DK + c] = ex2(between);
+        }
         if (I == 0) egl_out[c] = ex2(gl);  // exp(gam_last), natural base
     }
     asm volatile("" ::: "memory");  // this wave's own LDS writes are read back in order
@@ -235,8 +260,8 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
         for (int jj = 0; jj < 8; ++jj) {
             const int hh = jj >> 2, e = jj & 3;
             const int c = 32 * p + 16 * hh + 4 * gq + e;
-            const float kv = rv ? kin[p][hh][e] : 0.f;
-            const float qv = rv ? qin[p][hh][e] : 0.f;
+            const float kv = kin[p][hh][e];
+            const float qv = qin[p][hh][e];
             const float dz = x[p][jj] - md[jj];
             const float z = ex2(dz);
             const float zi = ex2(-dz);
@@ -305,30 +330,21 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
         f32x4 a = {0.f, 0.f, 0.f, 0.f}, pc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int p = 0; p < KC; ++p) {
-            half8 ok = bk[p], oq = bq[p];
+            half8 ak = s.sAs[(J * KC + p) * 64 + lane];
             if (J < I - 1) {
-                // blocks between J and I: scale by exp(gam_{16I-1} - gam_{16J+15})
+                // blocks between J and I: scale the key side by exp(gam_{16I-1} - gam_{16J+15})
+                half8 ef;
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const int cb = 32 * p + 16 * hh + 4 * gq;
-                    float ex[4] = {0.f, 0.f, 0.f, 0.f};
+                    const float4 e4 = *reinterpret_cast<const float4*>(
+                        s.sCon + (I * NCON + 4 + I - 2 - J) * DK + 32 * p + 16 * hh + 4 * gq);
 #pragma unroll
-                    for (int M = J + 1; M < I; ++M) {
-                        const float4 t4 = *reinterpret_cast<const float4*>(s.sTot + M * DK + cb);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) ex[e] += f4(t4, e);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float f = ex2(ex[e]);
-                        ok[4 * hh + e] = static_cast<_Float16>(static_cast<float>(ok[4 * hh + e]) * f);
-                        oq[4 * hh + e] = static_cast<_Float16>(static_cast<float>(oq[4 * hh + e]) * f);
-                    }
+                    for (int e = 0; e < 4; ++e) ef[4 * hh + e] = static_cast<_Float16>(f4(e4, e));
                 }
+                ak = ak * ef;
             }
-            const half8 ak = s.sAs[(J * KC + p) * 64 + lane];
-            a = mfma_f16(ak, ok, a);
-            pc = mfma_f16(ak, oq, pc);
+            a = mfma_f16(ak, bk[p], a);
+            pc = mfma_f16(ak, bq[p], pc);
         }
         aR[J] = a;
         pR[J] = pc;
@@ -455,7 +471,7 @@ __global__ __launch_bounds__(C * 4, 2) void chunk_prep_kernel(const TIn* __restr
     __shared__ __align__(16) _Float16 sKT[DK * Lds::KTP];
     __shared__ __align__(16) float sTot[NB * DK];
     __shared__ __align__(16) float sMid[NB * DK];
-    __shared__ __align__(16) float sCon[NB * 4 * DK];
+    __shared__ __align__(16) float sCon[NB * Lds::NCON * DK];
     __shared__ __align__(16) float sAT[NB * 256];
     __shared__ __align__(16) float sBeta[C];
     __shared__ __align__(16) unsigned char sU[Lds::SZ_U];

@@ -170,11 +170,13 @@ static int prefill_stages(const gdr_dims* dims, const void* q, const void* k, co
     if (st != GDR_OK) return st;
     const size_t need = workspace_bytes_unchecked(dims);
     if (need == 0) return GDR_ERR_SHAPE;
-    // The carry addresses one batch element's v/o rows and one head's chunk records with
-    // 31-bit buffer offsets.
+    // The kernels address one batch element's g/q/k/v/o rows (including the padding rows of
+    // the last chunk, which lie past the end and read as zero) and one head's chunk records
+    // with 31-bit buffer offsets.
     const gdr::ChunkRecord rec = gdr::ChunkRecord::make(dims->chunk, dims->dk);
     const size_t nchunk = (size_t)((dims->T + dims->chunk - 1) / dims->chunk);
-    if ((size_t)dims->T * dims->HV * dims->dv * 4 >= (size_t(1) << 31) ||
+    const size_t dmax = (size_t)(dims->dk > dims->dv ? dims->dk : dims->dv);
+    if ((size_t)(dims->T + dims->chunk) * dims->HV * dmax * 4 >= (size_t(1) << 31) ||
         nchunk * (size_t)rec.bytes >= (size_t(1) << 31))
         return GDR_ERR_SHAPE;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)

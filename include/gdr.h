@@ -30,9 +30,10 @@
  *     GDR_ERR_HIP.  The library never aborts or prints.  NaN/Inf inputs are not checked
  *     and propagate.
  *   - Supported: dk, dv in {32, 64, 128}; chunk in {16, 32, 64}; HV % HK == 0; B, T >= 1;
- *     q/k/v in bf16 or fp32.  Prefill also needs T*HV*dv*4 < 2^31 (one batch element's
- *     outputs) and ceil(T/chunk) * (workspace bytes per chunk) < 2^31 (one head's chunk
- *     records); about 130K tokens at HV = 32, dv = 128.  Decay values are expected to satisfy g <= 0 with the total
+ *     q/k/v in bf16 or fp32.  Prefill also needs (T + chunk)*HV*max(dk, dv)*4 < 2^31
+ *     (one batch element's g and o rows, padding rows of the last chunk included) and
+ *     ceil(T/chunk) * (workspace bytes per chunk) < 2^31 (one head's chunk records); about
+ *     130K tokens at HV = 32, dk = dv = 128.  Decay values are expected to satisfy g <= 0 with the total
  *     decay over any 8 consecutive tokens below 80 in every channel (exp(g) >= ~5e-5 per
  *     token); outside that range the prefill path's intra-chunk decay factors can
  *     overflow fp32.  The decode path has no such limit.

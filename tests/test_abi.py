@@ -144,6 +144,14 @@ def test_workspace_checks(L):
     assert prefill(L, d, ws=addr(8, 16)) == EWS
 
 
+def test_31_bit_offset_limit(L):
+    # (T + chunk) * HV * max(dk, dv) * 4 must stay below 2^31 (rows of one batch element,
+    # padding rows of the last chunk included): T = 131008 is the first length refused
+    d = dict(B=1, HK=16, HV=32, dk=128, dv=128, chunk=64)
+    assert prefill(L, dims(T=131008, **d)) == ESHAPE
+    assert prefill(L, dims(T=131007, **d), ws_bytes=1) == EWS  # passes the limit, fails later
+
+
 def test_workspace_size_formula(L):
     # one record per (batch, value head, chunk): fp16 operand fragments of 1 KiB each,
     # plus one 1 KiB block for the dk fp32 decay totals
