@@ -174,19 +174,27 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
         f32x4 e[OWN];
         uint32_t v[NT][ELT];     // raw bits of this wave's v rows of the chunk
     };
+    // A per-lane offset past every record range: such a load reads zeros without touching
+    // memory (the range check applies to the per-lane offset, not to the SGPR one).
+    constexpr int kBeyond = (int)0xFFFFFF00u;
     auto ld = [&](half8& dst, int vrec, int f) {
         dst = buf_load_half8(rs_rec, vrec, f * 1024);
         asm volatile("" ::: "memory");
     };
-    auto ld_egl = [&](int vrec, int ct) {  // exp(gam_last) for rows 16ct + 4gq .. +3
-        return buf_load_f32x4(rs_rec, vrec - lane * 16 + gq * 16, R.nfrag * 1024 + ct * 64);
+    // exp(gam_last) for rows 16ct + 4gq .. +3: one lane per 16-lane group loads it (the
+    // others read zeros from beyond the range) and shares it at use time
+    auto ld_egl = [&](int n, int ct) {
+        return buf_load_f32x4(rs_rec, li == 0 ? n * R.bytes + gq * 16 : kBeyond, R.nfrag * 1024 + ct * 64);
     };
     auto load_all = [&](Frags& F, int n) {
         const int vrec = n * R.bytes + lane * 16;
+        // Tb and P fragments above row tile w's diagonal are zero: read them from beyond the
+        // range instead of from memory (a per-wave choice of offset, no branch)
 #pragma unroll
         for (int qs = 0; qs < NQS; ++qs) {
-            ld(F.tb[qs], vrec, R.off_tb + w * NQS + qs);
-            ld(F.p[qs], vrec, R.off_p + w * NQS + qs);
+            const int vq = 2 * qs > w ? kBeyond : vrec;
+            ld(F.tb[qs], vq, R.off_tb + w * NQS + qs);
+            ld(F.p[qs], vq, R.off_p + w * NQS + qs);
         }
 #pragma unroll
         for (int p = 0; p < KC; ++p) {
@@ -199,7 +207,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
             if (ct < DKT) {
 #pragma unroll
                 for (int qs = 0; qs < NQS; ++qs) ld(F.kb[j][qs], vrec, R.off_kb + ct * NQS + qs);
-                F.e[j] = ld_egl(vrec, ct);
+                F.e[j] = ld_egl(n, ct);
             }
         }
         load_v(n, F.v);
@@ -283,7 +291,11 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
             const int ct = w + NW * j;
             if (ct < DKT) {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) S[j][nt] *= F.e[j];
+                f32x4 ej = F.e[j];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ej[i] = __shfl(ej[i], lane & ~15);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) S[j][nt] *= ej;
 #pragma unroll
                 for (int qs = 0; qs < NQS; ++qs)
 #pragma unroll
