@@ -297,10 +297,49 @@ def bench_decode(w, steps, warmup):
     wall_r, per_r = run(rot, True)
     per_c.sort()
     per_r.sort()
+
+    # The same carried steps replayed from one captured graph (no host launch cost).
+    gstate = h0.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        s = ptr(gstate)
+        for t in range(nstep):
+            q, k, v, g, b, o = args[t]
+            st = L.gdr_decode_step(ctypes.byref(dims), q, k, v, g, b, s, o, s, cs)
+            if st != 0:
+                raise RuntimeError(f"gdr_decode_step failed under capture: {st}")
+    graph.replay()
+    torch.cuda.synchronize()
+    ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ga.record()
+    graph.replay()
+    gb.record()
+    torch.cuda.synchronize()
+    graph_ms = ga.elapsed_time(gb) / nstep
+
+    # A plain device copy of the state's size (read + write the same bytes as one step's
+    # state stream), cycling over 8 buffer pairs like the rotating decode run.
+    nel = B * HV * dk * dv
+    srcs = [torch.randn(nel, device="cuda") for _ in range(8)]
+    dsts = [torch.empty(nel, device="cuda") for _ in range(8)]
+    for i in range(8):
+        dsts[i].copy_(srcs[i])
+    torch.cuda.synchronize()
+    ca, cb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 80
+    ca.record()
+    for i in range(reps):
+        dsts[i % 8].copy_(srcs[i % 8])
+    cb.record()
+    torch.cuda.synchronize()
+    copy_ms = ca.elapsed_time(cb) / reps
+    del srcs, dsts
     return {
         "nstep": nstep,
         "carried": {"wall_s": wall_c, "mean_ms": _mean(per_c), "median_ms": per_c[len(per_c) // 2]},
         "rotating8": {"wall_s": wall_r, "mean_ms": _mean(per_r), "median_ms": per_r[len(per_r) // 2]},
+        "graph_ms_per_step": graph_ms, "copy_ms": copy_ms,
         "inputs": x, "obuf": obuf, "state": state,
     }
 
@@ -365,12 +404,15 @@ def main():
                 "alg_bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 5)}
     path_gbs = (b_prep + b_carry) / (kern_ms * 1e-3) / 1e9
     path_tflops = (f_prep + f_carry) / (kern_ms * 1e-3) / 1e12
+    # the path's ceiling: its algorithmic bytes at HBM peak or its flops at MFMA peak
+    ceil_ms = max((b_prep + b_carry) / (HBM_PEAK_GBS * 1e9), (f_prep + f_carry) / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
     prefill = {
         "kernels_ms": {"chunk_prep": round(prep_ms, 5), "chunk_carry": round(carry_ms, 5)},
         "path_alg_bytes": b_prep + b_carry, "path_alg_flops": f_prep + f_carry,
         "path_hbm_GBps": round(path_gbs, 1), "path_hbm_frac": round(path_gbs / HBM_PEAK_GBS, 4),
         "path_mfma_TFLOPs": round(path_tflops, 2),
         "path_frac_of_bf16_mfma_peak": round(path_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "ceiling_ms": round(ceil_ms, 5), "path_frac_of_ceiling": round(ceil_ms / kern_ms, 4),
         "tokens_per_s_kernel_time": round(ntok / (kern_ms * 1e-3), 1),
     }
 
@@ -378,7 +420,9 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f16 mfma operands, f32 accumulate/state", "data": "synthetic",
+        "dtype": "f16", "arithmetic": "fp16 MFMA operands with fp32 accumulation; fp32 state, decay "
+                                       "factors, diagonal gram tiles and triangular solve",
+        "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} T={w.T} HK={w.HK} HV={w.HV} dk={w.dk} dv={w.dv} "
                                f"chunk={w.chunk} bf16 q/k/v, fp32 g/beta/state/o, h0={'yes' if w.h0 else 'no'}",
                    "global_batch": w.B, "seq_len": w.T, "parallelism": "single GPU"},
@@ -399,6 +443,13 @@ def main():
                          "wall_ms_per_step": round(r["wall_s"] / dres["nstep"] * 1e3, 5),
                          "state_GBps": round(sbytes / (r["mean_ms"] * 1e-3) / 1e9, 1),
                          "total_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        gms = dres["graph_ms_per_step"]
+        dec["graph_replay"] = {"ms_per_step": round(gms, 5), "total_GBps": round(dbytes / (gms * 1e-3) / 1e9, 1),
+                               "hbm_frac": round(dbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        cms = dres["copy_ms"]
+        dec["copy_reference"] = {"what": f"device copy of {sbytes // 2} B (state-sized read + write), 8 rotating buffers",
+                                 "ms": round(cms, 5), "GBps": round(sbytes / (cms * 1e-3) / 1e9, 1),
+                                 "decode_rotating8_frac_of_copy": round(cms / dres["rotating8"]["mean_ms"], 4)}
         line["decode"] = dec
 
     if not args.no_cpu_baseline:
