@@ -290,7 +290,6 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
         for (int j = 0; j < OWN; ++j) {
             const int ct = w + NW * j;
             if (ct < DKT) {
-#pragma unroll
                 f32x4 ej = F.e[j];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ej[i] = __shfl(ej[i], lane & ~15);
@@ -357,6 +356,9 @@ template <typename TIn, int DK, int DV, int C>
 static hipError_t dispatch_split(const LaunchArgs& a) {
     constexpr int CT = DV / 16;
     const long long tiles = (long long)a.B * a.HV * CT;
+    if constexpr (CT >= 4 && C >= 32) {
+        if (tiles > 1024) return launch_carry_t<TIn, DK, DV, C, 4>(a);
+    }
     if constexpr (CT >= 2) {
         if (tiles > 1024) return launch_carry_t<TIn, DK, DV, C, 2>(a);
     }
