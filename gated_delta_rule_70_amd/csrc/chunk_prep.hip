@@ -89,10 +89,20 @@ __device__ __forceinline__ float f4(const float4& v, int e) {
     return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
 }
 
-// Eight fp16 values: lo = 4 halves at p, hi = 4 halves at p + 16 (or zero).
-__device__ __forceinline__ half8 lds_pair4(const _Float16* p, bool hi_valid) {
-    const uint2 lo = *reinterpret_cast<const uint2*>(p);
-    const uint2 hi = hi_valid ? *reinterpret_cast<const uint2*>(p + 16) : uint2{0u, 0u};
+// token index of (channel c, token r) inside a transposed key tile row
+template <int C>
+__device__ __forceinline__ int kt_swz(int c, int r) {
+    if constexpr (C == 64) return r ^ (8 * (c & 7));
+    return r;
+}
+
+// Fragment of a transposed key tile: row (channel) c, tokens r0 .. r0+3 and r0+16 .. r0+19
+// (the second group zero if the chunk has no such tokens).
+template <int C, int KTP>
+__device__ __forceinline__ half8 kt_frag(const _Float16* tile, int c, int r0) {
+    const _Float16* row = tile + c * KTP;
+    const uint2 lo = *reinterpret_cast<const uint2*>(row + kt_swz<C>(c, r0));
+    const uint2 hi = C > 16 ? *reinterpret_cast<const uint2*>(row + kt_swz<C>(c, r0 + 16)) : uint2{0u, 0u};
     return __builtin_bit_cast(half8, uint4{lo.x, lo.y, hi.x, hi.y});
 }
 
@@ -100,24 +110,39 @@ template <int DK, int C>
 struct PrepLds {
     static constexpr int NB = C / 16;
     static constexpr int KC = DK / 32;
-    static constexpr int KTP = C + 8;  // halves per channel row of a transposed key tile
+    // Transposed key tiles [channel][token], fp16.  At C = 64 a row is exactly 64 tokens and
+    // the token index is XOR-swizzled by the channel (multiples of 8, so 4-token groups stay
+    // contiguous), which spreads a fragment read's 16 channels over the LDS banks; shorter
+    // chunks pad rows instead.
+    static constexpr int KTP = C == 64 ? 64 : C + 8;
     static constexpr int TTP = C + 4;  // floats per row of the transposed inverse
     static constexpr int SZ_KT = DK * KTP * 2;
     static constexpr int SZ_AS = (NB > 1 ? NB - 1 : 1) * KC * 1024;
     static constexpr int SZ_TT = C * TTP * 4;
     static constexpr int SZ_U = (SZ_KT + SZ_AS > SZ_TT) ? SZ_KT + SZ_AS : SZ_TT;
-    static constexpr int NCON = 4 + (NB > 2 ? NB - 2 : 0);  // decay constants per (block, channel)
+    // per block: prefix total, middle-row prefix (DK floats each); the block's diagonal
+    // gram tile (256 floats) reuses the same slot once both are dead
+    static constexpr int TMS = 2 * DK > 256 ? 2 * DK : 256;
+    // per-(block, channel) decay constants: 2 per block in fp32, and in fp16 (the precision
+    // they are applied in) one per off-diagonal tile J <= I - 2
+    __host__ __device__ static constexpr int ebase(int I) {
+        int b = 0;
+        for (int i = 2; i < I; ++i) b += i - 1;
+        return b;
+    }
+    static constexpr int NSE = ebase(NB) > 0 ? ebase(NB) : 1;
 };
+
 
 struct PrepCtx {
     _Float16* sKT;   // (exp(gam) k)^T          [channel][token]  (gram, W)
     _Float16* sKbT;  // (exp(gL - gam) k)^T     [channel][token]  (Kb)         } phase 2-3
     half8* sAs;      // off-diagonal key-side fragments [J][p][lane]           }
     float* sTT;      // Tinv^T                  [token s][token r]             } solve
-    float* sAT;      // diagonal blocks, transposed: A_II, then Tinv_II  [I][j][k] = X[k][j]
-    float* sTot;     // per-block prefix totals [I][channel]
-    float* sMid;     // per-block prefix at the middle row [I][channel]
-    float* sCon;     // per-block decay constants [I][NCON][channel]
+    float* sTM;      // per block [TMS]: prefix total and middle-row prefix [2][channel], later the
+                     // diagonal tile, transposed: A_II, then Tinv_II  [j][k] = X[k][j]
+    float* sCon;     // per-block decay constants [I][2][channel]
+    _Float16* sConE; // off-diagonal decay factors [ebase(I) + I - 2 - J][channel]
     float* sBeta;    // beta per row (0 past the chunk end)
 };
 
@@ -134,11 +159,12 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
     constexpr int DKT = DK / 16;
     constexpr int NQS = (C + 31) / 32;
     constexpr int KTP = PrepLds<DK, C>::KTP;
+    constexpr int TMS = PrepLds<DK, C>::TMS;
     constexpr int TTP = PrepLds<DK, C>::TTP;
     constexpr ChunkRecord R = ChunkRecord::make(C, DK);
     constexpr int NT = I / 2 + 1;  // token reduction steps of row tile I
 
-    constexpr int NCON = PrepLds<DK, C>::NCON;
+    constexpr int EB = PrepLds<DK, C>::ebase(I);  // this block's first off-diagonal factor
     constexpr int ELT = sizeof(TIn);
     const int lane = threadIdx.x & 63;
     const int li = lane & 15;
@@ -187,7 +213,7 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
             x[p][jj] = v;  // local prefix P_r (log2 units) through row r of the block
         }
     if (li == 15 || li == 7) {
-        float* dst = (li == 15 ? s.sTot : s.sMid) + I * DK;
+        float* dst = s.sTM + I * TMS + (li == 15 ? 0 : DK);
 #pragma unroll
         for (int p = 0; p < KC; ++p)
 #pragma unroll
@@ -202,57 +228,54 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
     f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
     half8 bk[KC], bq[KC];  // row-side operands of the off-diagonal tiles (I > 0)
     float* egl_out = reinterpret_cast<float*>(rec + (size_t)R.nfrag * 1024);
-    // Per-channel constants of block I (log2 units; m = middle row, e = gam at the block's
-    // last row, o = gam at the row before the block, gL = gam at the chunk's last row):
-    //   exp(P_m), exp(o + P_m), exp(gL - o - P_m), exp(e - o - P_m)
-    // so that every factor is one of the two per-element exponentials Z = exp(P - P_m),
-    // Zi = exp(P_m - P) times a constant.  One lane per channel computes them.
-    float* con = s.sCon + I * NCON * DK;
+    // Per-channel constants of block I (log2 units; m = middle row, o = gam at the row
+    // before the block, gL = gam at the chunk's last row):
+    //   slot 0: exp(o + P_m), slot 1: exp(gL - o - P_m), so that exp(gam) and
+    //   exp(gL - gam) are the per-element Z = exp(P - P_m) or Zi = exp(P_m - P) times a
+    //   constant; factor I - 2 - J: exp(gam_{16I-1} - gam_{16J+15}) for the off-diagonal
+    //   tiles J <= I - 2 (the decay over the blocks strictly between J and I), in fp16.
+    // One lane per channel computes them.
+    float* con = s.sCon + I * 2 * DK;
 #pragma unroll
     for (int c = lane; c < DK; c += 64) {
-        const float md = s.sMid[I * DK + c];
-        float off = 0.f, gl = 0.f, ti = 0.f;
+        const float md = s.sTM[I * TMS + DK + c];
+        float off = 0.f, gl = 0.f;
 #pragma unroll
         for (int J = 0; J < NB; ++J) {
-            const float v = s.sTot[J * DK + c];
+            const float v = s.sTM[J * TMS + c];
             gl += v;
             if (J < I) off += v;
-            if (J == I) ti = v;
         }
-        con[c] = ex2(md);
-        con[DK + c] = ex2(off + md);
-        con[2 * DK + c] = ex2(gl - off - md);
-        con[3 * DK + c] = ex2(ti - md);
-        // exp(gam_{16I-1} - gam_{16J+15}) for the off-diagonal tiles J <= I - 2 (the decay over
-        // the blocks strictly between J and I), slot 4 + (I - 2 - J)
+        con[c] = ex2(off + md);
+        con[DK + c] = ex2(gl - off - md);
         float between = 0.f;
 #pragma unroll
         for (int J = I - 2; J >= 0; --J) {
-            between += s.sTot[(J + 1) * DK + c];
-            con[(4 + I - 2 - J) * DK + c] = ex2(between);
+            between += s.sTM[(J + 1) * TMS + c];
+            s.sConE[(EB + I - 2 - J) * DK + c] = static_cast<_Float16>(ex2(between));
         }
         if (I == 0) egl_out[c] = ex2(gl);  // exp(gam_last), natural base
     }
-    asm volatile("" ::: "memory");  // this wave's own LDS writes are read back in order
+    // Every wave is past reading the other blocks' totals once this barrier is passed, so a
+    // wave may reuse its own block's slot for its diagonal tile later in this phase.
+    lds_barrier();  // B1b
 #pragma unroll
     for (int p = 0; p < KC; ++p) {
         asm volatile("" ::: "memory");  // keep this step's LDS reads here (register pressure)
-        float md[8], c1[8], c2[8], c3[8], c4[8];
+        float md[8], ti[8], c2[8], c3[8];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int cb = 32 * p + 16 * hh + 4 * gq;
-            const float4 m4 = *reinterpret_cast<const float4*>(s.sMid + I * DK + cb);
-            const float4 k1 = *reinterpret_cast<const float4*>(con + cb);
-            const float4 k2 = *reinterpret_cast<const float4*>(con + DK + cb);
-            const float4 k3 = *reinterpret_cast<const float4*>(con + 2 * DK + cb);
-            const float4 k4 = *reinterpret_cast<const float4*>(con + 3 * DK + cb);
+            const float4 m4 = *reinterpret_cast<const float4*>(s.sTM + I * TMS + DK + cb);
+            const float4 t4 = *reinterpret_cast<const float4*>(s.sTM + I * TMS + cb);
+            const float4 k2 = *reinterpret_cast<const float4*>(con + cb);
+            const float4 k3 = *reinterpret_cast<const float4*>(con + DK + cb);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 md[4 * hh + e] = f4(m4, e);
-                c1[4 * hh + e] = f4(k1, e);
+                ti[4 * hh + e] = f4(t4, e);
                 c2[4 * hh + e] = f4(k2, e);
                 c3[4 * hh + e] = f4(k3, e);
-                c4[4 * hh + e] = f4(k4, e);
             }
         }
         half8 qt, as;
@@ -267,19 +290,19 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
             const float zi = ex2(-dz);
             const float eg = z * c2[jj];
             qt[jj] = static_cast<_Float16>(qv * eg);
-            s.sKT[c * KTP + r] = static_cast<_Float16>(kv * eg);
-            s.sKbT[c * KTP + r] = static_cast<_Float16>(kv * (zi * c3[jj]));
+            s.sKT[c * KTP + kt_swz<C>(c, r)] = static_cast<_Float16>(kv * eg);
+            s.sKbT[c * KTP + kt_swz<C>(c, r)] = static_cast<_Float16>(kv * (zi * c3[jj]));
             // diagonal tiles on the fp32 matrix cores: reduction step = this slot's channel
             // in each of the four lane groups
             const float a = kv * zi;
             accA = mfma_f32(a, kv * z, accA);
             accP = mfma_f32(a, qv * z, accP);
             if constexpr (I > 0) {
-                const float zs = z * c1[jj];
+                const float zs = ex2(x[p][jj]);  // exp(gam - gam_{16I-1}) <= 1
                 bk[p][jj] = static_cast<_Float16>(kv * zs);
                 bq[p][jj] = static_cast<_Float16>(qv * zs);
             }
-            if constexpr (I < NB - 1) as[jj] = static_cast<_Float16>(kv * (zi * c4[jj]));
+            if constexpr (I < NB - 1) as[jj] = static_cast<_Float16>(kv * ex2(ti[jj] - x[p][jj]));
         }
         frags[(size_t)(R.off_qt + I * KC + p) * 64 + lane] = qt;
         if constexpr (I < NB - 1) s.sAs[(I * KC + p) * 64 + lane] = as;
@@ -294,7 +317,7 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
 
     // ---- diagonal block inverse, rows by lane: T_II = (I + A_II)^-1 ----------------------
     // Only this wave's rows are involved, so it runs while the other waves finish phase 2.
-    float* at = s.sAT + I * 256;
+    float* at = s.sTM + I * TMS;  // this block's totals are dead (barrier B1b)
 #pragma unroll
     for (int i = 0; i < 4; ++i) at[(4 * gq + i) * 16 + li] = accA[i];
     asm volatile("" ::: "memory");
@@ -333,15 +356,10 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
             half8 ak = s.sAs[(J * KC + p) * 64 + lane];
             if (J < I - 1) {
                 // blocks between J and I: scale the key side by exp(gam_{16I-1} - gam_{16J+15})
-                half8 ef;
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const float4 e4 = *reinterpret_cast<const float4*>(
-                        s.sCon + (I * NCON + 4 + I - 2 - J) * DK + 32 * p + 16 * hh + 4 * gq);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) ef[4 * hh + e] = static_cast<_Float16>(f4(e4, e));
-                }
-                ak = ak * ef;
+                const _Float16* er = s.sConE + (EB + I - 2 - J) * DK + 32 * p + 4 * gq;
+                const uint2 e0 = *reinterpret_cast<const uint2*>(er);
+                const uint2 e1 = *reinterpret_cast<const uint2*>(er + 16);
+                ak = ak * __builtin_bit_cast(half8, uint4{e0.x, e0.y, e1.x, e1.y});
             }
             a = mfma_f16(ak, bk[p], a);
             pc = mfma_f16(ak, bq[p], pc);
@@ -353,14 +371,14 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
     for (int f = I; f < DKT * NQS; f += NB) {
         const int ct = f / NQS, qs = f % NQS;
         frags[(size_t)(R.off_kb + f) * 64 + lane] =
-            lds_pair4(s.sKbT + (16 * ct + li) * KTP + 32 * qs + 4 * gq, C > 16);
+            kt_frag<C, KTP>(s.sKbT, 16 * ct + li, 32 * qs + 4 * gq);
     }
 #pragma unroll
     for (int J = 0; J < I; ++J)
 #pragma unroll
         for (int i = 0; i < 4; ++i) aR[J][i] *= bta;
 #pragma unroll
-    for (int qs = 0; qs < NQS; ++qs) {
+    for (int qs = 0; qs < NT; ++qs) {  // fragments above the diagonal are zero and never read
         half8 v;
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
@@ -407,17 +425,15 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
             }
             frags[(size_t)(R.off_tb + I * NQS + qs) * 64 + lane] = tb[qs];
         }
-#pragma unroll
-        for (int qs = NT; qs < NQS; ++qs)
-            frags[(size_t)(R.off_tb + I * NQS + qs) * 64 + lane] = half8{};
+
         // W^T = (exp(gam) K)^T Tb^T: A operand from the transposed key tile, B operand Tb
 #pragma unroll
         for (int p = 0; p < KC; ++p) {
             f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int qs = 0; qs < NT; ++qs) {
-                const half8 k0 = lds_pair4(s.sKT + (32 * p + li) * KTP + 32 * qs + 4 * gq, C > 16);
-                const half8 k1 = lds_pair4(s.sKT + (32 * p + 16 + li) * KTP + 32 * qs + 4 * gq, C > 16);
+                const half8 k0 = kt_frag<C, KTP>(s.sKT, 32 * p + li, 32 * qs + 4 * gq);
+                const half8 k1 = kt_frag<C, KTP>(s.sKT, 32 * p + 16 + li, 32 * qs + 4 * gq);
                 a0 = mfma_f16(k0, tb[qs], a0);
                 a1 = mfma_f16(k1, tb[qs], a1);
             }
@@ -459,7 +475,7 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
 }
 
 template <typename TIn, int DK, int C>
-__global__ __launch_bounds__(C * 4, 2) void chunk_prep_kernel(const TIn* __restrict__ q,
+__global__ __launch_bounds__(C * 4, 3) void chunk_prep_kernel(const TIn* __restrict__ q,
                                                               const TIn* __restrict__ k,
                                                               const float* __restrict__ g,
                                                               const float* __restrict__ beta,
@@ -469,10 +485,9 @@ __global__ __launch_bounds__(C * 4, 2) void chunk_prep_kernel(const TIn* __restr
     constexpr int NB = C / 16;
     constexpr ChunkRecord R = ChunkRecord::make(C, DK);
     __shared__ __align__(16) _Float16 sKT[DK * Lds::KTP];
-    __shared__ __align__(16) float sTot[NB * DK];
-    __shared__ __align__(16) float sMid[NB * DK];
-    __shared__ __align__(16) float sCon[NB * Lds::NCON * DK];
-    __shared__ __align__(16) float sAT[NB * 256];
+    __shared__ __align__(16) float sTM[NB * Lds::TMS];
+    __shared__ __align__(16) float sCon[NB * 2 * DK];
+    __shared__ __align__(16) _Float16 sConE[Lds::NSE * DK];
     __shared__ __align__(16) float sBeta[C];
     __shared__ __align__(16) unsigned char sU[Lds::SZ_U];
     PrepCtx s;
@@ -480,18 +495,27 @@ __global__ __launch_bounds__(C * 4, 2) void chunk_prep_kernel(const TIn* __restr
     s.sKbT = reinterpret_cast<_Float16*>(sU);
     s.sAs = reinterpret_cast<half8*>(sU + Lds::SZ_KT);
     s.sTT = reinterpret_cast<float*>(sU);
-    s.sAT = sAT;
+    s.sTM = sTM;
     s.sCon = sCon;
-    s.sTot = sTot;
-    s.sMid = sMid;
+    s.sConE = sConE;
     s.sBeta = sBeta;
 
-    const int item = blockIdx.x;
-    const int n = item % NC;
-    const int bh = item / NC;
-    const int h = bh % HV;
-    const int b = bh / HV;
-    const int kh = h / (HV / HK);
+    // Block -> item: the G value heads that share a key head (and so read the same q and k
+    // rows) get blocks 8 apart, i.e. the same XCD (blocks are dealt round-robin to the 8
+    // XCDs) at about the same time, so all but the first read of each q/k row hit that
+    // XCD's L2.  Runs of 8G blocks cover 8 (batch, key head, chunk) triples; the last run's
+    // unused blocks return at once.
+    const int G = HV / HK;
+    const int blk = blockIdx.x;
+    const int within = blk % (8 * G);
+    const int pair = (blk / (8 * G)) * 8 + within % 8;
+    if (pair >= B * HK * NC) return;
+    const int n = pair % NC;
+    const int bk = pair / NC;
+    const int kh = bk % HK;
+    const int b = bk / HK;
+    const int h = kh * G + within / 8;
+    const int bh = b * HV + h;
     const int t0 = n * C;
     const int L = min(C, T - t0);
     unsigned char* rec = ws + ((size_t)bh * NC + n) * R.bytes;
@@ -509,8 +533,9 @@ __global__ __launch_bounds__(C * 4, 2) void chunk_prep_kernel(const TIn* __restr
 template <typename TIn, int DK, int C>
 hipError_t launch_prep_t(const LaunchArgs& a) {
     const int NC = (a.T + C - 1) / C;
-    const long long items = (long long)a.B * a.HV * NC;
-    hipLaunchKernelGGL((chunk_prep_kernel<TIn, DK, C>), dim3((unsigned)items), dim3(C * 4), 0,
+    const long long pairs = (long long)a.B * a.HK * NC;  // (batch, key head, chunk) triples
+    const long long blocks = (pairs + 7) / 8 * 8 * (a.HV / a.HK);
+    hipLaunchKernelGGL((chunk_prep_kernel<TIn, DK, C>), dim3((unsigned)blocks), dim3(C * 4), 0,
                        (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g, a.beta,
                        (unsigned char*)a.workspace, a.B, a.T, a.HK, a.HV, NC);
     return hipGetLastError();

@@ -33,8 +33,9 @@ struct LaunchArgs {
 //   Kb  [dkt][nqs]  decay-to-end keys, transposed           (rows c, reduction over tokens)
 //   Tb  [nb][nqs]   Tinv diag(beta)                         (rows r, reduction over tokens)
 //   P   [nb][nqs]   causal q.k terms                        (rows r, reduction over tokens)
-// Tb and P are lower triangular; their all-zero fragments are stored too, so every row
-// tile reads the same operand count.
+// Tb and P are lower triangular: the slots of their all-zero fragments (token steps above
+// a row tile's diagonal) are left unwritten, and the carry reads them as zeros from
+// beyond the buffer range, so every row tile issues the same operand loads.
 struct ChunkRecord {
     int nb;        // 16-row blocks per chunk (C / 16)
     int nqs;       // 32-wide token reduction steps (ceil(C / 32))
