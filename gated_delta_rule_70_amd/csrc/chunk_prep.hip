@@ -50,6 +50,13 @@ __device__ __forceinline__ float row_shr(float x) {
                                                                  0x110 + N, 0xF, 0xF, false));
 }
 
+// x from row lane N of the same 16-lane DPP row, in every lane of the row.
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 0x150 + N, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // D(16x16) += A(16x4) B(4x16) in fp32.  Lane l supplies A[l % 16][l / 16] and
@@ -120,11 +127,11 @@ struct PrepLds {
     static constexpr int SZ_AS = (NB > 1 ? NB - 1 : 1) * KC * 1024;
     static constexpr int SZ_TT = C * TTP * 4;
     static constexpr int SZ_U = (SZ_KT + SZ_AS > SZ_TT) ? SZ_KT + SZ_AS : SZ_TT;
-    // per block: prefix total, middle-row prefix (DK floats each); the block's diagonal
-    // gram tile (256 floats) reuses the same slot once both are dead
+    // per block: prefix total, middle-row prefix (DK floats each); then the block's two
+    // per-channel decay constants; then its diagonal gram tile (256 floats)
     static constexpr int TMS = 2 * DK > 256 ? 2 * DK : 256;
-    // per-(block, channel) decay constants: 2 per block in fp32, and in fp16 (the precision
-    // they are applied in) one per off-diagonal tile J <= I - 2
+    // per-(block, channel) off-diagonal decay factors in fp16 (the precision they are
+    // applied in), one per off-diagonal tile J <= I - 2
     __host__ __device__ static constexpr int ebase(int I) {
         int b = 0;
         for (int i = 2; i < I; ++i) b += i - 1;
@@ -139,9 +146,9 @@ struct PrepCtx {
     _Float16* sKbT;  // (exp(gL - gam) k)^T     [channel][token]  (Kb)         } phase 2-3
     half8* sAs;      // off-diagonal key-side fragments [J][p][lane]           }
     float* sTT;      // Tinv^T                  [token s][token r]             } solve
-    float* sTM;      // per block [TMS]: prefix total and middle-row prefix [2][channel], later the
-                     // diagonal tile, transposed: A_II, then Tinv_II  [j][k] = X[k][j]
-    float* sCon;     // per-block decay constants [I][2][channel]
+    float* sTM;      // per block [TMS]: prefix total and middle-row prefix [2][channel], then the
+                     // block's decay constants [2][channel], then the diagonal tile,
+                     // transposed: A_II, then Tinv_II  [j][k] = X[k][j]
     _Float16* sConE; // off-diagonal decay factors [ebase(I) + I - 2 - J][channel]
     float* sBeta;    // beta per row (0 past the chunk end)
 };
@@ -234,10 +241,14 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
     //   exp(gL - gam) are the per-element Z = exp(P - P_m) or Zi = exp(P_m - P) times a
     //   constant; factor I - 2 - J: exp(gam_{16I-1} - gam_{16J+15}) for the off-diagonal
     //   tiles J <= I - 2 (the decay over the blocks strictly between J and I), in fp16.
-    // One lane per channel computes them.
-    float* con = s.sCon + I * 2 * DK;
+    // One lane per channel computes them; slots 0 and 1 go to this block's sTM slot once
+    // no wave reads the totals any more.
+    constexpr int NCL = (DK + 63) / 64;  // channels per lane
+    float c0[NCL], c1[NCL];
 #pragma unroll
-    for (int c = lane; c < DK; c += 64) {
+    for (int u = 0; u < NCL; ++u) {
+        const int c = lane + 64 * u;
+        if (c >= DK) break;
         const float md = s.sTM[I * TMS + DK + c];
         float off = 0.f, gl = 0.f;
 #pragma unroll
@@ -246,8 +257,8 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
             gl += v;
             if (J < I) off += v;
         }
-        con[c] = ex2(off + md);
-        con[DK + c] = ex2(gl - off - md);
+        c0[u] = ex2(off + md);
+        c1[u] = ex2(gl - off - md);
         float between = 0.f;
 #pragma unroll
         for (int J = I - 2; J >= 0; --J) {
@@ -257,23 +268,37 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
         if (I == 0) egl_out[c] = ex2(gl);  // exp(gam_last), natural base
     }
     // Every wave is past reading the other blocks' totals once this barrier is passed, so a
-    // wave may reuse its own block's slot for its diagonal tile later in this phase.
+    // wave may reuse its own block's slot: first for its decay constants, after this phase
+    // for its diagonal tile.  Only this wave reads the slot from here on, and a wave's LDS
+    // accesses complete in issue order.
     lds_barrier();  // B1b
+    float* con = s.sTM + I * TMS;
+#pragma unroll
+    for (int u = 0; u < NCL; ++u) {
+        const int c = lane + 64 * u;
+        if (c >= DK) break;
+        con[c] = c0[u];
+        con[DK + c] = c1[u];
+    }
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int p = 0; p < KC; ++p) {
         asm volatile("" ::: "memory");  // keep this step's LDS reads here (register pressure)
+        // middle-row prefix and block total of each channel: rows 7 and 15 of the lane's
+        // 16-lane row, which holds one token row per lane for the same channels
         float md[8], ti[8], c2[8], c3[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            md[jj] = row_bcast<7>(x[p][jj]);
+            ti[jj] = row_bcast<15>(x[p][jj]);
+        }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int cb = 32 * p + 16 * hh + 4 * gq;
-            const float4 m4 = *reinterpret_cast<const float4*>(s.sTM + I * TMS + DK + cb);
-            const float4 t4 = *reinterpret_cast<const float4*>(s.sTM + I * TMS + cb);
             const float4 k2 = *reinterpret_cast<const float4*>(con + cb);
             const float4 k3 = *reinterpret_cast<const float4*>(con + DK + cb);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                md[4 * hh + e] = f4(m4, e);
-                ti[4 * hh + e] = f4(t4, e);
                 c2[4 * hh + e] = f4(k2, e);
                 c3[4 * hh + e] = f4(k3, e);
             }
@@ -317,7 +342,7 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
 
     // ---- diagonal block inverse, rows by lane: T_II = (I + A_II)^-1 ----------------------
     // Only this wave's rows are involved, so it runs while the other waves finish phase 2.
-    float* at = s.sTM + I * TMS;  // this block's totals are dead (barrier B1b)
+    float* at = s.sTM + I * TMS;  // this block's decay constants are dead (phase 2 is over)
 #pragma unroll
     for (int i = 0; i < 4; ++i) at[(4 * gq + i) * 16 + li] = accA[i];
     asm volatile("" ::: "memory");
@@ -486,7 +511,6 @@ __global__ __launch_bounds__(C * 4, 3) void chunk_prep_kernel(const TIn* __restr
     constexpr ChunkRecord R = ChunkRecord::make(C, DK);
     __shared__ __align__(16) _Float16 sKT[DK * Lds::KTP];
     __shared__ __align__(16) float sTM[NB * Lds::TMS];
-    __shared__ __align__(16) float sCon[NB * 2 * DK];
     __shared__ __align__(16) _Float16 sConE[Lds::NSE * DK];
     __shared__ __align__(16) float sBeta[C];
     __shared__ __align__(16) unsigned char sU[Lds::SZ_U];
@@ -496,7 +520,6 @@ __global__ __launch_bounds__(C * 4, 3) void chunk_prep_kernel(const TIn* __restr
     s.sAs = reinterpret_cast<half8*>(sU + Lds::SZ_KT);
     s.sTT = reinterpret_cast<float*>(sU);
     s.sTM = sTM;
-    s.sCon = sCon;
     s.sConE = sConE;
     s.sBeta = sBeta;
 
