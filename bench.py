@@ -24,6 +24,14 @@ match the digest recorded with it:
 traffic (a 256 MiB fp32 negation: 256 MiB read, 256 MiB written); the counters of every
 kernel are scaled by what they read for it.  ``--summarize-stats <dir>`` turns a
 ``rocprofv3 --kernel-trace --stats`` run into the kernel-time summary under profiles/.
+
+Matrix-core use and the sustained clock come from a third counter run (same rule for the
+digest):
+
+    rocprofv3 --kernel-trace --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F16 \
+        SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE -d <dirU> -o run -f csv \
+        -- python3 bench.py --profile-run
+    python3 bench.py --summarize-util <dirU>            # -> profiles/mfma_util_...md
 """
 from __future__ import annotations
 
@@ -55,6 +63,11 @@ KERNEL_SYMBOL = {"chunk_prep": "chunk_prep_kernel", "chunk_carry": "chunk_carry_
                  "decode": "decode_kernel"}
 CALIB_BYTES = 256 << 20           # calibration kernel: reads and writes this many bytes
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_b1_t4097_decode_b32.md")
+UTIL_SUMMARY = os.path.join(ROOT, "profiles", "mfma_util_prefill_b1_t4097_decode_b32.md")
+UTIL_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_F32",
+                 "GRBM_GUI_ACTIVE"]
+SIMD_NUM = 1024                # 256 CUs x 4 SIMDs
+XCD_NUM = 8                    # the counter CSV sums GRBM_GUI_ACTIVE over the 8 XCDs
 
 
 def source_digest(kernel):
@@ -138,6 +151,109 @@ def summarize_pmc(fetch_dir, write_dir):
     with open(TRAFFIC_SUMMARY, "w") as f:
         f.write("\n".join(lines))
     print(f"wrote {TRAFFIC_SUMMARY}")
+
+
+def _per_dispatch(rows, counter, reduce):
+    """kernel name -> list over dispatches of `counter` reduced over the rows of a dispatch
+    (one row per agent dimension: SE, SIMD, XCD...)."""
+    disp = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        disp.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), []).append(float(r["Counter_Value"]))
+    out = {}
+    for (name, did), vals in disp.items():
+        out.setdefault(name, {})[did] = reduce(vals)
+    return out
+
+
+def _dispatch_ns(d):
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    ns = {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                ns[(r["Kernel_Name"], r["Dispatch_Id"])] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    return ns
+
+
+def summarize_util(util_dir):
+    """Matrix-core busy fraction (MFMA busy cycles summed over SIMDs / (one XCD's GUI-active
+    cycles x SIMDs), the profiler's MfmaUtil) and counted matrix flops (MOPS x 512), per
+    launch and per second of traced dispatch time."""
+    rows = _counter_rows(util_dir)
+    busy = _per_dispatch(rows, "SQ_VALU_MFMA_BUSY_CYCLES", sum)
+    m16 = _per_dispatch(rows, "SQ_INSTS_VALU_MFMA_MOPS_F16", sum)
+    m32 = _per_dispatch(rows, "SQ_INSTS_VALU_MFMA_MOPS_F32", sum)
+    gui = _per_dispatch(rows, "GRBM_GUI_ACTIVE", max)
+    dur = _dispatch_ns(util_dir)
+    out = {"kernels": {}}
+    for kern, sym in KERNEL_SYMBOL.items():
+        names = [k for k in gui if sym in k]
+        if not names:
+            continue
+        nm = max(names, key=lambda k: max(gui[k].values()))  # the instantiation the workload launches
+        ids = sorted(gui[nm])
+        ns = [dur[(nm, i)] for i in ids if (nm, i) in dur]
+        mean = lambda dct: sum(dct.get(i, 0.0) for i in ids) / len(ids)
+        g, b = mean(gui[nm]) / XCD_NUM, mean(busy.get(nm, {}))
+        f16, f32 = mean(m16.get(nm, {})) * 512, mean(m32.get(nm, {})) * 512
+        t = sum(ns) / len(ns) * 1e-9 if ns else None
+        out["kernels"][kern] = {
+            "symbol": nm, "dispatches": len(ids), "gui_active_cycles": g, "mfma_busy_cycles": b,
+            "mfma_busy_frac": b / (g * SIMD_NUM) if g else None,
+            "mfma_f16_flops": f16, "mfma_f32_flops": f32,
+            "traced_us": t * 1e6 if t else None,
+            "mfma_f16_TFLOPs": f16 / t / 1e12 if t else None,
+            "source_digest": source_digest(kern)}
+    cmd = ("rocprofv3 --kernel-trace --pmc " + " ".join(UTIL_COUNTERS) +
+           " -d gpurun_out/pmc_util -o run -f csv -- python3 bench.py --profile-run")
+    lines = ["# Matrix-core use and clock per launch: prefill B=1 T=4097 HV=32 dk=dv=128 and decode B=32",
+             "",
+             "One counter run of the short benchmark with a kernel trace beside it.  MFMA busy =",
+             "busy cycles summed over the 1024 SIMDs / (GUI-active cycles of one XCD x 1024), the",
+             "profiler's MfmaUtil (the CSV sums GRBM_GUI_ACTIVE over the 8 XCDs); matrix flops =",
+             "MOPS x 512 (the counters count add or multiply operations in units of 512).  The",
+             "GUI-active window of a dispatch is somewhat longer than its traced time, so the busy",
+             "fraction is a slight underestimate and no clock is derived from it; the profiler",
+             "serialises dispatches while it counts, so the traced times are not the benchmark's.",
+             "`source_digest` identifies the kernel sources; bench.py reports the figures only",
+             "while the sources still match.",
+             "",
+             "Commands (repository root, one MI355X):",
+             "",
+             "```",
+             cmd,
+             "python3 bench.py --summarize-util gpurun_out/pmc_util",
+             "```",
+             "",
+             "| kernel | traced us | MFMA busy | f16 matrix GFLOP | f16 matrix TFLOP/s | f32 matrix GFLOP |",
+             "|---|---|---|---|---|---|"]
+    for kern, v in out["kernels"].items():
+        fmt = lambda x, f: "n/a" if x is None else format(x, f)
+        lines.append(f"| `{kern}` | {fmt(v['traced_us'], '.2f')} | {fmt(v['mfma_busy_frac'], '.2%')} | "
+                     f"{v['mfma_f16_flops'] / 1e9:.3f} | {fmt(v['mfma_f16_TFLOPs'], '.1f')} | "
+                     f"{v['mfma_f32_flops'] / 1e9:.3f} |")
+    lines += ["", "```json", json.dumps(out, indent=1), "```", ""]
+    with open(UTIL_SUMMARY, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {UTIL_SUMMARY}")
+
+
+def read_util(kernel):
+    """Matrix-core figures of `kernel` for the current sources, or None."""
+    try:
+        with open(UTIL_SUMMARY) as f:
+            blob = json.loads(f.read().split("```json", 1)[1].split("```", 1)[0])
+        k = blob["kernels"][kernel]
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
+    if k.get("source_digest") != source_digest(kernel):
+        return None
+    return {"mfma_busy_frac": k["mfma_busy_frac"],
+            "mfma_f16_flops_counted": k["mfma_f16_flops"], "mfma_f32_flops_counted": k["mfma_f32_flops"]}
 
 
 def read_traffic(kernel):
@@ -356,8 +472,12 @@ def main():
     ap.add_argument("--profile-run", action="store_true",
                     help="short run for counter collection, plus the calibration kernel")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-util", metavar="UTIL_DIR")
     ap.add_argument("--summarize-stats", nargs=3, metavar=("DIR", "NAME", "COMMAND"))
     args = ap.parse_args()
+    if args.summarize_util:
+        summarize_util(args.summarize_util)
+        return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
@@ -414,6 +534,7 @@ def main():
         "path_frac_of_bf16_mfma_peak": round(path_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "ceiling_ms": round(ceil_ms, 5), "path_frac_of_ceiling": round(ceil_ms / kern_ms, 4),
         "tokens_per_s_kernel_time": round(ntok / (kern_ms * 1e-3), 1),
+        "counters": {"chunk_prep": read_util("chunk_prep"), "chunk_carry": read_util("chunk_carry")},
     }
 
     line = {
