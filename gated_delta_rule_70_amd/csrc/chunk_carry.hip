@@ -37,6 +37,19 @@ namespace gdr {
 
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
+// x from lane j (0..15) of the same 16-lane DPP row, in every lane of the row; j must fold
+// to a constant.
+__device__ __forceinline__ float row_lane(float x, int j) {
+#define GDR_BC(J) \
+    case J: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J, 0xF, 0xF, false));
+    switch (j) {
+        GDR_BC(0) GDR_BC(1) GDR_BC(2) GDR_BC(3) GDR_BC(4) GDR_BC(5) GDR_BC(6) GDR_BC(7)
+        GDR_BC(8) GDR_BC(9) GDR_BC(10) GDR_BC(11) GDR_BC(12) GDR_BC(13) GDR_BC(14)
+        default: GDR_BC(15)
+    }
+#undef GDR_BC
+}
+
 __device__ __forceinline__ half4 to_half4(f32x4 x) {
     return half4{static_cast<_Float16>(x[0]), static_cast<_Float16>(x[1]), static_cast<_Float16>(x[2]),
                  static_cast<_Float16>(x[3])};
@@ -156,14 +169,14 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
                 V[qs][nt] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
     };
-    // outputs of row tile w of chunk n (rows past T fall outside the buffer and are dropped;
-    // the row stays in the per-lane offset so one form serves every chunk)
+    // outputs of row tile w of chunk n, held transposed (lane (i, g): row 16w + i, columns
+    // 4g .. 4g+3 of each column tile), so one 16-byte store per lane and tile; rows past T
+    // fall outside the buffer and are dropped (the row stays in the per-lane offset so one
+    // form serves every chunk)
     auto store_o = [&](int n, const f32x4 (&O)[NT]) {
-        const int obase = ((n * C + 16 * w + 4 * gq) * HV + h) * DV * 4;
+        const int obase = ((n * C + 16 * w + li) * HV + h) * DV * 4 + (16 * cg * NT + 4 * gq) * 4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) buf_store_f32(O[nt][i], rs_o, obase + jcol[nt] * 4 + i * rowo, 0);
+        for (int nt = 0; nt < NT; ++nt) buf_store_f32x4(O[nt], rs_o, obase, nt * 64);
     };
 
     // This wave's operand fragments, in registers, in a ring of three sets (the empty asm
@@ -171,7 +184,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
     // use and stall).  The chunk loop is unrolled by three so each set has fixed registers.
     struct Frags {
         half8 tb[NQS], w[KC], q[KC], p[NQS], kb[OWN][NQS];
-        f32x4 e[OWN];
+        f32x4 e;                 // exp(gam_last) of owned state tile j, in row lane j
         uint32_t v[NT][ELT];     // raw bits of this wave's v rows of the chunk
     };
     // A per-lane offset past every record range: such a load reads zeros without touching
@@ -181,13 +194,20 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
         dst = buf_load_half8(rs_rec, vrec, f * 1024);
         asm volatile("" ::: "memory");
     };
-    // exp(gam_last) for rows 16ct + 4gq .. +3: one lane per 16-lane group loads it (the
-    // others read zeros from beyond the range) and shares it at use time
-    auto ld_egl = [&](int n, int ct) {
-        return buf_load_f32x4(rs_rec, li == 0 ? n * R.bytes + gq * 16 : kBeyond, R.nfrag * 1024 + ct * 64);
+    // exp(gam_last) of the owned state tiles, one load per wave: row lane j of lane group g
+    // reads rows 16 ct_j + 4g .. +3 (the other lanes read zeros from beyond the range); the
+    // values are broadcast along the row at use time
+    auto ld_egl = [&](int n) {
+        const int ct = w + NW * li;
+        const bool on = li < OWN && ct < DKT;
+        return buf_load_f32x4(rs_rec, on ? n * R.bytes + ct * 64 + gq * 16 : kBeyond, R.nfrag * 1024);
     };
-    auto load_all = [&](Frags& F, int n) {
+    // A chunk's operands are requested in four groups spread over the step two chunks
+    // earlier, so the vector-memory unit works through them while the step computes
+    // instead of holding up the wave behind a burst of requests.
+    auto ld_g1 = [&](Frags& F, int n) {  // v rows, Tb, P
         const int vrec = n * R.bytes + lane * 16;
+        load_v(n, F.v);
         // Tb and P fragments above row tile w's diagonal are zero: read them from beyond the
         // range instead of from memory (a per-wave choice of offset, no branch)
 #pragma unroll
@@ -196,28 +216,41 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
             ld(F.tb[qs], vq, R.off_tb + w * NQS + qs);
             ld(F.p[qs], vq, R.off_p + w * NQS + qs);
         }
+    };
+    auto ld_g2 = [&](Frags& F, int n) {  // W
+        const int vrec = n * R.bytes + lane * 16;
 #pragma unroll
-        for (int p = 0; p < KC; ++p) {
-            ld(F.w[p], vrec, R.off_w + w * KC + p);
-            ld(F.q[p], vrec, R.off_qt + w * KC + p);
-        }
+        for (int p = 0; p < KC; ++p) ld(F.w[p], vrec, R.off_w + w * KC + p);
+    };
+    auto ld_g3 = [&](Frags& F, int n) {  // Qt
+        const int vrec = n * R.bytes + lane * 16;
+#pragma unroll
+        for (int p = 0; p < KC; ++p) ld(F.q[p], vrec, R.off_qt + w * KC + p);
+    };
+    auto ld_g4 = [&](Frags& F, int n) {  // Kb, exp(gam_last)
+        const int vrec = n * R.bytes + lane * 16;
 #pragma unroll
         for (int j = 0; j < OWN; ++j) {
             const int ct = w + NW * j;
             if (ct < DKT) {
 #pragma unroll
                 for (int qs = 0; qs < NQS; ++qs) ld(F.kb[j][qs], vrec, R.off_kb + ct * NQS + qs);
-                F.e[j] = ld_egl(n, ct);
             }
         }
-        load_v(n, F.v);
+        F.e = ld_egl(n);
+    };
+    auto load_all = [&](Frags& F, int n) {
+        ld_g1(F, n);
+        ld_g2(F, n);
+        ld_g3(F, n);
+        ld_g4(F, n);
     };
 
     f32x4 Op[NT];
     // One chunk: request chunk nn's operands into set Fn, consume set F (chunk n), using
     // exchange-buffer copy `par`.
     auto step = [&](Frags& F, Frags& Fn, int n, int nn, int par) {
-        load_all(Fn, nn);
+        ld_g1(Fn, nn);
         // The empty asm fixes where the raw v bits are consumed: the compiler would otherwise
         // convert them a step early, while their load may still be in flight.
 #pragma unroll
@@ -247,6 +280,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
         read_v(Vc, sV[par]);
 
         if (n > 0) store_o(n - 1, Op);
+        ld_g2(Fn, nn);
 
         // 2. U_w = Tb V - W S for row tile w
         f32x4 U[NT];
@@ -264,13 +298,15 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             *(reinterpret_cast<half4*>(&sUB[par][((w >> 1) * NT + nt) * 64 + lane]) + (w & 1)) = to_half4(U[nt]);
-        // 4. O_w = Qt S (independent of U; overlaps the exchange)
+        ld_g3(Fn, nn);
+        // 4. O_w^T = S^T Qt^T (independent of U; overlaps the exchange).  The operands swap
+        // places: a fragment reads the same as an A operand of X and a B operand of X^T.
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) Op[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int p = 0; p < KC; ++p)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) Op[nt] = mfma_f16(F.q[p], SB[p][nt], Op[nt]);
+            for (int nt = 0; nt < NT; ++nt) Op[nt] = mfma_f16(SB[p][nt], F.q[p], Op[nt]);
         lds_barrier();
         half8 UB[NQS][NT];
 #pragma unroll
@@ -284,15 +320,16 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
                 }
                 UB[qs][nt] = x;
             }
+        ld_g4(Fn, nn);
 
         // 5. S' = diag(exp(gam_last)) S + Kb^T U for the owned state tiles
 #pragma unroll
         for (int j = 0; j < OWN; ++j) {
             const int ct = w + NW * j;
             if (ct < DKT) {
-                f32x4 ej = F.e[j];
+                f32x4 ej;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ej[i] = __shfl(ej[i], lane & ~15);
+                for (int i = 0; i < 4; ++i) ej[i] = row_lane(F.e[i], j);
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) S[j][nt] *= ej;
 #pragma unroll
@@ -301,11 +338,11 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
                     for (int nt = 0; nt < NT; ++nt) S[j][nt] = mfma_f16(F.kb[j][qs], UB[qs][nt], S[j][nt]);
             }
         }
-        // 6. O_w += P U
+        // 6. O_w^T += U^T P^T
 #pragma unroll
         for (int qs = 0; qs < NQS; ++qs)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) Op[nt] = mfma_f16(F.p[qs], UB[qs][nt], Op[nt]);
+            for (int nt = 0; nt < NT; ++nt) Op[nt] = mfma_f16(UB[qs][nt], F.p[qs], Op[nt]);
     };
 
     Frags FA, FB, FC;

@@ -11,6 +11,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Raw 16-bit storage of bf16 inputs.
 struct bf16_t {
@@ -66,6 +67,9 @@ __device__ __forceinline__ float raw_to_f32(uint32_t x, float) { return __uint_a
 __device__ __forceinline__ float raw_to_f32(uint32_t x, bf16_t) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ void buf_store_f32(float x, rsrc_t r, int voff, int soff) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_store_f32x4(f32x4 x, rsrc_t r, int voff, int soff) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, voff, soff, 0);
 }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
