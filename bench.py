@@ -60,7 +60,7 @@ KERNEL_SOURCES = {  # kernel -> the sources its machine code is built from
     "decode": ["decode.hip", "gdr_device.h", "gdr_launch.h"],
 }
 KERNEL_SYMBOL = {"chunk_prep": "chunk_prep_kernel", "chunk_carry": "chunk_carry_kernel",
-                 "decode": "decode_kernel"}
+                 "decode": "token_kernel"}
 CALIB_BYTES = 256 << 20           # calibration kernel: reads and writes this many bytes
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_b1_t4097_decode_b32.md")
 UTIL_SUMMARY = os.path.join(ROOT, "profiles", "mfma_util_prefill_b1_t4097_decode_b32.md")
@@ -460,6 +460,78 @@ def bench_decode(w, steps, warmup):
     }
 
 
+SHORT_T = (1, 2, 4, 8, 16, 32, 64)
+
+
+def bench_short_calls(w, reps=10):
+    """Short multi-token calls at the decode workload's shape: for each T, one call's time
+    as T decode launches, as one fused-recurrent launch and as the chunked prefill (best of
+    chunk 16/32/64), all on the same inputs, calls issued back to back and timed with HIP
+    events on the launch stream."""
+    import torch
+
+    import gated_delta_rule_70_amd as gdr
+    from gdr_synth import make_inputs
+
+    B, HK, HV, dk, dv = w.B, w.HK, w.HV, w.dk, w.dv
+    tmax = max(SHORT_T)
+    x = make_inputs(B, tmax, HK, HV, dk, dv, dtype=w.dtype, seed=w.seed + 7, h0=True)
+    d = {k: v.cuda() for k, v in x.items()}
+    state = d["h0"].clone()
+    out = {"T": list(SHORT_T), "decode_loop_ms": [], "fused_recurrent_ms": [], "chunked_ms": [],
+           "chunked_best_chunk": [], "fused_recurrent_state_GBps": [], "fastest": []}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    for T in SHORT_T:
+        sl = {n: d[n][:, :T].contiguous() for n in ("q", "k", "v", "g", "beta")}
+        steps = [{n: d[n][:, t:t + 1].contiguous() for n in ("q", "k", "v", "g", "beta")} for t in range(T)]
+        o = torch.empty(B, T, HV, dv, device="cuda")
+        o1 = torch.empty(B, 1, HV, dv, device="cuda")
+
+        def loop():
+            for st in steps:
+                gdr.decode_step(st["q"], st["k"], st["v"], st["g"], st["beta"], state, o=o1)
+
+        def fused():
+            gdr.fused_recurrent(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], h0=state, o=o, ht=state)
+
+        t_loop, t_fused = timed(loop), timed(fused)
+        best = None
+        for C in (16, 32, 64):
+            if C > 16 and C > T:
+                continue
+            ws = torch.empty(gdr.workspace_bytes(B, T, HK, HV, dk, dv, C), dtype=torch.uint8, device="cuda")
+
+            def chunked():
+                gdr.chunk_prefill(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], h0=state, chunk=C, o=o,
+                                  ht=state, workspace=ws)
+
+            tc = timed(chunked)
+            if best is None or tc < best[0]:
+                best = (tc, C)
+            del ws
+        out["decode_loop_ms"].append(round(t_loop, 5))
+        out["fused_recurrent_ms"].append(round(t_fused, 5))
+        out["chunked_ms"].append(round(best[0], 5))
+        out["chunked_best_chunk"].append(best[1])
+        out["fused_recurrent_state_GBps"].append(round(2 * B * HV * dk * dv * 4 / (t_fused * 1e-3) / 1e9, 1))
+        out["fastest"].append(min((t_loop, "decode_loop"), (t_fused, "fused_recurrent"),
+                                  (best[0], "chunked"))[1])
+    out["workload"] = (f"B={B} HK={HK} HV={HV} dk=dv={dk} bf16 q/k/v, h0 given, one call of T tokens; "
+                       f"{reps} calls back to back per figure")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -468,6 +540,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-short-calls", action="store_true")
     ap.add_argument("--workload", default="prefill_b1_t4097")
     ap.add_argument("--profile-run", action="store_true",
                     help="short run for counter collection, plus the calibration kernel")
@@ -572,6 +645,9 @@ def main():
                                  "ms": round(cms, 5), "GBps": round(sbytes / (cms * 1e-3) / 1e9, 1),
                                  "decode_rotating8_frac_of_copy": round(cms / dres["rotating8"]["mean_ms"], 4)}
         line["decode"] = dec
+
+    if not args.no_short_calls and not args.profile_run:
+        line["short_calls"] = bench_short_calls(DECODE)
 
     if not args.no_cpu_baseline:
         import numpy as np

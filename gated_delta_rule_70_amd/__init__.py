@@ -8,6 +8,7 @@ if the library is missing, the calls raise.
     import torch, gated_delta_rule_70_amd as gdr
     o, ht = gdr.chunk_prefill(q, k, v, g, beta, h0=None, chunk=64)   # prefill, any T >= 1
     o = gdr.decode_step(q1, k1, v1, g1, beta1, state)                  # T == 1, state in place
+    o, ht = gdr.fused_recurrent(q, k, v, g, beta, h0=state)          # short calls, T tokens
 
 Layouts (dense, row-major, on the GPU): q, k ``[B,T,HK,dk]`` and v ``[B,T,HV,dv]`` in
 bf16 or fp32; g ``[B,T,HV,dk]`` and beta ``[B,T,HV]`` in fp32; states ``[B,HV,dk,dv]``
@@ -20,11 +21,12 @@ import os
 
 import torch
 
-__all__ = ["decode_step", "chunk_prefill", "workspace_bytes", "GdrError", "lib", "Dims",
-           "LIB_PATH", "ABI_VERSION"]
+__all__ = ["decode_step", "fused_recurrent", "chunk_prefill", "forward", "workspace_bytes",
+           "GdrError", "lib", "Dims", "LIB_PATH", "ABI_VERSION", "RECURRENT_MAX_T"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
+RECURRENT_MAX_T = 8  # gdr_forward: calls of at most this many tokens take the fused recurrence
 BF16, F32 = 0, 1
 
 
@@ -58,6 +60,10 @@ def lib():
     L.gdr_status_str.argtypes = [ctypes.c_int]
     L.gdr_decode_step.restype = ctypes.c_int
     L.gdr_decode_step.argtypes = [ctypes.POINTER(Dims)] + [_VP] * 9
+    L.gdr_fused_recurrent.restype = ctypes.c_int
+    L.gdr_fused_recurrent.argtypes = [ctypes.POINTER(Dims)] + [_VP] * 9
+    L.gdr_forward.restype = ctypes.c_int
+    L.gdr_forward.argtypes = [ctypes.POINTER(Dims)] + [_VP] * 9 + [ctypes.c_size_t, _VP]
     L.gdr_chunk_prefill_workspace_bytes.restype = ctypes.c_size_t
     L.gdr_chunk_prefill_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
     L.gdr_chunk_prefill.restype = ctypes.c_int
@@ -178,4 +184,56 @@ def chunk_prefill(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
     _check(getattr(lib(), entry)(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                    _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht), _ptr(workspace),
                                    ctypes.c_size_t(workspace.numel()), _stream(stream)))
+    return o, ht
+
+
+def fused_recurrent(q, k, v, g, beta, h0=None, o=None, ht=None, want_state: bool = True,
+                    stream=None):
+    """The token recurrence over all T tokens in one launch (gdr_fused_recurrent): the state
+    stays on chip for the whole call.  Returns ``(o, ht)``; ``ht`` may be ``h0`` itself
+    (in-place), and is None if not wanted."""
+    _check_inputs(q, k, v, g, beta)
+    B, T, HK, dk = q.shape
+    HV, dv = v.shape[2], v.shape[3]
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    if o is None:
+        o = torch.empty(B, T, HV, dv, device=q.device, dtype=torch.float32)
+    _need(o, "o", torch.float32)
+    if ht is None and want_state:
+        ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
+    if ht is not None:
+        _need(ht, "ht", torch.float32)
+    d = _dims(q, v, 0)
+    _check(lib().gdr_fused_recurrent(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                     _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht), _stream(stream)))
+    return o, ht
+
+
+def forward(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None, workspace=None,
+            want_state: bool = True, stream=None):
+    """Routed call (gdr_forward): the fused recurrence for T <= RECURRENT_MAX_T, the chunked
+    prefill otherwise.  Returns ``(o, ht)``."""
+    _check_inputs(q, k, v, g, beta)
+    B, T, HK, dk = q.shape
+    HV, dv = v.shape[2], v.shape[3]
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    if o is None:
+        o = torch.empty(B, T, HV, dv, device=q.device, dtype=torch.float32)
+    _need(o, "o", torch.float32)
+    if ht is None and want_state:
+        ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
+    if ht is not None:
+        _need(ht, "ht", torch.float32)
+    d = _dims(q, v, chunk)
+    if T > RECURRENT_MAX_T and workspace is None:
+        need = int(lib().gdr_chunk_prefill_workspace_bytes(ctypes.byref(d)))
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
+    _check(lib().gdr_forward(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(h0), _ptr(o), _ptr(ht), _ptr(workspace),
+                             ctypes.c_size_t(0 if workspace is None else workspace.numel()),
+                             _stream(stream)))
     return o, ht

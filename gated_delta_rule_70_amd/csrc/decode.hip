@@ -1,39 +1,45 @@
-// Decode step of the channelwise gated delta rule (T == 1), gfx950.
+// Token recurrence of the channelwise gated delta rule, gfx950: the decode step (T == 1)
+// and the fused recurrent form for short multi-token calls (T tokens in one launch).
 //
 // The two-pass token recurrence of ExecuTorch PR #21021 ("Reorder channelwise gated delta
 // rule chunked hot loops for autovectorization", first commit summary), mapped to a
-// memory-bound GPU kernel:
+// memory-bound GPU kernel; per token:
 //   pass 1: pred_j = sum_i exp(g_i) S_ij k_i              (decay folded into the prediction)
 //   pass 2: S_ij  <- exp(g_i) S_ij + k_i beta (v_j - pred_j);   o_j = sum_i S_ij q_i
 // The state slice a workgroup owns is loaded from HBM once into registers, kept there
-// between the passes and stored once: one read and one write of S per step, the minimum.
+// across the passes and across all T tokens of the call, and stored once: one read and one
+// write of S per call, the minimum.  The page routes only T == 1 to this path (commit
+// summary 2 of the same PR); running it for T > 1 in one launch is what short calls
+// (speculative chains, a few tokens) use instead of T separate decode steps.
 //
 // Launch: one 256-thread workgroup per (batch, value head, BVD-wide column block).
 // Thread t owns column quad cq = t % (BVD/4) (a float4 of columns) and the rows
 // rl, rl + NRL, ... with rl = t / (BVD/4); a wave therefore touches 64/(BVD/4) rows with
 // fully coalesced 16-byte loads along dv.  Column sums over rows are reduced first with
-// cross-lane shuffles inside the wave, then across the four waves through LDS.
+// cross-lane shuffles inside the wave, then across the four waves through LDS (two
+// barriers per token; the two reduction buffers alternate so no third one is needed).
+// The next token's inputs are requested while the current one is processed.
 #include "gdr_device.h"
 #include "gdr_launch.h"
 
 namespace gdr {
 
 template <typename TIn, int DK, int DV>
-__global__ __launch_bounds__(256) void decode_kernel(const TIn* __restrict__ q,
-                                                     const TIn* __restrict__ k,
-                                                     const TIn* __restrict__ v,
-                                                     const float* __restrict__ g,
-                                                     const float* __restrict__ beta,
-                                                     const float* h0, float* __restrict__ o,
-                                                     float* ht, int HK, int HV) {
+__global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
+                                                    const TIn* __restrict__ k,
+                                                    const TIn* __restrict__ v,
+                                                    const float* __restrict__ g,
+                                                    const float* __restrict__ beta,
+                                                    const float* h0, float* __restrict__ o,
+                                                    float* ht, int T, int HK, int HV) {
     constexpr int BVD = DV < 64 ? DV : 64;   // columns per workgroup
     constexpr int NQ = BVD / 4;              // column quads per row
     constexpr int NRL = 256 / NQ;            // row lanes
     constexpr int RPT = DK / NRL;            // rows per thread
-    constexpr int LPW = 64 / NQ;             // row lanes per wave
     static_assert(RPT >= 1 && DK % NRL == 0, "unsupported dk/dv combination");
 
-    __shared__ f32x4 red[4][NQ];
+    __shared__ f32x4 red_p[4][NQ];  // pass-1 partial sums of each wave
+    __shared__ f32x4 red_o[4][NQ];  // output partial sums of each wave
 
     const int ncb = DV / BVD;
     const int blk = blockIdx.x;
@@ -42,10 +48,10 @@ __global__ __launch_bounds__(256) void decode_kernel(const TIn* __restrict__ q,
     const int h = bh % HV;
     const int b = bh / HV;
     const int kh = h / (HV / HK);
-    const int t = threadIdx.x;
-    const int cq = t % NQ;
-    const int rl = t / NQ;
-    const int wave = t >> 6;
+    const int tid = threadIdx.x;
+    const int cq = tid % NQ;
+    const int rl = tid / NQ;
+    const int wave = tid >> 6;
     const int col = cb * BVD + 4 * cq;
 
     const size_t sbase = (size_t)bh * DK * DV + col;
@@ -59,83 +65,109 @@ __global__ __launch_bounds__(256) void decode_kernel(const TIn* __restrict__ q,
         for (int m = 0; m < RPT; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const size_t kq = ((size_t)b * HK + kh) * DK;
-    const size_t gb = (size_t)bh * DK;
-    float e[RPT], kk[RPT], qq[RPT];
-#pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const int i = rl + NRL * m;
-        e[m] = __expf(g[gb + i]);
-        kk[m] = to_f32(k[kq + i]);
-        qq[m] = to_f32(q[kq + i]);
-    }
+    // Token tok of this (batch, head): q/k row, g row, v/o columns, beta.
+    const size_t kq0 = ((size_t)b * T * HK + kh) * DK;
+    const size_t gb0 = ((size_t)b * T * HV + h) * DK;
+    const size_t vb0 = ((size_t)b * T * HV + h) * DV + col;
+    const size_t bb0 = (size_t)b * T * HV + h;
+    const size_t kq_t = (size_t)HK * DK, gb_t = (size_t)HV * DK, vb_t = (size_t)HV * DV;
 
-    // pass 1: prediction with the decay folded in
-    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+    // raw inputs of the next token, requested one token ahead
+    float gn[RPT];
+    TIn kn[RPT], qn[RPT], vn[4];
+    float btn;
+    auto request = [&](int tok) {
+        const size_t kq = kq0 + tok * kq_t, gb = gb0 + tok * gb_t, vb = vb0 + tok * vb_t;
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        S[m] *= e[m];
-        p += S[m] * kk[m];
-    }
+        for (int m = 0; m < RPT; ++m) {
+            const int i = rl + NRL * m;
+            gn[m] = g[gb + i];
+            kn[m] = k[kq + i];
+            qn[m] = q[kq + i];
+        }
 #pragma unroll
-    for (int off = NQ; off < 64; off <<= 1) {
-        p.x += __shfl_xor(p.x, off);
-        p.y += __shfl_xor(p.y, off);
-        p.z += __shfl_xor(p.z, off);
-        p.w += __shfl_xor(p.w, off);
-    }
-    if ((t & 63) < NQ) red[wave][cq] = p;
-    __syncthreads();
-    const f32x4 pred = red[0][cq] + red[1][cq] + red[2][cq] + red[3][cq];
+        for (int c = 0; c < 4; ++c) vn[c] = v[vb + c];
+        btn = beta[bb0 + tok * HV];
+    };
+    request(0);
 
-    const float bt = beta[bh];
-    const size_t vb = (size_t)bh * DV + col;
-    const f32x4 vv = {to_f32(v[vb + 0]), to_f32(v[vb + 1]), to_f32(v[vb + 2]), to_f32(v[vb + 3])};
-    const f32x4 d = (vv - pred) * bt;
-
-    // pass 2: rank-one update of the (already decayed) state, output partial sums
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int tok = 0; tok < T; ++tok) {
+        float e[RPT], kk[RPT], qq[RPT];
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        S[m] += d * kk[m];
-        acc += S[m] * qq[m];
+        for (int m = 0; m < RPT; ++m) {
+            e[m] = __expf(gn[m]);
+            kk[m] = to_f32(kn[m]);
+            qq[m] = to_f32(qn[m]);
+        }
+        const f32x4 vv = {to_f32(vn[0]), to_f32(vn[1]), to_f32(vn[2]), to_f32(vn[3])};
+        const float bt = btn;
+        if (tok + 1 < T) request(tok + 1);
+
+        // pass 1: prediction with the decay folded in
+        f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            S[m] *= e[m];
+            p += S[m] * kk[m];
+        }
+#pragma unroll
+        for (int off = NQ; off < 64; off <<= 1) {
+            p.x += __shfl_xor(p.x, off);
+            p.y += __shfl_xor(p.y, off);
+            p.z += __shfl_xor(p.z, off);
+            p.w += __shfl_xor(p.w, off);
+        }
+        // red_p is free: every thread read the previous token's sums before the previous
+        // token's second barrier
+        if ((tid & 63) < NQ) red_p[wave][cq] = p;
+        __syncthreads();
+        const f32x4 pred = red_p[0][cq] + red_p[1][cq] + red_p[2][cq] + red_p[3][cq];
+        const f32x4 d = (vv - pred) * bt;
+
+        // pass 2: rank-one update of the (already decayed) state, output partial sums
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            S[m] += d * kk[m];
+            acc += S[m] * qq[m];
+        }
+#pragma unroll
+        for (int off = NQ; off < 64; off <<= 1) {
+            acc.x += __shfl_xor(acc.x, off);
+            acc.y += __shfl_xor(acc.y, off);
+            acc.z += __shfl_xor(acc.z, off);
+            acc.w += __shfl_xor(acc.w, off);
+        }
+        // red_o is free: its readers read the previous token's sums before this token's
+        // first barrier
+        if ((tid & 63) < NQ) red_o[wave][cq] = acc;
+        __syncthreads();
+        if (tid < NQ) {
+            const f32x4 out = red_o[0][cq] + red_o[1][cq] + red_o[2][cq] + red_o[3][cq];
+            *reinterpret_cast<f32x4*>(o + vb0 + tok * vb_t) = out;
+        }
     }
     if (ht != nullptr) {
 #pragma unroll
         for (int m = 0; m < RPT; ++m)
             *reinterpret_cast<f32x4*>(ht + sbase + (size_t)(rl + NRL * m) * DV) = S[m];
     }
-#pragma unroll
-    for (int off = NQ; off < 64; off <<= 1) {
-        acc.x += __shfl_xor(acc.x, off);
-        acc.y += __shfl_xor(acc.y, off);
-        acc.z += __shfl_xor(acc.z, off);
-        acc.w += __shfl_xor(acc.w, off);
-    }
-    __syncthreads();  // every wave has read red[] for pred
-    if ((t & 63) < NQ) red[wave][cq] = acc;
-    __syncthreads();
-    if (t < NQ) {
-        const f32x4 out = red[0][cq] + red[1][cq] + red[2][cq] + red[3][cq];
-        *reinterpret_cast<f32x4*>(o + vb) = out;
-    }
-    (void)LPW;
 }
 
 template <typename TIn, int DK, int DV>
-static hipError_t launch_decode_t(const LaunchArgs& a) {
+static hipError_t launch_tokens_t(const LaunchArgs& a) {
     constexpr int BVD = DV < 64 ? DV : 64;
     const long long nblk = (long long)a.B * a.HV * (DV / BVD);
-    hipLaunchKernelGGL((decode_kernel<TIn, DK, DV>), dim3((unsigned)nblk), dim3(256), 0,
+    hipLaunchKernelGGL((token_kernel<TIn, DK, DV>), dim3((unsigned)nblk), dim3(256), 0,
                        (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
-                       a.g, a.beta, a.h0, a.o, a.ht, a.HK, a.HV);
+                       a.g, a.beta, a.h0, a.o, a.ht, a.T, a.HK, a.HV);
     return hipGetLastError();
 }
 
 template <typename TIn>
 static hipError_t dispatch_dims(const LaunchArgs& a) {
 #define GDR_CASE(DK_, DV_) \
-    if (a.dk == DK_ && a.dv == DV_) return launch_decode_t<TIn, DK_, DV_>(a);
+    if (a.dk == DK_ && a.dv == DV_) return launch_tokens_t<TIn, DK_, DV_>(a);
     GDR_CASE(32, 32) GDR_CASE(32, 64) GDR_CASE(32, 128)
     GDR_CASE(64, 32) GDR_CASE(64, 64) GDR_CASE(64, 128)
     GDR_CASE(128, 32) GDR_CASE(128, 64) GDR_CASE(128, 128)
@@ -143,7 +175,8 @@ static hipError_t dispatch_dims(const LaunchArgs& a) {
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const LaunchArgs& a) {
+// Decode step (T == 1) and fused recurrent call (any T): the same kernel.
+hipError_t launch_tokens(const LaunchArgs& a) {
     return a.qkv_f32 ? dispatch_dims<float>(a) : dispatch_dims<bf16_t>(a);
 }
 

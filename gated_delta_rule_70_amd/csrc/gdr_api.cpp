@@ -55,21 +55,26 @@ bool tensor_sizes(const gdr_dims& d, size_t elt, Sizes* s) {
     return true;
 }
 
+// Which entry point is validating: the decode step (T == 1), the fused token recurrence
+// (any T, chunk ignored) or the chunked prefill (chunk checked).
+enum class Path { decode, tokens, chunked };
+
 // Shared validation of dims, pointers, alignment and aliasing.
-int validate(const gdr_dims* d, bool decode, const void* q, const void* k, const void* v,
+int validate(const gdr_dims* d, Path path, const void* q, const void* k, const void* v,
              const float* g, const float* beta, const float* h0, const float* o,
              const float* ht, Sizes* sizes) {
     if (!d || !q || !k || !v || !g || !beta || !o) return GDR_ERR_NULL;
     if (d->B < 1 || d->T < 1 || d->HK < 1 || d->HV < 1 || d->HV % d->HK != 0) return GDR_ERR_SHAPE;
-    if (decode && d->T != 1) return GDR_ERR_SHAPE;
+    if (path == Path::decode && d->T != 1) return GDR_ERR_SHAPE;
     if (!supported_head_dim(d->dk) || !supported_head_dim(d->dv)) return GDR_ERR_UNSUPPORTED;
     if (d->qkv_dtype != GDR_BF16 && d->qkv_dtype != GDR_F32) return GDR_ERR_UNSUPPORTED;
-    if (!decode && d->chunk != 16 && d->chunk != 32 && d->chunk != 64) return GDR_ERR_UNSUPPORTED;
+    if (path == Path::chunked && d->chunk != 16 && d->chunk != 32 && d->chunk != 64)
+        return GDR_ERR_UNSUPPORTED;
     const size_t elt = d->qkv_dtype == GDR_F32 ? 4 : 2;
     if (!tensor_sizes(*d, elt, sizes)) return GDR_ERR_SHAPE;
     // Grid sizes must fit the launch limits: (B*HV) heads times chunks or column tiles.
     const long long heads = (long long)d->B * d->HV;
-    const long long nchunk = decode ? 1 : (d->T + d->chunk - 1) / d->chunk;
+    const long long nchunk = path == Path::chunked ? (d->T + d->chunk - 1) / d->chunk : 1;
     if (heads * nchunk >= (1LL << 31) || heads * (d->dv / 16) >= (1LL << 31)) return GDR_ERR_SHAPE;
 
     const void* ptrs[] = {q, k, v, g, beta, h0, o, ht};
@@ -146,10 +151,20 @@ int gdr_decode_step(const gdr_dims* dims, const void* q, const void* k, const vo
                     const float* g, const float* beta, const float* h0, float* o, float* ht,
                     void* stream) {
     Sizes s;
-    const int st = validate(dims, true, q, k, v, g, beta, h0, o, ht, &s);
+    const int st = validate(dims, Path::decode, q, k, v, g, beta, h0, o, ht, &s);
     if (st != GDR_OK) return st;
     const gdr::LaunchArgs a = make_args(dims, q, k, v, g, beta, h0, o, ht, nullptr, stream);
-    return gdr::launch_decode(a) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+    return gdr::launch_tokens(a) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+int gdr_fused_recurrent(const gdr_dims* dims, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const float* h0, float* o, float* ht,
+                        void* stream) {
+    Sizes s;
+    const int st = validate(dims, Path::tokens, q, k, v, g, beta, h0, o, ht, &s);
+    if (st != GDR_OK) return st;
+    const gdr::LaunchArgs a = make_args(dims, q, k, v, g, beta, h0, o, ht, nullptr, stream);
+    return gdr::launch_tokens(a) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
 size_t gdr_chunk_prefill_workspace_bytes(const gdr_dims* dims) {
@@ -166,7 +181,7 @@ static int prefill_stages(const gdr_dims* dims, const void* q, const void* k, co
                           void* workspace, size_t workspace_bytes, void* stream, bool prep,
                           bool carry) {
     Sizes s;
-    const int st = validate(dims, false, q, k, v, g, beta, h0, o, ht, &s);
+    const int st = validate(dims, Path::chunked, q, k, v, g, beta, h0, o, ht, &s);
     if (st != GDR_OK) return st;
     const size_t need = workspace_bytes_unchecked(dims);
     if (need == 0) return GDR_ERR_SHAPE;
@@ -212,6 +227,14 @@ int gdr_chunk_carry(const gdr_dims* dims, const void* q, const void* k, const vo
                     void* workspace, size_t workspace_bytes, void* stream) {
     return prefill_stages(dims, q, k, v, g, beta, h0, o, ht, workspace, workspace_bytes, stream,
                           false, true);
+}
+
+int gdr_forward(const gdr_dims* dims, const void* q, const void* k, const void* v,
+                const float* g, const float* beta, const float* h0, float* o, float* ht,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    if (dims && dims->T >= 1 && dims->T <= GDR_RECURRENT_MAX_T)
+        return gdr_fused_recurrent(dims, q, k, v, g, beta, h0, o, ht, stream);
+    return gdr_chunk_prefill(dims, q, k, v, g, beta, h0, o, ht, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

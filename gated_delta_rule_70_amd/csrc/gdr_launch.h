@@ -66,7 +66,8 @@ struct ChunkRecord {
     }
 };
 
-hipError_t launch_decode(const LaunchArgs& a);
+// token recurrence over a.T tokens in one launch (the decode step is a.T == 1)
+hipError_t launch_tokens(const LaunchArgs& a);
 hipError_t launch_chunk_prep(const LaunchArgs& a);
 hipError_t launch_chunk_carry(const LaunchArgs& a);
 

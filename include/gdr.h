@@ -36,7 +36,7 @@
  *     130K tokens at HV = 32, dk = dv = 128.  Decay values are expected to satisfy g <= 0 with the total
  *     decay over any 8 consecutive tokens below 80 in every channel (exp(g) >= ~5e-5 per
  *     token); outside that range the prefill path's intra-chunk decay factors can
- *     overflow fp32.  The decode path has no such limit.
+ *     overflow fp32.  The decode and fused recurrent paths have no such limit.
  *   - Results are bitwise reproducible for identical inputs and dims (no atomics).
  */
 #ifndef GDR_H
@@ -49,13 +49,13 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 1
+#define GDR_ABI_VERSION 2
 
 typedef enum {
     GDR_OK = 0,
     GDR_ERR_NULL = 1,        /* a required pointer (dims, q, k, v, g, beta, o) is NULL     */
-    GDR_ERR_SHAPE = 2,       /* B/T/HK/HV < 1, HV % HK != 0, decode with T != 1, a size
-                                past the limits below                                      */
+    GDR_ERR_SHAPE = 2,       /* B/T/HK/HV < 1, HV % HK != 0, decode step with T != 1, a
+                                size past the limits below                                 */
     GDR_ERR_UNSUPPORTED = 3, /* dk/dv/chunk/dtype outside the supported set               */
     GDR_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned                   */
     GDR_ERR_ALIAS = 5,       /* o overlaps an input/h0/ht, or ht partially overlaps h0    */
@@ -67,7 +67,7 @@ typedef enum { GDR_BF16 = 0, GDR_F32 = 1 } gdr_dtype;
 
 typedef struct {
     int32_t B, T, HK, HV, dk, dv;
-    int32_t chunk;      /* prefill chunk length C (ignored by the decode step)             */
+    int32_t chunk;      /* prefill chunk length C (ignored by the token-recurrence calls)  */
     int32_t qkv_dtype;  /* gdr_dtype of q, k and v                                         */
 } gdr_dims;
 
@@ -81,6 +81,21 @@ typedef struct {
 int gdr_decode_step(const gdr_dims* dims, const void* q, const void* k, const void* v,
                     const float* g, const float* beta, const float* h0, float* o, float* ht,
                     void* stream);
+
+/*
+ * The same two-pass token recurrence for T >= 1 tokens in one launch (chunk ignored):
+ * each workgroup loads its slice of the state once, applies the T tokens in order with
+ * the slice held in registers, writes o for every token and stores the state once.  The
+ * pages route only T == 1 to the token recurrence (ExecuTorch PR #21021, second commit
+ * summary); this is the same recurrence for short multi-token calls (a speculative chain
+ * of a few tokens, a short continuation), where T decode steps would move the whole
+ * state T times and the chunked path pays its fixed cost.  Arguments, layouts and
+ * checks are those of gdr_decode_step with any T >= 1; T == 1 gives bitwise the result of
+ * gdr_decode_step.  Uses no workspace.
+ */
+int gdr_fused_recurrent(const gdr_dims* dims, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const float* h0, float* o, float* ht,
+                        void* stream);
 
 /*
  * Bytes of device workspace gdr_chunk_prefill needs for these dims (0 if dims are
@@ -124,6 +139,19 @@ int gdr_chunk_prep(const gdr_dims* dims, const void* q, const void* k, const voi
 int gdr_chunk_carry(const gdr_dims* dims, const void* q, const void* k, const void* v,
                     const float* g, const float* beta, const float* h0, float* o, float* ht,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Routed call for any T >= 1, in the spirit of the length routing of ExecuTorch PR #21021
+ * (second commit summary), with the threshold set by measurement on MI355X: T <=
+ * GDR_RECURRENT_MAX_T runs gdr_fused_recurrent (workspace may be NULL), longer calls run
+ * gdr_chunk_prefill (workspace as documented there).  Measured at B = 32, HV = 32,
+ * dk = dv = 128: one fused launch beats T decode steps from T = 2 and the chunked path up
+ * to T = 8; the chunked path wins from T = 16.
+ */
+#define GDR_RECURRENT_MAX_T 8
+int gdr_forward(const gdr_dims* dims, const void* q, const void* k, const void* v,
+                const float* g, const float* beta, const float* h0, float* o, float* ht,
+                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static English text for a status code (never NULL). */
 const char* gdr_status_str(int status);

@@ -36,7 +36,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "gdr_abi_version", "gdr_chunk_carry", "gdr_chunk_prefill", "gdr_chunk_prefill_workspace_bytes",
-        "gdr_chunk_prep", "gdr_decode_step", "gdr_status_str"])
+        "gdr_chunk_prep", "gdr_decode_step", "gdr_forward", "gdr_fused_recurrent", "gdr_status_str"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -80,10 +80,10 @@ def prefill(L, d, ws_bytes=None, entry="gdr_chunk_prefill", **ptrs):
                                None)
 
 
-def decode(L, d, **ptrs):
+def decode(L, d, entry="gdr_decode_step", **ptrs):
     p = {n: addr(i) for i, n in enumerate(["q", "k", "v", "g", "beta", "h0", "o", "ht"])}
     p.update(ptrs)
-    return L.gdr_decode_step(None if d is None else ctypes.byref(d), p["q"], p["k"], p["v"], p["g"],
+    return getattr(L, entry)(None if d is None else ctypes.byref(d), p["q"], p["k"], p["v"], p["g"],
                              p["beta"], p["h0"], p["o"], p["ht"], None)
 
 
@@ -103,6 +103,22 @@ def test_bad_shapes(L, kw):
 
 def test_decode_requires_one_token(L):
     assert decode(L, dims(T=2)) == ESHAPE
+
+
+def test_fused_recurrent_validates_like_decode_for_any_T(L):
+    rec = dict(entry="gdr_fused_recurrent")
+    assert decode(L, None, **rec) == ENULL
+    for name in ("q", "k", "v", "g", "beta", "o"):
+        assert decode(L, dims(T=7), **rec, **{name: None}) == ENULL, name
+    assert decode(L, dims(T=0), **rec) == ESHAPE
+    assert decode(L, dims(HK=3, HV=4), **rec) == ESHAPE
+    assert decode(L, dims(dk=48), **rec) == EUNSUP
+    assert decode(L, dims(qkv_dtype=2), **rec) == EUNSUP
+    # the chunk length is ignored: an unsupported one gets as far as the alignment check
+    assert decode(L, dims(T=7, chunk=8), q=addr(0, 8), **rec) == EALIGN
+    assert decode(L, dims(T=7), q=addr(0, 8), **rec) == EALIGN
+    assert decode(L, dims(T=7), o=addr(0, 256), **rec) == EALIAS
+    assert decode(L, dims(T=7), ht=addr(5, 256), **rec) == EALIAS
 
 
 @pytest.mark.parametrize("kw", [dict(dk=48), dict(dv=256), dict(dk=16), dict(chunk=8),
@@ -133,6 +149,16 @@ def test_stage_entries_validate_like_prefill(L, entry):
     assert prefill(L, dims(), entry=entry, q=addr(0, 8)) == EALIGN
     assert prefill(L, dims(), entry=entry, o=addr(0, 256)) == EALIAS
     assert prefill(L, dims(), entry=entry, ws_bytes=1) == EWS
+
+
+def test_forward_routes_by_length(L):
+    # short calls take the recurrence (no workspace needed), longer ones the chunked path
+    # (which checks its workspace); both stop at validation here
+    assert prefill(L, dims(T=8), entry="gdr_forward", q=addr(0, 8), ws=None, ws_bytes=0) == EALIGN
+    assert prefill(L, dims(T=9), entry="gdr_forward", ws=None, ws_bytes=0) == EWS
+    assert prefill(L, dims(T=9, chunk=8), entry="gdr_forward") == EUNSUP
+    assert prefill(L, dims(T=8, chunk=8), entry="gdr_forward", q=addr(0, 8)) == EALIGN
+    assert prefill(L, None, entry="gdr_forward") == ENULL
 
 
 def test_workspace_checks(L):
@@ -177,3 +203,4 @@ def test_valid_arguments_reach_the_runtime_without_a_gpu(L):
     # with no GPU, a call that passes validation fails at the first HIP call, cleanly
     assert prefill(L, dims(), ht=addr(5, 0)) == EHIP        # in-place ht == h0 is allowed
     assert decode(L, dims(T=1), ht=addr(5, 0)) == EHIP
+    assert decode(L, dims(T=9, chunk=8), ht=addr(5, 0), entry="gdr_fused_recurrent") == EHIP
