@@ -98,6 +98,37 @@ def make_inputs(B: int, T: int, HK: int, HV: int, dk: int, dv: int, *,
     }
 
 
+TREE_KINDS = ("chain", "star", "random", "binary")
+
+
+def make_tree(B: int, T: int, kind: str = "random", seed: int = 0) -> torch.Tensor:
+    """Parent index of every node of a token tree, one tree per batch element: int32
+    ``[B,T]`` with ``parent[b][t]`` in ``[-1, t)`` (nodes in topological order; -1 = a
+    child of the initial state).
+
+    chain  -- parent t-1 (a plain sequence)
+    star   -- every node a child of the initial state
+    random -- parent drawn uniformly from [-1, t)
+    binary -- the complete binary tree in breadth-first order: a shallow, wide tree like
+              the candidate trees of speculative decoding (depth ~ log2 T)
+    """
+    if kind == "chain":
+        par = torch.arange(T, dtype=torch.int32) - 1
+        return par.expand(B, T).contiguous()
+    if kind == "star":
+        return torch.full((B, T), -1, dtype=torch.int32)
+    if kind == "binary":
+        t = torch.arange(T, dtype=torch.int32)
+        par = torch.where(t == 0, torch.full_like(t, -1), (t - 1) // 2)
+        return par.expand(B, T).contiguous()
+    if kind == "random":
+        gen = torch.Generator("cpu").manual_seed(int(seed))
+        u = torch.rand(B, T, generator=gen)
+        t = torch.arange(T, dtype=torch.float32)
+        return (torch.floor(u * (t + 1)) - 1).to(torch.int32).contiguous()
+    raise ValueError(f"unknown tree kind {kind!r}")
+
+
 def workload_inputs(w: Workload, *, T: int | None = None, B: int | None = None) -> dict:
     """Inputs for a named workload (a decode workload draws all its steps as T=steps)."""
     T = T if T is not None else (w.steps if w.steps else w.T)

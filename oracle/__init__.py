@@ -12,6 +12,9 @@ Two routes to the same result, both in fp64 (see ``gdr_oracle.c`` for the arithm
   autovectorization".
 * :func:`chunked` -- the chunkwise WY/UT form of the second commit summary of that page,
   with an exact forward-substitution solve; it can export its per-chunk intermediates.
+* :func:`tree` -- the same token step over a tree of tokens per batch element (every node
+  continues from its parent's state), the setting of the tree-verify solve of uzu PR #576
+  ("Support TreeUpdateSolve kernel").
 
 Inputs may be numpy arrays or torch CPU tensors of any float dtype (bf16 values are
 upcast exactly).  Layouts: q, k ``[B,T,HK,dk]``; v ``[B,T,HV,dv]``; g ``[B,T,HV,dk]``;
@@ -70,6 +73,9 @@ def _bind(lib):
     lib.oracle_gdr_sequential.argtypes = [_I64] * 6 + [_DP] * 8 + [ctypes.c_int]
     lib.oracle_gdr_chunked.restype = ctypes.c_int
     lib.oracle_gdr_chunked.argtypes = [_I64] * 7 + [_DP] * 14 + [ctypes.c_int]
+    lib.oracle_gdr_tree.restype = ctypes.c_int
+    lib.oracle_gdr_tree.argtypes = [_I64] * 6 + [_DP] * 6 + [ctypes.POINTER(ctypes.c_int32), _DP,
+                                                              ctypes.c_int]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     return lib
@@ -155,6 +161,25 @@ def chunked(q, k, v, g, beta, h0=None, chunk: int = 64, threads: int = 0,
     if rc != 0:
         raise RuntimeError(f"oracle_gdr_chunked failed ({rc})")
     return (o, ht, mids) if intermediates else (o, ht)
+
+
+def tree(q, k, v, g, beta, h0, parent, threads: int = 0, lib=None):
+    """Token recurrence over a tree, in fp64.  ``parent`` is ``[B,T]`` int with entries in
+    ``[-1, t)`` (-1: the node continues from h0, or from zero if h0 is None).  Returns
+    ``o`` ``[B,T,HV,dv]``: each node's output from the state at the end of its path."""
+    lib = lib or load()
+    q, k, v, g, beta, h0 = (_f64(x) for x in (q, k, v, g, beta, h0))
+    B, T, HK, HV, dk, dv = _dims(q, k, v, g, beta, h0)
+    par = np.ascontiguousarray(np.asarray(parent), dtype=np.int32)
+    if par.shape != (B, T):
+        raise ValueError(f"parent must be [B,T] = {(B, T)}, got {par.shape}")
+    o = np.empty((B, T, HV, dv), np.float64)
+    rc = lib.oracle_gdr_tree(B, T, HK, HV, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(h0), par.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(o),
+                             int(threads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gdr_tree failed ({rc})")
+    return o
 
 
 def num_threads() -> int:

@@ -31,7 +31,14 @@
  *   q, k  [B][T][HK][dk]      v, o  [B][T][HV][dv]
  *   g     [B][T][HV][dk]      beta  [B][T][HV]
  *   h0,ht [B][HV][dk][dv]     (h0 may be NULL = zero state; ht may be NULL)
- * Return value: 0 on success, -1 on invalid sizes, -2 on allocation failure.
+ * oracle_gdr_tree() runs the same token step over a tree of T nodes per batch element (the
+ * speculative token tree that the tree-verify solve of uzu PR #576 serves): node t
+ * continues from the state its parent node reached, parent[b][t] in [-1, t) with -1
+ * meaning the initial state, and its output is taken from its own updated state.  A chain
+ * (parent t-1) is exactly the sequential recurrence.
+ *
+ * Return value: 0 on success, -1 on invalid sizes, -2 on allocation failure, -3 on a
+ * parent index outside [-1, t).
  */
 #include <math.h>
 #include <stdint.h>
@@ -284,6 +291,79 @@ int oracle_gdr_chunked(int64_t B, int64_t T, int64_t HK, int64_t HV, int64_t dk,
         }
         if (ht) memcpy(ht + bh * dk * dv, S, sizeof(double) * (size_t)(dk * dv));
         free(S);
+    }
+    return failed ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Token recurrence over a tree: every node continues from its parent's state.           */
+/* ------------------------------------------------------------------------------------ */
+int oracle_gdr_tree(int64_t B, int64_t T, int64_t HK, int64_t HV, int64_t dk, int64_t dv,
+                    const double* q, const double* k, const double* v, const double* g,
+                    const double* beta, const double* h0, const int32_t* parent, double* o,
+                    int nthreads) {
+    if (!dims_ok(B, T, HK, HV, dk, dv) || !parent) return -1;
+    for (int64_t i = 0; i < B * T; ++i)
+        if (parent[i] < -1 || parent[i] >= i % T) return -3;
+    set_threads(nthreads);
+    const int64_t G = HV / HK;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < B * HV; ++bh) {
+        const int64_t b = bh / HV, h = bh % HV, kh = h / G;
+        /* the state every node reached, then two dv scratch rows */
+        double* states = (double*)malloc(sizeof(double) * (size_t)(T * dk * dv + 2 * dv));
+        if (!states) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        double* pred = states + T * dk * dv;
+        double* d = pred + dv;
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t p = parent[b * T + t];
+            double* S = states + t * dk * dv;
+            if (p >= 0)
+                memcpy(S, states + p * dk * dv, sizeof(double) * (size_t)(dk * dv));
+            else if (h0)
+                memcpy(S, h0 + bh * dk * dv, sizeof(double) * (size_t)(dk * dv));
+            else
+                memset(S, 0, sizeof(double) * (size_t)(dk * dv));
+            const double* kt = k + ((b * T + t) * HK + kh) * dk;
+            const double* qt = q + ((b * T + t) * HK + kh) * dk;
+            const double* vt = v + ((b * T + t) * HV + h) * dv;
+            const double* gt = g + ((b * T + t) * HV + h) * dk;
+            const double bt = beta[(b * T + t) * HV + h];
+            double* ot = o + ((b * T + t) * HV + h) * dv;
+            /* decay */
+            for (int64_t i = 0; i < dk; ++i) {
+                const double e = exp(gt[i]);
+                double* Si = S + i * dv;
+                for (int64_t j = 0; j < dv; ++j) Si[j] *= e;
+            }
+            /* predict from the decayed state */
+            for (int64_t j = 0; j < dv; ++j) pred[j] = 0.0;
+            for (int64_t i = 0; i < dk; ++i) {
+                const double ki = kt[i];
+                const double* Si = S + i * dv;
+                for (int64_t j = 0; j < dv; ++j) pred[j] += ki * Si[j];
+            }
+            /* rank-one delta update */
+            for (int64_t j = 0; j < dv; ++j) d[j] = bt * (vt[j] - pred[j]);
+            for (int64_t i = 0; i < dk; ++i) {
+                const double ki = kt[i];
+                double* Si = S + i * dv;
+                for (int64_t j = 0; j < dv; ++j) Si[j] += ki * d[j];
+            }
+            /* output from the node's updated state */
+            for (int64_t j = 0; j < dv; ++j) ot[j] = 0.0;
+            for (int64_t i = 0; i < dk; ++i) {
+                const double qi = qt[i];
+                const double* Si = S + i * dv;
+                for (int64_t j = 0; j < dv; ++j) ot[j] += qi * Si[j];
+            }
+        }
+        free(states);
     }
     return failed ? -2 : 0;
 }

@@ -15,6 +15,14 @@ import oracle
 from oracle_pins import ALL_PINS, TOL
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "gdr_oracle.c")
+# The tree route, at the end of the file, repeats the token step; these slips target the
+# sequential and chunked routes before it (test_oracle_tree.py plants its own).
+TREE_MARK = "/* Token recurrence over a tree"
+
+
+def _split(src):
+    i = src.index(TREE_MARK)
+    return src[:i], src[i:]
 
 # (name, route, old, new); route: which oracle route the pins exercise for this slip
 MUTANTS = [
@@ -62,14 +70,14 @@ def _swap_blocks(src, first, second, end):
 
 def _mutate(name, old, new):
     with open(SRC) as f:
-        src = f.read()
+        head, tail = _split(f.read())
     if name == "output_before_update":
-        return _swap_blocks(src, "/* 3. rank-one delta update */", "/* 4. output from the updated state */",
-                            "        }\n        if (ht) memcpy")
+        return _swap_blocks(head, "/* 3. rank-one delta update */", "/* 4. output from the updated state */",
+                            "        }\n        if (ht) memcpy") + tail
     if name == "predict_before_decay":
-        return _swap_blocks(src, "/* 1. decay */", "/* 2. predict */", "/* 3. rank-one delta update */")
-    assert src.count(old) == 1, f"mutation anchor for {name} not unique/present"
-    return src.replace(old, new)
+        return _swap_blocks(head, "/* 1. decay */", "/* 2. predict */", "/* 3. rank-one delta update */") + tail
+    assert head.count(old) == 1, f"mutation anchor for {name} not unique/present"
+    return head.replace(old, new) + tail
 
 
 @pytest.mark.parametrize("name,route,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
@@ -93,7 +101,7 @@ def test_pins_catch_planted_mistake(tmp_path, name, route, old, new):
 def test_mutation_anchors_are_live():
     # guard against the mutants silently going stale when the oracle is edited
     with open(SRC) as f:
-        src = f.read()
+        src, _ = _split(f.read())
     for name, _, old, _ in MUTANTS:
         if old is not None:
             assert src.count(old) == 1, name
