@@ -58,9 +58,10 @@ KERNEL_SOURCES = {  # kernel -> the sources its machine code is built from
     "chunk_prep": ["chunk_prep.hip", "gdr_device.h", "gdr_launch.h"],
     "chunk_carry": ["chunk_carry.hip", "gdr_device.h", "gdr_launch.h"],
     "decode": ["decode.hip", "gdr_device.h", "gdr_launch.h"],
+    "tree_verify": ["tree_verify.hip", "gdr_device.h", "gdr_launch.h"],
 }
 KERNEL_SYMBOL = {"chunk_prep": "chunk_prep_kernel", "chunk_carry": "chunk_carry_kernel",
-                 "decode": "token_kernel"}
+                 "decode": "token_kernel", "tree_verify": "tree_verify_kernel"}
 CALIB_BYTES = 256 << 20           # calibration kernel: reads and writes this many bytes
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_b1_t4097_decode_b32.md")
 UTIL_SUMMARY = os.path.join(ROOT, "profiles", "mfma_util_prefill_b1_t4097_decode_b32.md")
@@ -532,6 +533,44 @@ def bench_short_calls(w, reps=10):
     return out
 
 
+TREE_CASES = ((1, 33, "binary"), (1, 49, "binary"), (1, 64, "binary"), (1, 64, "random"),
+              (1, 64, "chain"), (8, 64, "binary"))
+
+
+def bench_tree(w, reps=20):
+    """Tree-verify solve at the decode workload's head shape (HK=16, HV=32, dk=dv=128, h0
+    given) on the tree sizes of the uzu tree-solve measurements: one call's time, calls
+    issued back to back and timed with HIP events."""
+    import torch
+
+    import gated_delta_rule_70_amd as gdr
+    from gdr_synth import make_inputs, make_tree
+
+    out = []
+    for B, T, kind in TREE_CASES:
+        x = make_inputs(B, T, w.HK, w.HV, w.dk, w.dv, dtype=w.dtype, seed=w.seed + 11, h0=True)
+        d = {k: v.cuda() for k, v in x.items()}
+        par = make_tree(B, T, kind, seed=w.seed).cuda()
+        o = torch.empty(B, T, w.HV, w.dv, device="cuda")
+
+        def call():
+            gdr.tree_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], par, h0=d["h0"], o=o)
+
+        call()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        out.append({"B": B, "T": T, "tree": kind, "us_per_call": round(ms * 1e3, 2),
+                    "nodes_per_s": round(B * T / (ms * 1e-3), 1)})
+    return {"workload": f"HK={w.HK} HV={w.HV} dk=dv={w.dk} bf16 q/k/v, h0 given; {reps} calls back to back",
+            "cases": out}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -648,6 +687,7 @@ def main():
 
     if not args.no_short_calls and not args.profile_run:
         line["short_calls"] = bench_short_calls(DECODE)
+        line["tree_verify"] = bench_tree(DECODE)
 
     if not args.no_cpu_baseline:
         import numpy as np

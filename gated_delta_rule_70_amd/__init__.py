@@ -21,12 +21,14 @@ import os
 
 import torch
 
-__all__ = ["decode_step", "fused_recurrent", "chunk_prefill", "forward", "workspace_bytes",
-           "GdrError", "lib", "Dims", "LIB_PATH", "ABI_VERSION", "RECURRENT_MAX_T"]
+__all__ = ["decode_step", "fused_recurrent", "chunk_prefill", "forward", "tree_verify",
+           "workspace_bytes", "GdrError", "lib", "Dims", "LIB_PATH", "ABI_VERSION",
+           "RECURRENT_MAX_T", "TREE_MAX_T"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so")
 ABI_VERSION = 2
 RECURRENT_MAX_T = 8  # gdr_forward: calls of at most this many tokens take the fused recurrence
+TREE_MAX_T = 64      # gdr_tree_verify: most nodes per tree
 BF16, F32 = 0, 1
 
 
@@ -62,6 +64,8 @@ def lib():
     L.gdr_decode_step.argtypes = [ctypes.POINTER(Dims)] + [_VP] * 9
     L.gdr_fused_recurrent.restype = ctypes.c_int
     L.gdr_fused_recurrent.argtypes = [ctypes.POINTER(Dims)] + [_VP] * 9
+    L.gdr_tree_verify.restype = ctypes.c_int
+    L.gdr_tree_verify.argtypes = [ctypes.POINTER(Dims)] + [_VP] * 9
     L.gdr_forward.restype = ctypes.c_int
     L.gdr_forward.argtypes = [ctypes.POINTER(Dims)] + [_VP] * 9 + [ctypes.c_size_t, _VP]
     L.gdr_chunk_prefill_workspace_bytes.restype = ctypes.c_size_t
@@ -237,3 +241,24 @@ def forward(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None, workspa
                              ctypes.c_size_t(0 if workspace is None else workspace.numel()),
                              _stream(stream)))
     return o, ht
+
+
+def tree_verify(q, k, v, g, beta, parent, h0=None, o=None, stream=None):
+    """Tree-verify solve (gdr_tree_verify): ``parent`` is an int32 GPU tensor ``[B,T]`` of
+    parent node indices (-1: continues from ``h0``).  Returns ``o`` ``[B,T,HV,dv]``, each
+    node's output along its root path."""
+    _check_inputs(q, k, v, g, beta)
+    B, T, HK, dk = q.shape
+    HV, dv = v.shape[2], v.shape[3]
+    _need(parent, "parent", torch.int32)
+    if tuple(parent.shape) != (B, T):
+        raise ValueError(f"parent must be [B,T] = {(B, T)}")
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    if o is None:
+        o = torch.empty(B, T, HV, dv, device=q.device, dtype=torch.float32)
+    _need(o, "o", torch.float32)
+    d = _dims(q, v, 0)
+    _check(lib().gdr_tree_verify(ctypes.byref(d), _ptr(parent), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                 _ptr(beta), _ptr(h0), _ptr(o), _stream(stream)))
+    return o

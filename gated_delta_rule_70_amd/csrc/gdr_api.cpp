@@ -229,6 +229,20 @@ int gdr_chunk_carry(const gdr_dims* dims, const void* q, const void* k, const vo
                           false, true);
 }
 
+int gdr_tree_verify(const gdr_dims* dims, const int32_t* parent, const void* q, const void* k,
+                    const void* v, const float* g, const float* beta, const float* h0, float* o,
+                    void* stream) {
+    if (!parent) return GDR_ERR_NULL;
+    Sizes s;
+    const int st = validate(dims, Path::tokens, q, k, v, g, beta, h0, o, nullptr, &s);
+    if (st != GDR_OK) return st;
+    if (dims->T > GDR_TREE_MAX_T) return GDR_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(parent) & 3u) != 0) return GDR_ERR_ALIGN;
+    if (overlap(range_of(o, s.o), range_of(parent, (size_t)dims->B * dims->T * 4))) return GDR_ERR_ALIAS;
+    const gdr::LaunchArgs a = make_args(dims, q, k, v, g, beta, h0, o, nullptr, nullptr, stream);
+    return gdr::launch_tree_verify(a, parent) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
 int gdr_forward(const gdr_dims* dims, const void* q, const void* k, const void* v,
                 const float* g, const float* beta, const float* h0, float* o, float* ht,
                 void* workspace, size_t workspace_bytes, void* stream) {

@@ -70,5 +70,7 @@ struct ChunkRecord {
 hipError_t launch_tokens(const LaunchArgs& a);
 hipError_t launch_chunk_prep(const LaunchArgs& a);
 hipError_t launch_chunk_carry(const LaunchArgs& a);
+// tree-verify solve over trees of a.T <= 64 nodes; parent [B][T] int32 on the device
+hipError_t launch_tree_verify(const LaunchArgs& a, const int32_t* parent);
 
 }  // namespace gdr

@@ -153,6 +153,24 @@ int gdr_forward(const gdr_dims* dims, const void* q, const void* k, const void* 
                 const float* g, const float* beta, const float* h0, float* o, float* ht,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Tree-verify solve (uzu PR #576, "Support TreeUpdateSolve kernel": a gram over a
+ * speculative token tree, keys times the initial state, an exact triangular solve).  Each
+ * batch element holds a tree of T <= GDR_TREE_MAX_T tokens in topological order:
+ * parent[b][t] is the parent node of node t, in [-1, t), -1 meaning the node continues
+ * from the initial state h0 (zero if h0 is NULL); entries outside that range are read
+ * as -1.  Node t's output o[b][t] is the output of the recurrence run along its root
+ * path (every node continues from its parent's state).  The final states are not
+ * written.  parent is a device array [B][T] of int32, 4-byte aligned; the other
+ * arguments, layouts and checks are those of gdr_fused_recurrent (chunk ignored).  The
+ * cumulative decay along any root path must stay above -80 in every channel.  Uses no
+ * workspace.  T above GDR_TREE_MAX_T returns GDR_ERR_UNSUPPORTED.
+ */
+#define GDR_TREE_MAX_T 64
+int gdr_tree_verify(const gdr_dims* dims, const int32_t* parent, const void* q, const void* k,
+                    const void* v, const float* g, const float* beta, const float* h0, float* o,
+                    void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* gdr_status_str(int status);
 

@@ -36,7 +36,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "gdr_abi_version", "gdr_chunk_carry", "gdr_chunk_prefill", "gdr_chunk_prefill_workspace_bytes",
-        "gdr_chunk_prep", "gdr_decode_step", "gdr_forward", "gdr_fused_recurrent", "gdr_status_str"])
+        "gdr_chunk_prep", "gdr_decode_step", "gdr_forward", "gdr_fused_recurrent", "gdr_status_str",
+        "gdr_tree_verify"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -161,6 +162,25 @@ def test_forward_routes_by_length(L):
     assert prefill(L, None, entry="gdr_forward") == ENULL
 
 
+def tree(L, d, parent=addr(10), **ptrs):
+    p = {n: addr(i) for i, n in enumerate(["q", "k", "v", "g", "beta", "h0", "o"])}
+    p.update(ptrs)
+    return L.gdr_tree_verify(None if d is None else ctypes.byref(d), parent, p["q"], p["k"], p["v"],
+                             p["g"], p["beta"], p["h0"], p["o"], None)
+
+
+def test_tree_verify_checks(L):
+    assert tree(L, dims(T=9), parent=None) == ENULL
+    assert tree(L, None) == ENULL
+    assert tree(L, dims(T=9), q=None) == ENULL
+    assert tree(L, dims(T=65)) == EUNSUP                        # at most 64 nodes
+    assert tree(L, dims(T=9, dk=48)) == EUNSUP
+    assert tree(L, dims(T=9), parent=addr(10, 2)) == EALIGN      # int32 entries
+    assert tree(L, dims(T=9), q=addr(0, 8)) == EALIGN
+    assert tree(L, dims(T=9), o=addr(10, 0)) == EALIAS           # o over parent
+    assert tree(L, dims(T=9), o=addr(0, 256)) == EALIAS          # o inside q
+
+
 def test_workspace_checks(L):
     d = dims()
     need = L.gdr_chunk_prefill_workspace_bytes(ctypes.byref(d))
@@ -204,3 +224,4 @@ def test_valid_arguments_reach_the_runtime_without_a_gpu(L):
     assert prefill(L, dims(), ht=addr(5, 0)) == EHIP        # in-place ht == h0 is allowed
     assert decode(L, dims(T=1), ht=addr(5, 0)) == EHIP
     assert decode(L, dims(T=9, chunk=8), ht=addr(5, 0), entry="gdr_fused_recurrent") == EHIP
+    assert tree(L, dims(T=64, dv=64)) == EHIP
