@@ -16,9 +16,19 @@
 // Kh = exp(-gam) k; every term that survives the ancestry mask is bounded by 1, the
 // masked ones are finite while the path decay stays above -80 in every channel.
 //
-// One 256-thread workgroup per (batch, value head, 32-column block of v): the node-level
-// terms live in LDS; the products run on the fp32 matrix cores (16x16x4); the forward
-// substitution runs in one wave, its lanes split over columns and ancestor parity.
+// One 256-thread workgroup per (batch, value head, 32-column block of v), all of a tree's
+// rows in LDS.  Every phase is parallel across nodes:
+//   0. all global reads issued at once (parents, beta, g, k, q rows, the block's columns
+//      of h0 and v);
+//   1. root-path decay prefixes and ancestor masks by pointer doubling (6 rounds cover
+//      any depth below 64), then the decayed rows;
+//   2. Kt h0 and Qt h0 on the fp32 matrix cores (16x16x4), the right-hand side;
+//   3. A and P on the matrix cores, masked by ancestry;
+//   4. forward substitution level by level (nodes of equal depth are independent);
+//   5. O = Qt h0 + P U on the matrix cores.
+// In the matrix-core products lane group g reduces over a contiguous quarter of the
+// reduction index (16-byte LDS reads); the order of a sum's terms is free as long as both
+// operands use the same one.
 #include "gdr_device.h"
 #include "gdr_launch.h"
 
@@ -34,23 +44,42 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// sum over a K-long reduction of X[rowA][.] * Y[rowB][.] for a 16x16 tile: lane (i, g)
+// reads K/4 contiguous floats of row i of each operand, starting at g*K/4
+template <int K>
+__device__ __forceinline__ f32x4 tile_dot(const float* xa, const float* yb, f32x4 acc) {
+#pragma unroll
+    for (int c = 0; c < K / 4; c += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(xa + c);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(yb + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = mfma4(a[e], b[e], acc);
+    }
+    return acc;
+}
+
 template <typename TIn, int DK>
 __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int32_t* __restrict__ parent, const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
     const float* __restrict__ h0, float* __restrict__ o, int T, int HK, int HV, int DV) {
-    constexpr int KP = DK + 4;   // row pitch: lanes reading 16 rows at one column hit 16 banks
+    constexpr int KP = DK + 4;   // row pitch (floats): 16 rows read at one offset hit 16 banks
     constexpr int AP = TM + 4;
     constexpr int UP = CB + 4;
-    __shared__ float sKt[TM * KP];  // gam, then exp(gam) k
-    __shared__ float sKh[TM * KP];  // k, then exp(-gam) k
-    __shared__ float sQt[TM * KP];  // q, then exp(gam) q
-    __shared__ float sA[TM * AP];
-    __shared__ float sP[TM * AP];
-    __shared__ float sU[TM * UP];   // right-hand side, then U
-    __shared__ int sPar[TM];
+    constexpr int HP = DK + 4;   // transposed h0 / v columns
+    constexpr int ELT = sizeof(TIn);
+    static_assert(CB * HP <= TM * AP && CB * (TM + 4) <= TM * AP, "staging must fit A and P");
+    __shared__ __attribute__((aligned(16))) float sKt[TM * KP];  // gam, then exp(gam) k
+    __shared__ __attribute__((aligned(16))) float sKh[TM * KP];  // k, then exp(-gam) k
+    __shared__ __attribute__((aligned(16))) float sQt[TM * KP];  // q, then exp(gam) q
+    __shared__ __attribute__((aligned(16))) float sA[TM * AP];   // h0 columns [j][c], then A
+    __shared__ __attribute__((aligned(16))) float sP[TM * AP];   // v columns [j][t], then P
+    __shared__ __attribute__((aligned(16))) float sU[TM * UP];   // right-hand side, then U
+    __shared__ int sJ[TM];                                      // pointer-doubling jumps
     __shared__ unsigned long long sAnc[TM];
     __shared__ float sBeta[TM];
+    __shared__ int sDep[TM];
+    __shared__ int sMaxDep;
 
     const int ncb = DV / CB;
     const int cb = blockIdx.x % ncb;
@@ -67,60 +96,201 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int NB = T16 / 16;
     const int col0 = cb * CB;
 
-    // ---- 0. parents (out-of-range entries read as -1), beta, raw g/k/q rows --------------
-    for (int t = tid; t < TM; t += 256) {
+    // ---- 0. global reads, all requested before any is used --------------------------------
+    // g/k/q: thread t covers 4 channels of rows t / (DK/4) + (256 / (DK/4)) * m
+    constexpr int QPR = DK / 4;            // 4-channel groups per row
+    constexpr int RPI = 256 / QPR;         // rows per pass
+    constexpr int NPASS = TM / RPI;
+    const int c4 = 4 * (tid % QPR);
+    f32x4 gv[NPASS];
+    uint32_t kraw[NPASS][ELT], qraw[NPASS][ELT];
+#pragma unroll
+    for (int m = 0; m < NPASS; ++m) {
+        const int t = tid / QPR + RPI * m;
+        gv[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < ELT; ++e) kraw[m][e] = qraw[m][e] = 0u;
+        if (t < T) {
+            gv[m] = *reinterpret_cast<const f32x4*>(g + (((size_t)b * T + t) * HV + h) * DK + c4);
+            const size_t kq = (((size_t)b * T + t) * HK + kh) * DK + c4;
+            if constexpr (ELT == 2) {
+                const uint2 kk = *reinterpret_cast<const uint2*>(k + kq);
+                const uint2 qq = *reinterpret_cast<const uint2*>(q + kq);
+                kraw[m][0] = kk.x; kraw[m][1] = kk.y;
+                qraw[m][0] = qq.x; qraw[m][1] = qq.y;
+            } else {
+                const uint4 kk = *reinterpret_cast<const uint4*>(k + kq);
+                const uint4 qq = *reinterpret_cast<const uint4*>(q + kq);
+                kraw[m][0] = kk.x; kraw[m][1] = kk.y; kraw[m][2] = kk.z; kraw[m][3] = kk.w;
+                qraw[m][0] = qq.x; qraw[m][1] = qq.y; qraw[m][2] = qq.z; qraw[m][3] = qq.w;
+            }
+        }
+    }
+    // h0 columns col0 .. col0+31: thread covers row c = tid / 8 + 32 m, 4 columns
+    constexpr int HPASS = DK / 32;
+    f32x4 hv[HPASS];
+#pragma unroll
+    for (int m = 0; m < HPASS; ++m) {
+        hv[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (h0 != nullptr)
+            hv[m] = *reinterpret_cast<const f32x4*>(h0 + ((size_t)bh * DK + tid / 8 + 32 * m) * DV +
+                                                    col0 + 4 * (tid % 8));
+    }
+    // v rows: thread covers node t = tid / 8 + 32 m, 4 columns
+    uint32_t vraw[2][ELT];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int t = tid / 8 + 32 * m;
+#pragma unroll
+        for (int e = 0; e < ELT; ++e) vraw[m][e] = 0u;
+        if (t < T) {
+            const size_t vo = (((size_t)b * T + t) * HV + h) * DV + col0 + 4 * (tid % 8);
+            if constexpr (ELT == 2) {
+                const uint2 x = *reinterpret_cast<const uint2*>(v + vo);
+                vraw[m][0] = x.x; vraw[m][1] = x.y;
+            } else {
+                const uint4 x = *reinterpret_cast<const uint4*>(v + vo);
+                vraw[m][0] = x.x; vraw[m][1] = x.y; vraw[m][2] = x.z; vraw[m][3] = x.w;
+            }
+        }
+    }
+    if (tid < TM) {
         int p = -1;
         float bt = 0.f;
-        if (t < T) {
-            p = parent[(size_t)b * T + t];
-            if (p < -1 || p >= t) p = -1;
-            bt = beta[((size_t)b * T + t) * HV + h];
+        if (tid < T) {
+            p = parent[(size_t)b * T + tid];
+            if (p < -1 || p >= tid) p = -1;  // not an earlier node: a child of the initial state
+            bt = beta[((size_t)b * T + tid) * HV + h];
         }
-        sPar[t] = p;
-        sBeta[t] = bt;
+        sJ[tid] = p;
+        sAnc[tid] = p >= 0 ? 1ull << p : 0ull;
+        sBeta[tid] = bt;
     }
-    for (int e = tid; e < T16 * DK; e += 256) {
-        const int t = e / DK, c = e % DK;
-        float gv = 0.f, kv = 0.f, qv = 0.f;
-        if (t < T) {
-            gv = g[(((size_t)b * T + t) * HV + h) * DK + c];
-            kv = to_f32(k[(((size_t)b * T + t) * HK + kh) * DK + c]);
-            qv = to_f32(q[(((size_t)b * T + t) * HK + kh) * DK + c]);
+    if (tid == 0) sMaxDep = 0;
+    auto raw4 = [&](const uint32_t (&r)[ELT]) {
+        f32x4 x;
+        if constexpr (ELT == 2) {
+            x[0] = __uint_as_float(r[0] << 16); x[1] = __uint_as_float(r[0] & 0xFFFF0000u);
+            x[2] = __uint_as_float(r[1] << 16); x[3] = __uint_as_float(r[1] & 0xFFFF0000u);
+        } else {
+            x[0] = __uint_as_float(r[0]); x[1] = __uint_as_float(r[1]);
+            x[2] = __uint_as_float(r[2]); x[3] = __uint_as_float(r[3]);
         }
-        sKt[t * KP + c] = gv;
-        sKh[t * KP + c] = kv;
-        sQt[t * KP + c] = qv;
+        return x;
+    };
+#pragma unroll
+    for (int m = 0; m < NPASS; ++m) {
+        const int t = tid / QPR + RPI * m;
+        *reinterpret_cast<f32x4*>(sKt + t * KP + c4) = gv[m];
+        *reinterpret_cast<f32x4*>(sKh + t * KP + c4) = raw4(kraw[m]);
+        *reinterpret_cast<f32x4*>(sQt + t * KP + c4) = raw4(qraw[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < HPASS; ++m) {  // transposed: sA[j * HP + c]
+        const int c = tid / 8 + 32 * m;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sA[(4 * (tid % 8) + e) * HP + c] = hv[m][e];
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {  // transposed: sP[j * (TM + 4) + t]
+        const int t = tid / 8 + 32 * m;
+        const f32x4 x = raw4(vraw[m]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sP[(4 * (tid % 8) + e) * (TM + 4) + t] = x[e];
     }
     __syncthreads();
 
-    // ---- 1. ancestor masks (walk up: parents are strictly smaller, so every walk ends) and
-    //         decay prefixes along the root path (parents come first in each channel) ------
+    // ---- 1. decay prefixes and ancestors by pointer doubling ------------------------------
+    // After round r, gam_t sums g over the 2^r nearest nodes of t's root path (t included)
+    // and J_t is the node 2^r steps up (-1 past the root).  Each round reads, synchronises,
+    // then writes, so every read sees the previous round.
+#pragma unroll 1
+    for (int round = 0; round < 6; ++round) {
+        float add[NPASS][4];
+#pragma unroll
+        for (int m = 0; m < NPASS; ++m) {
+            const int t = tid / QPR + RPI * m;
+            const int j = sJ[t];
+            const f32x4 x = j >= 0 ? *reinterpret_cast<const f32x4*>(sKt + j * KP + c4)
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) add[m][e] = x[e];
+        }
+        int jn = -1;
+        unsigned long long an = 0;
+        if (tid < TM) {
+            const int j = sJ[tid];
+            jn = j >= 0 ? sJ[j] : -1;
+            an = sAnc[tid] | (j >= 0 ? sAnc[j] : 0ull);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < NPASS; ++m) {
+            const int t = tid / QPR + RPI * m;
+            f32x4* p = reinterpret_cast<f32x4*>(sKt + t * KP + c4);
+            f32x4 x = *p;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] += add[m][e];
+            *p = x;
+        }
+        if (tid < TM) {
+            sJ[tid] = jn;
+            sAnc[tid] = an;
+        }
+        __syncthreads();
+    }
+    // decayed rows; node depths
+#pragma unroll
+    for (int m = 0; m < NPASS; ++m) {
+        const int t = tid / QPR + RPI * m;
+        const int i = t * KP + c4;
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(sKt + i);
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(sKh + i);
+        const f32x4 qv = *reinterpret_cast<const f32x4*>(sQt + i);
+        f32x4 kt, kb, qt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float ep = __expf(gm[e]);
+            kt[e] = ep * kv[e];
+            kb[e] = __expf(-gm[e]) * kv[e];
+            qt[e] = ep * qv[e];
+        }
+        *reinterpret_cast<f32x4*>(sKt + i) = kt;
+        *reinterpret_cast<f32x4*>(sKh + i) = kb;
+        *reinterpret_cast<f32x4*>(sQt + i) = qt;
+    }
     if (tid < T) {
-        unsigned long long m = 0;
-        for (int r = sPar[tid]; r >= 0; r = sPar[r]) m |= 1ull << r;
-        sAnc[tid] = m;
+        const int dep = __builtin_popcountll(sAnc[tid]);
+        sDep[tid] = dep;
+        atomicMax(&sMaxDep, dep);
     }
-    if (tid < DK) {
-        for (int t = 1; t < T; ++t) {
-            const int p = sPar[t];
-            if (p >= 0) sKt[t * KP + tid] += sKt[p * KP + tid];
+    __syncthreads();
+
+    // ---- 2. Kt h0, Qt h0 and the right-hand side beta (v - Kt h0) -------------------------
+    // tile (I, N): rows 16I.., columns 16N.. of this block; wave w owns tiles w and w + 4 and
+    // keeps its Qt h0 tiles for the output
+    f32x4 qh[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int tile = wave + 4 * u;
+        f32x4 kacc = {0.f, 0.f, 0.f, 0.f}, qacc = {0.f, 0.f, 0.f, 0.f};
+        if (tile < 2 * NB) {
+            const int I = tile >> 1, N = tile & 1;
+            const int cq = gq * (DK / 4);
+            const float* hb = sA + (16 * N + li) * HP + cq;
+            kacc = tile_dot<DK>(sKt + (16 * I + li) * KP + cq, hb, kacc);
+            qacc = tile_dot<DK>(sQt + (16 * I + li) * KP + cq, hb, qacc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * I + 4 * gq + i;
+                sU[r * UP + 16 * N + li] = sBeta[r] * (sP[(16 * N + li) * (TM + 4) + r] - kacc[i]);
+            }
         }
+        qh[u] = qacc;
     }
     __syncthreads();
 
-    // ---- 2. decayed rows ---------------------------------------------------------------
-    for (int e = tid; e < T16 * DK; e += 256) {
-        const int i = (e / DK) * KP + e % DK;
-        const float gm = sKt[i];
-        const float kv = sKh[i];
-        sKt[i] = __expf(gm) * kv;
-        sKh[i] = __expf(-gm) * kv;
-        sQt[i] *= __expf(gm);
-    }
-    __syncthreads();
-
-    // ---- 3. A and P tiles on the matrix cores, masked by ancestry ------------------------
-    // products: tile (I, J), J <= I, of A (x = 0) and P (x = 1); upper tiles are zero
+    // ---- 3. A and P tiles, masked by ancestry (upper tiles are zero) -----------------------
     const int ntile = NB * NB;
     for (int job = wave; job < 2 * ntile; job += 4) {
         const int x = job / ntile;
@@ -128,10 +298,9 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         float* dst = x == 0 ? sA : sP;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if (J <= I) {
-            const float* ra = (x == 0 ? sKt : sQt) + (16 * I + li) * KP + gq;
-            const float* rb = sKh + (16 * J + li) * KP + gq;
-#pragma unroll 8
-            for (int c = 0; c < DK; c += 4) acc = mfma4(ra[c], rb[c], acc);
+            const int cq = gq * (DK / 4);
+            acc = tile_dot<DK>((x == 0 ? sKt : sQt) + (16 * I + li) * KP + cq,
+                               sKh + (16 * J + li) * KP + cq, acc);
         }
         const int s = 16 * J + li;
 #pragma unroll
@@ -146,65 +315,30 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
             dst[r * AP + s] = val;
         }
     }
-
-    // ---- 4. Kt h0 and Qt h0 for this column block; right-hand side beta (v - Kt h0) -------
-    // tile (I, N): rows 16I.., columns col0 + 16N..; wave w owns tiles w, w+4, ... and keeps
-    // its Qt h0 tiles for the output
-    f32x4 qh[2];  // NB * 2 <= 8 tiles, at most 2 per wave
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int tile = wave + 4 * u;
-        f32x4 kacc = {0.f, 0.f, 0.f, 0.f}, qacc = {0.f, 0.f, 0.f, 0.f};
-        if (tile < 2 * NB) {
-            const int I = tile >> 1, N = tile & 1;
-            if (h0 != nullptr) {
-                const float* hb = h0 + ((size_t)bh * DK + gq) * DV + col0 + 16 * N + li;
-                const float* ra = sKt + (16 * I + li) * KP + gq;
-                const float* rq = sQt + (16 * I + li) * KP + gq;
-#pragma unroll 8
-                for (int c = 0; c < DK; c += 4) {
-                    const float hv = hb[(size_t)c * DV];
-                    kacc = mfma4(ra[c], hv, kacc);
-                    qacc = mfma4(rq[c], hv, qacc);
-                }
-            }
-            const int j = 16 * N + li;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * I + 4 * gq + i;
-                float rhs = 0.f;
-                if (r < T) {
-                    const float vv = to_f32(v[(((size_t)b * T + r) * HV + h) * DV + col0 + j]);
-                    rhs = sBeta[r] * (vv - kacc[i]);
-                }
-                sU[r * UP + j] = rhs;
-            }
-        }
-        qh[u] = qacc;
-    }
     __syncthreads();
 
-    // ---- 5. forward substitution: U_r = rhs_r - sum_{s ancestor of r} A_rs U_s ------------
-    // one wave: lane (j, half) sums the ancestors of parity `half` for column j
-    if (wave == 0) {
-        const int j = lane & (CB - 1);
-        const int half = lane >> 5;
-        for (int r = 1; r < T; ++r) {
-            unsigned long long m = sAnc[r] & (half ? 0xAAAAAAAAAAAAAAAAull : 0x5555555555555555ull);
-            float acc = 0.f;
-            while (m) {
-                const int s = __builtin_ctzll(m);
-                m &= m - 1;
-                acc += sA[r * AP + s] * sU[s * UP + j];
+    // ---- 4. forward substitution, one depth level at a time --------------------------------
+    // U_r = rhs_r - sum_{s ancestor of r} A_rs U_s; every ancestor is shallower than r, so
+    // the nodes of one level read only rows finished in earlier levels.
+    const int maxdep = sMaxDep;
+    for (int L = 1; L <= maxdep; ++L) {
+        for (int item = tid; item < T * CB; item += 256) {
+            const int r = item / CB, j = item % CB;
+            if (sDep[r] == L) {
+                unsigned long long m = sAnc[r];
+                float acc = sU[r * UP + j];
+                while (m) {
+                    const int s = __builtin_ctzll(m);
+                    m &= m - 1;
+                    acc -= sA[r * AP + s] * sU[s * UP + j];
+                }
+                sU[r * UP + j] = acc;
             }
-            acc += __shfl_xor(acc, 32);
-            if (half == 0) sU[r * UP + j] -= acc;
-            // the next row reads this one: same wave, LDS accesses complete in order
         }
+        __syncthreads();
     }
-    __syncthreads();
 
-    // ---- 6. O = Qt h0 + P U ------------------------------------------------------------
+    // ---- 5. O = Qt h0 + P U ----------------------------------------------------------------
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int tile = wave + 4 * u;
