@@ -24,7 +24,8 @@
 //      any depth below 64), then the decayed rows;
 //   2. Kt h0 and Qt h0 on the fp32 matrix cores (16x16x4), the right-hand side;
 //   3. A and P on the matrix cores, masked by ancestry;
-//   4. forward substitution level by level (nodes of equal depth are independent);
+//   4. forward substitution level by level (nodes of equal depth are independent; a level
+//      of few nodes splits each ancestor sum over several threads);
 //   5. O = Qt h0 + P U on the matrix cores.
 // In the matrix-core products lane group g reduces over a contiguous quarter of the
 // reduction index (16-byte LDS reads); the order of a sum's terms is free as long as both
@@ -79,6 +80,10 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     __shared__ unsigned long long sAnc[TM];
     __shared__ float sBeta[TM];
     __shared__ int sDep[TM];
+    __shared__ int sCnt[TM];    // nodes per depth
+    __shared__ int sStart[TM];  // first slot of each depth in sList
+    __shared__ int sList[TM];   // nodes ordered by depth
+    __shared__ float sRed[256]; // partial ancestor sums of the substitution
     __shared__ int sMaxDep;
 
     const int ncb = DV / CB;
@@ -167,6 +172,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         sBeta[tid] = bt;
     }
     if (tid == 0) sMaxDep = 0;
+    if (tid < TM) sCnt[tid] = 0;
     auto raw4 = [&](const uint32_t (&r)[ELT]) {
         f32x4 x;
         if constexpr (ELT == 2) {
@@ -263,8 +269,16 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         const int dep = __builtin_popcountll(sAnc[tid]);
         sDep[tid] = dep;
         atomicMax(&sMaxDep, dep);
+        atomicAdd(&sCnt[dep], 1);
     }
     __syncthreads();
+    if (tid == 0) {  // first slot of each depth (counts are in place; the order is fixed)
+        int acc = 0;
+        for (int L = 0; L < TM; ++L) {
+            sStart[L] = acc;
+            acc += sCnt[L];
+        }
+    }
 
     // ---- 2. Kt h0, Qt h0 and the right-hand side beta (v - Kt h0) -------------------------
     // tile (I, N): rows 16I.., columns 16N.. of this block; wave w owns tiles w and w + 4 and
@@ -289,6 +303,14 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         qh[u] = qacc;
     }
     __syncthreads();
+
+    // nodes by depth, in index order within a depth
+    if (tid < T) {
+        const int dep = sDep[tid];
+        int rank = 0;
+        for (int u = 0; u < tid; ++u) rank += sDep[u] == dep;
+        sList[sStart[dep] + rank] = tid;
+    }
 
     // ---- 3. A and P tiles, masked by ancestry (upper tiles are zero) -----------------------
     const int ntile = NB * NB;
@@ -319,12 +341,40 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 
     // ---- 4. forward substitution, one depth level at a time --------------------------------
     // U_r = rhs_r - sum_{s ancestor of r} A_rs U_s; every ancestor is shallower than r, so
-    // the nodes of one level read only rows finished in earlier levels.
+    // the nodes of one level read only rows finished in earlier levels.  A level with few
+    // nodes (a deep, narrow tree) splits each ancestor sum over ns threads, which leave
+    // partial sums that one thread then combines in a fixed order.
     const int maxdep = sMaxDep;
     for (int L = 1; L <= maxdep; ++L) {
-        for (int item = tid; item < T * CB; item += 256) {
-            const int r = item / CB, j = item % CB;
-            if (sDep[r] == L) {
+        const int base = sStart[L];
+        const int cols = sCnt[L] * CB;  // (node, column) pairs of this level
+        // ns threads per pair (a power of two); part p takes the ancestors s = p mod ns
+        const int ns = cols <= 32 ? 8 : cols <= 64 ? 4 : cols <= 128 ? 2 : 1;
+        if (ns > 1) {
+            float part = 0.f;
+            if (tid < cols * ns) {
+                const int rc = tid / ns, pid = tid % ns;
+                const int r = sList[base + rc / CB], j = rc % CB;
+                const unsigned long long sel = ns == 8 ? 0x0101010101010101ull
+                                             : ns == 4 ? 0x1111111111111111ull : 0x5555555555555555ull;
+                unsigned long long m = sAnc[r] & (sel << pid);
+                while (m) {
+                    const int s = __builtin_ctzll(m);
+                    m &= m - 1;
+                    part += sA[r * AP + s] * sU[s * UP + j];
+                }
+            }
+            sRed[tid] = part;
+            __syncthreads();
+            if (tid < cols) {
+                const int r = sList[base + tid / CB], j = tid % CB;
+                float acc = sU[r * UP + j];
+                for (int p = 0; p < ns; ++p) acc -= sRed[tid * ns + p];
+                sU[r * UP + j] = acc;
+            }
+        } else {
+            for (int item = tid; item < cols; item += 256) {
+                const int r = sList[base + item / CB], j = item % CB;
                 unsigned long long m = sAnc[r];
                 float acc = sU[r * UP + j];
                 while (m) {
