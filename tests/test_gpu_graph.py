@@ -79,3 +79,31 @@ def test_prefill_replayed_from_a_graph(T):
         torch.cuda.synchronize()
         assert torch.equal(o, o_e), f"replay {rep}: o differs"
         assert torch.equal(ht, ht_e), f"replay {rep}: final state differs"
+
+
+def test_fused_recurrence_and_tree_verify_replayed_from_a_graph():
+    from gdr_synth import make_tree
+
+    B, T, HK, HV, dk, dv = 2, 12, 2, 4, 128, 64
+    x = dev(small_inputs(B, T, HK, HV, dk, dv, seed=73))
+    par = make_tree(B, T, "random", seed=5).cuda()
+    note(f"graph fused recurrence + tree verify B={B} T={T}")
+    o_r, ht_r = gdr.fused_recurrent(x["q"], x["k"], x["v"], x["g"], x["beta"], h0=x["h0"])
+    o_t = gdr.tree_verify(x["q"], x["k"], x["v"], x["g"], x["beta"], par, h0=x["h0"])
+    torch.cuda.synchronize()
+
+    o1 = torch.empty_like(o_r)
+    ht1 = torch.empty_like(ht_r)
+    o2 = torch.empty_like(o_t)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gdr.fused_recurrent(x["q"], x["k"], x["v"], x["g"], x["beta"], h0=x["h0"], o=o1, ht=ht1)
+        gdr.tree_verify(x["q"], x["k"], x["v"], x["g"], x["beta"], par, h0=x["h0"], o=o2)
+    for rep in range(3):
+        for t in (o1, ht1, o2):
+            t.fill_(float("nan"))          # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o_r) and torch.equal(ht1, ht_r), f"replay {rep}: fused recurrence differs"
+        assert torch.equal(o2, o_t), f"replay {rep}: tree verify differs"
