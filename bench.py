@@ -52,6 +52,9 @@ if ROOT not in sys.path:
 METRIC = "prefill tokens/s (HV=32,dk=dv=128) + decode state GB/s, % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak, published
+# fp32 vector operations per second without packed fp32 instructions (which this build does
+# not use): 256 CUs x 64 lanes x 2.4 GHz; the published 157.3 TFLOP/s counts packed FMAs
+VALU_F32_OPS_PEAK = 256 * 64 * 2.4e9
 
 CSRC = os.path.join(ROOT, "gated_delta_rule_70_amd", "csrc")
 KERNEL_SOURCES = {  # kernel -> the sources its machine code is built from
@@ -480,7 +483,8 @@ def bench_short_calls(w, reps=10):
     d = {k: v.cuda() for k, v in x.items()}
     state = d["h0"].clone()
     out = {"T": list(SHORT_T), "decode_loop_ms": [], "fused_recurrent_ms": [], "chunked_ms": [],
-           "chunked_best_chunk": [], "fused_recurrent_state_GBps": [], "fastest": []}
+           "chunked_best_chunk": [], "fused_recurrent_state_GBps": [], "fused_recurrent_valu_frac": [],
+           "fastest": []}
 
     def timed(fn):
         fn()
@@ -526,10 +530,14 @@ def bench_short_calls(w, reps=10):
         out["chunked_ms"].append(round(best[0], 5))
         out["chunked_best_chunk"].append(best[1])
         out["fused_recurrent_state_GBps"].append(round(2 * B * HV * dk * dv * 4 / (t_fused * 1e-3) / 1e9, 1))
+        # 4 vector operations per state element per token: decay, prediction, update, output
+        out["fused_recurrent_valu_frac"].append(
+            round(4 * B * HV * dk * dv * T / (t_fused * 1e-3) / VALU_F32_OPS_PEAK, 4))
         out["fastest"].append(min((t_loop, "decode_loop"), (t_fused, "fused_recurrent"),
                                   (best[0], "chunked"))[1])
     out["workload"] = (f"B={B} HK={HK} HV={HV} dk=dv={dk} bf16 q/k/v, h0 given, one call of T tokens; "
                        f"{reps} calls back to back per figure")
+    out["valu_peak_ops_per_s"] = VALU_F32_OPS_PEAK
     return out
 
 
@@ -565,8 +573,28 @@ def bench_tree(w, reps=20):
         b.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / reps
+        # algorithmic work: inputs and outputs once; per head the ancestry-masked gram and
+        # causal terms (2 dk flops per ancestor pair), keys/queries times h0 (4 T dk dv),
+        # the substitution (2 dv per ancestor pair) and P U (2 dv per pair incl. the node)
+        p = par.cpu()
+        pairs = 0
+        for bb in range(B):
+            for t in range(T):
+                r = int(p[bb, t])
+                while r >= 0:
+                    pairs += 1
+                    r = int(p[bb, r])
+        pairs_h = pairs * w.HV
+        flops = (pairs_h * 2 * w.dk * 2 + B * T * w.HV * w.dk * 2 * w.dk  # A and P (incl. diagonal)
+                 + 4 * B * T * w.HV * w.dk * w.dv                           # Kt h0, Qt h0
+                 + pairs_h * 2 * w.dv + (pairs_h + B * T * w.HV) * 2 * w.dv)
+        elt = 2 if w.dtype == torch.bfloat16 else 4
+        nbytes = (B * T * (2 * w.HK * w.dk * elt + w.HV * (w.dv * elt + w.dk * 4 + 4 + w.dv * 4))
+                  + B * w.HV * w.dk * w.dv * 4 + B * T * 4)
         out.append({"B": B, "T": T, "tree": kind, "us_per_call": round(ms * 1e3, 2),
-                    "nodes_per_s": round(B * T / (ms * 1e-3), 1)})
+                    "nodes_per_s": round(B * T / (ms * 1e-3), 1), "alg_flops": flops,
+                    "alg_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                    "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 3)})
     return {"workload": f"HK={w.HK} HV={w.HV} dk=dv={w.dk} bf16 q/k/v, h0 given; {reps} calls back to back",
             "cases": out}
 
