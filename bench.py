@@ -52,8 +52,9 @@ if ROOT not in sys.path:
 METRIC = "prefill tokens/s (HV=32,dk=dv=128) + decode state GB/s, % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak, published
-# fp32 vector operations per second without packed fp32 instructions (which this build does
-# not use): 256 CUs x 64 lanes x 2.4 GHz; the published 157.3 TFLOP/s counts packed FMAs
+# fp32 vector operations per second without packed fp32 instructions (which the library's
+# kernels do not use): 256 CUs x 64 lanes x 2.4 GHz; the published 157.3 TFLOP/s counts
+# packed FMAs
 VALU_F32_OPS_PEAK = 256 * 64 * 2.4e9
 
 CSRC = os.path.join(ROOT, "gated_delta_rule_70_amd", "csrc")
@@ -140,9 +141,9 @@ def summarize_pmc(fetch_dir, write_dir):
              "Commands (repository root, one MI355X):",
              "",
              "```",
-             "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run -f csv -- python3 bench.py --profile-run",
-             "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run -f csv -- python3 bench.py --profile-run",
-             "python3 bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write",
+             f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run -f csv -- python3 bench.py --profile-run",
+             f"rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o run -f csv -- python3 bench.py --profile-run",
+             f"python3 bench.py --summarize-pmc {fetch_dir} {write_dir}",
              "```",
              "",
              "| kernel | fetch MB | write MB | traffic MB |",
@@ -213,7 +214,7 @@ def summarize_util(util_dir):
             "mfma_f16_TFLOPs": f16 / t / 1e12 if t else None,
             "source_digest": source_digest(kern)}
     cmd = ("rocprofv3 --kernel-trace --pmc " + " ".join(UTIL_COUNTERS) +
-           " -d gpurun_out/pmc_util -o run -f csv -- python3 bench.py --profile-run")
+           f" -d {util_dir} -o run -f csv -- python3 bench.py --profile-run")
     lines = ["# Matrix-core use and clock per launch: prefill B=1 T=4097 HV=32 dk=dv=128 and decode B=32",
              "",
              "One counter run of the short benchmark with a kernel trace beside it.  MFMA busy =",
@@ -230,7 +231,7 @@ def summarize_util(util_dir):
              "",
              "```",
              cmd,
-             "python3 bench.py --summarize-util gpurun_out/pmc_util",
+             f"python3 bench.py --summarize-util {util_dir}",
              "```",
              "",
              "| kernel | traced us | MFMA busy | f16 matrix GFLOP | f16 matrix TFLOP/s | f32 matrix GFLOP |",
