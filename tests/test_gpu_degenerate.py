@@ -1,0 +1,69 @@
+"""Degenerate inputs of the method on every GPU path, against the fp64 oracle: no updates
+(beta = 0: the state only decays), no decay (g = 0), and decay at the edge of the
+documented range of the chunked path (eight consecutive tokens decaying by ~76)."""
+import pytest
+import torch
+
+import gated_delta_rule_70_amd as gdr
+import oracle
+from gdr_synth import make_tree
+from gpu_util import TOL, dev, err, note, small_inputs
+
+pytestmark = pytest.mark.gpu
+
+B, T, HK, HV, dk, dv = 2, 70, 2, 4, 128, 128
+
+
+def _inputs(kind, seed):
+    x = small_inputs(B, T, HK, HV, dk, dv, seed=seed)
+    if kind == "beta0":
+        x["beta"] = torch.zeros_like(x["beta"])
+    elif kind == "g0":
+        x["g"] = torch.zeros_like(x["g"])
+    elif kind == "steep":
+        # -9.5 per token in every channel: 76 over eight tokens, inside the chunked path's range
+        x["g"] = torch.full_like(x["g"], -9.5)
+    return x
+
+
+@pytest.mark.parametrize("kind", ["beta0", "g0", "steep"])
+def test_prefill_and_fused_recurrence(kind):
+    x = _inputs(kind, seed=400)
+    o_ref, ht_ref = oracle.sequential(**x)
+    d = dev(x)
+    note(f"degenerate {kind}: chunked prefill (C=64, 32) and fused recurrence")
+    outs = []
+    for C in (64, 32):
+        outs.append(gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], chunk=C))
+    outs.append(gdr.fused_recurrent(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"]))
+    torch.cuda.synchronize()
+    for o, ht in outs:
+        assert torch.isfinite(o).all() and torch.isfinite(ht).all()
+        assert err(o, o_ref) < TOL, f"o {err(o, o_ref):.2e}"
+        assert err(ht, ht_ref) < TOL, f"state {err(ht, ht_ref):.2e}"
+
+
+@pytest.mark.parametrize("kind", ["beta0", "g0"])
+def test_decode_step(kind):
+    x = _inputs(kind, seed=401)
+    one = {n: (x[n][:, :1].contiguous() if n != "h0" else x[n]) for n in x}
+    o_ref, ht_ref = oracle.sequential(**one)
+    d = dev(one)
+    note(f"degenerate {kind}: decode step")
+    state = d["h0"].clone()
+    o = gdr.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state)
+    torch.cuda.synchronize()
+    assert err(o, o_ref) < TOL and err(state, ht_ref) < TOL
+
+
+@pytest.mark.parametrize("kind", ["beta0", "g0"])
+def test_tree_verify(kind):
+    x = _inputs(kind, seed=402)
+    x = {n: (x[n][:, :48].contiguous() if n != "h0" else x[n]) for n in x}
+    par = make_tree(B, 48, "random", seed=9)
+    ref = oracle.tree(**x, parent=par.numpy())
+    d = dev(x)
+    note(f"degenerate {kind}: tree verify T=48")
+    o = gdr.tree_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], par.cuda(), h0=d["h0"])
+    torch.cuda.synchronize()
+    assert err(o, ref) < TOL
