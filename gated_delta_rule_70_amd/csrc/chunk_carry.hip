@@ -421,7 +421,7 @@ static hipError_t dispatch_carry(const LaunchArgs& a) {
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_chunk_carry(const LaunchArgs& a) {
+hipError_t launch_carry_split(const LaunchArgs& a) {
     return a.qkv_f32 ? dispatch_carry<float>(a) : dispatch_carry<bf16_t>(a);
 }
 

@@ -124,7 +124,9 @@ size_t workspace_bytes_unchecked(const gdr_dims* d) {
     const size_t nchunk = (size_t)((d->T + d->chunk - 1) / d->chunk);
     size_t x;
     if (!mul_ok((size_t)d->B * (size_t)d->HV, nchunk, &x) || !mul_ok(x, rec.bytes, &x)) return 0;
-    return x;
+    // the carry's segment summaries and start states (at most 256 heads x segments of
+    // dk x dk fp32 matrices each) follow the records
+    return gdr::carry_layout(d->B, d->HV, d->T, d->dk, d->dv, d->chunk).total;
 }
 
 }  // namespace

@@ -66,10 +66,58 @@ struct ChunkRecord {
     }
 };
 
+// Workspace layout of the chunked prefill and the carry's plan.  The chunk records come
+// first.  The whole-head carry (dk == dv in {64, 128}) is used where it beats the
+// column-split one on an MI355X (256 compute units):
+//   * more than 128 heads: one segment, one workgroup per head;
+//   * fewer heads but enough chunks that the sequence can be cut into 256 / heads segments
+//     of at least 16 chunks each: that many segments, so ~256 workgroups carry at once.
+// (Measured at HV = 32, 128 x 128: B = 8 T = 512 carry 57 vs 64 us, B = 4 T = 4097 349 vs
+// 572 us, B = 1 T = 32768 704 vs 779 us; B = 1 T = 4097, 8 segments of 8 chunks, 127 vs
+// 88 us, so the column-split carry keeps that case.)  With more than one segment the
+// workspace also holds each segment's summary [S_loc | M] (fp32, [heads][nseg - 1][2][dk]
+// [dk]) and start state (fp32, [heads][nseg][dk][dv]).  A pure function of the dims, so
+// the size query and the launch agree.
+struct CarryLayout {
+    bool wide;
+    int nseg;
+    size_t rec_bytes, xsum_off, sstart_off, total;
+};
+
+inline CarryLayout carry_layout(int B, int HV, int T, int dk, int dv, int chunk) {
+    CarryLayout L{};
+    const ChunkRecord R = ChunkRecord::make(chunk, dk);
+    const long long NC = (T + (long long)chunk - 1) / chunk;
+    const long long NH = (long long)B * HV;
+    L.rec_bytes = (size_t)NH * (size_t)NC * (size_t)R.bytes;
+    const bool dims_ok = dk == dv && (dk == 64 || dk == 128);
+    L.nseg = 1;
+    L.wide = false;
+    if (dims_ok) {
+        if (NH > 128) {
+            L.wide = true;
+        } else {
+            const long long want = 256 / NH;  // >= 2
+            if (NC >= 16 * want) {
+                L.wide = true;
+                L.nseg = (int)want;
+            }
+        }
+    }
+    const size_t mat = (size_t)dk * dk * 4;
+    L.xsum_off = L.rec_bytes;
+    L.sstart_off = L.xsum_off + (L.nseg > 1 ? (size_t)NH * (L.nseg - 1) * 2 * mat : 0);
+    L.total = L.sstart_off + (L.nseg > 1 ? (size_t)NH * L.nseg * mat : 0);
+    return L;
+}
+
 // token recurrence over a.T tokens in one launch (the decode step is a.T == 1)
 hipError_t launch_tokens(const LaunchArgs& a);
 hipError_t launch_chunk_prep(const LaunchArgs& a);
+// the carry: whole-head segmented kernels where carry_layout says so, else the
+// column-split kernel (launch_carry_split)
 hipError_t launch_chunk_carry(const LaunchArgs& a);
+hipError_t launch_carry_split(const LaunchArgs& a);
 // tree-verify solve over trees of a.T <= 64 nodes; parent [B][T] int32 on the device
 hipError_t launch_tree_verify(const LaunchArgs& a, const int32_t* parent);
 

@@ -101,7 +101,10 @@ int gdr_fused_recurrent(const gdr_dims* dims, const void* q, const void* k, cons
  * Bytes of device workspace gdr_chunk_prefill needs for these dims (0 if dims are
  * invalid).  The workspace holds per-chunk operands that the chunk-parallel kernel hands
  * to the sequential state-carry kernel -- the per-worker scratch arena of ExecuTorch PR
- * #21021 (second commit summary), carved per (batch, head, chunk).
+ * #21021 (second commit summary), carved per (batch, head, chunk).  When the carry splits
+ * the sequence into segments (few heads, many chunks), it also holds, per head, each
+ * segment's fp32 summary (the state it produces from zero and its dk x dk transition
+ * matrix) and each segment's fp32 start state.  The size depends on the dims only.
  */
 size_t gdr_chunk_prefill_workspace_bytes(const gdr_dims* dims);
 
@@ -127,10 +130,14 @@ int gdr_chunk_prefill(const gdr_dims* dims, const void* q, const void* k, const 
  *                      decay prefixes, gram A and causal terms P on the matrix cores, the
  *                      16x16-block solve of (I + A), WY pseudo-keys; writes the workspace.
  *                      Reads q, k, g, beta; never touches v, h0, o or ht.
- *   gdr_chunk_carry -- sequential stage (chunks in order, value dimension split across
- *                      workgroups): pseudo-values, outputs and the state carry.  Reads
- *                      the workspace written by gdr_chunk_prep for the same inputs, v
- *                      and h0; writes o and ht.
+ *   gdr_chunk_carry -- sequential stage (chunks in order): pseudo-values, outputs and
+ *                      the state carry, either with the value dimension split across
+ *                      workgroups or one workgroup per head; with few heads and many
+ *                      chunks the sequence is cut into segments that carry in parallel
+ *                      (segment summaries, then their ordered combination, then every
+ *                      segment from its start state).  Reads the workspace written by
+ *                      gdr_chunk_prep for the same inputs, v and h0; writes o and ht (and
+ *                      the carry's part of the workspace).
  * Splitting them lets a caller time or overlap the stages.
  */
 int gdr_chunk_prep(const gdr_dims* dims, const void* q, const void* k, const void* v,

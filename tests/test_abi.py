@@ -212,6 +212,36 @@ def test_workspace_size_formula(L):
     assert L.gdr_chunk_prefill_workspace_bytes(None) == 0
 
 
+def _records(B, T, HV, dk, C):
+    nb, nqs, kc, dkt = C // 16, (C + 31) // 32, dk // 32, dk // 16
+    return B * HV * (-(-T // C)) * ((2 * nb * kc + dkt * nqs + 2 * nb * nqs + 1) * 1024)
+
+
+def test_workspace_carry_segments(L):
+    """The segmented carry's extra workspace: with at most 128 (batch, head) pairs and
+    enough chunks for 256 / heads segments of >= 16 chunks each, every segment but the last
+    keeps an fp32 [S_loc | M] summary (2 dk x dk matrices) and every segment a start state
+    (dk x dv); otherwise the workspace is the chunk records alone."""
+    def ws(**kw):
+        return L.gdr_chunk_prefill_workspace_bytes(ctypes.byref(dims(**kw)))
+    # 2 heads, 2048 chunks of 16: 128 segments
+    kw = dict(B=1, HK=1, HV=2, dk=128, dv=128, chunk=16, T=32768)
+    nseg, mat = 128, 128 * 128 * 4
+    assert ws(**kw) == _records(1, 32768, 2, 128, 16) + 2 * (nseg - 1) * 2 * mat + 2 * nseg * mat
+    # 32 heads, 512 chunks of 64: 8 segments
+    kw = dict(B=1, HK=16, HV=32, dk=128, dv=128, chunk=64, T=32768)
+    assert ws(**kw) == _records(1, 32768, 32, 128, 64) + 32 * 7 * 2 * mat + 32 * 8 * mat
+    # 32 heads, 65 chunks: too few for 8 segments of 16 -> column-split carry, records only
+    kw = dict(B=1, HK=16, HV=32, dk=128, dv=128, chunk=64, T=4097)
+    assert ws(**kw) == _records(1, 4097, 32, 128, 64)
+    # 256 heads: whole-head carry with a single segment, records only
+    kw = dict(B=8, HK=16, HV=32, dk=128, dv=128, chunk=64, T=512)
+    assert ws(**kw) == _records(8, 512, 32, 128, 64)
+    # dk != dv: column-split carry
+    kw = dict(B=1, HK=1, HV=2, dk=128, dv=64, chunk=16, T=32768)
+    assert ws(**kw) == _records(1, 32768, 2, 128, 16)
+
+
 def _gpu_visible():
     import torch
 

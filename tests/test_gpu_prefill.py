@@ -158,3 +158,53 @@ def test_chunk_size_invariance():
     o_ref, ht_ref = oracle.sequential(**x)
     for o, ht in res:
         assert err(o, o_ref) < TOL and err(ht, ht_ref) < TOL
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+@pytest.mark.parametrize("mode", ["h0", "no_h0", "in_place"])
+def test_segmented_carry(dk, mode):
+    """Two heads and 2048 chunks: the carry cuts the sequence into 128 segments of 16
+    chunks, summarises each, combines the summaries in order and re-runs every segment
+    from its start state; the result must still be the sequential recurrence.  The decay
+    is slowed (g / 100) so each segment's transition matrix is far from zero and the
+    combine step carries real weight."""
+    T, C = 32768, 16
+    x = small_inputs(1, T, 1, 2, dk, dk, seed=dk + len(mode), h0=mode != "no_h0")
+    x["g"] = x["g"] / 100
+    o_ref, ht_ref = oracle.sequential(**x)
+    d = dev(x)
+    note(f"segmented carry T={T} C={C} dk={dk} {mode}")
+    if mode == "in_place":
+        state = d["h0"].clone()
+        o, _ = gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=state, ht=state, chunk=C)
+        ht = state
+    else:
+        o, ht = run_prefill(d, C, h0=mode == "h0")
+    torch.cuda.synchronize()
+    eo, es = err(o, o_ref), err(ht, ht_ref)
+    assert eo < TOL and es < TOL, f"o {eo:.2e} state {es:.2e}"
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("T", [33, 97])
+@pytest.mark.parametrize("dk", [64, 128])
+@pytest.mark.parametrize("h0", [True, False])
+def test_wide_carry_many_heads(C, T, dk, h0):
+    """More than 128 (batch, head) pairs: the carry runs one whole-head workgroup per head."""
+    x = small_inputs(2, T, 40, 80, dk, dk, seed=C + T + dk + h0, h0=h0)
+    o_ref, ht_ref = oracle.sequential(**x)
+    note(f"wide carry B=2 HV=80 T={T} C={C} dk={dk} h0={h0}")
+    o, ht = run_prefill(dev(x), C, h0=h0)
+    torch.cuda.synchronize()
+    eo, es = err(o, o_ref), err(ht, ht_ref)
+    assert eo < TOL and es < TOL, f"o {eo:.2e} state {es:.2e}"
+
+
+def test_wide_carry_fp32_inputs():
+    x = small_inputs(2, 70, 40, 80, 128, 128, dtype=torch.float32, seed=3)
+    o_ref, ht_ref = oracle.sequential(**x)
+    note("wide carry fp32 q/k/v")
+    o, ht = run_prefill(dev(x), 64)
+    torch.cuda.synchronize()
+    eo, es = err(o, o_ref), err(ht, ht_ref)
+    assert eo < TOL and es < TOL, f"o {eo:.2e} state {es:.2e}"
