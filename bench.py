@@ -61,14 +61,33 @@ CSRC = os.path.join(ROOT, "gated_delta_rule_70_amd", "csrc")
 KERNEL_SOURCES = {  # kernel -> the sources its machine code is built from
     "chunk_prep": ["chunk_prep.hip", "gdr_device.h", "gdr_launch.h"],
     "chunk_carry": ["chunk_carry.hip", "gdr_device.h", "gdr_launch.h"],
+    "carry_full": ["chunk_carry_wide.hip", "gdr_device.h", "gdr_launch.h"],
+    "carry_sum": ["chunk_carry_wide.hip", "gdr_device.h", "gdr_launch.h"],
+    "carry_combine": ["chunk_carry_wide.hip", "gdr_device.h", "gdr_launch.h"],
     "decode": ["decode.hip", "gdr_device.h", "gdr_launch.h"],
     "tree_verify": ["tree_verify.hip", "gdr_device.h", "gdr_launch.h"],
 }
-KERNEL_SYMBOL = {"chunk_prep": "chunk_prep_kernel", "chunk_carry": "chunk_carry_kernel",
-                 "decode": "token_kernel", "tree_verify": "tree_verify_kernel"}
+# kernel -> substrings that all appear in its (demangled) name in profiler output; the
+# column-split carry is chunk_carry_kernel, the whole-head carry's full and summary passes
+# are carry_wide_kernel<..., false> and <..., true>
+KERNEL_SYMBOL = {"chunk_prep": ("chunk_prep_kernel",), "chunk_carry": ("chunk_carry_kernel",),
+                 "carry_full": ("carry_wide_kernel", "false>"), "carry_sum": ("carry_wide_kernel", "true>"),
+                 "carry_combine": ("carry_combine_kernel",),
+                 "decode": ("token_kernel",), "tree_verify": ("tree_verify_kernel",)}
 CALIB_BYTES = 256 << 20           # calibration kernel: reads and writes this many bytes
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_b1_t4097_decode_b32.md")
-UTIL_SUMMARY = os.path.join(ROOT, "profiles", "mfma_util_prefill_b1_t4097_decode_b32.md")
+HEADLINE_PROFILE = "prefill_b1_t4097_decode_b32"  # the default run's profile summaries
+
+
+def _matches(sym, name):
+    return all(part in name for part in sym)
+
+
+def traffic_summary(profile=HEADLINE_PROFILE):
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{profile}.md")
+
+
+def util_summary(profile=HEADLINE_PROFILE):
+    return os.path.join(ROOT, "profiles", f"mfma_util_{profile}.md")
 UTIL_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_F32",
                  "GRBM_GUI_ACTIVE"]
 SIMD_NUM = 1024                # 256 CUs x 4 SIMDs
@@ -109,7 +128,7 @@ def _per_dispatch_kib(rows, counter):
     return {k: sum(v) / len(v) for k, v in by_kernel.items()}
 
 
-def summarize_pmc(fetch_dir, write_dir):
+def summarize_pmc(fetch_dir, write_dir, profile=HEADLINE_PROFILE, run_args="--profile-run"):
     fetch = _per_dispatch_kib(_counter_rows(fetch_dir), "FETCH_SIZE")
     write = _per_dispatch_kib(_counter_rows(write_dir), "WRITE_SIZE")
     calib = [k for k in fetch if "neg" in k.lower()]
@@ -122,7 +141,7 @@ def summarize_pmc(fetch_dir, write_dir):
                            "fetch_factor": f_fac, "write_factor": w_fac},
            "kernels": {}}
     for kern, sym in KERNEL_SYMBOL.items():
-        names = [k for k in fetch if sym in k]
+        names = [k for k in fetch if _matches(sym, k)]
         if not names:
             continue
         nm = max(names, key=lambda k: fetch[k])  # the instantiation the workload launches
@@ -131,7 +150,7 @@ def summarize_pmc(fetch_dir, write_dir):
         out["kernels"][kern] = {"symbol": nm, "fetch_kib": fetch[nm], "write_kib": write.get(nm, 0.0),
                                 "fetch_bytes": round(fb), "write_bytes": round(wb),
                                 "traffic_bytes": round(fb + wb), "source_digest": source_digest(kern)}
-    lines = ["# HBM traffic per launch: prefill B=1 T=4097 HV=32 dk=dv=128 and decode B=32",
+    lines = [f"# HBM traffic per launch: {profile}",
              "",
              "Two counter runs of the same short benchmark (FETCH_SIZE, then WRITE_SIZE, KiB per",
              "dispatch), each scaled by what the counter reads for a calibration kernel of known",
@@ -141,9 +160,9 @@ def summarize_pmc(fetch_dir, write_dir):
              "Commands (repository root, one MI355X):",
              "",
              "```",
-             f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run -f csv -- python3 bench.py --profile-run",
-             f"rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o run -f csv -- python3 bench.py --profile-run",
-             f"python3 bench.py --summarize-pmc {fetch_dir} {write_dir}",
+             f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run -f csv -- python3 bench.py {run_args}",
+             f"rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o run -f csv -- python3 bench.py {run_args}",
+             f"python3 bench.py --summarize-pmc {fetch_dir} {write_dir} --profile-name {profile}",
              "```",
              "",
              "| kernel | fetch MB | write MB | traffic MB |",
@@ -153,9 +172,9 @@ def summarize_pmc(fetch_dir, write_dir):
                      f"{v['traffic_bytes'] / 1e6:.2f} |")
     lines += ["", f"Calibration factors: fetch {f_fac:.4f}, write {w_fac:.4f} (bytes per counted byte).",
               "", "```json", json.dumps(out, indent=1), "```", ""]
-    with open(TRAFFIC_SUMMARY, "w") as f:
+    with open(traffic_summary(profile), "w") as f:
         f.write("\n".join(lines))
-    print(f"wrote {TRAFFIC_SUMMARY}")
+    print(f"wrote {traffic_summary(profile)}")
 
 
 def _per_dispatch(rows, counter, reduce):
@@ -184,7 +203,7 @@ def _dispatch_ns(d):
     return ns
 
 
-def summarize_util(util_dir):
+def summarize_util(util_dir, profile=HEADLINE_PROFILE, run_args="--profile-run"):
     """Matrix-core busy fraction (MFMA busy cycles summed over SIMDs / (one XCD's GUI-active
     cycles x SIMDs), the profiler's MfmaUtil) and counted matrix flops (MOPS x 512), per
     launch and per second of traced dispatch time."""
@@ -196,7 +215,7 @@ def summarize_util(util_dir):
     dur = _dispatch_ns(util_dir)
     out = {"kernels": {}}
     for kern, sym in KERNEL_SYMBOL.items():
-        names = [k for k in gui if sym in k]
+        names = [k for k in gui if _matches(sym, k)]
         if not names:
             continue
         nm = max(names, key=lambda k: max(gui[k].values()))  # the instantiation the workload launches
@@ -214,8 +233,8 @@ def summarize_util(util_dir):
             "mfma_f16_TFLOPs": f16 / t / 1e12 if t else None,
             "source_digest": source_digest(kern)}
     cmd = ("rocprofv3 --kernel-trace --pmc " + " ".join(UTIL_COUNTERS) +
-           f" -d {util_dir} -o run -f csv -- python3 bench.py --profile-run")
-    lines = ["# Matrix-core use and clock per launch: prefill B=1 T=4097 HV=32 dk=dv=128 and decode B=32",
+           f" -d {util_dir} -o run -f csv -- python3 bench.py {run_args}")
+    lines = [f"# Matrix-core use and clock per launch: {profile}",
              "",
              "One counter run of the short benchmark with a kernel trace beside it.  MFMA busy =",
              "busy cycles summed over the 1024 SIMDs / (GUI-active cycles of one XCD x 1024), the",
@@ -231,7 +250,7 @@ def summarize_util(util_dir):
              "",
              "```",
              cmd,
-             f"python3 bench.py --summarize-util {util_dir}",
+             f"python3 bench.py --summarize-util {util_dir} --profile-name {profile}",
              "```",
              "",
              "| kernel | traced us | MFMA busy | f16 matrix GFLOP | f16 matrix TFLOP/s | f32 matrix GFLOP |",
@@ -242,15 +261,15 @@ def summarize_util(util_dir):
                      f"{v['mfma_f16_flops'] / 1e9:.3f} | {fmt(v['mfma_f16_TFLOPs'], '.1f')} | "
                      f"{v['mfma_f32_flops'] / 1e9:.3f} |")
     lines += ["", "```json", json.dumps(out, indent=1), "```", ""]
-    with open(UTIL_SUMMARY, "w") as f:
+    with open(util_summary(profile), "w") as f:
         f.write("\n".join(lines))
-    print(f"wrote {UTIL_SUMMARY}")
+    print(f"wrote {util_summary(profile)}")
 
 
-def read_util(kernel):
+def read_util(kernel, profile=HEADLINE_PROFILE):
     """Matrix-core figures of `kernel` for the current sources, or None."""
     try:
-        with open(UTIL_SUMMARY) as f:
+        with open(util_summary(profile)) as f:
             blob = json.loads(f.read().split("```json", 1)[1].split("```", 1)[0])
         k = blob["kernels"][kernel]
     except (OSError, IndexError, KeyError, ValueError):
@@ -261,11 +280,11 @@ def read_util(kernel):
             "mfma_f16_flops_counted": k["mfma_f16_flops"], "mfma_f32_flops_counted": k["mfma_f32_flops"]}
 
 
-def read_traffic(kernel):
+def read_traffic(kernel, profile=HEADLINE_PROFILE):
     """Calibrated HBM bytes per launch of `kernel`, or None if there is no summary for the
     current sources."""
     try:
-        with open(TRAFFIC_SUMMARY) as f:
+        with open(traffic_summary(profile)) as f:
             text = f.read()
         blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
         k = blob["kernels"][kernel]
@@ -320,6 +339,42 @@ def prefill_flops(B, T, HV, dk, dv, C):
         carry += dv * L * (L - 1) + 6 * L * dk * dv + dv * L * (L + 1)
         t -= L
     return prep * B * HV, carry * B * HV
+
+
+def carry_plan(B, T, HV, dk, dv, C):
+    """Which carry the library runs for these dims (its shape rule, restated for reporting):
+    the whole-head carry with more than 128 (batch, head) pairs, or with 256 / heads
+    segments when every segment gets at least 16 chunks; the column-split carry otherwise."""
+    nh, nc = B * HV, -(-T // C)
+    if dk != dv or dk not in (64, 128):
+        return "column-split"
+    if nh > 128:
+        return "whole-head, 1 segment"
+    want = 256 // nh
+    if nc >= 16 * want:
+        return f"whole-head, {want} segments"
+    return "column-split"
+
+
+OTHER_PREFILLS = ("prefill_b8_t512", "prefill_b8_t97", "prefill_b1_t32768")
+
+
+def bench_other_prefills(steps=5, warmup=1):
+    """The other full-size prefill workloads: per-stage kernel times (HIP events on the launch
+    stream, back-to-back calls), throughput, and which carry the library picks."""
+    from gdr_synth import WORKLOADS
+
+    out = []
+    for name in OTHER_PREFILLS:
+        w = WORKLOADS[name]
+        x, o, ht, wall, prep_ms, carry_ms = bench_prefill(w, steps, warmup)
+        out.append({"workload": name, "B": w.B, "T": w.T, "h0": w.h0,
+                    "prep_ms": round(prep_ms, 5), "carry_ms": round(carry_ms, 5),
+                    "ms_per_step": round(wall / steps * 1e3, 5),
+                    "tokens_per_s": round(w.B * w.T / (wall / steps), 1),
+                    "carry": carry_plan(w.B, w.T, w.HV, w.dk, w.dv, w.chunk)})
+        del x, o, ht
+    return out
 
 
 def decode_bytes(B, HK, HV, dk, dv, elt):
@@ -615,12 +670,17 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-util", metavar="UTIL_DIR")
     ap.add_argument("--summarize-stats", nargs=3, metavar=("DIR", "NAME", "COMMAND"))
+    ap.add_argument("--profile-name", default=HEADLINE_PROFILE,
+                    help="profile summaries to write: the default run's, or a prefill workload's "
+                         "(counter runs of `--profile-run --workload <name> --no-decode`)")
     args = ap.parse_args()
+    run_args = ("--profile-run" if args.profile_name == HEADLINE_PROFILE
+                else f"--profile-run --workload {args.profile_name} --no-decode")
     if args.summarize_util:
-        summarize_util(args.summarize_util)
+        summarize_util(args.summarize_util, args.profile_name, run_args)
         return
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc)
+        summarize_pmc(*args.summarize_pmc, profile=args.profile_name, run_args=run_args)
         return
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats)
@@ -675,6 +735,7 @@ def main():
         "path_frac_of_bf16_mfma_peak": round(path_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "ceiling_ms": round(ceil_ms, 5), "path_frac_of_ceiling": round(ceil_ms / kern_ms, 4),
         "tokens_per_s_kernel_time": round(ntok / (kern_ms * 1e-3), 1),
+        "carry": carry_plan(w.B, w.T, w.HV, w.dk, w.dv, w.chunk),
         "counters": {"chunk_prep": read_util("chunk_prep"), "chunk_carry": read_util("chunk_carry")},
     }
 
@@ -717,6 +778,7 @@ def main():
     if not args.no_short_calls and not args.profile_run:
         line["short_calls"] = bench_short_calls(DECODE)
         line["tree_verify"] = bench_tree(DECODE)
+        line["other_prefills"] = bench_other_prefills()
 
     if not args.no_cpu_baseline:
         import numpy as np

@@ -255,3 +255,21 @@ def test_valid_arguments_reach_the_runtime_without_a_gpu(L):
     assert decode(L, dims(T=1), ht=addr(5, 0)) == EHIP
     assert decode(L, dims(T=9, chunk=8), ht=addr(5, 0), entry="gdr_fused_recurrent") == EHIP
     assert tree(L, dims(T=64, dv=64)) == EHIP
+
+
+def test_bench_carry_plan_matches_library(L):
+    """bench.py reports which carry ran from a restatement of the library's shape rule;
+    the workspace size (records, plus segment summaries and start states when segmented)
+    shows the library's own choice, so the two must agree."""
+    import bench
+
+    mat = lambda dk: dk * dk * 4
+    for B, HV, T, dk, C in [(1, 32, 4097, 128, 64), (1, 32, 32768, 128, 64), (8, 32, 512, 128, 64),
+                            (2, 32, 4097, 128, 64), (4, 32, 4097, 64, 32), (2, 32, 512, 128, 64),
+                            (1, 2, 32768, 64, 16), (1, 2, 600, 64, 16), (1, 4, 9000, 32, 16)]:
+        d = dims(B=B, HK=HV // 2 if HV > 1 else 1, HV=HV, dk=dk, dv=dk, chunk=C, T=T)
+        got = L.gdr_chunk_prefill_workspace_bytes(ctypes.byref(d))
+        plan = bench.carry_plan(B, T, HV, dk, dk, C)
+        nseg = int(plan.split(", ")[1].split()[0]) if "segments" in plan else 1
+        extra = B * HV * ((nseg - 1) * 2 * mat(dk) + nseg * mat(dk)) if nseg > 1 else 0
+        assert got == _records(B, T, HV, dk, C) + extra, (B, HV, T, dk, C, plan)
