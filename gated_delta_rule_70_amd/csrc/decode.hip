@@ -154,13 +154,122 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
     }
 }
 
+// The decode step alone (T == 1): the same workgroup shape, thread-to-state mapping and
+// operation order as token_kernel, so its results equal token_kernel's bit for bit, but
+// without the next-token request buffers: the step's decay factors, keys and queries are
+// staged once per workgroup in LDS (one load per thread instead of one per owned row).
+// That keeps a thread within 64 registers, so eight waves fit per SIMD and every
+// workgroup of a decode step is resident at once: the whole state is requested in one
+// round instead of two.
+template <typename TIn, int DK, int DV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+                   const float* __restrict__ g, const float* __restrict__ beta, const float* h0,
+                   float* __restrict__ o, float* ht, int HK, int HV) {
+    constexpr int BVD = DV < 64 ? DV : 64;
+    constexpr int NQ = BVD / 4;
+    constexpr int NRL = 256 / NQ;
+    constexpr int RPT = DK / NRL;
+    static_assert(RPT >= 1 && DK % NRL == 0 && DK <= 256, "unsupported dk/dv combination");
+
+    __shared__ float s_e[DK], s_k[DK], s_q[DK];
+    __shared__ f32x4 red_p[4][NQ];
+    __shared__ f32x4 red_o[4][NQ];
+
+    const int ncb = DV / BVD;
+    const int blk = blockIdx.x;
+    const int cb = blk % ncb;
+    const int bh = blk / ncb;
+    const int h = bh % HV;
+    const int b = bh / HV;
+    const int kh = h / (HV / HK);
+    const int tid = threadIdx.x;
+    const int cq = tid % NQ;
+    const int rl = tid / NQ;
+    const int wave = tid >> 6;
+    const int col = cb * BVD + 4 * cq;
+
+    const size_t sbase = (size_t)bh * DK * DV + col;
+    f32x4 S[RPT];
+    if (h0 != nullptr) {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m)
+            S[m] = *reinterpret_cast<const f32x4*>(h0 + sbase + (size_t)(rl + NRL * m) * DV);
+    } else {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const size_t kq = ((size_t)b * HK + kh) * DK;
+    const size_t gb = ((size_t)b * HV + h) * DK;
+    const size_t vb = ((size_t)b * HV + h) * DV + col;
+    if (tid < DK) {
+        s_e[tid] = __expf(g[gb + tid]);
+        s_k[tid] = to_f32(k[kq + tid]);
+        s_q[tid] = to_f32(q[kq + tid]);
+    }
+    const f32x4 vv = {to_f32(v[vb]), to_f32(v[vb + 1]), to_f32(v[vb + 2]), to_f32(v[vb + 3])};
+    const float bt = beta[(size_t)b * HV + h];
+    __syncthreads();
+
+    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rl + NRL * m;
+        S[m] *= s_e[i];
+        p += S[m] * s_k[i];
+    }
+#pragma unroll
+    for (int off = NQ; off < 64; off <<= 1) {
+        p.x += __shfl_xor(p.x, off);
+        p.y += __shfl_xor(p.y, off);
+        p.z += __shfl_xor(p.z, off);
+        p.w += __shfl_xor(p.w, off);
+    }
+    if ((tid & 63) < NQ) red_p[wave][cq] = p;
+    __syncthreads();
+    const f32x4 pred = red_p[0][cq] + red_p[1][cq] + red_p[2][cq] + red_p[3][cq];
+    const f32x4 d = (vv - pred) * bt;
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rl + NRL * m;
+        S[m] += d * s_k[i];
+        acc += S[m] * s_q[i];
+    }
+#pragma unroll
+    for (int off = NQ; off < 64; off <<= 1) {
+        acc.x += __shfl_xor(acc.x, off);
+        acc.y += __shfl_xor(acc.y, off);
+        acc.z += __shfl_xor(acc.z, off);
+        acc.w += __shfl_xor(acc.w, off);
+    }
+    if ((tid & 63) < NQ) red_o[wave][cq] = acc;
+    __syncthreads();
+    if (tid < NQ) {
+        const f32x4 out = red_o[0][cq] + red_o[1][cq] + red_o[2][cq] + red_o[3][cq];
+        *reinterpret_cast<f32x4*>(o + vb) = out;
+    }
+    if (ht != nullptr) {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m)
+            *reinterpret_cast<f32x4*>(ht + sbase + (size_t)(rl + NRL * m) * DV) = S[m];
+    }
+}
+
 template <typename TIn, int DK, int DV>
 static hipError_t launch_tokens_t(const LaunchArgs& a) {
     constexpr int BVD = DV < 64 ? DV : 64;
     const long long nblk = (long long)a.B * a.HV * (DV / BVD);
-    hipLaunchKernelGGL((token_kernel<TIn, DK, DV>), dim3((unsigned)nblk), dim3(256), 0,
-                       (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
-                       a.g, a.beta, a.h0, a.o, a.ht, a.T, a.HK, a.HV);
+    if (a.T == 1) {
+        hipLaunchKernelGGL((decode_kernel<TIn, DK, DV>), dim3((unsigned)nblk), dim3(256), 0,
+                           (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
+                           a.g, a.beta, a.h0, a.o, a.ht, a.HK, a.HV);
+    } else {
+        hipLaunchKernelGGL((token_kernel<TIn, DK, DV>), dim3((unsigned)nblk), dim3(256), 0,
+                           (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
+                           a.g, a.beta, a.h0, a.o, a.ht, a.T, a.HK, a.HV);
+    }
     return hipGetLastError();
 }
 
@@ -175,7 +284,7 @@ static hipError_t dispatch_dims(const LaunchArgs& a) {
     return hipErrorInvalidValue;
 }
 
-// Decode step (T == 1) and fused recurrent call (any T): the same kernel.
+// Decode step and fused recurrent call: decode_kernel for T == 1, token_kernel otherwise.
 hipError_t launch_tokens(const LaunchArgs& a) {
     return a.qkv_f32 ? dispatch_dims<float>(a) : dispatch_dims<bf16_t>(a);
 }
