@@ -316,13 +316,13 @@ def summarize_stats(d, out_name, command):
     print(f"wrote {path}")
 
 
-def prefill_bytes(B, T, HK, HV, dk, dv, elt, h0):
+def prefill_bytes(B, T, HK, HV, dk, dv, elt, h0, g_elt=4):
     """Algorithmic HBM bytes of one prefill, split by the kernel that must move them.
 
-    prep  : q, k (once per key head), g, beta
+    prep  : q, k (once per key head), g (g_elt bytes per value), beta
     carry : v, o, the initial state (if any) and the final state
     """
-    prep = B * T * (2 * HK * dk * elt + HV * (dk * 4 + 4))
+    prep = B * T * (2 * HK * dk * elt + HV * (dk * g_elt + 4))
     carry = B * T * HV * (dv * elt + dv * 4) + B * HV * dk * dv * 4 * (2 if h0 else 1)
     return prep, carry
 
@@ -359,6 +359,21 @@ def carry_plan(B, T, HV, dk, dv, C):
 OTHER_PREFILLS = ("prefill_b8_t512", "prefill_b8_t97", "prefill_b1_t32768")
 
 
+def bench_io_lean(w, steps=10, warmup=2):
+    """The same prefill with g stored as bf16 (GDR_G_BF16): per-stage kernel times and
+    throughput, and the path's algorithmic bytes at that input format."""
+    import torch
+
+    x, o, ht, wall, prep_ms, carry_ms = bench_prefill(w, steps, warmup, g_bf16=True)
+    elt = 2 if w.dtype == torch.bfloat16 else 4
+    b_prep, b_carry = prefill_bytes(w.B, w.T, w.HK, w.HV, w.dk, w.dv, elt, w.h0, g_elt=2)
+    kern = prep_ms + carry_ms
+    return {"workload": f"{w.name} with bf16 g", "prep_ms": round(prep_ms, 5), "carry_ms": round(carry_ms, 5),
+            "ms_per_step": round(wall / steps * 1e3, 5), "tokens_per_s": round(w.B * w.T / (wall / steps), 1),
+            "path_alg_bytes": b_prep + b_carry,
+            "path_hbm_frac": round((b_prep + b_carry) / (kern * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def bench_other_prefills(steps=5, warmup=1):
     """The other full-size prefill workloads: per-stage kernel times (HIP events on the launch
     stream, back-to-back calls), throughput, and which carry the library picks."""
@@ -385,7 +400,7 @@ def _mean(xs):
     return sum(xs) / len(xs)
 
 
-def bench_prefill(w, steps, warmup):
+def bench_prefill(w, steps, warmup, g_bf16=False):
     import torch
 
     import gated_delta_rule_70_amd as gdr
@@ -393,6 +408,8 @@ def bench_prefill(w, steps, warmup):
 
     x = workload_inputs(w)
     d = {k: (None if v is None else v.cuda()) for k, v in x.items()}
+    if g_bf16:  # the I/O-lean input format: log-decays stored as bf16
+        d["g"] = d["g"].to(torch.bfloat16)
     B, T, HK, HV, dk, dv, C = w.B, w.T, w.HK, w.HV, w.dk, w.dv, w.chunk
     ws = torch.empty(gdr.workspace_bytes(B, T, HK, HV, dk, dv, C), dtype=torch.uint8, device="cuda")
     o = torch.empty(B, T, HV, dv, device="cuda")
@@ -779,6 +796,7 @@ def main():
         line["short_calls"] = bench_short_calls(DECODE)
         line["tree_verify"] = bench_tree(DECODE)
         line["other_prefills"] = bench_other_prefills()
+        line["io_lean"] = bench_io_lean(w)
 
     if not args.no_cpu_baseline:
         import numpy as np

@@ -26,16 +26,17 @@ __all__ = ["decode_step", "fused_recurrent", "chunk_prefill", "forward", "tree_v
            "RECURRENT_MAX_T", "TREE_MAX_T"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 RECURRENT_MAX_T = 8  # gdr_forward: calls of at most this many tokens take the fused recurrence
 TREE_MAX_T = 64      # gdr_tree_verify: most nodes per tree
 BF16, F32 = 0, 1
+G_BF16 = 0x1  # gdr_dims.flags: g stored as bf16
 
 
 class Dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("HK", ctypes.c_int32),
                 ("HV", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
-                ("chunk", ctypes.c_int32), ("qkv_dtype", ctypes.c_int32)]
+                ("chunk", ctypes.c_int32), ("qkv_dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class GdrError(RuntimeError):
@@ -108,10 +109,11 @@ def _need(t: torch.Tensor, name: str, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
-def _dims(q, v, chunk) -> Dims:
+def _dims(q, v, chunk, g=None) -> Dims:
     B, T, HK, dk = q.shape
     HV, dv = v.shape[2], v.shape[3]
-    return Dims(B, T, HK, HV, dk, dv, int(chunk), _qkv_dtype(q))
+    flags = G_BF16 if g is not None and g.dtype == torch.bfloat16 else 0
+    return Dims(B, T, HK, HV, dk, dv, int(chunk), _qkv_dtype(q), flags)
 
 
 def _stream(stream):
@@ -124,7 +126,8 @@ def _check_inputs(q, k, v, g, beta):
     dt = q.dtype
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, dt)
-    _need(g, "g", torch.float32)
+    # g is fp32, or bf16 with bf16 q/k/v (the library's I/O-lean input format)
+    _need(g, "g", torch.bfloat16 if (g.dtype == torch.bfloat16 and dt == torch.bfloat16) else torch.float32)
     _need(beta, "beta", torch.float32)
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4:
         raise ValueError("q, k must be [B,T,HK,dk] and v [B,T,HV,dv]")
@@ -152,7 +155,7 @@ def decode_step(q, k, v, g, beta, state, o=None, out_state=None, stream=None):
     ht = state if out_state is None else out_state
     if ht is not None:
         _need(ht, "out_state", torch.float32)
-    d = _dims(q, v, 0)
+    d = _dims(q, v, 0, g)
     _check(lib().gdr_decode_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                  _ptr(state), _ptr(o), _ptr(ht), _stream(stream)))
     return o
@@ -180,7 +183,7 @@ def chunk_prefill(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
         ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
     if ht is not None:
         _need(ht, "ht", torch.float32)
-    d = _dims(q, v, chunk)
+    d = _dims(q, v, chunk, g)
     need = int(lib().gdr_chunk_prefill_workspace_bytes(ctypes.byref(d)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
@@ -208,7 +211,7 @@ def fused_recurrent(q, k, v, g, beta, h0=None, o=None, ht=None, want_state: bool
         ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
     if ht is not None:
         _need(ht, "ht", torch.float32)
-    d = _dims(q, v, 0)
+    d = _dims(q, v, 0, g)
     _check(lib().gdr_fused_recurrent(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                      _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht), _stream(stream)))
     return o, ht
@@ -230,7 +233,7 @@ def forward(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None, workspa
         ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
     if ht is not None:
         _need(ht, "ht", torch.float32)
-    d = _dims(q, v, chunk)
+    d = _dims(q, v, chunk, g)
     if T > RECURRENT_MAX_T and workspace is None:
         need = int(lib().gdr_chunk_prefill_workspace_bytes(ctypes.byref(d)))
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
@@ -258,7 +261,7 @@ def tree_verify(q, k, v, g, beta, parent, h0=None, o=None, stream=None):
     if o is None:
         o = torch.empty(B, T, HV, dv, device=q.device, dtype=torch.float32)
     _need(o, "o", torch.float32)
-    d = _dims(q, v, 0)
+    d = _dims(q, v, 0, g)
     _check(lib().gdr_tree_verify(ctypes.byref(d), _ptr(parent), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                  _ptr(beta), _ptr(h0), _ptr(o), _stream(stream)))
     return o

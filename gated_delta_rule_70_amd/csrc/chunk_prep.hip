@@ -156,9 +156,9 @@ struct PrepCtx {
 // The whole per-chunk computation as seen by wave I (a compile-time block index, so that
 // every per-block register array is indexed statically).  All waves pass the same number
 // of workgroup barriers.
-template <typename TIn, int DK, int C, int I>
+template <typename TIn, typename TG, int DK, int C, int I>
 __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restrict__ q,
-                                          const TIn* __restrict__ k, const float* __restrict__ g,
+                                          const TIn* __restrict__ k, const TG* __restrict__ g,
                                           const float* __restrict__ beta, unsigned char* rec, int b,
                                           int T, int HK, int HV, int h, int kh, int t0, int L) {
     constexpr int NB = C / 16;
@@ -183,7 +183,8 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
     // Buffer resources over this batch element's rows: a row past the sequence end lies
     // beyond the range and reads as zero, which is exactly the zero padding of the ragged
     // last chunk (g = 0, k = q = 0, beta = 0).  The host keeps every offset below 2^31.
-    const rsrc_t rs_g = make_rsrc(g + (size_t)b * T * HV * DK, (uint32_t)T * HV * DK * 4);
+    constexpr int GE = sizeof(TG);  // bytes per g element (fp32 or bf16)
+    const rsrc_t rs_g = make_rsrc(g + (size_t)b * T * HV * DK, (uint32_t)T * HV * DK * GE);
     const rsrc_t rs_k = make_rsrc(k + (size_t)b * T * HK * DK, (uint32_t)T * HK * DK * ELT);
     const rsrc_t rs_q = make_rsrc(q + (size_t)b * T * HK * DK, (uint32_t)T * HK * DK * ELT);
     const rsrc_t rs_b = make_rsrc(beta + (size_t)b * T * HV, (uint32_t)T * HV * 4);
@@ -196,7 +197,14 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int cb = 32 * p + 16 * hh + 4 * gq;
-            const f32x4 gv = buf_load_f32x4(rs_g, ((tr * HV + h) * DK + cb) * 4, 0);
+            f32x4 gv;
+            if constexpr (GE == 4) {
+                gv = buf_load_f32x4(rs_g, ((tr * HV + h) * DK + cb) * 4, 0);
+            } else {  // four bf16 values, widened exactly
+                const auto u = __builtin_amdgcn_raw_buffer_load_b64(rs_g, ((tr * HV + h) * DK + cb) * 2, 0, 0);
+                gv = f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xFFFF0000u),
+                           __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xFFFF0000u)};
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[p][4 * hh + e] = gv[e];
         }
@@ -499,10 +507,10 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
     if constexpr (I == NB - 1) finish_row();
 }
 
-template <typename TIn, int DK, int C>
+template <typename TIn, typename TG, int DK, int C>
 __global__ __launch_bounds__(C * 4, 3) void chunk_prep_kernel(const TIn* __restrict__ q,
                                                               const TIn* __restrict__ k,
-                                                              const float* __restrict__ g,
+                                                              const TG* __restrict__ g,
                                                               const float* __restrict__ beta,
                                                               unsigned char* __restrict__ ws, int B,
                                                               int T, int HK, int HV, int NC) {
@@ -546,28 +554,28 @@ __global__ __launch_bounds__(C * 4, 3) void chunk_prep_kernel(const TIn* __restr
 #define GDR_WAVE(I_)                                                                             \
     if (I == I_) {                                                                               \
         if constexpr (I_ < NB)                                                                   \
-            prep_wave<TIn, DK, C, I_>(s, q, k, g, beta, rec, b, T, HK, HV, h, kh, t0, L);        \
+            prep_wave<TIn, TG, DK, C, I_>(s, q, k, g, beta, rec, b, T, HK, HV, h, kh, t0, L);    \
         return;                                                                                  \
     }
     GDR_WAVE(0) GDR_WAVE(1) GDR_WAVE(2) GDR_WAVE(3)
 #undef GDR_WAVE
 }
 
-template <typename TIn, int DK, int C>
+template <typename TIn, typename TG, int DK, int C>
 hipError_t launch_prep_t(const LaunchArgs& a) {
     const int NC = (a.T + C - 1) / C;
     const long long pairs = (long long)a.B * a.HK * NC;  // (batch, key head, chunk) triples
     const long long blocks = (pairs + 7) / 8 * 8 * (a.HV / a.HK);
-    hipLaunchKernelGGL((chunk_prep_kernel<TIn, DK, C>), dim3((unsigned)blocks), dim3(C * 4), 0,
-                       (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g, a.beta,
+    hipLaunchKernelGGL((chunk_prep_kernel<TIn, TG, DK, C>), dim3((unsigned)blocks), dim3(C * 4), 0,
+                       (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TG*)a.g, a.beta,
                        (unsigned char*)a.workspace, a.B, a.T, a.HK, a.HV, NC);
     return hipGetLastError();
 }
 
-template <typename TIn>
+template <typename TIn, typename TG>
 hipError_t dispatch_prep(const LaunchArgs& a) {
 #define GDR_CASE(DK_, C_) \
-    if (a.dk == DK_ && a.chunk == C_) return launch_prep_t<TIn, DK_, C_>(a);
+    if (a.dk == DK_ && a.chunk == C_) return launch_prep_t<TIn, TG, DK_, C_>(a);
     GDR_CASE(32, 16) GDR_CASE(32, 32) GDR_CASE(32, 64)
     GDR_CASE(64, 16) GDR_CASE(64, 32) GDR_CASE(64, 64)
     GDR_CASE(128, 16) GDR_CASE(128, 32) GDR_CASE(128, 64)
@@ -578,7 +586,8 @@ hipError_t dispatch_prep(const LaunchArgs& a) {
 }  // namespace
 
 hipError_t launch_chunk_prep(const LaunchArgs& a) {
-    return a.qkv_f32 ? dispatch_prep<float>(a) : dispatch_prep<bf16_t>(a);
+    if (a.qkv_f32) return dispatch_prep<float, float>(a);
+    return a.g_bf16 ? dispatch_prep<bf16_t, bf16_t>(a) : dispatch_prep<bf16_t, float>(a);
 }
 
 }  // namespace gdr

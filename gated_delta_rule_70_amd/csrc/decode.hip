@@ -24,11 +24,11 @@
 
 namespace gdr {
 
-template <typename TIn, int DK, int DV>
+template <typename TIn, typename TG, int DK, int DV>
 __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
                                                     const TIn* __restrict__ k,
                                                     const TIn* __restrict__ v,
-                                                    const float* __restrict__ g,
+                                                    const TG* __restrict__ g,
                                                     const float* __restrict__ beta,
                                                     const float* h0, float* __restrict__ o,
                                                     float* ht, int T, int HK, int HV) {
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
             const int i = rl + NRL * m;
-            gn[m] = g[gb + i];
+            gn[m] = to_f32(g[gb + i]);
             kn[m] = k[kq + i];
             qn[m] = q[kq + i];
         }
@@ -161,10 +161,10 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
 // That keeps a thread within 64 registers, so eight waves fit per SIMD and every
 // workgroup of a decode step is resident at once: the whole state is requested in one
 // round instead of two.
-template <typename TIn, int DK, int DV>
+template <typename TIn, typename TG, int DK, int DV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
-                   const float* __restrict__ g, const float* __restrict__ beta, const float* h0,
+                   const TG* __restrict__ g, const float* __restrict__ beta, const float* h0,
                    float* __restrict__ o, float* ht, int HK, int HV) {
     constexpr int BVD = DV < 64 ? DV : 64;
     constexpr int NQ = BVD / 4;
@@ -203,7 +203,7 @@ void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const T
     const size_t gb = ((size_t)b * HV + h) * DK;
     const size_t vb = ((size_t)b * HV + h) * DV + col;
     if (tid < DK) {
-        s_e[tid] = __expf(g[gb + tid]);
+        s_e[tid] = __expf(to_f32(g[gb + tid]));
         s_k[tid] = to_f32(k[kq + tid]);
         s_q[tid] = to_f32(q[kq + tid]);
     }
@@ -257,26 +257,26 @@ void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const T
     }
 }
 
-template <typename TIn, int DK, int DV>
+template <typename TIn, typename TG, int DK, int DV>
 static hipError_t launch_tokens_t(const LaunchArgs& a) {
     constexpr int BVD = DV < 64 ? DV : 64;
     const long long nblk = (long long)a.B * a.HV * (DV / BVD);
     if (a.T == 1) {
-        hipLaunchKernelGGL((decode_kernel<TIn, DK, DV>), dim3((unsigned)nblk), dim3(256), 0,
+        hipLaunchKernelGGL((decode_kernel<TIn, TG, DK, DV>), dim3((unsigned)nblk), dim3(256), 0,
                            (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
-                           a.g, a.beta, a.h0, a.o, a.ht, a.HK, a.HV);
+                           (const TG*)a.g, a.beta, a.h0, a.o, a.ht, a.HK, a.HV);
     } else {
-        hipLaunchKernelGGL((token_kernel<TIn, DK, DV>), dim3((unsigned)nblk), dim3(256), 0,
+        hipLaunchKernelGGL((token_kernel<TIn, TG, DK, DV>), dim3((unsigned)nblk), dim3(256), 0,
                            (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
-                           a.g, a.beta, a.h0, a.o, a.ht, a.T, a.HK, a.HV);
+                           (const TG*)a.g, a.beta, a.h0, a.o, a.ht, a.T, a.HK, a.HV);
     }
     return hipGetLastError();
 }
 
-template <typename TIn>
+template <typename TIn, typename TG>
 static hipError_t dispatch_dims(const LaunchArgs& a) {
 #define GDR_CASE(DK_, DV_) \
-    if (a.dk == DK_ && a.dv == DV_) return launch_tokens_t<TIn, DK_, DV_>(a);
+    if (a.dk == DK_ && a.dv == DV_) return launch_tokens_t<TIn, TG, DK_, DV_>(a);
     GDR_CASE(32, 32) GDR_CASE(32, 64) GDR_CASE(32, 128)
     GDR_CASE(64, 32) GDR_CASE(64, 64) GDR_CASE(64, 128)
     GDR_CASE(128, 32) GDR_CASE(128, 64) GDR_CASE(128, 128)
@@ -286,7 +286,8 @@ static hipError_t dispatch_dims(const LaunchArgs& a) {
 
 // Decode step and fused recurrent call: decode_kernel for T == 1, token_kernel otherwise.
 hipError_t launch_tokens(const LaunchArgs& a) {
-    return a.qkv_f32 ? dispatch_dims<float>(a) : dispatch_dims<bf16_t>(a);
+    if (a.qkv_f32) return dispatch_dims<float, float>(a);
+    return a.g_bf16 ? dispatch_dims<bf16_t, bf16_t>(a) : dispatch_dims<bf16_t, float>(a);
 }
 
 }  // namespace gdr

@@ -40,12 +40,13 @@ bool mul_ok(size_t a, size_t b, size_t* out) {
 }
 
 bool tensor_sizes(const gdr_dims& d, size_t elt, Sizes* s) {
+    const size_t gelt = (d.flags & GDR_G_BF16) ? 2 : 4;
     size_t bt, bth, btv, x;
     if (!mul_ok((size_t)d.B, (size_t)d.T, &bt)) return false;
     if (!mul_ok(bt, (size_t)d.HK, &bth) || !mul_ok(bt, (size_t)d.HV, &btv)) return false;
     if (!mul_ok(bth, (size_t)d.dk, &x) || !mul_ok(x, elt, &s->q)) return false;
     if (!mul_ok(btv, (size_t)d.dv, &x) || !mul_ok(x, elt, &s->v)) return false;
-    if (!mul_ok(btv, (size_t)d.dk, &x) || !mul_ok(x, 4, &s->g)) return false;
+    if (!mul_ok(btv, (size_t)d.dk, &x) || !mul_ok(x, gelt, &s->g)) return false;
     if (!mul_ok(btv, 4, &s->beta)) return false;
     if (!mul_ok(btv, (size_t)d.dv, &x) || !mul_ok(x, 4, &s->o)) return false;
     size_t bh;
@@ -61,13 +62,15 @@ enum class Path { decode, tokens, chunked };
 
 // Shared validation of dims, pointers, alignment and aliasing.
 int validate(const gdr_dims* d, Path path, const void* q, const void* k, const void* v,
-             const float* g, const float* beta, const float* h0, const float* o,
+             const void* g, const float* beta, const float* h0, const float* o,
              const float* ht, Sizes* sizes) {
     if (!d || !q || !k || !v || !g || !beta || !o) return GDR_ERR_NULL;
     if (d->B < 1 || d->T < 1 || d->HK < 1 || d->HV < 1 || d->HV % d->HK != 0) return GDR_ERR_SHAPE;
     if (path == Path::decode && d->T != 1) return GDR_ERR_SHAPE;
     if (!supported_head_dim(d->dk) || !supported_head_dim(d->dv)) return GDR_ERR_UNSUPPORTED;
     if (d->qkv_dtype != GDR_BF16 && d->qkv_dtype != GDR_F32) return GDR_ERR_UNSUPPORTED;
+    if ((d->flags & ~GDR_G_BF16) != 0) return GDR_ERR_UNSUPPORTED;
+    if ((d->flags & GDR_G_BF16) && d->qkv_dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
     if (path == Path::chunked && d->chunk != 16 && d->chunk != 32 && d->chunk != 64)
         return GDR_ERR_UNSUPPORTED;
     const size_t elt = d->qkv_dtype == GDR_F32 ? 4 : 2;
@@ -95,7 +98,7 @@ int validate(const gdr_dims* d, Path path, const void* q, const void* k, const v
 }
 
 gdr::LaunchArgs make_args(const gdr_dims* d, const void* q, const void* k, const void* v,
-                          const float* g, const float* beta, const float* h0, float* o, float* ht,
+                          const void* g, const float* beta, const float* h0, float* o, float* ht,
                           void* workspace, void* stream) {
     gdr::LaunchArgs a;
     a.B = d->B;
@@ -106,6 +109,7 @@ gdr::LaunchArgs make_args(const gdr_dims* d, const void* q, const void* k, const
     a.dv = d->dv;
     a.chunk = d->chunk;
     a.qkv_f32 = d->qkv_dtype == GDR_F32;
+    a.g_bf16 = (d->flags & GDR_G_BF16) != 0;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -150,7 +154,7 @@ const char* gdr_status_str(int status) {
 }
 
 int gdr_decode_step(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                    const float* g, const float* beta, const float* h0, float* o, float* ht,
+                    const void* g, const float* beta, const float* h0, float* o, float* ht,
                     void* stream) {
     Sizes s;
     const int st = validate(dims, Path::decode, q, k, v, g, beta, h0, o, ht, &s);
@@ -160,7 +164,7 @@ int gdr_decode_step(const gdr_dims* dims, const void* q, const void* k, const vo
 }
 
 int gdr_fused_recurrent(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                        const float* g, const float* beta, const float* h0, float* o, float* ht,
+                        const void* g, const float* beta, const float* h0, float* o, float* ht,
                         void* stream) {
     Sizes s;
     const int st = validate(dims, Path::tokens, q, k, v, g, beta, h0, o, ht, &s);
@@ -179,7 +183,7 @@ size_t gdr_chunk_prefill_workspace_bytes(const gdr_dims* dims) {
 }
 
 static int prefill_stages(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                          const float* g, const float* beta, const float* h0, float* o, float* ht,
+                          const void* g, const float* beta, const float* h0, float* o, float* ht,
                           void* workspace, size_t workspace_bytes, void* stream, bool prep,
                           bool carry) {
     Sizes s;
@@ -211,28 +215,28 @@ static int prefill_stages(const gdr_dims* dims, const void* q, const void* k, co
 }
 
 int gdr_chunk_prefill(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                      const float* g, const float* beta, const float* h0, float* o, float* ht,
+                      const void* g, const float* beta, const float* h0, float* o, float* ht,
                       void* workspace, size_t workspace_bytes, void* stream) {
     return prefill_stages(dims, q, k, v, g, beta, h0, o, ht, workspace, workspace_bytes, stream,
                           true, true);
 }
 
 int gdr_chunk_prep(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                   const float* g, const float* beta, const float* h0, float* o, float* ht,
+                   const void* g, const float* beta, const float* h0, float* o, float* ht,
                    void* workspace, size_t workspace_bytes, void* stream) {
     return prefill_stages(dims, q, k, v, g, beta, h0, o, ht, workspace, workspace_bytes, stream,
                           true, false);
 }
 
 int gdr_chunk_carry(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                    const float* g, const float* beta, const float* h0, float* o, float* ht,
+                    const void* g, const float* beta, const float* h0, float* o, float* ht,
                     void* workspace, size_t workspace_bytes, void* stream) {
     return prefill_stages(dims, q, k, v, g, beta, h0, o, ht, workspace, workspace_bytes, stream,
                           false, true);
 }
 
 int gdr_tree_verify(const gdr_dims* dims, const int32_t* parent, const void* q, const void* k,
-                    const void* v, const float* g, const float* beta, const float* h0, float* o,
+                    const void* v, const void* g, const float* beta, const float* h0, float* o,
                     void* stream) {
     if (!parent) return GDR_ERR_NULL;
     Sizes s;
@@ -246,7 +250,7 @@ int gdr_tree_verify(const gdr_dims* dims, const int32_t* parent, const void* q, 
 }
 
 int gdr_forward(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                const float* g, const float* beta, const float* h0, float* o, float* ht,
+                const void* g, const float* beta, const float* h0, float* o, float* ht,
                 void* workspace, size_t workspace_bytes, void* stream) {
     if (dims && dims->T >= 1 && dims->T <= GDR_RECURRENT_MAX_T)
         return gdr_fused_recurrent(dims, q, k, v, g, beta, h0, o, ht, stream);

@@ -23,6 +23,17 @@ __device__ __forceinline__ float to_f32(bf16_t x) {
     return __uint_as_float(static_cast<uint32_t>(x.bits) << 16);
 }
 
+// Four consecutive log-decay values (index i a multiple of 4) as fp32, from fp32 or bf16
+// storage (bf16 widens exactly).
+__device__ __forceinline__ f32x4 load_g4(const float* g, size_t i) {
+    return *reinterpret_cast<const f32x4*>(g + i);
+}
+__device__ __forceinline__ f32x4 load_g4(const bf16_t* g, size_t i) {
+    const uint2 u = *reinterpret_cast<const uint2*>(g + i);
+    return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                 __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u)};
+}
+
 // Split an fp32 value into a bf16 high part and a bf16 remainder (round to nearest even
 // on both), so that hi + lo carries ~16 significant bits with fp32's exponent range.
 __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {

@@ -11,10 +11,11 @@ namespace gdr {
 struct LaunchArgs {
     int B, T, HK, HV, dk, dv, chunk;
     bool qkv_f32;
+    bool g_bf16;  // g stored as bf16 (only with bf16 q/k/v)
     const void* q;
     const void* k;
     const void* v;
-    const float* g;
+    const void* g;
     const float* beta;
     const float* h0;
     float* o;

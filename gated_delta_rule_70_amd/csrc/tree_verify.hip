@@ -59,10 +59,10 @@ __device__ __forceinline__ f32x4 tile_dot(const float* xa, const float* yb, f32x
     return acc;
 }
 
-template <typename TIn, int DK>
+template <typename TIn, typename TG, int DK>
 __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int32_t* __restrict__ parent, const TIn* __restrict__ q, const TIn* __restrict__ k,
-    const TIn* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
+    const TIn* __restrict__ v, const TG* __restrict__ g, const float* __restrict__ beta,
     const float* __restrict__ h0, float* __restrict__ o, int T, int HK, int HV, int DV) {
     constexpr int KP = DK + 4;   // row pitch (floats): 16 rows read at one offset hit 16 banks
     constexpr int AP = TM + 4;
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 #pragma unroll
         for (int e = 0; e < ELT; ++e) kraw[m][e] = qraw[m][e] = 0u;
         if (t < T) {
-            gv[m] = *reinterpret_cast<const f32x4*>(g + (((size_t)b * T + t) * HV + h) * DK + c4);
+            gv[m] = load_g4(g, (((size_t)b * T + t) * HV + h) * DK + c4);
             const size_t kq = (((size_t)b * T + t) * HK + kh) * DK + c4;
             if constexpr (ELT == 2) {
                 const uint2 kk = *reinterpret_cast<const uint2*>(k + kq);
@@ -408,20 +408,20 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     }
 }
 
-template <typename TIn, int DK>
+template <typename TIn, typename TG, int DK>
 hipError_t launch_tree_t(const LaunchArgs& a, const int32_t* parent) {
     const long long nblk = (long long)a.B * a.HV * (a.dv / CB);
-    hipLaunchKernelGGL((tree_verify_kernel<TIn, DK>), dim3((unsigned)nblk), dim3(256), 0,
+    hipLaunchKernelGGL((tree_verify_kernel<TIn, TG, DK>), dim3((unsigned)nblk), dim3(256), 0,
                        (hipStream_t)a.stream, parent, (const TIn*)a.q, (const TIn*)a.k,
-                       (const TIn*)a.v, a.g, a.beta, a.h0, a.o, a.T, a.HK, a.HV, a.dv);
+                       (const TIn*)a.v, (const TG*)a.g, a.beta, a.h0, a.o, a.T, a.HK, a.HV, a.dv);
     return hipGetLastError();
 }
 
-template <typename TIn>
+template <typename TIn, typename TG>
 hipError_t dispatch_tree(const LaunchArgs& a, const int32_t* parent) {
-    if (a.dk == 32) return launch_tree_t<TIn, 32>(a, parent);
-    if (a.dk == 64) return launch_tree_t<TIn, 64>(a, parent);
-    if (a.dk == 128) return launch_tree_t<TIn, 128>(a, parent);
+    if (a.dk == 32) return launch_tree_t<TIn, TG, 32>(a, parent);
+    if (a.dk == 64) return launch_tree_t<TIn, TG, 64>(a, parent);
+    if (a.dk == 128) return launch_tree_t<TIn, TG, 128>(a, parent);
     return hipErrorInvalidValue;
 }
 
@@ -429,7 +429,8 @@ hipError_t dispatch_tree(const LaunchArgs& a, const int32_t* parent) {
 
 hipError_t launch_tree_verify(const LaunchArgs& a, const int32_t* parent) {
     if (a.T < 1 || a.T > TM || a.dv % CB != 0) return hipErrorInvalidValue;
-    return a.qkv_f32 ? dispatch_tree<float>(a, parent) : dispatch_tree<bf16_t>(a, parent);
+    if (a.qkv_f32) return dispatch_tree<float, float>(a, parent);
+    return a.g_bf16 ? dispatch_tree<bf16_t, bf16_t>(a, parent) : dispatch_tree<bf16_t, float>(a, parent);
 }
 
 }  // namespace gdr

@@ -15,7 +15,8 @@
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers to dense row-major arrays, 16-byte aligned:
  *       q, k  [B][T][HK][dk]   (qkv_dtype)      v     [B][T][HV][dv]  (qkv_dtype)
- *       g     [B][T][HV][dk]   fp32 log-decay   beta  [B][T][HV]      fp32
+ *       g     [B][T][HV][dk]   log-decay, fp32 (bf16 with GDR_G_BF16)
+ *       beta  [B][T][HV]       fp32
  *       h0,ht [B][HV][dk][dv]  fp32 state       o     [B][T][HV][dv]  fp32
  *     value head h reads key head h / (HV/HK) (contiguous GQA groups).
  *   - h0 == NULL means a zero initial state; ht == NULL means the final state is not
@@ -49,7 +50,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 2
+#define GDR_ABI_VERSION 3
 
 typedef enum {
     GDR_OK = 0,
@@ -65,10 +66,22 @@ typedef enum {
 
 typedef enum { GDR_BF16 = 0, GDR_F32 = 1 } gdr_dtype;
 
+/*
+ * Input-format flags (gdr_dims.flags; 0 = the defaults above).
+ *   GDR_G_BF16  g is stored as bf16 instead of fp32 -- the I/O-lean input of the
+ *               follow-up work on the prefill's HBM bytes: g is the largest input (dk values
+ *               per token and value head), and bf16 halves it.  The kernels widen each value
+ *               exactly to fp32, so a call gives bitwise the result of the same call with an
+ *               fp32 g holding the same (bf16-representable) values.  Requires bf16 q/k/v.
+ * Any other bit, or GDR_G_BF16 with fp32 q/k/v, returns GDR_ERR_UNSUPPORTED.
+ */
+#define GDR_G_BF16 0x1
+
 typedef struct {
     int32_t B, T, HK, HV, dk, dv;
     int32_t chunk;      /* prefill chunk length C (ignored by the token-recurrence calls)  */
     int32_t qkv_dtype;  /* gdr_dtype of q, k and v                                         */
+    int32_t flags;      /* input-format flags (GDR_G_BF16); 0 for the defaults             */
 } gdr_dims;
 
 /*
@@ -79,7 +92,7 @@ typedef struct {
  * Normally called in place (ht == h0).  Uses no workspace.
  */
 int gdr_decode_step(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                    const float* g, const float* beta, const float* h0, float* o, float* ht,
+                    const void* g, const float* beta, const float* h0, float* o, float* ht,
                     void* stream);
 
 /*
@@ -94,7 +107,7 @@ int gdr_decode_step(const gdr_dims* dims, const void* q, const void* k, const vo
  * gdr_decode_step.  Uses no workspace.
  */
 int gdr_fused_recurrent(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                        const float* g, const float* beta, const float* h0, float* o, float* ht,
+                        const void* g, const float* beta, const float* h0, float* o, float* ht,
                         void* stream);
 
 /*
@@ -119,7 +132,7 @@ size_t gdr_chunk_prefill_workspace_bytes(const gdr_dims* dims);
  * gdr_chunk_prefill_workspace_bytes(dims) bytes; its contents on entry are ignored.
  */
 int gdr_chunk_prefill(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                      const float* g, const float* beta, const float* h0, float* o, float* ht,
+                      const void* g, const float* beta, const float* h0, float* o, float* ht,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -141,10 +154,10 @@ int gdr_chunk_prefill(const gdr_dims* dims, const void* q, const void* k, const 
  * Splitting them lets a caller time or overlap the stages.
  */
 int gdr_chunk_prep(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                   const float* g, const float* beta, const float* h0, float* o, float* ht,
+                   const void* g, const float* beta, const float* h0, float* o, float* ht,
                    void* workspace, size_t workspace_bytes, void* stream);
 int gdr_chunk_carry(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                    const float* g, const float* beta, const float* h0, float* o, float* ht,
+                    const void* g, const float* beta, const float* h0, float* o, float* ht,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -157,7 +170,7 @@ int gdr_chunk_carry(const gdr_dims* dims, const void* q, const void* k, const vo
  */
 #define GDR_RECURRENT_MAX_T 8
 int gdr_forward(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                const float* g, const float* beta, const float* h0, float* o, float* ht,
+                const void* g, const float* beta, const float* h0, float* o, float* ht,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -175,7 +188,7 @@ int gdr_forward(const gdr_dims* dims, const void* q, const void* k, const void* 
  */
 #define GDR_TREE_MAX_T 64
 int gdr_tree_verify(const gdr_dims* dims, const int32_t* parent, const void* q, const void* k,
-                    const void* v, const float* g, const float* beta, const float* h0, float* o,
+                    const void* v, const void* g, const float* beta, const float* h0, float* o,
                     void* stream);
 
 /* Static English text for a status code (never NULL). */

@@ -273,3 +273,29 @@ def test_bench_carry_plan_matches_library(L):
         nseg = int(plan.split(", ")[1].split()[0]) if "segments" in plan else 1
         extra = B * HV * ((nseg - 1) * 2 * mat(dk) + nseg * mat(dk)) if nseg > 1 else 0
         assert got == _records(B, T, HV, dk, C) + extra, (B, HV, T, dk, C, plan)
+
+
+def test_input_format_flags(L):
+    """gdr_dims.flags: only GDR_G_BF16 is defined, and only with bf16 q/k/v; anything else is
+    refused before any HIP call on every entry point."""
+    for bad in (dict(flags=2), dict(flags=1 << 30), dict(flags=-1), dict(flags=1, qkv_dtype=1)):
+        assert prefill(L, dims(**bad)) == EUNSUP, bad
+        assert decode(L, dims(T=1, **bad)) == EUNSUP, bad
+        assert decode(L, dims(T=3, **bad), entry="gdr_fused_recurrent") == EUNSUP, bad
+        assert tree(L, dims(T=8, dv=64, **bad)) == EUNSUP, bad
+
+
+def test_bf16_g_extent_in_alias_checks(L):
+    """With GDR_G_BF16, g spans B*T*HV*dk*2 bytes: o over its last 16 bytes overlaps it."""
+    gbytes = 2 * 5 * 4 * 64 * 2
+    assert prefill(L, dims(flags=1), o=addr(3, gbytes - 16)) == EALIAS
+    assert prefill(L, dims(flags=0), o=addr(3, 2 * gbytes - 16)) == EALIAS  # fp32 g: twice the bytes
+
+
+@pytest.mark.skipif("_gpu_visible()", reason="valid fake pointers would reach a real GPU")
+def test_bf16_g_valid_arguments_reach_the_runtime_without_a_gpu(L):
+    # o right after the bf16 g extent does not overlap it; the call passes validation and
+    # fails only at the first HIP call
+    gbytes = 2 * 5 * 4 * 64 * 2
+    assert prefill(L, dims(flags=1), o=addr(3, gbytes)) == EHIP
+    assert decode(L, dims(T=1, flags=1), ht=addr(5, 0)) == EHIP
