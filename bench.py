@@ -65,15 +65,18 @@ KERNEL_SOURCES = {  # kernel -> the sources its machine code is built from
     "carry_sum": ["chunk_carry_wide.hip", "gdr_device.h", "gdr_launch.h"],
     "carry_combine": ["chunk_carry_wide.hip", "gdr_device.h", "gdr_launch.h"],
     "decode": ["decode.hip", "gdr_device.h", "gdr_launch.h"],
+    "fused_recurrent": ["decode.hip", "gdr_device.h", "gdr_launch.h"],
     "tree_verify": ["tree_verify.hip", "gdr_device.h", "gdr_launch.h"],
 }
 # kernel -> substrings that all appear in its (demangled) name in profiler output; the
 # column-split carry is chunk_carry_kernel, the whole-head carry's full and summary passes
-# are carry_wide_kernel<..., false> and <..., true>
+# are carry_wide_kernel<..., false> and <..., true>; the decode step is decode_kernel and a
+# multi-token fused recurrence token_kernel
 KERNEL_SYMBOL = {"chunk_prep": ("chunk_prep_kernel",), "chunk_carry": ("chunk_carry_kernel",),
                  "carry_full": ("carry_wide_kernel", "false>"), "carry_sum": ("carry_wide_kernel", "true>"),
                  "carry_combine": ("carry_combine_kernel",),
-                 "decode": ("token_kernel",), "tree_verify": ("tree_verify_kernel",)}
+                 "decode": ("decode_kernel",), "fused_recurrent": ("token_kernel",),
+                 "tree_verify": ("tree_verify_kernel",)}
 CALIB_BYTES = 256 << 20           # calibration kernel: reads and writes this many bytes
 HEADLINE_PROFILE = "prefill_b1_t4097_decode_b32"  # the default run's profile summaries
 

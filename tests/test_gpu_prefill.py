@@ -208,3 +208,17 @@ def test_wide_carry_fp32_inputs():
     torch.cuda.synchronize()
     eo, es = err(o, o_ref), err(ht, ht_ref)
     assert eo < TOL and es < TOL, f"o {eo:.2e} state {es:.2e}"
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+def test_segmented_carry_fp32_inputs(dk):
+    """The segmented carry with fp32 q/k/v (the summary and full passes load v rows in
+    fp32): 2 heads, 2048 chunks of 16, 128 segments, slowed decay."""
+    x = small_inputs(1, 32768, 1, 2, dk, dk, dtype=torch.float32, seed=97 + dk)
+    x["g"] = x["g"] / 100
+    o_ref, ht_ref = oracle.sequential(**x)
+    note(f"segmented carry fp32 q/k/v dk={dk}")
+    o, ht = run_prefill(dev(x), 16)
+    torch.cuda.synchronize()
+    eo, es = err(o, o_ref), err(ht, ht_ref)
+    assert eo < TOL and es < TOL, f"o {eo:.2e} state {es:.2e}"
