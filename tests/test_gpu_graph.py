@@ -49,9 +49,16 @@ def test_decode_steps_replayed_from_a_graph():
             assert torch.equal(outs[t], o_eager[t]), f"replay {rep}: o of step {t} differs"
 
 
-@pytest.mark.parametrize("T", [97, 200])
-def test_prefill_replayed_from_a_graph(T):
-    B, HK, HV, dk, dv, C = 2, 2, 4, 128, 128, 64
+# (B, T, HK, HV, dk, chunk): column-split carry; whole-head carry (> 128 heads); the
+# segmented carry (summary, combine and full launches; 2 heads x 2048 chunks, 128 segments)
+GRAPH_PREFILLS = [(2, 97, 2, 4, 128, 64), (2, 200, 2, 4, 128, 64), (2, 97, 40, 80, 64, 32),
+                  (1, 32768, 1, 2, 64, 16)]
+
+
+@pytest.mark.parametrize("case", GRAPH_PREFILLS, ids=lambda c: "B{}T{}HV{}dk{}C{}".format(c[0], c[1], c[3], c[4], c[5]))
+def test_prefill_replayed_from_a_graph(case):
+    B, T, HK, HV, dk, C = case
+    dv = dk
     x = dev(small_inputs(B, T, HK, HV, dk, dv, seed=72))
     note(f"graph prefill B={B} T={T} HV={HV} {dk}x{dv} C={C}")
     ws = torch.empty(gdr.workspace_bytes(B, T, HK, HV, dk, dv, C), dtype=torch.uint8, device="cuda")
