@@ -299,3 +299,16 @@ def test_bf16_g_valid_arguments_reach_the_runtime_without_a_gpu(L):
     gbytes = 2 * 5 * 4 * 64 * 2
     assert prefill(L, dims(flags=1), o=addr(3, gbytes)) == EHIP
     assert decode(L, dims(T=1, flags=1), ht=addr(5, 0)) == EHIP
+
+
+def test_header_is_plain_c_and_links(L, tmp_path):
+    """A C99 program using only include/gdr.h builds with gcc, links against libgdr.so and
+    gets the documented host-side answers (no call in it reaches a GPU)."""
+    src = os.path.join(ROOT, "tests", "c_abi", "abi_smoke.c")
+    exe = str(tmp_path / "abi_smoke")
+    libdir = os.path.dirname(gdr.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"), src,
+                    "-o", exe, "-L", libdir, "-lgdr", f"-Wl,-rpath,{libdir}"], check=True)
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr
+    assert "c abi ok" in res.stdout
