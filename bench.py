@@ -403,7 +403,7 @@ def _mean(xs):
     return sum(xs) / len(xs)
 
 
-def bench_prefill(w, steps, warmup, g_bf16=False):
+def bench_prefill(w, steps, warmup, g_bf16=False, graph=False):
     import torch
 
     import gated_delta_rule_70_amd as gdr
@@ -438,6 +438,21 @@ def bench_prefill(w, steps, warmup, g_bf16=False):
     wall = time.perf_counter() - t0
     prep_ms = _mean([e[0].elapsed_time(e[1]) for e in ev])
     carry_ms = _mean([e[1].elapsed_time(e[2]) for e in ev])
+    bench_prefill.graph_ms = None
+    if graph:  # the same call captured once and replayed `steps` times (no host launch cost)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call("both")
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        bench_prefill.graph_ms = a.elapsed_time(b) / steps
+        del g
     return x, o, ht, wall, prep_ms, carry_ms
 
 
@@ -729,7 +744,8 @@ def main():
         torch.neg(xc, out=yc)
         torch.cuda.synchronize()
         del xc, yc
-    x, o, ht, wall, prep_ms, carry_ms = bench_prefill(w, args.steps, args.warmup)
+    x, o, ht, wall, prep_ms, carry_ms = bench_prefill(w, args.steps, args.warmup, graph=not args.profile_run)
+    graph_ms = bench_prefill.graph_ms
     ntok = w.B * w.T
     ms_per_step = wall / args.steps * 1e3
     value = ntok / (wall / args.steps)
@@ -756,6 +772,9 @@ def main():
         "ceiling_ms": round(ceil_ms, 5), "path_frac_of_ceiling": round(ceil_ms / kern_ms, 4),
         "tokens_per_s_kernel_time": round(ntok / (kern_ms * 1e-3), 1),
         "carry": carry_plan(w.B, w.T, w.HV, w.dk, w.dv, w.chunk),
+        # the same step replayed from a HIP graph: no host launch cost between the kernels
+        "graph_replay": None if graph_ms is None else {
+            "ms_per_step": round(graph_ms, 5), "tokens_per_s": round(ntok / (graph_ms * 1e-3), 1)},
         "counters": {"chunk_prep": read_util("chunk_prep"), "chunk_carry": read_util("chunk_carry")},
     }
 
