@@ -222,3 +222,25 @@ def test_segmented_carry_fp32_inputs(dk):
     torch.cuda.synchronize()
     eo, es = err(o, o_ref), err(ht, ht_ref)
     assert eo < TOL and es < TOL, f"o {eo:.2e} state {es:.2e}"
+
+
+def test_maximum_length_prefill():
+    """The longest sequence the prefill accepts at HV=32, 128x128, chunk 64 (T = 131007:
+    one batch element's g and o rows, padding included, just under 2^31 bytes), so every
+    31-bit buffer offset in the kernels is exercised near its limit; the carry runs in 8
+    segments of 256 chunks.  One key-head group against the oracle."""
+    B, T, HK, HV, dk = 1, 131007, 16, 32, 128
+    assert (T + 64) * HV * dk * 4 < 2 ** 31 <= (T + 1 + 64) * HV * dk * 4  # T + 1 is refused
+    x = small_inputs(B, T, HK, HV, dk, dk, seed=101)
+    note(f"maximum-length prefill T={T}")
+    d = dev(x)
+    o, ht = run_prefill(d, 64)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(ht).all()
+    G = HV // HK
+    kh = HK - 1  # the last key head: the largest offsets
+    ref = oracle_on_groups(x, [(0, kh)], G)
+    o_r, ht_r = ref[(0, kh)]
+    hv = slice(kh * G, (kh + 1) * G)
+    eo, es = err(o[0, :, hv].cpu(), o_r), err(ht[0, hv].cpu(), ht_r)
+    assert eo < TOL and es < TOL, f"o {eo:.2e} state {es:.2e}"
