@@ -367,7 +367,7 @@ def bench_io_lean(w, steps=10, warmup=2):
     throughput, and the path's algorithmic bytes at that input format."""
     import torch
 
-    x, o, ht, wall, prep_ms, carry_ms = bench_prefill(w, steps, warmup, g_bf16=True)
+    x, o, ht, wall, prep_ms, carry_ms, _ = bench_prefill(w, steps, warmup, g_bf16=True)
     elt = 2 if w.dtype == torch.bfloat16 else 4
     b_prep, b_carry = prefill_bytes(w.B, w.T, w.HK, w.HV, w.dk, w.dv, elt, w.h0, g_elt=2)
     kern = prep_ms + carry_ms
@@ -385,7 +385,7 @@ def bench_other_prefills(steps=5, warmup=1):
     out = []
     for name in OTHER_PREFILLS:
         w = WORKLOADS[name]
-        x, o, ht, wall, prep_ms, carry_ms = bench_prefill(w, steps, warmup)
+        x, o, ht, wall, prep_ms, carry_ms, _ = bench_prefill(w, steps, warmup)
         out.append({"workload": name, "B": w.B, "T": w.T, "h0": w.h0,
                     "prep_ms": round(prep_ms, 5), "carry_ms": round(carry_ms, 5),
                     "ms_per_step": round(wall / steps * 1e3, 5),
@@ -438,7 +438,7 @@ def bench_prefill(w, steps, warmup, g_bf16=False, graph=False):
     wall = time.perf_counter() - t0
     prep_ms = _mean([e[0].elapsed_time(e[1]) for e in ev])
     carry_ms = _mean([e[1].elapsed_time(e[2]) for e in ev])
-    bench_prefill.graph_ms = None
+    graph_ms = None
     if graph:  # the same call captured once and replayed `steps` times (no host launch cost)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -451,9 +451,9 @@ def bench_prefill(w, steps, warmup, g_bf16=False, graph=False):
             g.replay()
         b.record()
         torch.cuda.synchronize()
-        bench_prefill.graph_ms = a.elapsed_time(b) / steps
+        graph_ms = a.elapsed_time(b) / steps
         del g
-    return x, o, ht, wall, prep_ms, carry_ms
+    return x, o, ht, wall, prep_ms, carry_ms, graph_ms
 
 
 def bench_decode(w, steps, warmup):
@@ -744,8 +744,8 @@ def main():
         torch.neg(xc, out=yc)
         torch.cuda.synchronize()
         del xc, yc
-    x, o, ht, wall, prep_ms, carry_ms = bench_prefill(w, args.steps, args.warmup, graph=not args.profile_run)
-    graph_ms = bench_prefill.graph_ms
+    x, o, ht, wall, prep_ms, carry_ms, graph_ms = bench_prefill(w, args.steps, args.warmup,
+                                                                 graph=not args.profile_run)
     ntok = w.B * w.T
     ms_per_step = wall / args.steps * 1e3
     value = ntok / (wall / args.steps)
