@@ -45,6 +45,27 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// tile_dot with every operand read issued first and the reduction split over four
+// accumulators (four independent chains of matrix-core operations), summed at the end.
+template <int K>
+__device__ __forceinline__ f32x4 tile_dot4(const float* xa, const float* yb) {
+    constexpr int N = K / 16;  // 16-byte reads per operand and lane
+    f32x4 xs[N], ys[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        xs[i] = *reinterpret_cast<const f32x4*>(xa + 4 * i);
+        ys[i] = *reinterpret_cast<const f32x4*>(yb + 4 * i);
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i & 3] = mfma4(xs[i][e], ys[i][e], acc[i & 3]);
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
 // sum over a K-long reduction of X[rowA][.] * Y[rowB][.] for a 16x16 tile: lane (i, g)
 // reads K/4 contiguous floats of row i of each operand, starting at g*K/4
 template <int K>
@@ -243,7 +264,9 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
             sJ[tid] = jn;
             sAnc[tid] = an;
         }
-        __syncthreads();
+        // once no node has a jump left the prefixes and masks are final (a tree of depth
+        // below 2^r needs r rounds): every thread sees the same answer and stops together
+        if (!__syncthreads_or(jn >= 0)) break;
     }
     // decayed rows; node depths
 #pragma unroll
@@ -265,20 +288,32 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         *reinterpret_cast<f32x4*>(sKh + i) = kb;
         *reinterpret_cast<f32x4*>(sQt + i) = qt;
     }
-    if (tid < T) {
-        const int dep = __builtin_popcountll(sAnc[tid]);
-        sDep[tid] = dep;
-        atomicMax(&sMaxDep, dep);
-        atomicAdd(&sCnt[dep], 1);
-    }
-    __syncthreads();
-    if (tid == 0) {  // first slot of each depth (counts are in place; the order is fixed)
-        int acc = 0;
-        for (int L = 0; L < TM; ++L) {
-            sStart[L] = acc;
-            acc += sCnt[L];
+    // Nodes listed by depth, in index order within a depth, by wave 0 alone: for each depth
+    // d a ballot of the nodes at d gives its count; a node's slot is the number of nodes at
+    // smaller depths plus those of its own depth with a smaller index.  The loop ends once
+    // every node is placed (the ballots make every bound wave-uniform).
+    if (wave == 0) {
+        const int dep = lane < T ? __builtin_popcountll(sAnc[lane]) : TM;
+        int pos = 0, cnt = 0, start = 0, placed = 0, maxd = 0;
+        for (int d = 0; d < TM && placed < T; ++d) {
+            const unsigned long long bal = __ballot(dep == d);
+            const int c = __popcll(bal);
+            if (lane == d) {
+                cnt = c;
+                start = placed;
+            }
+            if (d < dep) pos += c;
+            else if (d == dep) pos += __popcll(bal & ((1ull << lane) - 1ull));
+            if (c > 0) maxd = d;
+            placed += c;
         }
+        sCnt[lane] = cnt;
+        sStart[lane] = start;
+        sDep[lane] = dep;
+        if (lane < T) sList[pos] = lane;
+        if (lane == 0) sMaxDep = maxd;
     }
+    __syncthreads();  // decayed rows (read across threads below) and the depth lists complete
 
     // ---- 2. Kt h0, Qt h0 and the right-hand side beta (v - Kt h0) -------------------------
     // tile (I, N): rows 16I.., columns 16N.. of this block; wave w owns tiles w and w + 4 and
@@ -304,32 +339,29 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     }
     __syncthreads();
 
-    // nodes by depth, in index order within a depth
-    if (tid < T) {
-        const int dep = sDep[tid];
-        int rank = 0;
-        for (int u = 0; u < tid; ++u) rank += sDep[u] == dep;
-        sList[sStart[dep] + rank] = tid;
-    }
-
     // ---- 3. A and P tiles, masked by ancestry (upper tiles are zero) -----------------------
-    const int ntile = NB * NB;
-    for (int job = wave; job < 2 * ntile; job += 4) {
-        const int x = job / ntile;
-        const int I = (job % ntile) / NB, J = (job % ntile) % NB;
-        float* dst = x == 0 ? sA : sP;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (J <= I) {
-            const int cq = gq * (DK / 4);
-            acc = tile_dot<DK>((x == 0 ? sKt : sQt) + (16 * I + li) * KP + cq,
-                               sKh + (16 * J + li) * KP + cq, acc);
+    // Only the NB(NB+1)/2 lower tiles of each hold products; they are dealt evenly to the
+    // waves.  The upper tiles of P are zero-filled (the output product reads whole rows of
+    // P); those of A are never read.
+    const int nlow = NB * (NB + 1) / 2;
+    for (int job = wave; job < 2 * nlow; job += 4) {
+        const int x = job / nlow;
+        int t = job % nlow, I = 0;
+        while (t > I) {
+            t -= I + 1;
+            ++I;
         }
+        const int J = t;
+        float* dst = x == 0 ? sA : sP;
+        const int cq = gq * (DK / 4);
+        const f32x4 acc = tile_dot4<DK>((x == 0 ? sKt : sQt) + (16 * I + li) * KP + cq,
+                                        sKh + (16 * J + li) * KP + cq);
         const int s = 16 * J + li;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * I + 4 * gq + i;
             float val = 0.f;
-            if (J <= I && r < T && s < T) {
+            if (r < T && s < T) {
                 const bool anc = (sAnc[r] >> s) & 1ull;
                 if (x == 0) val = anc ? sBeta[r] * acc[i] : 0.f;
                 else val = (anc || s == r) ? acc[i] : 0.f;
@@ -337,6 +369,11 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
             dst[r * AP + s] = val;
         }
     }
+    for (int I = 0; I + 1 < NB; ++I)  // P's upper tiles: zeros (a row segment per thread)
+        for (int e = tid; e < 16 * 16 * (NB - 1 - I); e += 256) {
+            const int row = e / (16 * (NB - 1 - I)), c = e % (16 * (NB - 1 - I));
+            sP[(16 * I + row) * AP + 16 * (I + 1) + c] = 0.f;
+        }
     __syncthreads();
 
     // ---- 4. forward substitution, one depth level at a time --------------------------------
