@@ -705,6 +705,9 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-util", metavar="UTIL_DIR")
     ap.add_argument("--summarize-stats", nargs=3, metavar=("DIR", "NAME", "COMMAND"))
+    ap.add_argument("--section", choices=("tree", "short_calls"),
+                    help="run only this part of the benchmark (tree-verify cases or short calls) "
+                         "and print its JSON; for kernel traces of those kernels")
     ap.add_argument("--profile-name", default=HEADLINE_PROFILE,
                     help="profile summaries to write: the default run's, or a prefill workload's "
                          "(counter runs of `--profile-run --workload <name> --no-decode`)")
@@ -736,6 +739,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.section:
+        res = bench_tree(DECODE) if args.section == "tree" else bench_short_calls(DECODE)
+        print(json.dumps({"section": args.section, **res}), flush=True)
+        return
     w = WORKLOADS[args.workload]
     elt = 2 if w.dtype == torch.bfloat16 else 4
     if args.profile_run:  # calibration kernel of known traffic for the counter runs
