@@ -844,6 +844,19 @@ def main():
                                 "cores": oracle.num_threads(), "kind": "oracle",
                                 "sample": f"the full {w.name} workload ({ntok} tokens x {w.HV} value heads), "
                                           f"fp64 sequential recurrence, {runs} runs in {cpu_s:.1f} s"}
+        # the same recurrence on one host thread, over one key head's group of value heads
+        # (a bounded sample), scaled to the whole workload's tokens per second
+        from gdr_synth import head_group
+
+        G = w.HV // w.HK
+        sub = head_group(x, 0, 0, G)
+        t1 = time.perf_counter()
+        oracle.sequential(**sub, threads=1)
+        one_s = time.perf_counter() - t1
+        line["cpu_baseline"]["single_thread"] = {
+            "value": round(ntok / (one_s * w.B * w.HK), 1), "unit": "tokens/s", "cores": 1,
+            "sample": f"one key head's {G} value heads of {w.name} (batch 0), {one_s:.2f} s, "
+                      f"scaled by the {w.B * w.HK} such groups of the workload"}
         line["parity_vs_oracle"] = {
             "o": float(oracle.rel_err(o.double().cpu().numpy(), o_ref)),
             "state": float(oracle.rel_err(ht.double().cpu().numpy(), ht_ref)),
