@@ -244,3 +244,23 @@ def test_maximum_length_prefill():
     hv = slice(kh * G, (kh + 1) * G)
     eo, es = err(o[0, :, hv].cpu(), o_r), err(ht[0, hv].cpu(), ht_r)
     assert eo < TOL and es < TOL, f"o {eo:.2e} state {es:.2e}"
+
+
+@pytest.mark.parametrize("case", [(2, 97, 2, 4, 128, 64), (2, 70, 40, 80, 128, 64), (1, 32768, 1, 2, 64, 16)],
+                         ids=["column_split", "whole_head", "segmented"])
+def test_two_stage_calls_equal_one_call(case):
+    """gdr_chunk_prep followed by gdr_chunk_carry on the same workspace gives bitwise the
+    result of gdr_chunk_prefill, on every carry path."""
+    B, T, HK, HV, dk, C = case
+    x = small_inputs(B, T, HK, HV, dk, dk, seed=T + HV)
+    d = dev(x)
+    note(f"two-stage prefill {case}")
+    o1, h1 = run_prefill(d, C)
+    ws = torch.empty(gdr.workspace_bytes(B, T, HK, HV, dk, dk, C), dtype=torch.uint8, device="cuda")
+    o2 = torch.empty_like(o1)
+    h2 = torch.empty_like(h1)
+    for stage in ("prep", "carry"):
+        gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], chunk=C, o=o2, ht=h2,
+                          workspace=ws, stage=stage)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
