@@ -18,9 +18,12 @@
 // With a single segment only step 3 runs, from h0.
 //
 // One workgroup owns a whole head (all dv columns) for its segment, so every byte of a
-// chunk record is fetched from memory once per head: the record is staged into LDS (two
-// buffers, the next chunk's copy in flight while the current one is used), and each wave
-// owns 16*CTW columns of the state for all dk rows.  A wave therefore computes every row
+// chunk record is fetched from memory once per head: the record is staged into LDS by
+// LDS-DMA loads (two buffers; the next chunk's copy is issued at the start of each step,
+// and since each wave picks its copy slots at run time the compiler makes the step's first
+// LDS read wait for that copy, so copy and compute take turns -- with many heads the pass
+// runs at the HBM rate regardless), and each wave owns 16*CTW columns of the state for
+// all dk rows.  A wave therefore computes every row
 // of U and O for its columns and needs no operand from another wave: the only workgroup
 // synchronisation is one barrier per chunk for the staged record.  Accumulator tiles of
 // S and U feed the B operands of the next products directly (reduction slots follow
@@ -128,7 +131,7 @@ __device__ __forceinline__ int seg_begin(int s, int NC, int NSEG) {
 // SUM = true : waves 0..3 carry S_loc (from zero, with v), waves 4..7 carry M (from the
 //              identity, without v); both are written to `xsum` at the segment's end.
 // The staged records fill most of the LDS, so one workgroup runs per CU (full pass: one wave
-// per SIMD; summary pass: two); telling the compiler so lets it keep many LDS reads in flight.
+// per SIMD; summary pass: two); the attribute states that occupancy to the compiler.
 template <typename TIn, int D, int C, bool SUM>
 __global__ __launch_bounds__(SUM ? 512 : 256) __attribute__((amdgpu_waves_per_eu(SUM ? 2 : 1, SUM ? 2 : 1)))
 void carry_wide_kernel(
@@ -196,7 +199,8 @@ void carry_wide_kernel(
 
     // Record staging: each wave copies its share of the copy list straight from memory into
     // the LDS buffer with LDS-DMA loads (16 bytes per lane, no registers); the copy of chunk
-    // n + 1 runs while chunk n is computed and is waited for (vmcnt) before the next barrier.
+    // n + 1 is issued at the start of chunk n's step and waited for (vmcnt) before the next
+    // barrier (the compiler also waits for it before the step's first LDS read).
     typedef __attribute__((address_space(3))) void lds_void;
     auto issue_rec = [&](int n, int buf) {
 #define GDR_LD(J)                                                                                  \
