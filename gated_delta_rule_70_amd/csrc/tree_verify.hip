@@ -24,8 +24,10 @@
 //      any depth below 64), then the decayed rows;
 //   2. Kt h0 and Qt h0 on the fp32 matrix cores (16x16x4), the right-hand side;
 //   3. A and P on the matrix cores, masked by ancestry;
-//   4. forward substitution level by level (nodes of equal depth are independent; a level
-//      of few nodes splits each ancestor sum over several threads);
+//   4. (I + A) U = rhs by 16-row blocks: each diagonal block (unit lower triangular, since
+//      node order is a topological order) is inverted in registers by forward substitution
+//      down its columns, then block I takes U_I = inv(D_I) (rhs_I - sum_{J<I} A_IJ U_J) on
+//      the matrix cores; the serial depth is the number of blocks, whatever the tree's depth;
 //   5. O = Qt h0 + P U on the matrix cores.
 // In the matrix-core products lane group g reduces over a contiguous quarter of the
 // reduction index (16-byte LDS reads); the order of a sum's terms is free as long as both
@@ -100,12 +102,6 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     __shared__ int sJ[TM];                                      // pointer-doubling jumps
     __shared__ unsigned long long sAnc[TM];
     __shared__ float sBeta[TM];
-    __shared__ int sDep[TM];
-    __shared__ int sCnt[TM];    // nodes per depth
-    __shared__ int sStart[TM];  // first slot of each depth in sList
-    __shared__ int sList[TM];   // nodes ordered by depth
-    __shared__ float sRed[256]; // partial ancestor sums of the substitution
-    __shared__ int sMaxDep;
 
     const int ncb = DV / CB;
     const int cb = blockIdx.x % ncb;
@@ -192,8 +188,6 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         sAnc[tid] = p >= 0 ? 1ull << p : 0ull;
         sBeta[tid] = bt;
     }
-    if (tid == 0) sMaxDep = 0;
-    if (tid < TM) sCnt[tid] = 0;
     auto raw4 = [&](const uint32_t (&r)[ELT]) {
         f32x4 x;
         if constexpr (ELT == 2) {
@@ -268,7 +262,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         // below 2^r needs r rounds): every thread sees the same answer and stops together
         if (!__syncthreads_or(jn >= 0)) break;
     }
-    // decayed rows; node depths
+    // decayed rows
 #pragma unroll
     for (int m = 0; m < NPASS; ++m) {
         const int t = tid / QPR + RPI * m;
@@ -288,32 +282,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         *reinterpret_cast<f32x4*>(sKh + i) = kb;
         *reinterpret_cast<f32x4*>(sQt + i) = qt;
     }
-    // Nodes listed by depth, in index order within a depth, by wave 0 alone: for each depth
-    // d a ballot of the nodes at d gives its count; a node's slot is the number of nodes at
-    // smaller depths plus those of its own depth with a smaller index.  The loop ends once
-    // every node is placed (the ballots make every bound wave-uniform).
-    if (wave == 0) {
-        const int dep = lane < T ? __builtin_popcountll(sAnc[lane]) : TM;
-        int pos = 0, cnt = 0, start = 0, placed = 0, maxd = 0;
-        for (int d = 0; d < TM && placed < T; ++d) {
-            const unsigned long long bal = __ballot(dep == d);
-            const int c = __popcll(bal);
-            if (lane == d) {
-                cnt = c;
-                start = placed;
-            }
-            if (d < dep) pos += c;
-            else if (d == dep) pos += __popcll(bal & ((1ull << lane) - 1ull));
-            if (c > 0) maxd = d;
-            placed += c;
-        }
-        sCnt[lane] = cnt;
-        sStart[lane] = start;
-        sDep[lane] = dep;
-        if (lane < T) sList[pos] = lane;
-        if (lane == 0) sMaxDep = maxd;
-    }
-    __syncthreads();  // decayed rows (read across threads below) and the depth lists complete
+    __syncthreads();  // decayed rows (read across threads below)
 
     // ---- 2. Kt h0, Qt h0 and the right-hand side beta (v - Kt h0) -------------------------
     // tile (I, N): rows 16I.., columns 16N.. of this block; wave w owns tiles w and w + 4 and
@@ -343,29 +312,35 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     // Only the NB(NB+1)/2 lower tiles of each hold products; they are dealt evenly to the
     // waves.  The upper tiles of P are zero-filled (the output product reads whole rows of
     // P); those of A are never read.
-    const int nlow = NB * (NB + 1) / 2;
+    const int nlow = NB * (NB + 1) / 2;  // <= 10 (NB <= 4)
     for (int job = wave; job < 2 * nlow; job += 4) {
-        const int x = job / nlow;
-        int t = job % nlow, I = 0;
-        while (t > I) {
-            t -= I + 1;
-            ++I;
-        }
-        const int J = t;
+        const int x = job >= nlow;  // 0: A, 1: P
+        const int t = job - x * nlow;
+        const int I = (t >= 1) + (t >= 3) + (t >= 6);  // lower tile t = I (I + 1) / 2 + J
+        const int J = t - I * (I + 1) / 2;
         float* dst = x == 0 ? sA : sP;
         const int cq = gq * (DK / 4);
-        const f32x4 acc = tile_dot4<DK>((x == 0 ? sKt : sQt) + (16 * I + li) * KP + cq,
-                                        sKh + (16 * J + li) * KP + cq);
         const int s = 16 * J + li;
+        // the rows' ancestor masks and betas are read before the products, so their LDS
+        // round trips overlap the matrix-core work
+        unsigned long long am[4];
+        float bt[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * I + 4 * gq + i;
-            float val = 0.f;
-            if (r < T && s < T) {
-                const bool anc = (sAnc[r] >> s) & 1ull;
-                if (x == 0) val = anc ? sBeta[r] * acc[i] : 0.f;
-                else val = (anc || s == r) ? acc[i] : 0.f;
-            }
+            am[i] = sAnc[r];
+            bt[i] = sBeta[r];
+        }
+        const f32x4 acc = tile_dot4<DK>((x == 0 ? sKt : sQt) + (16 * I + li) * KP + cq,
+                                        sKh + (16 * J + li) * KP + cq);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * I + 4 * gq + i;
+            const bool anc = (am[i] >> s) & 1ull;
+            float val;
+            if (x == 0) val = anc ? bt[i] * acc[i] : 0.f;
+            else val = (anc || s == r) ? acc[i] : 0.f;
+            if (r >= T || s >= T) val = 0.f;
             dst[r * AP + s] = val;
         }
     }
@@ -376,54 +351,56 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         }
     __syncthreads();
 
-    // ---- 4. forward substitution, one depth level at a time --------------------------------
-    // U_r = rhs_r - sum_{s ancestor of r} A_rs U_s; every ancestor is shallower than r, so
-    // the nodes of one level read only rows finished in earlier levels.  A level with few
-    // nodes (a deep, narrow tree) splits each ancestor sum over ns threads, which leave
-    // partial sums that one thread then combines in a fixed order.
-    const int maxdep = sMaxDep;
-    for (int L = 1; L <= maxdep; ++L) {
-        const int base = sStart[L];
-        const int cols = sCnt[L] * CB;  // (node, column) pairs of this level
-        // ns threads per pair (a power of two); part p takes the ancestors s = p mod ns
-        const int ns = cols <= 32 ? 8 : cols <= 64 ? 4 : cols <= 128 ? 2 : 1;
-        if (ns > 1) {
-            float part = 0.f;
-            if (tid < cols * ns) {
-                const int rc = tid / ns, pid = tid % ns;
-                const int r = sList[base + rc / CB], j = rc % CB;
-                const unsigned long long sel = ns == 8 ? 0x0101010101010101ull
-                                             : ns == 4 ? 0x1111111111111111ull : 0x5555555555555555ull;
-                unsigned long long m = sAnc[r] & (sel << pid);
-                while (m) {
-                    const int s = __builtin_ctzll(m);
-                    m &= m - 1;
-                    part += sA[r * AP + s] * sU[s * UP + j];
+    // ---- 4. (I + A) U = rhs by 16-row blocks ----------------------------------------------
+    // A_rs is nonzero only for s an ancestor of r, so s < r: I + A is unit lower triangular
+    // and so is each diagonal block D_I.  Waves 0 and 1 (column tiles 0 and 1 of U) each
+    // invert every diagonal block into a private LDS copy (sKt or sKh, both free now), so
+    // no barrier separates the inversion from its use; lane (block gq, column li) runs
+    // forward substitution down column li of inv(D_gq) in registers.  Then block by block
+    //   U_I = inv(D_I) (rhs_I - sum_{J<I} A_IJ U_J)
+    // with both products on the matrix cores; a wave reads only the U columns it wrote.
+    constexpr int DIP = 20;            // inverse row pitch: 16-byte reads of 16 rows, no conflict
+    constexpr int DIB = 16 * DIP + 16; // inverse block stride
+    static_assert(4 * DIB <= TM * KP, "block inverses must fit the free key rows");
+    if (wave < 2) {
+        float* sDi = wave == 0 ? sKt : sKh;
+        if (gq < NB) {
+            const float* ab = sA + 16 * gq * AP + 16 * gq;  // diagonal block gq
+            float xc[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = r == li ? 1.f : 0.f;
+#pragma unroll
+                for (int q4 = 0; q4 < (r + 3) / 4; ++q4) {
+                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(ab + r * AP + 4 * q4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * q4 + e < r) acc -= a4[e] * xc[4 * q4 + e];
                 }
+                xc[r] = acc;
             }
-            sRed[tid] = part;
-            __syncthreads();
-            if (tid < cols) {
-                const int r = sList[base + tid / CB], j = tid % CB;
-                float acc = sU[r * UP + j];
-                for (int p = 0; p < ns; ++p) acc -= sRed[tid * ns + p];
-                sU[r * UP + j] = acc;
-            }
-        } else {
-            for (int item = tid; item < cols; item += 256) {
-                const int r = sList[base + item / CB], j = item % CB;
-                unsigned long long m = sAnc[r];
-                float acc = sU[r * UP + j];
-                while (m) {
-                    const int s = __builtin_ctzll(m);
-                    m &= m - 1;
-                    acc -= sA[r * AP + s] * sU[s * UP + j];
-                }
-                sU[r * UP + j] = acc;
-            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sDi[gq * DIB + r * DIP + li] = xc[r];
         }
-        __syncthreads();
+        const int N = wave;
+        for (int I = 0; I < NB; ++I) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const float* ap = sA + (16 * I + li) * AP + gq;
+            const float* up = sU + gq * UP + 16 * N + li;
+            for (int s = 0; s < 16 * I; s += 4) acc = mfma4(ap[s], up[s * UP], acc);
+            f32x4 rr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rr[i] = sU[(16 * I + 4 * gq + i) * UP + 16 * N + li] - acc[i];
+            // step i pairs reduction slot gq with row 4 gq + i of the accumulator layout
+            const f32x4 di = *reinterpret_cast<const f32x4*>(sDi + I * DIB + li * DIP + 4 * gq);
+            f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) u = mfma4(di[i], rr[i], u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sU[(16 * I + 4 * gq + i) * UP + 16 * N + li] = u[i];
+        }
     }
+    __syncthreads();
 
     // ---- 5. O = Qt h0 + P U ----------------------------------------------------------------
 #pragma unroll
