@@ -102,6 +102,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     __shared__ int sJ[TM];                                      // pointer-doubling jumps
     __shared__ unsigned long long sAnc[TM];
     __shared__ float sBeta[TM];
+    __shared__ int sMore[2];  // round flags of the pointer doubling
 
     const int ncb = DV / CB;
     const int cb = blockIdx.x % ncb;
@@ -119,74 +120,123 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int col0 = cb * CB;
 
     // ---- 0. global reads, all requested before any is used --------------------------------
+    // Issued in the order they are needed: parents and beta, then g (the decay prefixes need
+    // only these), then k, q, the v tile and the h0 columns, which stay in flight through
+    // the pointer doubling (its barriers wait for LDS traffic only).  Every thread issues
+    // the same straight-line loads (rows past the tree read row T - 1 and are zeroed), so
+    // each use waits for exactly the loads issued before its own.
+    const int tp = min(lane, T - 1);
+    const int par = parent[(size_t)b * T + tp];
+    const float bta = beta[((size_t)b * T + tp) * HV + h];
     // g/k/q: thread t covers 4 channels of rows t / (DK/4) + (256 / (DK/4)) * m
     constexpr int QPR = DK / 4;            // 4-channel groups per row
     constexpr int RPI = 256 / QPR;         // rows per pass
     constexpr int NPASS = TM / RPI;
     const int c4 = 4 * (tid % QPR);
     f32x4 gv[NPASS];
+#pragma unroll
+    for (int m = 0; m < NPASS; ++m) {
+        const int t = min(tid / QPR + RPI * m, T - 1);
+        gv[m] = load_g4(g, (((size_t)b * T + t) * HV + h) * DK + c4);
+    }
     uint32_t kraw[NPASS][ELT], qraw[NPASS][ELT];
 #pragma unroll
     for (int m = 0; m < NPASS; ++m) {
-        const int t = tid / QPR + RPI * m;
-        gv[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int e = 0; e < ELT; ++e) kraw[m][e] = qraw[m][e] = 0u;
-        if (t < T) {
-            gv[m] = load_g4(g, (((size_t)b * T + t) * HV + h) * DK + c4);
-            const size_t kq = (((size_t)b * T + t) * HK + kh) * DK + c4;
-            if constexpr (ELT == 2) {
-                const uint2 kk = *reinterpret_cast<const uint2*>(k + kq);
-                const uint2 qq = *reinterpret_cast<const uint2*>(q + kq);
-                kraw[m][0] = kk.x; kraw[m][1] = kk.y;
-                qraw[m][0] = qq.x; qraw[m][1] = qq.y;
-            } else {
-                const uint4 kk = *reinterpret_cast<const uint4*>(k + kq);
-                const uint4 qq = *reinterpret_cast<const uint4*>(q + kq);
-                kraw[m][0] = kk.x; kraw[m][1] = kk.y; kraw[m][2] = kk.z; kraw[m][3] = kk.w;
-                qraw[m][0] = qq.x; qraw[m][1] = qq.y; qraw[m][2] = qq.z; qraw[m][3] = qq.w;
-            }
+        const int t = min(tid / QPR + RPI * m, T - 1);
+        const size_t kq = (((size_t)b * T + t) * HK + kh) * DK + c4;
+        if constexpr (ELT == 2) {
+            const uint2 kk = *reinterpret_cast<const uint2*>(k + kq);
+            const uint2 qq = *reinterpret_cast<const uint2*>(q + kq);
+            kraw[m][0] = kk.x; kraw[m][1] = kk.y;
+            qraw[m][0] = qq.x; qraw[m][1] = qq.y;
+        } else {
+            const uint4 kk = *reinterpret_cast<const uint4*>(k + kq);
+            const uint4 qq = *reinterpret_cast<const uint4*>(q + kq);
+            kraw[m][0] = kk.x; kraw[m][1] = kk.y; kraw[m][2] = kk.z; kraw[m][3] = kk.w;
+            qraw[m][0] = qq.x; qraw[m][1] = qq.y; qraw[m][2] = qq.z; qraw[m][3] = qq.w;
         }
-    }
-    // h0 columns col0 .. col0+31: thread covers row c = tid / 8 + 32 m, 4 columns
-    constexpr int HPASS = DK / 32;
-    f32x4 hv[HPASS];
-#pragma unroll
-    for (int m = 0; m < HPASS; ++m) {
-        hv[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (h0 != nullptr)
-            hv[m] = *reinterpret_cast<const f32x4*>(h0 + ((size_t)bh * DK + tid / 8 + 32 * m) * DV +
-                                                    col0 + 4 * (tid % 8));
     }
     // v rows: thread covers node t = tid / 8 + 32 m, 4 columns
     uint32_t vraw[2][ELT];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-        const int t = tid / 8 + 32 * m;
-#pragma unroll
-        for (int e = 0; e < ELT; ++e) vraw[m][e] = 0u;
-        if (t < T) {
-            const size_t vo = (((size_t)b * T + t) * HV + h) * DV + col0 + 4 * (tid % 8);
-            if constexpr (ELT == 2) {
-                const uint2 x = *reinterpret_cast<const uint2*>(v + vo);
-                vraw[m][0] = x.x; vraw[m][1] = x.y;
-            } else {
-                const uint4 x = *reinterpret_cast<const uint4*>(v + vo);
-                vraw[m][0] = x.x; vraw[m][1] = x.y; vraw[m][2] = x.z; vraw[m][3] = x.w;
-            }
+        const int t = min(tid / 8 + 32 * m, T - 1);
+        const size_t vo = (((size_t)b * T + t) * HV + h) * DV + col0 + 4 * (tid % 8);
+        if constexpr (ELT == 2) {
+            const uint2 x = *reinterpret_cast<const uint2*>(v + vo);
+            vraw[m][0] = x.x; vraw[m][1] = x.y;
+        } else {
+            const uint4 x = *reinterpret_cast<const uint4*>(v + vo);
+            vraw[m][0] = x.x; vraw[m][1] = x.y; vraw[m][2] = x.z; vraw[m][3] = x.w;
         }
     }
+    // h0 columns col0 .. col0+31: thread covers row c = tid / 8 + 32 m, 4 columns.  Buffer
+    // loads over this head's state, of range 0 without h0 (they then read zeros), so the
+    // loads are issued unconditionally.
+    constexpr int HPASS = DK / 32;
+    const rsrc_t rs_h0 = make_rsrc(h0 != nullptr ? h0 + (size_t)bh * DK * DV : nullptr,
+                                   h0 != nullptr ? (uint32_t)(DK * DV * 4) : 0u);
+    f32x4 hv[HPASS];
+#pragma unroll
+    for (int m = 0; m < HPASS; ++m)
+        hv[m] = buf_load_f32x4(rs_h0, ((tid / 8 + 32 * m) * DV + col0 + 4 * (tid % 8)) * 4, 0);
     if (tid < TM) {
-        int p = -1;
-        float bt = 0.f;
-        if (tid < T) {
-            p = parent[(size_t)b * T + tid];
-            if (p < -1 || p >= tid) p = -1;  // not an earlier node: a child of the initial state
-            bt = beta[((size_t)b * T + tid) * HV + h];
-        }
+        int p = tid < T ? par : -1;
+        if (p < -1 || p >= tid) p = -1;  // not an earlier node: a child of the initial state
         sJ[tid] = p;
         sAnc[tid] = p >= 0 ? 1ull << p : 0ull;
-        sBeta[tid] = bt;
+        sBeta[tid] = tid < T ? bta : 0.f;
+    }
+    if (tid == 0) sMore[0] = 0;
+#pragma unroll
+    for (int m = 0; m < NPASS; ++m) {
+        const int t = tid / QPR + RPI * m;
+        if (t >= T) gv[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(sKt + t * KP + c4) = gv[m];
+    }
+    lds_barrier();
+
+    // ---- 1. decay prefixes and ancestors by pointer doubling ------------------------------
+    // After round r, gam_t sums g over the 2^r nearest nodes of t's root path (t included)
+    // and J_t is the node 2^r steps up (-1 past the root).  Each round reads, synchronises,
+    // then writes, so every read sees the previous round.  A thread's own prefixes stay in
+    // gv (only it writes them).
+#pragma unroll 1
+    for (int round = 0; round < 6; ++round) {
+        f32x4 add[NPASS];
+#pragma unroll
+        for (int m = 0; m < NPASS; ++m) {
+            const int t = tid / QPR + RPI * m;
+            const int j = sJ[t];
+            add[m] = j >= 0 ? *reinterpret_cast<const f32x4*>(sKt + j * KP + c4)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        int jn = -1;
+        unsigned long long an = 0;
+        if (tid < TM) {
+            const int j = sJ[tid];
+            jn = j >= 0 ? sJ[j] : -1;
+            an = sAnc[tid] | (j >= 0 ? sAnc[j] : 0ull);
+        }
+        lds_barrier();
+#pragma unroll
+        for (int m = 0; m < NPASS; ++m) {
+            const int t = tid / QPR + RPI * m;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gv[m][e] += add[m][e];
+            *reinterpret_cast<f32x4*>(sKt + t * KP + c4) = gv[m];
+        }
+        if (tid < TM) {
+            sJ[tid] = jn;
+            sAnc[tid] = an;
+        }
+        // once no node has a jump left the prefixes and masks are final (a tree of depth
+        // below 2^r needs r rounds); the flag of round r is cleared in round r - 1 and read
+        // after this round's last barrier, so every thread takes the same exit
+        if (jn >= 0) sMore[round & 1] = 1;
+        if (tid == 0) sMore[(round + 1) & 1] = 0;
+        lds_barrier();
+        if (__builtin_amdgcn_readfirstlane(sMore[round & 1]) == 0) break;
     }
     auto raw4 = [&](const uint32_t (&r)[ELT]) {
         f32x4 x;
@@ -199,90 +249,40 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         }
         return x;
     };
-#pragma unroll
-    for (int m = 0; m < NPASS; ++m) {
-        const int t = tid / QPR + RPI * m;
-        *reinterpret_cast<f32x4*>(sKt + t * KP + c4) = gv[m];
-        *reinterpret_cast<f32x4*>(sKh + t * KP + c4) = raw4(kraw[m]);
-        *reinterpret_cast<f32x4*>(sQt + t * KP + c4) = raw4(qraw[m]);
-    }
-#pragma unroll
-    for (int m = 0; m < HPASS; ++m) {  // transposed: sA[j * HP + c]
-        const int c = tid / 8 + 32 * m;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sA[(4 * (tid % 8) + e) * HP + c] = hv[m][e];
-    }
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {  // transposed: sP[j * (TM + 4) + t]
-        const int t = tid / 8 + 32 * m;
-        const f32x4 x = raw4(vraw[m]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sP[(4 * (tid % 8) + e) * (TM + 4) + t] = x[e];
-    }
-    __syncthreads();
-
-    // ---- 1. decay prefixes and ancestors by pointer doubling ------------------------------
-    // After round r, gam_t sums g over the 2^r nearest nodes of t's root path (t included)
-    // and J_t is the node 2^r steps up (-1 past the root).  Each round reads, synchronises,
-    // then writes, so every read sees the previous round.
-#pragma unroll 1
-    for (int round = 0; round < 6; ++round) {
-        float add[NPASS][4];
-#pragma unroll
-        for (int m = 0; m < NPASS; ++m) {
-            const int t = tid / QPR + RPI * m;
-            const int j = sJ[t];
-            const f32x4 x = j >= 0 ? *reinterpret_cast<const f32x4*>(sKt + j * KP + c4)
-                                   : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) add[m][e] = x[e];
-        }
-        int jn = -1;
-        unsigned long long an = 0;
-        if (tid < TM) {
-            const int j = sJ[tid];
-            jn = j >= 0 ? sJ[j] : -1;
-            an = sAnc[tid] | (j >= 0 ? sAnc[j] : 0ull);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < NPASS; ++m) {
-            const int t = tid / QPR + RPI * m;
-            f32x4* p = reinterpret_cast<f32x4*>(sKt + t * KP + c4);
-            f32x4 x = *p;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] += add[m][e];
-            *p = x;
-        }
-        if (tid < TM) {
-            sJ[tid] = jn;
-            sAnc[tid] = an;
-        }
-        // once no node has a jump left the prefixes and masks are final (a tree of depth
-        // below 2^r needs r rounds): every thread sees the same answer and stops together
-        if (!__syncthreads_or(jn >= 0)) break;
-    }
-    // decayed rows
+    // decayed rows, from the prefixes and the k and q rows still in registers
 #pragma unroll
     for (int m = 0; m < NPASS; ++m) {
         const int t = tid / QPR + RPI * m;
         const int i = t * KP + c4;
-        const f32x4 gm = *reinterpret_cast<const f32x4*>(sKt + i);
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(sKh + i);
-        const f32x4 qv = *reinterpret_cast<const f32x4*>(sQt + i);
+        const f32x4 kv = raw4(kraw[m]);
+        const f32x4 qv = raw4(qraw[m]);
         f32x4 kt, kb, qt;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float ep = __expf(gm[e]);
-            kt[e] = ep * kv[e];
-            kb[e] = __expf(-gm[e]) * kv[e];
-            qt[e] = ep * qv[e];
+            const float ep = __expf(gv[m][e]);
+            kt[e] = t < T ? ep * kv[e] : 0.f;
+            kb[e] = t < T ? __expf(-gv[m][e]) * kv[e] : 0.f;
+            qt[e] = t < T ? ep * qv[e] : 0.f;
         }
         *reinterpret_cast<f32x4*>(sKt + i) = kt;
         *reinterpret_cast<f32x4*>(sKh + i) = kb;
         *reinterpret_cast<f32x4*>(sQt + i) = qt;
     }
-    __syncthreads();  // decayed rows (read across threads below)
+    // h0 columns and the v tile, transposed
+#pragma unroll
+    for (int m = 0; m < HPASS; ++m) {  // sA[j * HP + c]
+        const int c = tid / 8 + 32 * m;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sA[(4 * (tid % 8) + e) * HP + c] = hv[m][e];
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {  // sP[j * (TM + 4) + t]
+        const int t = tid / 8 + 32 * m;
+        const f32x4 x = raw4(vraw[m]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sP[(4 * (tid % 8) + e) * (TM + 4) + t] = t < T ? x[e] : 0.f;
+    }
+    __syncthreads();  // decayed rows, h0 columns and v tile (read across threads below)
 
     // ---- 2. Kt h0, Qt h0 and the right-hand side beta (v - Kt h0) -------------------------
     // tile (I, N): rows 16I.., columns 16N.. of this block; wave w owns tiles w and w + 4 and
