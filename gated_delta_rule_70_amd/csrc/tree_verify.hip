@@ -21,17 +21,17 @@
 //   0. all global reads issued at once (parents, beta, g, k, q rows, the block's columns
 //      of h0 and v);
 //   1. root-path decay prefixes and ancestor masks by pointer doubling (6 rounds cover
-//      any depth below 64), then the decayed rows;
-//   2. Kt h0 and Qt h0 on the fp32 matrix cores (16x16x4), the right-hand side;
-//   3. A and P on the matrix cores, masked by ancestry;
+//      any depth below 64), then the decayed rows, kept as bf16 high/low pairs;
+//   2. Kt h0 and Qt h0 (three bf16 matrix-core products per tile on the split operands,
+//      fp32 accumulation), the right-hand side;
+//   3. A and P the same way, masked by ancestry;
 //   4. (I + A) U = rhs by 16-row blocks: each diagonal block (unit lower triangular, since
 //      node order is a topological order) is inverted in registers by forward substitution
 //      down its columns, then block I takes U_I = inv(D_I) (rhs_I - sum_{J<I} A_IJ U_J) on
 //      the matrix cores; the serial depth is the number of blocks, whatever the tree's depth;
-//   5. O = Qt h0 + P U on the matrix cores.
-// In the matrix-core products lane group g reduces over a contiguous quarter of the
-// reduction index (16-byte LDS reads); the order of a sum's terms is free as long as both
-// operands use the same one.
+//   5. O = Qt h0 + P U on the fp32 matrix cores.
+// The solve and everything after it run in fp32; the split products of phases 2 and 3 keep
+// each product within ~3 * 2^-16 of the fp32 one.
 #include "gdr_device.h"
 #include "gdr_launch.h"
 
@@ -47,39 +47,45 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// tile_dot with every operand read issued first and the reduction split over four
-// accumulators (four independent chains of matrix-core operations), summed at the end.
-template <int K>
-__device__ __forceinline__ f32x4 tile_dot4(const float* xa, const float* yb) {
-    constexpr int N = K / 16;  // 16-byte reads per operand and lane
-    f32x4 xs[N], ys[N];
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Split of four fp32 values into bf16 high parts and bf16 remainders (round to nearest even
+// on both): x = hi + lo to 2^-16 relative.
+__device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        xs[i] = *reinterpret_cast<const f32x4*>(xa + 4 * i);
-        ys[i] = *reinterpret_cast<const f32x4*>(yb + 4 * i);
+    for (int e = 0; e < 4; ++e) {
+        __bf16 h, l;
+        split_bf16(x[e], h, l);
+        hi[e] = h;
+        lo[e] = l;
     }
-    f32x4 acc[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i & 3] = mfma4(xs[i][e], ys[i][e], acc[i & 3]);
-    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
-// sum over a K-long reduction of X[rowA][.] * Y[rowB][.] for a 16x16 tile: lane (i, g)
-// reads K/4 contiguous floats of row i of each operand, starting at g*K/4
+// sum over a K-long reduction of X[rowA][.] * Y[rowB][.] for a 16x16 tile, both operands
+// held as bf16 high/low pairs (each low part `xlo` / `ylo` elements after its high part),
+// as three bf16 matrix-core products hi*hi + hi*lo + lo*hi with fp32 accumulation: the
+// split and the dropped lo*lo term leave each product within ~3 * 2^-16 of the exact one.
+// Lane (i, g) reads 8 consecutive slots at 32 s + 8 g of row i of X and of Y (xa, yb point
+// at slot 8 g); D rows 4g .. 4g+3 of column i.  Every operand read is issued first.
 template <int K>
-__device__ __forceinline__ f32x4 tile_dot(const float* xa, const float* yb, f32x4 acc) {
+__device__ __forceinline__ f32x4 tile_dot_split(const __bf16* xa, int xlo, const __bf16* yb, int ylo) {
+    constexpr int NS = K / 32;
+    bf16x8 xh[NS], xl[NS], yh[NS], yl[NS];
 #pragma unroll
-    for (int c = 0; c < K / 4; c += 4) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(xa + c);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(yb + c);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc = mfma4(a[e], b[e], acc);
+    for (int st = 0; st < NS; ++st) {
+        xh[st] = *reinterpret_cast<const bf16x8*>(xa + 32 * st);
+        yh[st] = *reinterpret_cast<const bf16x8*>(yb + 32 * st);
+        xl[st] = *reinterpret_cast<const bf16x8*>(xa + xlo + 32 * st);
+        yl[st] = *reinterpret_cast<const bf16x8*>(yb + ylo + 32 * st);
     }
-    return acc;
+    f32x4 hh = {0.f, 0.f, 0.f, 0.f}, hl = hh, lh = hh;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        hh = mfma_bf16(xh[st], yh[st], hh);
+        hl = mfma_bf16(xh[st], yl[st], hl);
+        lh = mfma_bf16(xl[st], yh[st], lh);
+    }
+    return hh + (hl + lh);
 }
 
 template <typename TIn, typename TG, int DK>
@@ -87,16 +93,21 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int32_t* __restrict__ parent, const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const TG* __restrict__ g, const float* __restrict__ beta,
     const float* __restrict__ h0, float* __restrict__ o, int T, int HK, int HV, int DV) {
-    constexpr int KP = DK + 4;   // row pitch (floats): 16 rows read at one offset hit 16 banks
+    constexpr int KP = DK + 4;   // row pitch (floats) of the fp32 decay prefixes
     constexpr int AP = TM + 4;
     constexpr int UP = CB + 4;
-    constexpr int HP = DK + 4;   // transposed h0 / v columns
+    constexpr int BP = DK + 8;   // bf16 row pitch: 16-byte reads of 16 rows hit distinct banks
     constexpr int ELT = sizeof(TIn);
-    static_assert(CB * HP <= TM * AP && CB * (TM + 4) <= TM * AP, "staging must fit A and P");
-    __shared__ __attribute__((aligned(16))) float sKt[TM * KP];  // gam, then exp(gam) k
-    __shared__ __attribute__((aligned(16))) float sKh[TM * KP];  // k, then exp(-gam) k
-    __shared__ __attribute__((aligned(16))) float sQt[TM * KP];  // q, then exp(gam) q
-    __shared__ __attribute__((aligned(16))) float sA[TM * AP];   // h0 columns [j][c], then A
+    constexpr int LO = TM * BP;  // offset of the low parts in a split row array
+    static_assert(2 * CB * BP * 2 <= TM * AP * 4 && CB * (TM + 4) <= TM * AP,
+                  "staging must fit A and P");
+    static_assert(TM * KP * 4 <= 2 * TM * BP * 2, "the decay prefixes must fit a split row array");
+    // decayed rows as bf16 high parts [TM][BP] followed by low parts [TM][BP]
+    __shared__ __attribute__((aligned(16))) __bf16 sKt[2 * TM * BP];  // exp(gam) k
+    __shared__ __attribute__((aligned(16))) __bf16 sKh[2 * TM * BP];  // exp(-gam) k
+    __shared__ __attribute__((aligned(16))) __bf16 sQt[2 * TM * BP];  // exp(gam) q
+    float* sG = reinterpret_cast<float*>(sKt);  // fp32 decay prefixes [TM][KP] until then
+    __shared__ __attribute__((aligned(16))) float sA[TM * AP];   // split h0 columns [j][c], then A
     __shared__ __attribute__((aligned(16))) float sP[TM * AP];   // v columns [j][t], then P
     __shared__ __attribute__((aligned(16))) float sU[TM * UP];   // right-hand side, then U
     __shared__ int sJ[TM];                                      // pointer-doubling jumps
@@ -192,7 +203,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     for (int m = 0; m < NPASS; ++m) {
         const int t = tid / QPR + RPI * m;
         if (t >= T) gv[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f32x4*>(sKt + t * KP + c4) = gv[m];
+        *reinterpret_cast<f32x4*>(sG + t * KP + c4) = gv[m];
     }
     lds_barrier();
 
@@ -208,7 +219,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         for (int m = 0; m < NPASS; ++m) {
             const int t = tid / QPR + RPI * m;
             const int j = sJ[t];
-            add[m] = j >= 0 ? *reinterpret_cast<const f32x4*>(sKt + j * KP + c4)
+            add[m] = j >= 0 ? *reinterpret_cast<const f32x4*>(sG + j * KP + c4)
                             : f32x4{0.f, 0.f, 0.f, 0.f};
         }
         int jn = -1;
@@ -224,7 +235,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
             const int t = tid / QPR + RPI * m;
 #pragma unroll
             for (int e = 0; e < 4; ++e) gv[m][e] += add[m][e];
-            *reinterpret_cast<f32x4*>(sKt + t * KP + c4) = gv[m];
+            *reinterpret_cast<f32x4*>(sG + t * KP + c4) = gv[m];
         }
         if (tid < TM) {
             sJ[tid] = jn;
@@ -249,11 +260,13 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         }
         return x;
     };
-    // decayed rows, from the prefixes and the k and q rows still in registers
+    // decayed rows, from the prefixes and the k and q rows still in registers, stored as
+    // bf16 high/low pairs (the prefixes' LDS copy is dead: the last round read it before its
+    // barriers)
 #pragma unroll
     for (int m = 0; m < NPASS; ++m) {
         const int t = tid / QPR + RPI * m;
-        const int i = t * KP + c4;
+        const int i = t * BP + c4;
         const f32x4 kv = raw4(kraw[m]);
         const f32x4 qv = raw4(qraw[m]);
         f32x4 kt, kb, qt;
@@ -264,16 +277,30 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
             kb[e] = t < T ? __expf(-gv[m][e]) * kv[e] : 0.f;
             qt[e] = t < T ? ep * qv[e] : 0.f;
         }
-        *reinterpret_cast<f32x4*>(sKt + i) = kt;
-        *reinterpret_cast<f32x4*>(sKh + i) = kb;
-        *reinterpret_cast<f32x4*>(sQt + i) = qt;
+        bf16x4 hi, lo;
+        split4(kt, hi, lo);
+        *reinterpret_cast<bf16x4*>(sKt + i) = hi;
+        *reinterpret_cast<bf16x4*>(sKt + LO + i) = lo;
+        split4(kb, hi, lo);
+        *reinterpret_cast<bf16x4*>(sKh + i) = hi;
+        *reinterpret_cast<bf16x4*>(sKh + LO + i) = lo;
+        split4(qt, hi, lo);
+        *reinterpret_cast<bf16x4*>(sQt + i) = hi;
+        *reinterpret_cast<bf16x4*>(sQt + LO + i) = lo;
     }
-    // h0 columns and the v tile, transposed
+    // h0 columns (transposed, bf16 high/low pairs: high [CB][BP] then low [CB][BP], in sA's
+    // memory) and the v tile (transposed, fp32, in sP's)
+    __bf16* sH = reinterpret_cast<__bf16*>(sA);
 #pragma unroll
-    for (int m = 0; m < HPASS; ++m) {  // sA[j * HP + c]
+    for (int m = 0; m < HPASS; ++m) {  // sH[j * BP + c]
         const int c = tid / 8 + 32 * m;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sA[(4 * (tid % 8) + e) * HP + c] = hv[m][e];
+        for (int e = 0; e < 4; ++e) {
+            __bf16 h, l;
+            split_bf16(hv[m][e], h, l);
+            sH[(4 * (tid % 8) + e) * BP + c] = h;
+            sH[CB * BP + (4 * (tid % 8) + e) * BP + c] = l;
+        }
     }
 #pragma unroll
     for (int m = 0; m < 2; ++m) {  // sP[j * (TM + 4) + t]
@@ -294,10 +321,10 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         f32x4 kacc = {0.f, 0.f, 0.f, 0.f}, qacc = {0.f, 0.f, 0.f, 0.f};
         if (tile < 2 * NB) {
             const int I = tile >> 1, N = tile & 1;
-            const int cq = gq * (DK / 4);
-            const float* hb = sA + (16 * N + li) * HP + cq;
-            kacc = tile_dot<DK>(sKt + (16 * I + li) * KP + cq, hb, kacc);
-            qacc = tile_dot<DK>(sQt + (16 * I + li) * KP + cq, hb, qacc);
+            const int cq = 8 * gq;
+            const __bf16* hb = sH + (16 * N + li) * BP + cq;
+            kacc = tile_dot_split<DK>(sKt + (16 * I + li) * BP + cq, LO, hb, CB * BP);
+            qacc = tile_dot_split<DK>(sQt + (16 * I + li) * BP + cq, LO, hb, CB * BP);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * I + 4 * gq + i;
@@ -319,7 +346,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         const int I = (t >= 1) + (t >= 3) + (t >= 6);  // lower tile t = I (I + 1) / 2 + J
         const int J = t - I * (I + 1) / 2;
         float* dst = x == 0 ? sA : sP;
-        const int cq = gq * (DK / 4);
+        const int cq = 8 * gq;
         const int s = 16 * J + li;
         // the rows' ancestor masks and betas are read before the products, so their LDS
         // round trips overlap the matrix-core work
@@ -331,8 +358,8 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
             am[i] = sAnc[r];
             bt[i] = sBeta[r];
         }
-        const f32x4 acc = tile_dot4<DK>((x == 0 ? sKt : sQt) + (16 * I + li) * KP + cq,
-                                        sKh + (16 * J + li) * KP + cq);
+        const f32x4 acc = tile_dot_split<DK>((x == 0 ? sKt : sQt) + (16 * I + li) * BP + cq, LO,
+                                             sKh + (16 * J + li) * BP + cq, LO);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * I + 4 * gq + i;
@@ -361,9 +388,9 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     // with both products on the matrix cores; a wave reads only the U columns it wrote.
     constexpr int DIP = 20;            // inverse row pitch: 16-byte reads of 16 rows, no conflict
     constexpr int DIB = 16 * DIP + 16; // inverse block stride
-    static_assert(4 * DIB <= TM * KP, "block inverses must fit the free key rows");
+    static_assert(4 * DIB * 4 <= 2 * TM * BP * 2, "block inverses must fit the free key rows");
     if (wave < 2) {
-        float* sDi = wave == 0 ? sKt : sKh;
+        float* sDi = reinterpret_cast<float*>(wave == 0 ? sKt : sKh);
         if (gq < NB) {
             const float* ab = sA + 16 * gq * AP + 16 * gq;  // diagonal block gq
             float xc[16];
