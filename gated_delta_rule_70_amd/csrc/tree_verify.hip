@@ -88,6 +88,23 @@ __device__ __forceinline__ f32x4 tile_dot_split(const __bf16* xa, int xlo, const
     return hh + (hl + lh);
 }
 
+// acc + X[16 rows][0 .. 4L) Y[0 .. 4L)[16 columns] for one 16x16 tile in fp32 (16x16x4
+// products), lane group g taking the contiguous reduction range gL .. gL + L - 1: xa points
+// at element gL of row i (16-byte aligned), yb at row gL of column i, Y's rows ys apart.
+// Every read is issued before the products.
+template <int L>
+__device__ __forceinline__ f32x4 tile_rows_cols(const float* xa, const float* yb, int ys, f32x4 acc) {
+    f32x4 xv[L / 4];
+    float yv[L];
+#pragma unroll
+    for (int i = 0; i < L / 4; ++i) xv[i] = *reinterpret_cast<const f32x4*>(xa + 4 * i);
+#pragma unroll
+    for (int k = 0; k < L; ++k) yv[k] = yb[k * ys];
+#pragma unroll
+    for (int k = 0; k < L; ++k) acc = mfma4(xv[k / 4][k % 4], yv[k], acc);
+    return acc;
+}
+
 template <typename TIn, typename TG, int DK>
 __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int32_t* __restrict__ parent, const TIn* __restrict__ q, const TIn* __restrict__ k,
@@ -337,8 +354,8 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 
     // ---- 3. A and P tiles, masked by ancestry (upper tiles are zero) -----------------------
     // Only the NB(NB+1)/2 lower tiles of each hold products; they are dealt evenly to the
-    // waves.  The upper tiles of P are zero-filled (the output product reads whole rows of
-    // P); those of A are never read.
+    // waves.  The upper tiles are never read (the solve and the output product reduce over
+    // the lower ones only).
     const int nlow = NB * (NB + 1) / 2;  // <= 10 (NB <= 4)
     for (int job = wave; job < 2 * nlow; job += 4) {
         const int x = job >= nlow;  // 0: A, 1: P
@@ -371,11 +388,6 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
             dst[r * AP + s] = val;
         }
     }
-    for (int I = 0; I + 1 < NB; ++I)  // P's upper tiles: zeros (a row segment per thread)
-        for (int e = tid; e < 16 * 16 * (NB - 1 - I); e += 256) {
-            const int row = e / (16 * (NB - 1 - I)), c = e % (16 * (NB - 1 - I));
-            sP[(16 * I + row) * AP + 16 * (I + 1) + c] = 0.f;
-        }
     __syncthreads();
 
     // ---- 4. (I + A) U = rhs by 16-row blocks ----------------------------------------------
@@ -411,15 +423,21 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         }
         const int N = wave;
         for (int I = 0; I < NB; ++I) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const float* ap = sA + (16 * I + li) * AP + gq;
-            const float* up = sU + gq * UP + 16 * N + li;
-            for (int s = 0; s < 16 * I; s += 4) acc = mfma4(ap[s], up[s * UP], acc);
-            f32x4 rr;
+            f32x4 rhs;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rr[i] = sU[(16 * I + 4 * gq + i) * UP + 16 * N + li] - acc[i];
+            for (int i = 0; i < 4; ++i) rhs[i] = sU[(16 * I + 4 * gq + i) * UP + 16 * N + li];
             // step i pairs reduction slot gq with row 4 gq + i of the accumulator layout
             const f32x4 di = *reinterpret_cast<const f32x4*>(sDi + I * DIB + li * DIP + 4 * gq);
+            // sum_{J<I} A_IJ U_J: reduction over s < 16 I, lane group gq takes 4 I of them
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const float* ap = sA + (16 * I + li) * AP + gq * 4 * I;
+            const float* up = sU + gq * 4 * I * UP + 16 * N + li;
+            if (I == 1) acc = tile_rows_cols<4>(ap, up, UP, acc);
+            else if (I == 2) acc = tile_rows_cols<8>(ap, up, UP, acc);
+            else if (I == 3) acc = tile_rows_cols<12>(ap, up, UP, acc);
+            f32x4 rr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rr[i] = rhs[i] - acc[i];
             f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < 4; ++i) u = mfma4(di[i], rr[i], u);
@@ -435,10 +453,15 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         const int tile = wave + 4 * u;
         if (tile < 2 * NB) {
             const int I = tile >> 1, N = tile & 1;
+            // P's row tile I is zero right of its diagonal tile: reduce over s < 16 (I + 1),
+            // lane group gq taking 4 (I + 1) of them
             f32x4 acc = qh[u];
-            const float* rp = sP + (16 * I + li) * AP + gq;
-            const float* ub = sU + gq * UP + 16 * N + li;
-            for (int s = 0; s < T16; s += 4) acc = mfma4(rp[s], ub[s * UP], acc);
+            const float* rp = sP + (16 * I + li) * AP + gq * 4 * (I + 1);
+            const float* ub = sU + gq * 4 * (I + 1) * UP + 16 * N + li;
+            if (I == 0) acc = tile_rows_cols<4>(rp, ub, UP, acc);
+            else if (I == 1) acc = tile_rows_cols<8>(rp, ub, UP, acc);
+            else if (I == 2) acc = tile_rows_cols<12>(rp, ub, UP, acc);
+            else acc = tile_rows_cols<16>(rp, ub, UP, acc);
             const int col = col0 + 16 * N + li;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
