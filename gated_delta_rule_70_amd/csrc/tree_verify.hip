@@ -20,8 +20,9 @@
 // rows in LDS.  Every phase is parallel across nodes:
 //   0. all global reads issued at once (parents, beta, g, k, q rows, the block's columns
 //      of h0 and v);
-//   1. root-path decay prefixes and ancestor masks by pointer doubling (6 rounds cover
-//      any depth below 64), then the decayed rows, kept as bf16 high/low pairs;
+//   1. ancestor masks by pointer doubling in one wave's registers (6 rounds cover any depth
+//      below 64), root-path decay prefixes as one 0/1-matrix product on the fp32 matrix
+//      cores (whatever the depth), then the decayed rows, kept as bf16 high/low pairs;
 //   2. Kt h0 and Qt h0 (three bf16 matrix-core products per tile on the split operands,
 //      fp32 accumulation), the right-hand side;
 //   3. A and P the same way, masked by ancestry;
@@ -105,12 +106,27 @@ __device__ __forceinline__ f32x4 tile_rows_cols(const float* xa, const float* yb
     return acc;
 }
 
+// One 16x16 tile of M Y for a 0/1 matrix M given by bit masks: lane group g reduces over
+// L consecutive rows of Y, bit k of `bits` (the lane's row of M shifted to the group's
+// first column) selecting row k; yb points at the group's first row of column i, rows ys
+// apart.  Every read is issued before the products; the sums are plain fp32 sums.
+template <int L>
+__device__ __forceinline__ f32x4 prefix_tile(unsigned long long bits, const float* yb, int ys) {
+    float yv[L];
+#pragma unroll
+    for (int k = 0; k < L; ++k) yv[k] = yb[k * ys];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < L; ++k) acc = mfma4((bits >> k) & 1ull ? 1.f : 0.f, yv[k], acc);
+    return acc;
+}
+
 template <typename TIn, typename TG, int DK>
 __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int32_t* __restrict__ parent, const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const TG* __restrict__ g, const float* __restrict__ beta,
     const float* __restrict__ h0, float* __restrict__ o, int T, int HK, int HV, int DV) {
-    constexpr int KP = DK + 4;   // row pitch (floats) of the fp32 decay prefixes
+    constexpr int KP = DK + 4;   // row pitch (floats) of the fp32 g rows and decay prefixes
     constexpr int AP = TM + 4;
     constexpr int UP = CB + 4;
     constexpr int BP = DK + 8;   // bf16 row pitch: 16-byte reads of 16 rows hit distinct banks
@@ -118,19 +134,17 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     constexpr int LO = TM * BP;  // offset of the low parts in a split row array
     static_assert(2 * CB * BP * 2 <= TM * AP * 4 && CB * (TM + 4) <= TM * AP,
                   "staging must fit A and P");
-    static_assert(TM * KP * 4 <= 2 * TM * BP * 2, "the decay prefixes must fit a split row array");
+    static_assert(TM * KP * 4 <= 2 * TM * BP * 2, "g rows and prefixes must fit a split row array");
     // decayed rows as bf16 high parts [TM][BP] followed by low parts [TM][BP]
     __shared__ __attribute__((aligned(16))) __bf16 sKt[2 * TM * BP];  // exp(gam) k
     __shared__ __attribute__((aligned(16))) __bf16 sKh[2 * TM * BP];  // exp(-gam) k
     __shared__ __attribute__((aligned(16))) __bf16 sQt[2 * TM * BP];  // exp(gam) q
-    float* sG = reinterpret_cast<float*>(sKt);  // fp32 decay prefixes [TM][KP] until then
+    float* sG = reinterpret_cast<float*>(sKt);  // fp32 g rows [TM][KP] until then
     __shared__ __attribute__((aligned(16))) float sA[TM * AP];   // split h0 columns [j][c], then A
     __shared__ __attribute__((aligned(16))) float sP[TM * AP];   // v columns [j][t], then P
     __shared__ __attribute__((aligned(16))) float sU[TM * UP];   // right-hand side, then U
-    __shared__ int sJ[TM];                                      // pointer-doubling jumps
     __shared__ unsigned long long sAnc[TM];
     __shared__ float sBeta[TM];
-    __shared__ int sMore[2];  // round flags of the pointer doubling
 
     const int ncb = DV / CB;
     const int cb = blockIdx.x % ncb;
@@ -150,7 +164,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     // ---- 0. global reads, all requested before any is used --------------------------------
     // Issued in the order they are needed: parents and beta, then g (the decay prefixes need
     // only these), then k, q, the v tile and the h0 columns, which stay in flight through
-    // the pointer doubling (its barriers wait for LDS traffic only).  Every thread issues
+    // the masks and prefixes (their barriers wait for LDS traffic only).  Every thread issues
     // the same straight-line loads (rows past the tree read row T - 1 and are zeroed), so
     // each use waits for exactly the loads issued before its own.
     const int tp = min(lane, T - 1);
@@ -208,64 +222,73 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 #pragma unroll
     for (int m = 0; m < HPASS; ++m)
         hv[m] = buf_load_f32x4(rs_h0, ((tid / 8 + 32 * m) * DV + col0 + 4 * (tid % 8)) * 4, 0);
-    if (tid < TM) {
-        int p = tid < T ? par : -1;
-        if (p < -1 || p >= tid) p = -1;  // not an earlier node: a child of the initial state
-        sJ[tid] = p;
-        sAnc[tid] = p >= 0 ? 1ull << p : 0ull;
-        sBeta[tid] = tid < T ? bta : 0.f;
+    // ---- 1. ancestor masks, then the decay prefixes ---------------------------------------
+    // Wave 0, one node per lane, doubles parent pointers in registers (lane shuffles, no
+    // workgroup barrier): after round r, J is the node 2^r steps up (-1 past the root) and
+    // anc holds the 2^r nearest strict ancestors.  A tree of depth below 2^r needs r rounds;
+    // the ballot makes the exit wave-uniform.
+    if (wave == 0) {
+        int J = lane < T ? par : -1;
+        if (J < -1 || J >= lane) J = -1;  // not an earlier node: a child of the initial state
+        unsigned long long anc = J >= 0 ? 1ull << J : 0ull;
+        for (int round = 0; round < 6 && __ballot(J >= 0) != 0ull; ++round) {
+            const int src = J >= 0 ? J : lane;
+            const int jj = __shfl(J, src);
+            const uint32_t alo = __shfl((uint32_t)anc, src);
+            const uint32_t ahi = __shfl((uint32_t)(anc >> 32), src);
+            if (J >= 0) {
+                anc |= ((unsigned long long)ahi << 32) | alo;
+                J = jj;
+            }
+        }
+        sAnc[lane] = anc;
+        sBeta[lane] = lane < T ? bta : 0.f;
     }
-    if (tid == 0) sMore[0] = 0;
 #pragma unroll
-    for (int m = 0; m < NPASS; ++m) {
+    for (int m = 0; m < NPASS; ++m) {  // g rows, zero past the tree
         const int t = tid / QPR + RPI * m;
         if (t >= T) gv[m] = f32x4{0.f, 0.f, 0.f, 0.f};
         *reinterpret_cast<f32x4*>(sG + t * KP + c4) = gv[m];
     }
     lds_barrier();
-
-    // ---- 1. decay prefixes and ancestors by pointer doubling ------------------------------
-    // After round r, gam_t sums g over the 2^r nearest nodes of t's root path (t included)
-    // and J_t is the node 2^r steps up (-1 past the root).  Each round reads, synchronises,
-    // then writes, so every read sees the previous round.  A thread's own prefixes stay in
-    // gv (only it writes them).
-#pragma unroll 1
-    for (int round = 0; round < 6; ++round) {
-        f32x4 add[NPASS];
+    // gam = M g with M[t][s] = 1 for s = t or an ancestor of t (0 past the tree): fp32 matrix
+    // cores, rows of tile I reducing over s < 16 (I + 1) only; wave w takes the 16-channel
+    // tiles w (and w + 4), all four row tiles of each as straight-line code so every read is
+    // issued before the products (tiles past the tree have all-zero masks).  Every prefix is
+    // a plain fp32 sum of its path's g values.
+    float* sGam = reinterpret_cast<float*>(sKh);  // [TM][KP], free until the decayed rows
+    if (wave < DK / 16) {
+        constexpr int NCT = DK / 16 > 4 ? 2 : 1;  // channel tiles per wave
+        unsigned long long bits[4];  // this lane's row of M, from the lane group's first column
 #pragma unroll
-        for (int m = 0; m < NPASS; ++m) {
-            const int t = tid / QPR + RPI * m;
-            const int j = sJ[t];
-            add[m] = j >= 0 ? *reinterpret_cast<const f32x4*>(sG + j * KP + c4)
-                            : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int I = 0; I < 4; ++I) {
+            const int t = 16 * I + li;
+            bits[I] = (t < T ? (sAnc[t] | (1ull << t)) : 0ull) >> (gq * 4 * (I + 1));
         }
-        int jn = -1;
-        unsigned long long an = 0;
-        if (tid < TM) {
-            const int j = sJ[tid];
-            jn = j >= 0 ? sJ[j] : -1;
-            an = sAnc[tid] | (j >= 0 ? sAnc[j] : 0ull);
-        }
-        lds_barrier();
+        f32x4 acc[NCT][4];
 #pragma unroll
-        for (int m = 0; m < NPASS; ++m) {
-            const int t = tid / QPR + RPI * m;
+        for (int u = 0; u < NCT; ++u) {
+            const float* yc = sG + 16 * (wave + 4 * u) + li;
+            acc[u][0] = prefix_tile<4>(bits[0], yc + gq * 4 * KP, KP);
+            acc[u][1] = prefix_tile<8>(bits[1], yc + gq * 8 * KP, KP);
+            acc[u][2] = prefix_tile<12>(bits[2], yc + gq * 12 * KP, KP);
+            acc[u][3] = prefix_tile<16>(bits[3], yc + gq * 16 * KP, KP);
+        }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) gv[m][e] += add[m][e];
-            *reinterpret_cast<f32x4*>(sG + t * KP + c4) = gv[m];
-        }
-        if (tid < TM) {
-            sJ[tid] = jn;
-            sAnc[tid] = an;
-        }
-        // once no node has a jump left the prefixes and masks are final (a tree of depth
-        // below 2^r needs r rounds); the flag of round r is cleared in round r - 1 and read
-        // after this round's last barrier, so every thread takes the same exit
-        if (jn >= 0) sMore[round & 1] = 1;
-        if (tid == 0) sMore[(round + 1) & 1] = 0;
-        lds_barrier();
-        if (__builtin_amdgcn_readfirstlane(sMore[round & 1]) == 0) break;
+        for (int u = 0; u < NCT; ++u)
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sGam[(16 * I + 4 * gq + i) * KP + 16 * (wave + 4 * u) + li] = acc[u][I][i];
     }
+    lds_barrier();
+#pragma unroll
+    for (int m = 0; m < NPASS; ++m) {
+        const int t = tid / QPR + RPI * m;
+        gv[m] = *reinterpret_cast<const f32x4*>(sGam + t * KP + c4);
+    }
+    lds_barrier();  // every prefix is read before the decayed rows overwrite sKh
     auto raw4 = [&](const uint32_t (&r)[ELT]) {
         f32x4 x;
         if constexpr (ELT == 2) {
@@ -278,8 +301,8 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         return x;
     };
     // decayed rows, from the prefixes and the k and q rows still in registers, stored as
-    // bf16 high/low pairs (the prefixes' LDS copy is dead: the last round read it before its
-    // barriers)
+    // bf16 high/low pairs over the g rows and the prefixes (both read before the last
+    // barrier)
 #pragma unroll
     for (int m = 0; m < NPASS; ++m) {
         const int t = tid / QPR + RPI * m;
