@@ -1,6 +1,7 @@
 """Degenerate inputs of the method on every GPU path, against the fp64 oracle: no updates
-(beta = 0: the state only decays), no decay (g = 0), and decay at the edge of the
-documented range of the chunked path (eight consecutive tokens decaying by ~76)."""
+(beta = 0: the state only decays), no decay (g = 0), and decay near the edge of the
+documented range of the chunked path (eight consecutive tokens decaying by ~76) and of the
+tree path (root paths decaying by 57)."""
 import pytest
 import torch
 
@@ -56,11 +57,14 @@ def test_decode_step(kind):
     assert err(o, o_ref) < TOL and err(state, ht_ref) < TOL
 
 
-@pytest.mark.parametrize("kind", ["beta0", "g0"])
+@pytest.mark.parametrize("kind", ["beta0", "g0", "steep"])
 def test_tree_verify(kind):
     x = _inputs(kind, seed=402)
     x = {n: (x[n][:, :48].contiguous() if n != "h0" else x[n]) for n in x}
-    par = make_tree(B, 48, "random", seed=9)
+    # steep decay on a binary tree (depth 5): the deepest root path decays by 6 x 9.5 = 57,
+    # inside the tree kernel's range (path decay above -80 per channel), while masked-out
+    # pairs see factors up to e^57 that the ancestry mask must remove
+    par = make_tree(B, 48, "binary" if kind == "steep" else "random", seed=9)
     ref = oracle.tree(**x, parent=par.numpy())
     d = dev(x)
     note(f"degenerate {kind}: tree verify T=48")
