@@ -419,8 +419,8 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     // invert every diagonal block into a private LDS copy (sKt or sKh, both free now), so
     // no barrier separates the inversion from its use; lane (block gq, column li) runs
     // forward substitution down column li of inv(D_gq) in registers.  Then block by block
-    //   U_I = inv(D_I) (rhs_I - sum_{J<I} A_IJ U_J)
-    // with both products on the matrix cores; a wave reads only the U columns it wrote.
+    //   U_I = inv(D_I) R_I,  R_J <- R_J - A_JI U_I  for J > I   (R starts as the rhs)
+    // with both products on the matrix cores, so U_I = inv(D_I) (rhs_I - sum_{J<I} A_IJ U_J).
     constexpr int DIP = 20;            // inverse row pitch: 16-byte reads of 16 rows, no conflict
     constexpr int DIB = 16 * DIP + 16; // inverse block stride
     static_assert(4 * DIB * 4 <= 2 * TM * BP * 2, "block inverses must fit the free key rows");
@@ -444,28 +444,42 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) sDi[gq * DIB + r * DIP + li] = xc[r];
         }
+        // Right-looking block substitution with every operand in registers: each block's
+        // right-hand side R_I (rows 4 gq + i, column li of this wave's column tile) and U_I
+        // stay in the accumulator layout, which is also the B-operand layout of a 16x16x4
+        // product whose step i pairs reduction slot gq with row 4 gq + i; so U_I feeds the
+        // updates R_J -= A_JI U_I (J > I) directly.  All reads are issued first (blocks past
+        // the tree are read but never used).
         const int N = wave;
-        for (int I = 0; I < NB; ++I) {
-            f32x4 rhs;
+        f32x4 R[4], di[4], aJI[6];  // aJI: (J, I) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rhs[i] = sU[(16 * I + 4 * gq + i) * UP + 16 * N + li];
-            // step i pairs reduction slot gq with row 4 gq + i of the accumulator layout
-            const f32x4 di = *reinterpret_cast<const f32x4*>(sDi + I * DIB + li * DIP + 4 * gq);
-            // sum_{J<I} A_IJ U_J: reduction over s < 16 I, lane group gq takes 4 I of them
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const float* ap = sA + (16 * I + li) * AP + gq * 4 * I;
-            const float* up = sU + gq * 4 * I * UP + 16 * N + li;
-            if (I == 1) acc = tile_rows_cols<4>(ap, up, UP, acc);
-            else if (I == 2) acc = tile_rows_cols<8>(ap, up, UP, acc);
-            else if (I == 3) acc = tile_rows_cols<12>(ap, up, UP, acc);
-            f32x4 rr;
+        for (int I = 0; I < 4; ++I) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rr[i] = rhs[i] - acc[i];
-            f32x4 u = {0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < 4; ++i) R[I][i] = sU[(16 * I + 4 * gq + i) * UP + 16 * N + li];
+            di[I] = *reinterpret_cast<const f32x4*>(sDi + I * DIB + li * DIP + 4 * gq);
+        }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) u = mfma4(di[i], rr[i], u);
+        for (int J = 1, n = 0; J < 4; ++J)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sU[(16 * I + 4 * gq + i) * UP + 16 * N + li] = u[i];
+            for (int I = 0; I < J; ++I, ++n)
+                aJI[n] = *reinterpret_cast<const f32x4*>(sA + (16 * J + li) * AP + 16 * I + 4 * gq);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            if (I < NB) {
+                f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) u = mfma4(di[I][i], R[I][i], u);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sU[(16 * I + 4 * gq + i) * UP + 16 * N + li] = u[i];
+#pragma unroll
+                for (int J = I + 1; J < 4; ++J) {
+                    if (J < NB) {
+                        const f32x4 a = aJI[J * (J - 1) / 2 + I];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) R[J] = mfma4(-a[i], u[i], R[J]);
+                    }
+                }
+            }
         }
     }
     __syncthreads();
