@@ -50,15 +50,24 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 // Split of four fp32 values into bf16 high parts and bf16 remainders (round to nearest even
-// on both): x = hi + lo to 2^-16 relative.
+// on both): x = hi + lo to 2^-16 relative.  Pairs are converted together and the high
+// parts widened back by shifting their bits (x - hi is exact: hi is x's nearest bf16).
 __device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        __bf16 h, l;
-        split_bf16(x[e], h, l);
-        hi[e] = h;
-        lo[e] = l;
+    for (int h = 0; h < 2; ++h) {
+        const f32x2 v = {x[2 * h], x[2 * h + 1]};
+        const bf16x2 hb = __builtin_convertvector(v, bf16x2);
+        const uint32_t u = __builtin_bit_cast(uint32_t, hb);
+        const f32x2 hf = {__uint_as_float(u << 16), __uint_as_float(u & 0xFFFF0000u)};
+        const bf16x2 lb = __builtin_convertvector(v - hf, bf16x2);
+        hi[2 * h] = hb[0];
+        hi[2 * h + 1] = hb[1];
+        lo[2 * h] = lb[0];
+        lo[2 * h + 1] = lb[1];
     }
 }
 
@@ -307,15 +316,23 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     for (int m = 0; m < NPASS; ++m) {
         const int t = tid / QPR + RPI * m;
         const int i = t * BP + c4;
-        const f32x4 kv = raw4(kraw[m]);
-        const f32x4 qv = raw4(qraw[m]);
+        // rows past the tree: zero keys and queries (their prefixes are 0), so every
+        // decayed value is +0
+        uint32_t kr[ELT], qr[ELT];
+#pragma unroll
+        for (int e = 0; e < ELT; ++e) {
+            kr[e] = t < T ? kraw[m][e] : 0u;
+            qr[e] = t < T ? qraw[m][e] : 0u;
+        }
+        const f32x4 kv = raw4(kr);
+        const f32x4 qv = raw4(qr);
         f32x4 kt, kb, qt;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float ep = __expf(gv[m][e]);
-            kt[e] = t < T ? ep * kv[e] : 0.f;
-            kb[e] = t < T ? __expf(-gv[m][e]) * kv[e] : 0.f;
-            qt[e] = t < T ? ep * qv[e] : 0.f;
+            kt[e] = ep * kv[e];
+            kb[e] = __expf(-gv[m][e]) * kv[e];
+            qt[e] = ep * qv[e];
         }
         bf16x4 hi, lo;
         split4(kt, hi, lo);
@@ -334,12 +351,12 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 #pragma unroll
     for (int m = 0; m < HPASS; ++m) {  // sH[j * BP + c]
         const int c = tid / 8 + 32 * m;
+        bf16x4 hi, lo;
+        split4(hv[m], hi, lo);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            __bf16 h, l;
-            split_bf16(hv[m][e], h, l);
-            sH[(4 * (tid % 8) + e) * BP + c] = h;
-            sH[CB * BP + (4 * (tid % 8) + e) * BP + c] = l;
+            sH[(4 * (tid % 8) + e) * BP + c] = hi[e];
+            sH[CB * BP + (4 * (tid % 8) + e) * BP + c] = lo[e];
         }
     }
 #pragma unroll
