@@ -122,6 +122,31 @@ def _stream(stream):
     return _VP(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _shape_of(t) -> tuple:
+    return tuple(t.shape)
+
+
+def _check_shapes(q, k, v, g, beta, h0=None, o=None, ht=None, parent=None):
+    """Every tensor's shape against the dims taken from q and v, on the host, before any
+    pointer reaches the library (the C ABI sees no allocation sizes, so a short tensor
+    would otherwise be read or written past its end).  Returns (B, T, HK, HV, dk, dv)."""
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B,T,HK,dk], got shape {_shape_of(q)}")
+    B, T, HK, dk = _shape_of(q)
+    if _shape_of(k) != (B, T, HK, dk):
+        raise ValueError(f"k must have q's shape {(B, T, HK, dk)}, got {_shape_of(k)}")
+    if v.dim() != 4 or _shape_of(v)[:2] != (B, T):
+        raise ValueError(f"v must be [B,T,HV,dv] with B,T = {(B, T)}, got {_shape_of(v)}")
+    HV, dv = _shape_of(v)[2], _shape_of(v)[3]
+    want = {"g": (g, (B, T, HV, dk)), "beta": (beta, (B, T, HV)),
+            "h0": (h0, (B, HV, dk, dv)), "o": (o, (B, T, HV, dv)), "ht": (ht, (B, HV, dk, dv)),
+            "parent": (parent, (B, T))}
+    for name, (t, shape) in want.items():
+        if t is not None and _shape_of(t) != shape:
+            raise ValueError(f"{name} must be {list(shape)}, got {list(_shape_of(t))}")
+    return B, T, HK, HV, dk, dv
+
+
 def _check_inputs(q, k, v, g, beta):
     dt = q.dtype
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -129,8 +154,6 @@ def _check_inputs(q, k, v, g, beta):
     # g is fp32, or bf16 with bf16 q/k/v (the library's I/O-lean input format)
     _need(g, "g", torch.bfloat16 if (g.dtype == torch.bfloat16 and dt == torch.bfloat16) else torch.float32)
     _need(beta, "beta", torch.float32)
-    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4:
-        raise ValueError("q, k must be [B,T,HK,dk] and v [B,T,HV,dv]")
 
 
 def workspace_bytes(B, T, HK, HV, dk, dv, chunk=64, dtype=torch.bfloat16) -> int:
@@ -144,15 +167,14 @@ def decode_step(q, k, v, g, beta, state, o=None, out_state=None, stream=None):
     ``state`` may be None (zero initial state; then ``out_state`` receives the new state if
     given).  Returns ``o`` ``[B,1,HV,dv]`` fp32.
     """
+    ht = state if out_state is None else out_state
+    B, T, HK, HV, dk, dv = _check_shapes(q, k, v, g, beta, h0=state, o=o, ht=ht)
     _check_inputs(q, k, v, g, beta)
-    B, T, HK, dk = q.shape
-    HV, dv = v.shape[2], v.shape[3]
     if state is not None:
         _need(state, "state", torch.float32)
     if o is None:
         o = torch.empty(B, T, HV, dv, device=q.device, dtype=torch.float32)
     _need(o, "o", torch.float32)
-    ht = state if out_state is None else out_state
     if ht is not None:
         _need(ht, "out_state", torch.float32)
     d = _dims(q, v, 0, g)
@@ -171,9 +193,8 @@ def chunk_prefill(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
     (gdr_chunk_carry, which needs a workspace filled by "prep" for the same inputs).
     """
     entry = {"both": "gdr_chunk_prefill", "prep": "gdr_chunk_prep", "carry": "gdr_chunk_carry"}[stage]
+    B, T, HK, HV, dk, dv = _check_shapes(q, k, v, g, beta, h0=h0, o=o, ht=ht)
     _check_inputs(q, k, v, g, beta)
-    B, T, HK, dk = q.shape
-    HV, dv = v.shape[2], v.shape[3]
     if h0 is not None:
         _need(h0, "h0", torch.float32)
     if o is None:
@@ -199,9 +220,8 @@ def fused_recurrent(q, k, v, g, beta, h0=None, o=None, ht=None, want_state: bool
     """The token recurrence over all T tokens in one launch (gdr_fused_recurrent): the state
     stays on chip for the whole call.  Returns ``(o, ht)``; ``ht`` may be ``h0`` itself
     (in-place), and is None if not wanted."""
+    B, T, HK, HV, dk, dv = _check_shapes(q, k, v, g, beta, h0=h0, o=o, ht=ht)
     _check_inputs(q, k, v, g, beta)
-    B, T, HK, dk = q.shape
-    HV, dv = v.shape[2], v.shape[3]
     if h0 is not None:
         _need(h0, "h0", torch.float32)
     if o is None:
@@ -221,9 +241,8 @@ def forward(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None, workspa
             want_state: bool = True, stream=None):
     """Routed call (gdr_forward): the fused recurrence for T <= RECURRENT_MAX_T, the chunked
     prefill otherwise.  Returns ``(o, ht)``."""
+    B, T, HK, HV, dk, dv = _check_shapes(q, k, v, g, beta, h0=h0, o=o, ht=ht)
     _check_inputs(q, k, v, g, beta)
-    B, T, HK, dk = q.shape
-    HV, dv = v.shape[2], v.shape[3]
     if h0 is not None:
         _need(h0, "h0", torch.float32)
     if o is None:
@@ -250,12 +269,9 @@ def tree_verify(q, k, v, g, beta, parent, h0=None, o=None, stream=None):
     """Tree-verify solve (gdr_tree_verify): ``parent`` is an int32 GPU tensor ``[B,T]`` of
     parent node indices (-1: continues from ``h0``).  Returns ``o`` ``[B,T,HV,dv]``, each
     node's output along its root path."""
+    B, T, HK, HV, dk, dv = _check_shapes(q, k, v, g, beta, h0=h0, o=o, parent=parent)
     _check_inputs(q, k, v, g, beta)
-    B, T, HK, dk = q.shape
-    HV, dv = v.shape[2], v.shape[3]
     _need(parent, "parent", torch.int32)
-    if tuple(parent.shape) != (B, T):
-        raise ValueError(f"parent must be [B,T] = {(B, T)}")
     if h0 is not None:
         _need(h0, "h0", torch.float32)
     if o is None:
