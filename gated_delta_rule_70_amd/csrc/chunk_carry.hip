@@ -27,6 +27,17 @@
 // chunk step is straight-line code (no per-wave branches), which keeps the compiler's
 // memory-wait counts at the pipeline's real depth.
 //
+// Range.  The state and v enter the products as fp16, each in its own scaled domain: per
+// chunk each wave scales its state tiles by 2^-es_w and its v rows by 2^-ev_w (exponents of
+// their largest magnitudes) before publishing them with the exponents; a reader takes
+// E_S = max_w es_w, E_V = max_w ev_w and aligns every fragment half to them with exact fp16
+// power-of-two factors.  Tb V and W S go to separate accumulators and meet in fp32 at the
+// larger scale E_U = max(E_S, E_V), so a state far smaller than v (or the reverse) keeps its
+// precision; U is published at 2^-E_U, the state update adds 2^E_U Kb^T U, and the outputs
+// are 2^E_S Qt S + 2^E_U P U with the query rows' record multipliers (see chunk_prep).  So
+// every product stays inside fp16's range for state and v magnitudes within fp32's normal
+// range; U itself keeps fp16's precision while beta >= 2^-12 (or beta = 0 exactly).
+//
 // Launch: blocks = (B*HV) x (dv / (16*NT)), block index = colgroup * (B*HV) + head, so
 // all column groups of a head share one XCD (blocks are dealt round-robin to the 8 XCDs)
 // and read the head's records through one L2.
@@ -54,6 +65,31 @@ __device__ __forceinline__ half4 to_half4(f32x4 x) {
     return half4{static_cast<_Float16>(x[0]), static_cast<_Float16>(x[1]), static_cast<_Float16>(x[2]),
                  static_cast<_Float16>(x[3])};
 }
+// x * 2^e, then fp16
+__device__ __forceinline__ half4 to_half4_scaled(f32x4 x, int e) {
+    return half4{static_cast<_Float16>(ldexp2(x[0], e)), static_cast<_Float16>(ldexp2(x[1], e)),
+                 static_cast<_Float16>(ldexp2(x[2], e)), static_cast<_Float16>(ldexp2(x[3], e))};
+}
+
+// Scale exponents of the carry's fp16 operands: a published block of values with largest
+// magnitude m is stored times 2^-(exponent(m) - kTgt), i.e. with its maximum in [32, 64);
+// U = Tb V - W S then stays below 64 (|Tb|_1 + |W|_1) < 65504 for any well-conditioned
+// chunk.  kNoExp marks an all-zero block (it never sets the common exponent).
+constexpr int kTgt = 6;
+constexpr int kNoExp = -1000;
+__device__ __forceinline__ int scale_exponent(float m) { return m > 0.f ? exponent_of(m) - kTgt : kNoExp; }
+
+// Largest |x| over the raw bits of v held by a lane (bf16 pairs or fp32).
+template <typename TIn>
+__device__ __forceinline__ float raw_absmax(uint32_t x) {
+    if constexpr (sizeof(TIn) == 2) {
+        const uint32_t a = x & 0x7FFF7FFFu;  // bf16 magnitudes order like their bits
+        const uint32_t hi = a >> 16, lo = a & 0xFFFFu;
+        return __uint_as_float((hi > lo ? hi : lo) << 16);
+    } else {
+        return fabsf(__uint_as_float(x));
+    }
+}
 
 template <typename TIn, int DK, int DV, int C, int NT>
 __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
@@ -76,6 +112,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
     __shared__ half8 sSB[3][KC * NT * 64];
     __shared__ half8 sUB[3][NQS * NT * 64];
     __shared__ __attribute__((aligned(16))) _Float16 sV[3][NT * 16 * VP];
+    __shared__ int sE[3][8];  // each wave's state and v scale exponents, per exchange copy
 
     const int NH = B * HV;
     const int blk = blockIdx.x;
@@ -145,7 +182,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
             }
         }
     };
-    auto publish_v = [&](const VRaw& V, _Float16* dst) {  // -> [nt][col][row], fp16
+    auto publish_v = [&](const VRaw& V, _Float16* dst, int ew) {  // -> [nt][col][row], fp16 * 2^-ew
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -153,7 +190,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
                 float x;
                 if constexpr (ELT == 2) x = __uint_as_float((e & 1) ? (V[nt][e >> 1] & 0xFFFF0000u) : (V[nt][e >> 1] << 16));
                 else x = __uint_as_float(V[nt][e]);
-                dst[(nt * 16 + 4 * (lane & 3) + e) * VP + 16 * w + (lane >> 2)] = static_cast<_Float16>(x);
+                dst[(nt * 16 + 4 * (lane & 3) + e) * VP + 16 * w + (lane >> 2)] = static_cast<_Float16>(ldexp2(x, -ew));
             }
     };
     auto read_v = [&](half8 (&V)[NQS][NT], const _Float16* src) {
@@ -185,6 +222,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
     struct Frags {
         half8 tb[NQS], w[KC], q[KC], p[NQS], kb[OWN][NQS];
         f32x4 e;                 // exp(gam_last) of owned state tile j, in row lane j
+        float qs, ps;            // Qt and P row multipliers of this lane's token row
         uint32_t v[NT][ELT];     // raw bits of this wave's v rows of the chunk
     };
     // A per-lane offset past every record range: such a load reads zeros without touching
@@ -238,6 +276,9 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
             }
         }
         F.e = ld_egl(n);
+        const int rs = n * R.bytes + (16 * w + li) * 4;  // token row 16w + li of the chunk
+        F.qs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_rec, rs, R.nfrag * 1024 + R.qsc * 4, 0));
+        F.ps = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_rec, rs, R.nfrag * 1024 + R.psc * 4, 0));
     };
     auto load_all = [&](Frags& F, int n) {
         ld_g1(F, n);
@@ -246,7 +287,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
         ld_g4(F, n);
     };
 
-    f32x4 Op[NT];
+    f32x4 Op[NT];  // outputs of the previous chunk (true scale), stored one step late
     // One chunk: request chunk nn's operands into set Fn, consume set F (chunk n), using
     // exchange-buffer copy `par`.
     auto step = [&](Frags& F, Frags& Fn, int n, int nn, int par) {
@@ -257,9 +298,28 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int e = 0; e < ELT; ++e) asm volatile("" : "+v"(F.v[nt][e]));
-        publish_v(F.v, sV[par]);
 
-        // 1. publish this wave's state tiles as halves of the state B fragments
+        // 0. this wave's scale exponents: largest magnitudes of its state tiles and v rows
+        int es, ev;
+        {
+            float ms = 0.f, mv = 0.f;
+#pragma unroll
+            for (int j = 0; j < OWN; ++j)
+                if (w + NW * j < DKT)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) ms = fmaxf(ms, fabsf(S[j][nt][i]));
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int e = 0; e < ELT; ++e) mv = fmaxf(mv, raw_absmax<TIn>(F.v[nt][e]));
+            es = scale_exponent(wave_max(ms));
+            ev = scale_exponent(wave_max(mv));
+        }
+        publish_v(F.v, sV[par], ev);
+
+        // 1. publish this wave's state tiles (times 2^-es) as halves of the state B fragments
 #pragma unroll
         for (int j = 0; j < OWN; ++j) {
             const int ct = w + NW * j;
@@ -267,25 +327,60 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
                     *(reinterpret_cast<half4*>(&sSB[par][((ct >> 1) * NT + nt) * 64 + lane]) + (ct & 1)) =
-                        to_half4(S[j][nt]);
+                        to_half4_scaled(S[j][nt], -es);
             }
         }
+        if (lane == 0) {
+            sE[par][w] = es;
+            sE[par][4 + w] = ev;
+        }
         lds_barrier();
+        // common exponents and the factors 2^(e_w - E) that align each wave's halves to them
+        int esw[NW], evw[NW];
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            esw[ww] = sE[par][ww];
+            evw[ww] = sE[par][4 + ww];
+        }
+        int ES = esw[0], EV = evw[0];
+#pragma unroll
+        for (int ww = 1; ww < NW; ++ww) {
+            ES = max(ES, esw[ww]);
+            EV = max(EV, evw[ww]);
+        }
+        const int EU = max(ES, EV);
+        _Float16 fs[NW], fv[NW];
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            fs[ww] = half_pow2(esw[ww] - ES);
+            fv[ww] = half_pow2(evw[ww] - EV);
+        }
+        // a B fragment of reduction step p holds row tiles 2p and 2p+1 (owners (2p) % NW and
+        // (2p+1) % NW), a v fragment of token step qs rows 16(2qs) .. 16(2qs+2) (waves 2qs, 2qs+1)
+        auto align = [&](half8 x, const _Float16 (&f)[NW], int wa, int wb) {
+            const _Float16 a = f[wa % NW], b = f[wb % NW];
+            return x * half8{a, a, a, a, b, b, b, b};
+        };
         half8 SB[KC][NT];
 #pragma unroll
         for (int p = 0; p < KC; ++p)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) SB[p][nt] = sSB[par][(p * NT + nt) * 64 + lane];
+            for (int nt = 0; nt < NT; ++nt) SB[p][nt] = align(sSB[par][(p * NT + nt) * 64 + lane], fs, 2 * p, 2 * p + 1);
         half8 Vc[NQS][NT];
         read_v(Vc, sV[par]);
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) Vc[qs][nt] = align(Vc[qs][nt], fv, 2 * qs, 2 * qs + 1 < NW ? 2 * qs + 1 : 2 * qs);
+        // the scaled domains back to true scale
 
         if (n > 0) store_o(n - 1, Op);
         ld_g2(Fn, nn);
 
-        // 2. U_w = Tb V - W S for row tile w
-        f32x4 U[NT];
+        // 2. U_w = Tb V - W S for row tile w (times 2^-E_U; the two products meet in fp32)
+        f32x4 U[NT], US[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) U[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < NT; ++nt) U[nt] = US[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int qs = 0; qs < NQS; ++qs)
 #pragma unroll
@@ -293,7 +388,11 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
 #pragma unroll
         for (int p = 0; p < KC; ++p)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) U[nt] = mfma_f16(F.w[p], SB[p][nt], U[nt]);
+            for (int nt = 0; nt < NT; ++nt) US[nt] = mfma_f16(F.w[p], SB[p][nt], US[nt]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) U[nt][i] = ldexp2(U[nt][i], EV - EU) + ldexp2(US[nt][i], ES - EU);
         // 3. publish U_w as half of a U B fragment
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
@@ -301,12 +400,13 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
         ld_g3(Fn, nn);
         // 4. O_w^T = S^T Qt^T (independent of U; overlaps the exchange).  The operands swap
         // places: a fragment reads the same as an A operand of X and a B operand of X^T.
+        f32x4 OQ[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) Op[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < NT; ++nt) OQ[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int p = 0; p < KC; ++p)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) Op[nt] = mfma_f16(SB[p][nt], F.q[p], Op[nt]);
+            for (int nt = 0; nt < NT; ++nt) OQ[nt] = mfma_f16(SB[p][nt], F.q[p], OQ[nt]);
         lds_barrier();
         half8 UB[NQS][NT];
 #pragma unroll
@@ -322,7 +422,8 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
             }
         ld_g4(Fn, nn);
 
-        // 5. S' = diag(exp(gam_last)) S + Kb^T U for the owned state tiles
+        // 5. S' = diag(exp(gam_last)) S + 2^E_U Kb^T U for the owned state tiles
+        const float su = ldexp2(1.f, EU);
 #pragma unroll
         for (int j = 0; j < OWN; ++j) {
             const int ct = w + NW * j;
@@ -331,18 +432,25 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ej[i] = row_lane(F.e[i], j);
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) S[j][nt] *= ej;
+                for (int nt = 0; nt < NT; ++nt) {
+                    f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int qs = 0; qs < NQS; ++qs)
+                    for (int qs = 0; qs < NQS; ++qs) a = mfma_f16(F.kb[j][qs], UB[qs][nt], a);
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) S[j][nt] = mfma_f16(F.kb[j][qs], UB[qs][nt], S[j][nt]);
+                    for (int i = 0; i < 4; ++i) S[j][nt][i] = fmaf(a[i], su, S[j][nt][i] * ej[i]);
+                }
             }
         }
-        // 6. O_w^T += U^T P^T
+        // 6. O_w^T = qs 2^E_S S^T Qt^T + ps 2^E_U U^T P^T, the query rows' multipliers per lane
+        const float fq = F.qs * ldexp2(1.f, ES), fp = F.ps * su;
 #pragma unroll
-        for (int qs = 0; qs < NQS; ++qs)
+        for (int nt = 0; nt < NT; ++nt) {
+            f32x4 OP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) Op[nt] = mfma_f16(UB[qs][nt], F.p[qs], Op[nt]);
+            for (int qs = 0; qs < NQS; ++qs) OP = mfma_f16(UB[qs][nt], F.p[qs], OP);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Op[nt][i] = fmaf(OP[i], fp, OQ[nt][i] * fq);
+        }
     };
 
     Frags FA, FB, FC;

@@ -28,6 +28,17 @@
 // synchronisation is one barrier per chunk for the staged record.  Accumulator tiles of
 // S and U feed the B operands of the next products directly (reduction slots follow
 // perm_slot); v is transposed through a wave-private LDS tile.
+//
+// Range.  Each wave keeps its state columns in a scaled domain X' = X 2^-E (E per wave):
+// per chunk it checks the largest magnitude of X' against fp16's comfortable range and,
+// when it leaves it, moves E (an exact power-of-two rescale of X').  v enters the products
+// as V 2^-EV with its own per-chunk exponent EV, so a state far smaller than v (or the
+// reverse) keeps its precision; Tb V and W X meet in fp32 at EU = max(E, EV), U is
+// published at 2^-EU and the state moves to that domain with the update (2^(E - EU) is
+// folded into the decay factors).  O is 2^E Qt X' + 2^EU P U times the query rows' record
+// multipliers (see chunk_prep); the final state (or segment summary) is X' 2^E.  So every
+// fp16 operand stays inside fp16's range for state and v magnitudes within fp32's normal
+// range; U itself keeps fp16's precision while beta >= 2^-12 (or beta = 0 exactly).
 #include "gdr_device.h"
 #include "gdr_launch.h"
 
@@ -43,6 +54,32 @@ __device__ __forceinline__ half4w h4(f32x4 x) {
 __device__ __forceinline__ half8 cat(half4w a, half4w b) {
     return half8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
+
+// Scale bookkeeping of the wave's scaled domain: values are kept with their largest
+// magnitude at most 2^kTop (U = Tb V - W X' then stays below 2^kTop (|Tb|_1 + |W|_1), far
+// inside fp16) and rescaled to [2^(kTop-1), 2^kTop) once it exceeds that or falls below
+// 2^(kTop-kSlack).  kNoExp: the state and v are zero so far.
+constexpr int kTop = 6;
+constexpr int kSlack = 10;
+constexpr int kNoExp = -1000;
+
+// Largest |x| over raw v bits (bf16 pairs or fp32), as a packed/unpacked running maximum.
+typedef unsigned short u16x2w __attribute__((ext_vector_type(2)));
+template <typename TIn>
+struct VMax {
+    u16x2w m16 = {0, 0};
+    float m32 = 0.f;
+    __device__ __forceinline__ void add(uint32_t x) {
+        if constexpr (sizeof(TIn) == 2)
+            m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(u16x2w, x & 0x7FFF7FFFu));
+        else
+            m32 = fmaxf(m32, fabsf(__uint_as_float(x)));
+    }
+    __device__ __forceinline__ float get() const {
+        if constexpr (sizeof(TIn) == 2) return __uint_as_float((uint32_t)(m16[0] > m16[1] ? m16[0] : m16[1]) << 16);
+        return m32;
+    }
+};
 
 // LDS layout of one staged record (slots of 1 KiB, lane-major fragments) and the list of
 // record fragments copied into it.  Tb and P fragments above a row tile's diagonal are
@@ -190,6 +227,34 @@ void carry_wide_kernel(
             }
     }
 
+    // this wave's scaled domain: X' = X 2^-E (E wave-uniform; kNoExp while X and v are zero)
+    auto max_abs_x = [&]() {
+        float m = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < DKT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(X[rt][ct][i]));
+        return wave_max(m);
+    };
+    auto rescale_x = [&](int d) {  // X' *= 2^d
+#pragma unroll
+        for (int rt = 0; rt < DKT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) X[rt][ct][i] = ldexp2(X[rt][ct][i], d);
+    };
+    int E = kNoExp;
+    {
+        const float m = max_abs_x();
+        if (m > 0.f) {
+            E = __builtin_amdgcn_readfirstlane(exponent_of(m) - kTop);
+            rescale_x(-E);
+        }
+    }
+
     const unsigned char* rec0 = ws + (size_t)bh * NC * R.bytes;
     const rsrc_t rs_rec = make_rsrc(rec0, (uint32_t)NC * R.bytes);
     const int rowv = HV * D * ELT;
@@ -237,7 +302,7 @@ void carry_wide_kernel(
             asm volatile("" ::: "memory");
         }
     };
-    auto publish_v = [&](const VRegs& VR) {  // -> sV[wq][col][token], fp16
+    auto publish_v = [&](const VRegs& VR, int E) {  // -> sV[wq][col][token], fp16 * 2^-E
         if (!has_v || lane >= C) return;
         _Float16* dst = sV[wq];
 #pragma unroll
@@ -246,10 +311,11 @@ void carry_wide_kernel(
             for (int e = 0; e < 4; ++e) {
                 if constexpr (ELT == 2) {
                     const uint32_t u = VR[j][e];
-                    dst[(8 * j + 2 * e) * VP + lane] = static_cast<_Float16>(__uint_as_float(u << 16));
-                    dst[(8 * j + 2 * e + 1) * VP + lane] = static_cast<_Float16>(__uint_as_float(u & 0xFFFF0000u));
+                    dst[(8 * j + 2 * e) * VP + lane] = static_cast<_Float16>(ldexp2(__uint_as_float(u << 16), -E));
+                    dst[(8 * j + 2 * e + 1) * VP + lane] =
+                        static_cast<_Float16>(ldexp2(__uint_as_float(u & 0xFFFF0000u), -E));
                 } else {
-                    dst[(4 * j + e) * VP + lane] = static_cast<_Float16>(__uint_as_float(VR[j][e]));
+                    dst[(4 * j + e) * VP + lane] = static_cast<_Float16>(ldexp2(__uint_as_float(VR[j][e]), -E));
                 }
             }
     };
@@ -275,7 +341,32 @@ void carry_wide_kernel(
     // The last step requests its own chunk again (clamped index) rather than branching.
     auto step = [&](int n, int buf) {
         const int nn = min(n + 1, c1 - 1);
-        publish_v(VR);
+        // keep X' at most 2^kTop and not far below it; this chunk's v at 2^-EV, its maximum
+        // in [2^(kTop-1), 2^kTop)
+        int EV = kNoExp;
+        {
+            VMax<TIn> vm;
+            if (has_v) {
+#pragma unroll
+                for (int j = 0; j < VLD; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) vm.add(VR[j][e]);
+            }
+            const float mv = wave_max(vm.get());
+            EV = __builtin_amdgcn_readfirstlane(mv > 0.f ? exponent_of(mv) - kTop : kNoExp);
+            const float mx = E != kNoExp ? max_abs_x() : 0.f;
+            if (mx > 0.f) {
+                const int en = __builtin_amdgcn_readfirstlane(exponent_of(mx) + E - kTop);
+                if (en > E || en < E - kSlack) {
+                    rescale_x(E - en);
+                    E = en;
+                }
+            } else {
+                E = kNoExp;  // X' is zero
+            }
+        }
+        const int EU = max(E, EV);
+        publish_v(VR, EV);
         issue_v(VR, nn);
         lds_barrier();  // buffer `buf` complete; everyone is done with buffer buf ^ 1
         issue_rec(nn, buf ^ 1);
@@ -291,12 +382,12 @@ void carry_wide_kernel(
 #pragma unroll
             for (int ct = 0; ct < CTW; ++ct) XB[p][ct] = cat(h4(X[2 * p][ct]), h4(X[2 * p + 1][ct]));
 
-        // U = Tb V - W X
-        f32x4 U[NB][CTW];
+        // U = Tb V - W X, the two products at their own scales, combined in fp32 at 2^-EU
+        f32x4 U[NB][CTW], UX[NB][CTW];
 #pragma unroll
         for (int r = 0; r < NB; ++r)
 #pragma unroll
-            for (int ct = 0; ct < CTW; ++ct) U[r][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ct = 0; ct < CTW; ++ct) U[r][ct] = UX[r][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (has_v) {
             half8 Vb[NQS][CTW];
 #pragma unroll
@@ -326,8 +417,14 @@ void carry_wide_kernel(
             for (int p = 0; p < KC; ++p) {
                 const half8 a = A(ST::s_w + r * KC + p);  // -W
 #pragma unroll
-                for (int ct = 0; ct < CTW; ++ct) U[r][ct] = mfma_f16(a, XB[p][ct], U[r][ct]);
+                for (int ct = 0; ct < CTW; ++ct) UX[r][ct] = mfma_f16(a, XB[p][ct], UX[r][ct]);
             }
+#pragma unroll
+        for (int r = 0; r < NB; ++r)
+#pragma unroll
+            for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) U[r][ct][i] = ldexp2(U[r][ct][i], EV - EU) + ldexp2(UX[r][ct][i], E - EU);
         half8 UB[NQS][CTW];
 #pragma unroll
         for (int qs = 0; qs < NQS; ++qs)
@@ -341,37 +438,46 @@ void carry_wide_kernel(
             }
 
         if constexpr (!SUM) {
-            // O^T = X^T Qt^T + U^T P^T per row tile (lane (i, g): token 16r + i, columns
-            // col0 + 16ct + 4g .. +3): one 16-byte store per lane and tile; rows past T are
-            // beyond the buffer range and dropped
+            // O^T = qs 2^E X'^T Qt^T + ps 2^EU U'^T P^T per row tile (lane (i, g): token 16r + i,
+            // columns col0 + 16ct + 4g .. +3; qs, ps the token row's record multipliers): one
+            // 16-byte store per lane and tile; rows past T are beyond the buffer range and dropped
+            const float* rowm = reinterpret_cast<const float*>(&L[ST::s_e * 64]);
+            const float sc = ldexp2(1.f, E), su = ldexp2(1.f, EU);
 #pragma unroll
             for (int r = 0; r < NB; ++r) {
-                f32x4 O[CTW];
+                f32x4 OQ[CTW], OP[CTW];
 #pragma unroll
-                for (int ct = 0; ct < CTW; ++ct) O[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int ct = 0; ct < CTW; ++ct) OQ[ct] = OP[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int p = 0; p < KC; ++p) {
                     const half8 a = A(ST::s_qt + r * KC + p);
 #pragma unroll
-                    for (int ct = 0; ct < CTW; ++ct) O[ct] = mfma_f16(XB[p][ct], a, O[ct]);
+                    for (int ct = 0; ct < CTW; ++ct) OQ[ct] = mfma_f16(XB[p][ct], a, OQ[ct]);
                 }
 #pragma unroll
                 for (int qs = 0; qs < NQS; ++qs) {
                     if (2 * qs > r) continue;
                     const half8 a = A(ST::s_p + r * NQS + qs);
 #pragma unroll
-                    for (int ct = 0; ct < CTW; ++ct) O[ct] = mfma_f16(UB[qs][ct], a, O[ct]);
+                    for (int ct = 0; ct < CTW; ++ct) OP[ct] = mfma_f16(UB[qs][ct], a, OP[ct]);
                 }
+                const float fq = rowm[R.qsc + 16 * r + li] * sc, fp = rowm[R.psc + 16 * r + li] * su;
 #pragma unroll
-                for (int ct = 0; ct < CTW; ++ct) Oq[r][ct] = O[ct];
+                for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Oq[r][ct][i] = fmaf(OP[ct][i], fp, OQ[ct][i] * fq);
             }
         }
 
-        // X' = diag(exp(gam_last)) X + Kb^T U
+        // X' = diag(exp(gam_last)) X + Kb^T U, moved to the domain of U: 2^(E - EU) is folded
+        // into the decay factors (0 when X' is zero)
         const float* egl = reinterpret_cast<const float*>(&L[ST::s_e * 64]);
+        const int dsh = E - EU;
 #pragma unroll
         for (int rt = 0; rt < DKT; ++rt) {
-            const f32x4 e4 = *reinterpret_cast<const f32x4*>(egl + 16 * rt + 4 * gq);
+            f32x4 e4 = *reinterpret_cast<const f32x4*>(egl + 16 * rt + 4 * gq);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e4[i] = ldexp2(e4[i], dsh);
 #pragma unroll
             for (int ct = 0; ct < CTW; ++ct) X[rt][ct] *= e4;
 #pragma unroll
@@ -381,6 +487,7 @@ void carry_wide_kernel(
                 for (int ct = 0; ct < CTW; ++ct) X[rt][ct] = mfma_f16(a, UB[qs][ct], X[rt][ct]);
             }
         }
+        E = EU;
 
         wait_vm();
     };
@@ -402,7 +509,7 @@ void carry_wide_kernel(
             for (int ct = 0; ct < CTW; ++ct)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    dst[(size_t)(16 * rt + 4 * gq + i) * D + col0 + 16 * ct + li] = X[rt][ct][i];
+                    dst[(size_t)(16 * rt + 4 * gq + i) * D + col0 + 16 * ct + li] = ldexp2(X[rt][ct][i], E);
     }
 }
 
@@ -411,13 +518,17 @@ void carry_wide_kernel(
 // workgroup needs all of M_s, so fewer, wider workgroups move fewer bytes per step.  Wave w
 // owns state row tiles 2w and 2w + 1, i.e. exactly the rows of one 32-wide reduction step,
 // which it publishes to the other waves as hi/lo fp16 B fragments.  M and S_loc of the
-// next segment are requested while the current one is combined.
+// next segment are requested while the current one is combined.  Range: the start state
+// enters the products as S 2^-E (E from its largest magnitude over the workgroup, one extra
+// exchange per step), so its hi/lo halves stay inside fp16's range; the transition M is a
+// product of non-expansive maps (|M_ij| <= 1 for stable updates) and needs no scale.
 template <int D>
 __global__ __launch_bounds__(2 * D) void carry_combine_kernel(const float* h0, const float* xsum,
                                                            float* sstart, int NH, int NSEG) {
     constexpr int KC = D / 32;
     constexpr int CTC = D / 32;  // column tiles per workgroup
     __shared__ half8 sB[2][KC][CTC][2][64];
+    __shared__ float sMx[2][KC];  // each wave's largest |S|
     const int bh = blockIdx.x % NH;
     const int half = blockIdx.x / NH;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -468,10 +579,33 @@ __global__ __launch_bounds__(2 * D) void carry_combine_kernel(const float* h0, c
     for (int s = 0; s + 1 < NSEG; ++s) {
         if (s + 2 < NSEG) load_ops(nxt, s + 1);
         const int par = s & 1;
+        {
+            float m = 0.f;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int ct = 0; ct < CTC; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[j][ct][i]));
+            m = wave_max(m);
+            if (lane == 0) sMx[par][w] = m;
+        }
+        lds_barrier();
+        float mall = sMx[par][0];
+#pragma unroll
+        for (int ww = 1; ww < KC; ++ww) mall = fmaxf(mall, sMx[par][ww]);
+        const int E = mall > 0.f ? exponent_of(mall) - 6 : 0;
+        const float sc = ldexp2(1.f, E);
 #pragma unroll
         for (int ct = 0; ct < CTC; ++ct) {
-            const half4w h0a = h4(S[0][ct]), h1a = h4(S[1][ct]);
-            f32x4 r0 = S[0][ct], r1 = S[1][ct];
+            f32x4 s0 = S[0][ct], s1 = S[1][ct];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s0[i] = ldexp2(s0[i], -E);
+                s1[i] = ldexp2(s1[i], -E);
+            }
+            const half4w h0a = h4(s0), h1a = h4(s1);
+            f32x4 r0 = s0, r1 = s1;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 r0[i] -= static_cast<float>(h0a[i]);
@@ -485,7 +619,7 @@ __global__ __launch_bounds__(2 * D) void carry_combine_kernel(const float* h0, c
         for (int j = 0; j < 2; ++j) {
             f32x4 acc[CTC];
 #pragma unroll
-            for (int ct = 0; ct < CTC; ++ct) acc[ct] = cur.sl[j][ct];
+            for (int ct = 0; ct < CTC; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int p = 0; p < KC; ++p) {
                 half8 ah, al;
@@ -508,7 +642,9 @@ __global__ __launch_bounds__(2 * D) void carry_combine_kernel(const float* h0, c
                 }
             }
 #pragma unroll
-            for (int ct = 0; ct < CTC; ++ct) S[j][ct] = acc[ct];
+            for (int ct = 0; ct < CTC; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[j][ct][i] = fmaf(acc[ct][i], sc, cur.sl[j][ct][i]);
         }
         float* out = sstart + ((size_t)bh * NSEG + s + 1) * D * D;
 #pragma unroll

@@ -29,12 +29,22 @@
 //
 // Decay factors (log2 units; every exponential is a hardware exp2).  Inside block I,
 //   Z_r = exp(gam_r - gam_m), Zi_r = 1 / Z_r   (m = 16I + 7, the block's middle row)
-// for the diagonal tiles (bf16 hi + lo split, three products, fp32 range, ~16 bits);
+// for the diagonal tiles, which run on the fp32 matrix cores (16x16x4) so these factors
+// keep fp32's range and precision;
 // off-diagonal tiles J < I use, in fp16 and with both factors <= 1 while g <= 0,
 //   key side   k_s exp(gam_{16J+15} - gam_s)
 //   row side   k_r exp(gam_r - gam_{16I-1}) * exp(gam_{16I-1} - gam_{16J+15}).
 // Z and Zi stay finite while the decay over 8 consecutive tokens of a block is below ~88
 // (mean g above about -11 per token), the range documented in gdr.h.
+//
+// Query range.  Each wave scales its block's queries by an exact power of two 2^-eq
+// (eq = exponent of the block's largest |q|), so the row operands of the off-diagonal
+// causal tiles and the P fragments are inside fp16's range for any query magnitude.  Each
+// decayed query row Qt_r is formed in fp32 and stored times 2^-er, er = exponent of its own
+// largest entry (the decay inside one 16-row block can span more than fp16's range, so
+// the scale is per row): each 32-channel step of the row is converted with its own
+// exponent, and the steps are then aligned to the row's largest by exact fp16 factors.  The record holds the multipliers 2^er (Qt) and 2^eq (P) of every
+// row; the carry applies them to the outputs in fp32.
 #include "gdr_device.h"
 #include "gdr_launch.h"
 
@@ -90,6 +100,34 @@ struct In4<float> {
     __device__ __forceinline__ float operator[](int e) const {
         return e == 0 ? u.x : e == 1 ? u.y : e == 2 ? u.z : u.w;
     }
+};
+
+// Largest |q| over a lane's loaded elements.  bf16 magnitudes order like their bit
+// patterns with the sign cleared, so the maximum is taken on packed 16-bit integers and
+// widened once.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+template <typename TIn>
+struct AbsMax;
+template <>
+struct AbsMax<bf16_t> {
+    u16x2 m = {0, 0};
+    __device__ __forceinline__ void add(const In4<bf16_t>& x) {
+        const u16x2 a = __builtin_bit_cast(u16x2, x.u.x & 0x7FFF7FFFu);
+        const u16x2 b = __builtin_bit_cast(u16x2, x.u.y & 0x7FFF7FFFu);
+        m = __builtin_elementwise_max(m, __builtin_elementwise_max(a, b));
+    }
+    __device__ __forceinline__ float get() const {
+        const uint32_t bits = m[0] > m[1] ? m[0] : m[1];
+        return __uint_as_float(bits << 16);
+    }
+};
+template <>
+struct AbsMax<float> {
+    float m = 0.f;
+    __device__ __forceinline__ void add(const In4<float>& x) {
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(x.u.x), fabsf(x.u.y)), fmaxf(fabsf(x.u.z), fabsf(x.u.w))));
+    }
+    __device__ __forceinline__ float get() const { return m; }
 };
 
 __device__ __forceinline__ float f4(const float4& v, int e) {
@@ -254,6 +292,8 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
     constexpr int NCL = (DK + 63) / 64;  // channels per lane
     float c0[NCL], c1[NCL];
 #pragma unroll
+    for (int u = 0; u < NCL; ++u) c0[u] = c1[u] = 0.f;
+#pragma unroll
     for (int u = 0; u < NCL; ++u) {
         const int c = lane + 64 * u;
         if (c >= DK) break;
@@ -275,6 +315,17 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
         }
         if (I == 0) egl_out[c] = ex2(gl);  // exp(gam_last), natural base
     }
+    // query scale exponent of this block (wave-uniform), from the largest |q| of its rows
+    int eq;
+    {
+        AbsMax<TIn> am;
+#pragma unroll
+        for (int p = 0; p < KC; ++p)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) am.add(qin[p][hh]);
+        eq = exponent_of(wave_max(am.get()));
+    }
+    if (gq == 0) egl_out[R.psc + 16 * I + li] = ldexp2(1.f, eq);
     // Every wave is past reading the other blocks' totals once this barrier is passed, so a
     // wave may reuse its own block's slot: first for its decay constants, after this phase
     // for its diagonal tile.  Only this wave reads the slot from here on, and a wave's LDS
@@ -289,17 +340,16 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
         con[DK + c] = c1[u];
     }
     asm volatile("" ::: "memory");
+    half8 qh[KC];  // decayed query row, per 32-channel step times 2^-ep[p]
+    int ep[KC];
 #pragma unroll
     for (int p = 0; p < KC; ++p) {
         asm volatile("" ::: "memory");  // keep this step's LDS reads here (register pressure)
         // middle-row prefix and block total of each channel: rows 7 and 15 of the lane's
         // 16-lane row, which holds one token row per lane for the same channels
-        float md[8], ti[8], c2[8], c3[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            md[jj] = row_bcast<7>(x[p][jj]);
-            ti[jj] = row_bcast<15>(x[p][jj]);
-        }
+        half8 as;
+        float qe[8];
+        float pm = 0.f;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int cb = 32 * p + 16 * hh + 4 * gq;
@@ -307,45 +357,56 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
             const float4 k3 = *reinterpret_cast<const float4*>(con + DK + cb);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                c2[4 * hh + e] = f4(k2, e);
-                c3[4 * hh + e] = f4(k3, e);
+                const int jj = 4 * hh + e;
+                const int c = cb + e;
+                const float kv = kin[p][hh][e];
+                const float qv = qin[p][hh][e];
+                // middle-row prefix and block total of this channel: rows 7 and 15 of the
+                // lane's 16-lane row, which holds one token row per lane for the same channels
+                const float dz = x[p][jj] - row_bcast<7>(x[p][jj]);
+                const float z = ex2(dz);
+                const float zi = ex2(-dz);
+                const float eg = z * f4(k2, e);
+                qe[jj] = qv * eg;
+                pm = fmaxf(pm, fabsf(qe[jj]));
+                s.sKT[c * KTP + kt_swz<C>(c, r)] = static_cast<_Float16>(kv * eg);
+                s.sKbT[c * KTP + kt_swz<C>(c, r)] = static_cast<_Float16>(kv * (zi * f4(k3, e)));
+                // diagonal tiles on the fp32 matrix cores: reduction step = this slot's channel
+                // in each of the four lane groups
+                const float a = kv * zi;
+                accA = mfma_f32(a, kv * z, accA);
+                accP = mfma_f32(a, qv * z, accP);
+                if constexpr (I > 0) {
+                    const float zs = ex2(x[p][jj]);  // exp(gam - gam_{16I-1}) <= 1
+                    bk[p][jj] = static_cast<_Float16>(kv * zs);
+                    bq[p][jj] = static_cast<_Float16>(ldexp2(qv * zs, -eq));
+                }
+                if constexpr (I < NB - 1)
+                    as[jj] = static_cast<_Float16>(kv * ex2(row_bcast<15>(x[p][jj]) - x[p][jj]));
             }
         }
-        half8 qt, as;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const int hh = jj >> 2, e = jj & 3;
-            const int c = 32 * p + 16 * hh + 4 * gq + e;
-            const float kv = kin[p][hh][e];
-            const float qv = qin[p][hh][e];
-            const float dz = x[p][jj] - md[jj];
-            const float z = ex2(dz);
-            const float zi = ex2(-dz);
-            const float eg = z * c2[jj];
-            qt[jj] = static_cast<_Float16>(qv * eg);
-            s.sKT[c * KTP + kt_swz<C>(c, r)] = static_cast<_Float16>(kv * eg);
-            s.sKbT[c * KTP + kt_swz<C>(c, r)] = static_cast<_Float16>(kv * (zi * c3[jj]));
-            // diagonal tiles on the fp32 matrix cores: reduction step = this slot's channel
-            // in each of the four lane groups
-            const float a = kv * zi;
-            accA = mfma_f32(a, kv * z, accA);
-            accP = mfma_f32(a, qv * z, accP);
-            if constexpr (I > 0) {
-                const float zs = ex2(x[p][jj]);  // exp(gam - gam_{16I-1}) <= 1
-                bk[p][jj] = static_cast<_Float16>(kv * zs);
-                bq[p][jj] = static_cast<_Float16>(qv * zs);
-            }
-            if constexpr (I < NB - 1) as[jj] = static_cast<_Float16>(kv * ex2(ti[jj] - x[p][jj]));
-        }
-        frags[(size_t)(R.off_qt + I * KC + p) * 64 + lane] = qt;
         if constexpr (I < NB - 1) s.sAs[(I * KC + p) * 64 + lane] = as;
+        ep[p] = exponent_of(max_over_groups(pm));  // row r's entries of this step: lanes li + 16g
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) qh[p][jj] = static_cast<_Float16>(ldexp2(qe[jj], -ep[p]));
+    }
+    {  // Qt row r times 2^-er, er = the row's largest step exponent
+        int er = ep[0];
+#pragma unroll
+        for (int p = 1; p < KC; ++p) er = max(er, ep[p]);
+#pragma unroll
+        for (int p = 0; p < KC; ++p) {
+            const _Float16 f = half_pow2(ep[p] - er);
+            frags[(size_t)(R.off_qt + I * KC + p) * 64 + lane] = qh[p] * half8{f, f, f, f, f, f, f, f};
+        }
+        if (gq == 0) egl_out[R.qsc + 16 * I + li] = ldexp2(1.f, er);
     }
     // diagonal tiles in row layout: gram rows times beta_r, strictly lower; causal lower
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int sl = 4 * gq + i;
         accA[i] = sl < li ? accA[i] * bta : 0.f;
-        accP[i] = sl <= li ? accP[i] : 0.f;
+        accP[i] = sl <= li ? ldexp2(accP[i], -eq) : 0.f;
     }
 
     // ---- diagonal block inverse, rows by lane: T_II = (I + A_II)^-1 ----------------------

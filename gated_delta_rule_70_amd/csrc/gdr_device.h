@@ -94,6 +94,43 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// ---- magnitude reductions and power-of-two scaling --------------------------------------
+// Operands of the fp16 matrix-core products are brought into fp16's range by exact
+// power-of-two factors; these helpers find the exponents.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// max(x[l], x[l ^ 16]) and max(x[l], x[l ^ 32]) in every lane (gfx950 lane-swap moves)
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Maximum over the four lanes l % 16 + 16 * g (g = 0..3): one column of an accumulator tile.
+__device__ __forceinline__ float max_over_groups(float x) { return max_xor32(max_xor16(x)); }
+// Maximum over the whole wave, in every lane.
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_mov<0x124>(x));  // row_ror:4
+    x = fmaxf(x, dpp_mov<0x128>(x));  // row_ror:8
+    return max_over_groups(x);
+}
+// Exponent e with m = f * 2^e, f in [0.5, 1) (0 for m == 0, inf or NaN).
+__device__ __forceinline__ int exponent_of(float m) { return __builtin_amdgcn_frexp_expf(m); }
+// x * 2^e, exact while the result stays a normal fp32 number
+__device__ __forceinline__ float ldexp2(float x, int e) { return __builtin_amdgcn_ldexpf(x, e); }
+// 2^e as fp16 for e in [-24, 15] (0 below), the exact factor that aligns two scaled operands
+__device__ __forceinline__ _Float16 half_pow2(int e) {
+    if (e < -24) return static_cast<_Float16>(0.f);
+    return static_cast<_Float16>(ldexp2(1.f, e));
+}
+
 // Reduction-slot permutation used for every fragment that meets an accumulator tile.
 // Slot jj (0..7) of lane group g inside a 32-wide reduction step maps to index
 //   16 * (jj / 4) + 4 * g + (jj % 4)

@@ -26,9 +26,11 @@ struct LaunchArgs {
 
 // Per-(batch, head, chunk) record that the chunk-parallel kernel writes and the
 // sequential carry kernel reads: fp16 MFMA operand fragments (1 KiB each: 64 lanes x 8
-// halves, lane-major) followed by one 1 KiB block whose first dk floats hold the chunk's
-// total decay exp(gam_last).  Records are a whole number of KiB so the carry kernel can
-// stream one into LDS with 1 KiB wave-wide copies.
+// halves, lane-major) followed by one 1 KiB block of fp32 values: the chunk's total decay
+// exp(gam_last) [dk], then the row multipliers [C] of Qt and [C] of P (the query rows are
+// stored scaled by exact powers of two that keep them inside fp16's range; row r of the
+// true Qt is the stored row times its multiplier, likewise for P).  Records are a whole
+// number of KiB so the carry kernel can stream one into LDS with 1 KiB wave-wide copies.
 //   Qt  [nb][kc]    decayed queries exp(gam) * q           (rows r, reduction over dk)
 //   -W  [nb][kc]    negated WY pseudo-keys                  (rows r, reduction over dk)
 //   Kb  [dkt][nqs]  decay-to-end keys, transposed           (rows c, reduction over tokens)
@@ -49,6 +51,8 @@ struct ChunkRecord {
     int off_p;
     int nfrag;     // operand fragments; the decay block follows them
     int bytes;     // record stride: (nfrag + 1) KiB
+    int qsc;       // float offsets inside the decay block: Qt row multipliers [C]
+    int psc;       //                                       P row multipliers [C]
 
     __host__ __device__ static constexpr ChunkRecord make(int C, int dk) {
         ChunkRecord r{};
@@ -63,6 +67,8 @@ struct ChunkRecord {
         r.off_p = r.off_tb + r.nb * r.nqs;
         r.nfrag = r.off_p + r.nb * r.nqs;
         r.bytes = (r.nfrag + 1) * 1024;
+        r.qsc = dk;
+        r.psc = dk + C;  // dk + 2C <= 256 floats for dk <= 128, C <= 64
         return r;
     }
 };

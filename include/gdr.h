@@ -38,6 +38,16 @@
  *     decay over any 8 consecutive tokens below 80 in every channel (exp(g) >= ~5e-5 per
  *     token); outside that range the prefill path's intra-chunk decay factors can
  *     overflow fp32.  The decode and fused recurrent paths have no such limit.
+ *   - Magnitudes.  The prefill's matrix-core products take fp16 operands, each brought into
+ *     fp16's range by exact power-of-two scales: per query row (and 16-row block) for q, per
+ *     column group and chunk for the state and for v, each separately.  So q, v, h0 and the
+ *     state may take any magnitude within fp32's normal range, independently of each other,
+ *     and results match the fp64 recurrence to the same relative accuracy at any such scale.
+ *     Two limits remain: the pseudo-values U = Tb V - W S keep fp16's precision while
+ *     beta >= 2^-12 (beta = 0 exactly is exact), and the segmented carry's transition
+ *     matrices assume non-expansive updates (beta |k|^2 <= 2, e.g. unit-norm keys with beta
+ *     in [0, 1]).  Keys are used as given (no normalisation); their entries must be
+ *     representable in fp16 (|k| < 65504).
  *   - Results are bitwise reproducible for identical inputs and dims (no atomics).
  */
 #ifndef GDR_H

@@ -8,7 +8,7 @@ import torch
 import gated_delta_rule_70_amd as gdr
 import oracle
 from gdr_synth import make_tree
-from gpu_util import TOL, dev, err, note, small_inputs
+from gpu_util import TOL, dev, err, note, small_inputs, token_err
 
 pytestmark = pytest.mark.gpu
 
@@ -71,3 +71,31 @@ def test_tree_verify(kind):
     o = gdr.tree_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], par.cuda(), h0=d["h0"])
     torch.cuda.synchronize()
     assert err(o, ref) < TOL
+
+
+def test_beta0_per_token():
+    """beta = 0: every output is the decayed initial state read by that token's query, and
+    falls by ~e^-56 over the 70 tokens.  The whole-tensor bar only sees the first tokens,
+    so every token is held to the bar relative to its own largest output, on the chunked
+    path (chunks 64, 32, 16), the fused recurrence, the decode step and tree verify (a
+    chain, which is the sequential recurrence)."""
+    x = _inputs("beta0", seed=403)
+    o_ref, ht_ref = oracle.sequential(**x)
+    d = dev(x)
+    note("beta = 0 per-token bar: chunked, fused, decode, tree")
+    outs = {f"chunk{C}": gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], chunk=C)[0]
+            for C in (64, 32, 16)}
+    outs["fused"] = gdr.fused_recurrent(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"])[0]
+    state = d["h0"].clone()
+    steps = [gdr.decode_step(*(d[n][:, t:t + 1].contiguous() for n in ("q", "k", "v", "g", "beta")), state)
+             for t in range(T)]
+    outs["decode"] = torch.cat(steps, 1)
+    chain = make_tree(B, 48, "chain", seed=0).cuda()
+    sub = {n: (d[n][:, :48].contiguous() if n != "h0" else d[n]) for n in d}
+    o_tree = gdr.tree_verify(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], chain, h0=sub["h0"])
+    torch.cuda.synchronize()
+    for name, o in outs.items():
+        e = token_err(o, o_ref)
+        assert e < TOL, f"{name}: per-token error {e:.2e}"
+    e = token_err(o_tree, o_ref[:, :48])
+    assert e < TOL, f"tree: per-token error {e:.2e}"
