@@ -21,12 +21,14 @@ import os
 
 import torch
 
-__all__ = ["decode_step", "fused_recurrent", "chunk_prefill", "forward", "tree_verify",
+__all__ = ["decode_step", "fused_recurrent", "chunk_prefill", "chunk_prefill_noalloc", "forward",
+           "tree_verify", "NOALLOC_SCRATCH_BYTES",
            "workspace_bytes", "GdrError", "lib", "Dims", "LIB_PATH", "ABI_VERSION",
            "RECURRENT_MAX_T", "TREE_MAX_T"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so")
-ABI_VERSION = 3
+ABI_VERSION = 4
+NOALLOC_SCRATCH_BYTES = 64 << 20  # gdr_chunk_prefill_noalloc: the library's per-device scratch
 RECURRENT_MAX_T = 8  # gdr_forward: calls of at most this many tokens take the fused recurrence
 TREE_MAX_T = 64      # gdr_tree_verify: most nodes per tree
 BF16, F32 = 0, 1
@@ -73,6 +75,8 @@ def lib():
     L.gdr_chunk_prefill_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
     L.gdr_chunk_prefill.restype = ctypes.c_int
     L.gdr_chunk_prefill.argtypes = [ctypes.POINTER(Dims)] + [_VP] * 9 + [ctypes.c_size_t, _VP]
+    L.gdr_chunk_prefill_noalloc.restype = ctypes.c_int
+    L.gdr_chunk_prefill_noalloc.argtypes = [ctypes.POINTER(Dims)] + [_VP] * 9
     for name in ("gdr_chunk_prep", "gdr_chunk_carry"):
         fn = getattr(L, name)
         fn.restype = ctypes.c_int
@@ -212,6 +216,29 @@ def chunk_prefill(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
     _check(getattr(lib(), entry)(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                    _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht), _ptr(workspace),
                                    ctypes.c_size_t(workspace.numel()), _stream(stream)))
+    return o, ht
+
+
+def chunk_prefill_noalloc(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
+                          want_state: bool = True, stream=None):
+    """gdr_chunk_prefill_noalloc: the chunked prefill with the library's own per-device
+    scratch as workspace (no device allocation inside the call; pass ``o`` and ``ht`` to
+    allocate nothing here either).  Returns ``(o, ht)``.  Calls needing more than
+    ``NOALLOC_SCRATCH_BYTES`` of workspace raise GdrError (status GDR_ERR_SCRATCH)."""
+    B, T, HK, HV, dk, dv = _check_shapes(q, k, v, g, beta, h0=h0, o=o, ht=ht)
+    _check_inputs(q, k, v, g, beta)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    if o is None:
+        o = torch.empty(B, T, HV, dv, device=q.device, dtype=torch.float32)
+    _need(o, "o", torch.float32)
+    if ht is None and want_state:
+        ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
+    if ht is not None:
+        _need(ht, "ht", torch.float32)
+    d = _dims(q, v, chunk, g)
+    _check(lib().gdr_chunk_prefill_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                           _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht), _stream(stream)))
     return o, ht
 
 

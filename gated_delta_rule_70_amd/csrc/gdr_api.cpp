@@ -7,9 +7,33 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gdr_launch.h"
 
+// Workspace of the allocation-free prefill entry point (see gdr.h).  In host code `scratch`
+// is only a handle to the device array; its address on a device comes from
+// hipGetSymbolAddress, looked up once per device and cached.
+static __device__ __align__(256) unsigned char scratch[GDR_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (nullptr on a HIP error).
+void* scratch_on_current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
 
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
@@ -149,6 +173,7 @@ const char* gdr_status_str(int status) {
         case GDR_ERR_ALIAS: return "output buffers overlap inputs, or ht partially overlaps h0";
         case GDR_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case GDR_ERR_HIP: return "HIP runtime error or kernel launch failure";
+        case GDR_ERR_SCRATCH: return "call needs more workspace than the allocation-free entry point's scratch";
         default: return "unknown status";
     }
 }
@@ -218,6 +243,21 @@ int gdr_chunk_prefill(const gdr_dims* dims, const void* q, const void* k, const 
                       const void* g, const float* beta, const float* h0, float* o, float* ht,
                       void* workspace, size_t workspace_bytes, void* stream) {
     return prefill_stages(dims, q, k, v, g, beta, h0, o, ht, workspace, workspace_bytes, stream,
+                          true, true);
+}
+
+int gdr_chunk_prefill_noalloc(const gdr_dims* dims, const void* q, const void* k, const void* v,
+                              const void* g, const float* beta, const float* h0, float* o,
+                              float* ht, void* stream) {
+    Sizes s;
+    const int st = validate(dims, Path::chunked, q, k, v, g, beta, h0, o, ht, &s);
+    if (st != GDR_OK) return st;
+    const size_t need = workspace_bytes_unchecked(dims);
+    if (need == 0) return GDR_ERR_SHAPE;
+    if (need > GDR_NOALLOC_SCRATCH_BYTES) return GDR_ERR_SCRATCH;
+    void* ws = scratch_on_current_device();
+    if (!ws) return GDR_ERR_HIP;
+    return prefill_stages(dims, q, k, v, g, beta, h0, o, ht, ws, GDR_NOALLOC_SCRATCH_BYTES, stream,
                           true, true);
 }
 

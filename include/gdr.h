@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 3
+#define GDR_ABI_VERSION 4
 
 typedef enum {
     GDR_OK = 0,
@@ -71,7 +71,9 @@ typedef enum {
     GDR_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned                   */
     GDR_ERR_ALIAS = 5,       /* o overlaps an input/h0/ht, or ht partially overlaps h0    */
     GDR_ERR_WORKSPACE = 6,   /* workspace NULL, misaligned or smaller than required       */
-    GDR_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed                 */
+    GDR_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed                 */
+    GDR_ERR_SCRATCH = 8      /* gdr_chunk_prefill_noalloc: the call needs more workspace than
+                                GDR_NOALLOC_SCRATCH_BYTES                                   */
 } gdr_status;
 
 typedef enum { GDR_BF16 = 0, GDR_F32 = 1 } gdr_dtype;
@@ -200,6 +202,24 @@ int gdr_forward(const gdr_dims* dims, const void* q, const void* k, const void* 
 int gdr_tree_verify(const gdr_dims* dims, const int32_t* parent, const void* q, const void* k,
                     const void* v, const void* g, const float* beta, const float* h0, float* o,
                     void* stream);
+
+/*
+ * Allocation-free variant of gdr_chunk_prefill, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, checks and results as gdr_chunk_prefill, minus the
+ * workspace: the library uses its own per-device scratch array of GDR_NOALLOC_SCRATCH_BYTES
+ * (64 MiB: the chunk records of a 2048-token prefill at HV = 32, dk = 128, chunk 64), which
+ * each GPU the library runs on holds until the process ends.  Calls whose workspace
+ * (gdr_chunk_prefill_workspace_bytes) exceeds it return GDR_ERR_SCRATCH before any HIP
+ * call.  It calls no allocating routine (the array's device address is looked up once per
+ * device, on the first call made with that device current).  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (concurrent streams or threads) race and
+ * must be serialised by the caller.  The array's contents between calls are not meaningful.
+ */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int gdr_chunk_prefill_noalloc(const gdr_dims* dims, const void* q, const void* k, const void* v,
+                              const void* g, const float* beta, const float* h0, float* o,
+                              float* ht, void* stream);
 
 /* Static English text for a status code (never NULL). */
 const char* gdr_status_str(int status);

@@ -36,8 +36,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "gdr_abi_version", "gdr_chunk_carry", "gdr_chunk_prefill", "gdr_chunk_prefill_workspace_bytes",
-        "gdr_chunk_prep", "gdr_decode_step", "gdr_forward", "gdr_fused_recurrent", "gdr_status_str",
-        "gdr_tree_verify"])
+        "gdr_chunk_prefill_noalloc", "gdr_chunk_prep", "gdr_decode_step", "gdr_forward",
+        "gdr_fused_recurrent", "gdr_status_str", "gdr_tree_verify"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -51,8 +51,8 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_version_and_status_strings(L):
     assert L.gdr_abi_version() == gdr.ABI_VERSION
-    texts = {L.gdr_status_str(s).decode() for s in range(8)}
-    assert len(texts) == 8
+    texts = {L.gdr_status_str(s).decode() for s in range(9)}
+    assert len(texts) == 9
     assert L.gdr_status_str(99).decode() == "unknown status"
 
 
