@@ -377,6 +377,62 @@ def bench_io_lean(w, steps=10, warmup=2):
             "path_hbm_frac": round((b_prep + b_carry) / (kern * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def bench_prologue(w, steps=10, warmup=2):
+    """The fused input prologue (GDR_K_L2NORM | GDR_G_SOFTPLUS) on the headline prefill:
+    raw keys and gate logits handed to the library, against the caller doing the key
+    normalisation and the softplus decay as separate passes (torch on the GPU) and then
+    calling the plain prefill.  Reports both times and the HBM bytes the fusion removes (the
+    separate passes read and write k and g once each)."""
+    import torch
+    import torch.nn.functional as F
+
+    import gated_delta_rule_70_amd as gdr
+    from gdr_synth import workload_inputs
+
+    x = workload_inputs(w)
+    d = {k: (None if v is None else v.cuda()) for k, v in x.items()}
+    gen = torch.Generator("cpu").manual_seed(w.seed + 77)
+    a = torch.randn(w.B, w.T, w.HV, w.dk, generator=gen).cuda()   # gate logits
+    kraw = (d["k"].float() * 3.0).to(d["k"].dtype)                 # keys off the unit sphere
+    B, T, HK, HV, dk, dv, C = w.B, w.T, w.HK, w.HV, w.dk, w.dv, w.chunk
+    ws = torch.empty(gdr.workspace_bytes(B, T, HK, HV, dk, dv, C), dtype=torch.uint8, device="cuda")
+    o = torch.empty(B, T, HV, dv, device="cuda")
+    ht = torch.empty(B, HV, dk, dv, device="cuda")
+
+    def separate():
+        kn = F.normalize(kraw.float(), dim=-1).to(kraw.dtype)
+        g = -F.softplus(a)
+        gdr.chunk_prefill(d["q"], kn, d["v"], g, d["beta"], h0=d["h0"], chunk=C, o=o, ht=ht, workspace=ws)
+
+    def fused():
+        gdr.chunk_prefill(d["q"], kraw, d["v"], a, d["beta"], h0=d["h0"], chunk=C, o=o, ht=ht, workspace=ws,
+                          k_l2norm=True, g_softplus=True)
+
+    res = {}
+    for name, fn in (("separate_passes", separate), ("fused", fused)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) / steps, 5)
+    elt = 2 if w.dtype == torch.bfloat16 else 4
+    kbytes = B * T * HK * dk * elt
+    gbytes = B * T * HV * dk * 4
+    return {"workload": f"{w.name}, raw keys and gate logits", "ms_per_step": res,
+            "tokens_per_s_fused": round(B * T / (res["fused"] * 1e-3), 1),
+            "bytes_removed": 2 * (kbytes + gbytes),
+            "what": "the separate passes read and write k (bf16) and g (fp32) once each; "
+                    "the fused prologue reads the raw inputs where the kernels already read k and g"}
+
+
+OTHER_OUTPUTS = {}  # workload name -> (inputs, o, ht) of the last bench_other_prefills run
+
+
 def bench_other_prefills(steps=5, warmup=1):
     """The other full-size prefill workloads: per-stage kernel times (HIP events on the launch
     stream, back-to-back calls), throughput, and which carry the library picks."""
@@ -391,7 +447,9 @@ def bench_other_prefills(steps=5, warmup=1):
                     "ms_per_step": round(wall / steps * 1e3, 5),
                     "tokens_per_s": round(w.B * w.T / (wall / steps), 1),
                     "carry": carry_plan(w.B, w.T, w.HV, w.dk, w.dv, w.chunk)})
-        del x, o, ht
+        # this run's outputs, kept on the host for the parity check of the CPU-baseline leg
+        OTHER_OUTPUTS[name] = (x, o.cpu(), ht.cpu())
+        del o, ht
     return out
 
 
@@ -705,7 +763,7 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-util", metavar="UTIL_DIR")
     ap.add_argument("--summarize-stats", nargs=3, metavar=("DIR", "NAME", "COMMAND"))
-    ap.add_argument("--section", choices=("tree", "short_calls"),
+    ap.add_argument("--section", choices=("tree", "short_calls", "prologue"),
                     help="run only this part of the benchmark (tree-verify cases or short calls) "
                          "and print its JSON; for kernel traces of those kernels")
     ap.add_argument("--profile-name", default=HEADLINE_PROFILE,
@@ -740,7 +798,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     if args.section:
-        res = bench_tree(DECODE) if args.section == "tree" else bench_short_calls(DECODE)
+        if args.section == "prologue":
+            from gdr_synth import WORKLOADS
+            res = bench_prologue(WORKLOADS[args.workload])
+        else:
+            res = bench_tree(DECODE) if args.section == "tree" else bench_short_calls(DECODE)
         print(json.dumps({"section": args.section, **res}), flush=True)
         return
     w = WORKLOADS[args.workload]
@@ -826,6 +888,7 @@ def main():
         line["tree_verify"] = bench_tree(DECODE)
         line["other_prefills"] = bench_other_prefills()
         line["io_lean"] = bench_io_lean(w)
+        line["prologue"] = bench_prologue(w)
 
     if not args.no_cpu_baseline:
         import numpy as np
@@ -861,6 +924,14 @@ def main():
             "o": float(oracle.rel_err(o.double().cpu().numpy(), o_ref)),
             "state": float(oracle.rel_err(ht.double().cpu().numpy(), ht_ref)),
             "tolerance": 2e-3}
+        # the other full-size prefills of this run, every head, against the same oracle
+        # (for the long conditioning-stress sequence this is its final-state error)
+        for name, (xo, oo, hto) in OTHER_OUTPUTS.items():
+            oref, htref = oracle.sequential(**xo)
+            line["parity_vs_oracle"][name] = {
+                "o": float(oracle.rel_err(oo.double().numpy(), oref)),
+                "state": float(oracle.rel_err(hto.double().numpy(), htref))}
+            del oref, htref
         del np
     print(json.dumps(line), flush=True)
 

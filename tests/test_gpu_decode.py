@@ -6,7 +6,7 @@ import torch
 import gated_delta_rule_70_amd as gdr
 import oracle
 from gdr_synth import DECODE, workload_inputs
-from gpu_util import TOL, bf16_exact_unit_keys, dev, err, note, oracle_on_groups, sampled_groups, small_inputs
+from gpu_util import TOL, bf16_exact_unit_keys, dev, err, note, small_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -57,10 +57,10 @@ def test_decode_many_steps_in_place():
     assert err(obuf.transpose(0, 1), o_ref) < TOL and err(state, ht_ref) < TOL
 
 
-def test_decode_full_size_1000_steps_sampled():
-    """The measured decode workload: B=32, HK=16, HV=32, dk=dv=128, 1000 carried steps.
-    Every step runs at full size; sampled (batch, key-head) groups are checked against the
-    oracle on all 1000 outputs and on the final state."""
+def test_decode_full_size_1000_steps_all_heads():
+    """The measured decode workload: B=32, HK=16, HV=32, dk=dv=128, 1000 carried steps,
+    every (batch, value head) checked against the oracle on all 1000 outputs and on the
+    final state."""
     w = DECODE
     x = workload_inputs(w)
     d = dev(x)
@@ -70,16 +70,11 @@ def test_decode_full_size_1000_steps_sampled():
     note("decode full size 1000 steps")
     _run_steps(d, state, T, tm, obuf)
     torch.cuda.synchronize()
-    G = w.HV // w.HK
-    groups = sampled_groups(w.B, w.HK, 4, seed=2)
-    ref = oracle_on_groups(x, groups, G)
-    o_all = obuf.cpu()
-    st = state.cpu()
-    for (b, kh), (o_r, ht_r) in ref.items():
-        hv = slice(kh * G, (kh + 1) * G)
-        eo = err(o_all[:, b, hv], o_r)
-        es = err(st[b, hv], ht_r)
-        assert eo < TOL and es < TOL, f"group {(b, kh)}: o {eo:.2e} state {es:.2e}"
+    o_ref, ht_ref = oracle.sequential(**x)
+    eo = err(obuf.transpose(0, 1), o_ref)
+    es = err(state, ht_ref)
+    print(f"decode 1000 steps: o {eo:.2e} state {es:.2e}")
+    assert eo < TOL and es < TOL, f"o {eo:.2e} state {es:.2e}"
 
 
 def test_decode_exact_write():
