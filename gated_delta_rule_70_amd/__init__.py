@@ -27,12 +27,14 @@ __all__ = ["decode_step", "fused_recurrent", "chunk_prefill", "chunk_prefill_noa
            "RECURRENT_MAX_T", "TREE_MAX_T"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so")
-ABI_VERSION = 4
+ABI_VERSION = 5
 NOALLOC_SCRATCH_BYTES = 64 << 20  # gdr_chunk_prefill_noalloc: the library's per-device scratch
 RECURRENT_MAX_T = 8  # gdr_forward: calls of at most this many tokens take the fused recurrence
 TREE_MAX_T = 64      # gdr_tree_verify: most nodes per tree
 BF16, F32 = 0, 1
 G_BF16 = 0x1  # gdr_dims.flags: g stored as bf16
+K_L2NORM = 0x2  # keys given raw; the kernels normalise each key row (fused prologue)
+G_SOFTPLUS = 0x4  # g given as gate logits a; the kernels use -softplus(a)
 
 
 class Dims(ctypes.Structure):
@@ -113,10 +115,11 @@ def _need(t: torch.Tensor, name: str, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
-def _dims(q, v, chunk, g=None) -> Dims:
+def _dims(q, v, chunk, g=None, k_l2norm=False, g_softplus=False) -> Dims:
     B, T, HK, dk = q.shape
     HV, dv = v.shape[2], v.shape[3]
     flags = G_BF16 if g is not None and g.dtype == torch.bfloat16 else 0
+    flags |= (K_L2NORM if k_l2norm else 0) | (G_SOFTPLUS if g_softplus else 0)
     return Dims(B, T, HK, HV, dk, dv, int(chunk), _qkv_dtype(q), flags)
 
 
@@ -165,7 +168,8 @@ def workspace_bytes(B, T, HK, HV, dk, dv, chunk=64, dtype=torch.bfloat16) -> int
     return int(lib().gdr_chunk_prefill_workspace_bytes(ctypes.byref(d)))
 
 
-def decode_step(q, k, v, g, beta, state, o=None, out_state=None, stream=None):
+def decode_step(q, k, v, g, beta, state, o=None, out_state=None, stream=None, k_l2norm=False,
+                g_softplus=False):
     """One decode step (T == 1).  Updates ``state`` in place unless ``out_state`` is given.
 
     ``state`` may be None (zero initial state; then ``out_state`` receives the new state if
@@ -181,14 +185,15 @@ def decode_step(q, k, v, g, beta, state, o=None, out_state=None, stream=None):
     _need(o, "o", torch.float32)
     if ht is not None:
         _need(ht, "out_state", torch.float32)
-    d = _dims(q, v, 0, g)
+    d = _dims(q, v, 0, g, k_l2norm, g_softplus)
     _check(lib().gdr_decode_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                  _ptr(state), _ptr(o), _ptr(ht), _stream(stream)))
     return o
 
 
 def chunk_prefill(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
-                  workspace=None, want_state: bool = True, stream=None, stage: str = "both"):
+                  workspace=None, want_state: bool = True, stream=None, stage: str = "both",
+                  k_l2norm=False, g_softplus=False):
     """Chunkwise WY/UT prefill over all T tokens.  Returns ``(o, ht)`` (``ht`` None if not wanted).
 
     ``workspace`` (optional) is a uint8 GPU tensor of at least ``workspace_bytes(...)``
@@ -208,7 +213,7 @@ def chunk_prefill(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
         ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
     if ht is not None:
         _need(ht, "ht", torch.float32)
-    d = _dims(q, v, chunk, g)
+    d = _dims(q, v, chunk, g, k_l2norm, g_softplus)
     need = int(lib().gdr_chunk_prefill_workspace_bytes(ctypes.byref(d)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
@@ -220,7 +225,7 @@ def chunk_prefill(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
 
 
 def chunk_prefill_noalloc(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
-                          want_state: bool = True, stream=None):
+                          want_state: bool = True, stream=None, k_l2norm=False, g_softplus=False):
     """gdr_chunk_prefill_noalloc: the chunked prefill with the library's own per-device
     scratch as workspace (no device allocation inside the call; pass ``o`` and ``ht`` to
     allocate nothing here either).  Returns ``(o, ht)``.  Calls needing more than
@@ -236,14 +241,14 @@ def chunk_prefill_noalloc(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht
         ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
     if ht is not None:
         _need(ht, "ht", torch.float32)
-    d = _dims(q, v, chunk, g)
+    d = _dims(q, v, chunk, g, k_l2norm, g_softplus)
     _check(lib().gdr_chunk_prefill_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                            _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht), _stream(stream)))
     return o, ht
 
 
 def fused_recurrent(q, k, v, g, beta, h0=None, o=None, ht=None, want_state: bool = True,
-                    stream=None):
+                    stream=None, k_l2norm=False, g_softplus=False):
     """The token recurrence over all T tokens in one launch (gdr_fused_recurrent): the state
     stays on chip for the whole call.  Returns ``(o, ht)``; ``ht`` may be ``h0`` itself
     (in-place), and is None if not wanted."""
@@ -258,14 +263,14 @@ def fused_recurrent(q, k, v, g, beta, h0=None, o=None, ht=None, want_state: bool
         ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
     if ht is not None:
         _need(ht, "ht", torch.float32)
-    d = _dims(q, v, 0, g)
+    d = _dims(q, v, 0, g, k_l2norm, g_softplus)
     _check(lib().gdr_fused_recurrent(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                      _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht), _stream(stream)))
     return o, ht
 
 
 def forward(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None, workspace=None,
-            want_state: bool = True, stream=None):
+            want_state: bool = True, stream=None, k_l2norm=False, g_softplus=False):
     """Routed call (gdr_forward): the fused recurrence for T <= RECURRENT_MAX_T, the chunked
     prefill otherwise.  Returns ``(o, ht)``."""
     B, T, HK, HV, dk, dv = _check_shapes(q, k, v, g, beta, h0=h0, o=o, ht=ht)
@@ -279,7 +284,7 @@ def forward(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None, workspa
         ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
     if ht is not None:
         _need(ht, "ht", torch.float32)
-    d = _dims(q, v, chunk, g)
+    d = _dims(q, v, chunk, g, k_l2norm, g_softplus)
     if T > RECURRENT_MAX_T and workspace is None:
         need = int(lib().gdr_chunk_prefill_workspace_bytes(ctypes.byref(d)))
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
@@ -292,7 +297,8 @@ def forward(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None, workspa
     return o, ht
 
 
-def tree_verify(q, k, v, g, beta, parent, h0=None, o=None, stream=None):
+def tree_verify(q, k, v, g, beta, parent, h0=None, o=None, stream=None, k_l2norm=False,
+                g_softplus=False):
     """Tree-verify solve (gdr_tree_verify): ``parent`` is an int32 GPU tensor ``[B,T]`` of
     parent node indices (-1: continues from ``h0``).  Returns ``o`` ``[B,T,HV,dv]``, each
     node's output along its root path."""
@@ -304,7 +310,7 @@ def tree_verify(q, k, v, g, beta, parent, h0=None, o=None, stream=None):
     if o is None:
         o = torch.empty(B, T, HV, dv, device=q.device, dtype=torch.float32)
     _need(o, "o", torch.float32)
-    d = _dims(q, v, 0, g)
+    d = _dims(q, v, 0, g, k_l2norm, g_softplus)
     _check(lib().gdr_tree_verify(ctypes.byref(d), _ptr(parent), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                  _ptr(beta), _ptr(h0), _ptr(o), _stream(stream)))
     return o

@@ -45,6 +45,11 @@
 // the scale is per row): each 32-channel step of the row is converted with its own
 // exponent, and the steps are then aligned to the row's largest by exact fp16 factors.  The record holds the multipliers 2^er (Qt) and 2^eq (P) of every
 // row; the carry applies them to the outputs in fp32.
+//
+// Fused input prologue (template flags KN, GS): with KN the keys arrive raw and each row is
+// used divided by its L2 norm (the lane's row sum of squares, summed over its four lane
+// groups); with GS g arrives as gate logits a and the scan takes -softplus(a) directly in
+// log2 units.  Everything downstream is unchanged.
 #include "gdr_device.h"
 #include "gdr_launch.h"
 
@@ -194,7 +199,7 @@ struct PrepCtx {
 // The whole per-chunk computation as seen by wave I (a compile-time block index, so that
 // every per-block register array is indexed statically).  All waves pass the same number
 // of workgroup barriers.
-template <typename TIn, typename TG, int DK, int C, int I>
+template <typename TIn, typename TG, int DK, int C, int I, bool KN, bool GS>
 __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restrict__ q,
                                           const TIn* __restrict__ k, const TG* __restrict__ g,
                                           const float* __restrict__ beta, unsigned char* rec, int b,
@@ -258,7 +263,9 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
     for (int p = 0; p < KC; ++p)
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-            float v = x[p][jj] * kLog2e;
+            // rows past the sequence end are padding with no decay (a zero logit would
+            // still decay by ln 2)
+            float v = GS ? (tr < T ? neg_softplus_log2(x[p][jj]) : 0.f) : x[p][jj] * kLog2e;
             v += row_shr<1>(v);
             v += row_shr<2>(v);
             v += row_shr<4>(v);
@@ -326,6 +333,18 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
         eq = exponent_of(wave_max(am.get()));
     }
     if (gq == 0) egl_out[R.psc + 16 * I + li] = ldexp2(1.f, eq);
+    // with raw keys, this row's 1 / |k|_2 (its dk entries sit in lanes li + 16g)
+    float rn = 1.f;
+    if constexpr (KN) {
+        float s2 = 0.f;
+#pragma unroll
+        for (int p = 0; p < KC; ++p)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s2 = fmaf(kin[p][hh][e], kin[p][hh][e], s2);
+        rn = inv_key_norm(sum_over_groups(s2));
+    }
     // Every wave is past reading the other blocks' totals once this barrier is passed, so a
     // wave may reuse its own block's slot: first for its decay constants, after this phase
     // for its diagonal tile.  Only this wave reads the slot from here on, and a wave's LDS
@@ -359,7 +378,7 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
             for (int e = 0; e < 4; ++e) {
                 const int jj = 4 * hh + e;
                 const int c = cb + e;
-                const float kv = kin[p][hh][e];
+                const float kv = KN ? kin[p][hh][e] * rn : kin[p][hh][e];
                 const float qv = qin[p][hh][e];
                 // middle-row prefix and block total of this channel: rows 7 and 15 of the
                 // lane's 16-lane row, which holds one token row per lane for the same channels
@@ -568,8 +587,10 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
     if constexpr (I == NB - 1) finish_row();
 }
 
-template <typename TIn, typename TG, int DK, int C>
-__global__ __launch_bounds__(C * 4, 3) void chunk_prep_kernel(const TIn* __restrict__ q,
+// Three workgroups per CU (LDS and the 168-register budget allow it); the raw-key variant
+// needs a few more registers and runs two per CU rather than spill.
+template <typename TIn, typename TG, int DK, int C, bool KN, bool GS>
+__global__ __launch_bounds__(C * 4, KN ? 2 : 3) void chunk_prep_kernel(const TIn* __restrict__ q,
                                                               const TIn* __restrict__ k,
                                                               const TG* __restrict__ g,
                                                               const float* __restrict__ beta,
@@ -615,28 +636,28 @@ __global__ __launch_bounds__(C * 4, 3) void chunk_prep_kernel(const TIn* __restr
 #define GDR_WAVE(I_)                                                                             \
     if (I == I_) {                                                                               \
         if constexpr (I_ < NB)                                                                   \
-            prep_wave<TIn, TG, DK, C, I_>(s, q, k, g, beta, rec, b, T, HK, HV, h, kh, t0, L);    \
+            prep_wave<TIn, TG, DK, C, I_, KN, GS>(s, q, k, g, beta, rec, b, T, HK, HV, h, kh, t0, L); \
         return;                                                                                  \
     }
     GDR_WAVE(0) GDR_WAVE(1) GDR_WAVE(2) GDR_WAVE(3)
 #undef GDR_WAVE
 }
 
-template <typename TIn, typename TG, int DK, int C>
+template <typename TIn, typename TG, int DK, int C, bool KN, bool GS>
 hipError_t launch_prep_t(const LaunchArgs& a) {
     const int NC = (a.T + C - 1) / C;
     const long long pairs = (long long)a.B * a.HK * NC;  // (batch, key head, chunk) triples
     const long long blocks = (pairs + 7) / 8 * 8 * (a.HV / a.HK);
-    hipLaunchKernelGGL((chunk_prep_kernel<TIn, TG, DK, C>), dim3((unsigned)blocks), dim3(C * 4), 0,
+    hipLaunchKernelGGL((chunk_prep_kernel<TIn, TG, DK, C, KN, GS>), dim3((unsigned)blocks), dim3(C * 4), 0,
                        (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TG*)a.g, a.beta,
                        (unsigned char*)a.workspace, a.B, a.T, a.HK, a.HV, NC);
     return hipGetLastError();
 }
 
-template <typename TIn, typename TG>
+template <typename TIn, typename TG, bool KN, bool GS>
 hipError_t dispatch_prep(const LaunchArgs& a) {
 #define GDR_CASE(DK_, C_) \
-    if (a.dk == DK_ && a.chunk == C_) return launch_prep_t<TIn, TG, DK_, C_>(a);
+    if (a.dk == DK_ && a.chunk == C_) return launch_prep_t<TIn, TG, DK_, C_, KN, GS>(a);
     GDR_CASE(32, 16) GDR_CASE(32, 32) GDR_CASE(32, 64)
     GDR_CASE(64, 16) GDR_CASE(64, 32) GDR_CASE(64, 64)
     GDR_CASE(128, 16) GDR_CASE(128, 32) GDR_CASE(128, 64)
@@ -644,11 +665,17 @@ hipError_t dispatch_prep(const LaunchArgs& a) {
     return hipErrorInvalidValue;
 }
 
+template <bool KN, bool GS>
+hipError_t dispatch_prep_types(const LaunchArgs& a) {
+    if (a.qkv_f32) return dispatch_prep<float, float, KN, GS>(a);
+    return a.g_bf16 ? dispatch_prep<bf16_t, bf16_t, KN, GS>(a) : dispatch_prep<bf16_t, float, KN, GS>(a);
+}
+
 }  // namespace
 
 hipError_t launch_chunk_prep(const LaunchArgs& a) {
-    if (a.qkv_f32) return dispatch_prep<float, float>(a);
-    return a.g_bf16 ? dispatch_prep<bf16_t, bf16_t>(a) : dispatch_prep<bf16_t, float>(a);
+    if (a.k_l2norm) return a.g_softplus ? dispatch_prep_types<true, true>(a) : dispatch_prep_types<true, false>(a);
+    return a.g_softplus ? dispatch_prep_types<false, true>(a) : dispatch_prep_types<false, false>(a);
 }
 
 }  // namespace gdr

@@ -19,12 +19,17 @@
 // cross-lane shuffles inside the wave, then across the four waves through LDS (two
 // barriers per token; the two reduction buffers alternate so no third one is needed).
 // The next token's inputs are requested while the current one is processed.
+//
+// Fused input prologue (template flags KN, GS): with raw keys (KN) the prediction is formed
+// with the raw key and scaled by 1 / |k|_2 after its reduction (it is linear in k), the
+// sum of squares riding along in the same reduction, and the update uses d / |k|_2; with gate
+// logits (GS) the decay factor is exp(-softplus(a)) = 1 / (1 + e^a).
 #include "gdr_device.h"
 #include "gdr_launch.h"
 
 namespace gdr {
 
-template <typename TIn, typename TG, int DK, int DV>
+template <typename TIn, typename TG, int DK, int DV, bool KN, bool GS>
 __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
                                                     const TIn* __restrict__ k,
                                                     const TIn* __restrict__ v,
@@ -40,6 +45,7 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
 
     __shared__ f32x4 red_p[4][NQ];  // pass-1 partial sums of each wave
     __shared__ f32x4 red_o[4][NQ];  // output partial sums of each wave
+    __shared__ float red_k[4];      // each wave's sum of squared key entries (raw keys)
 
     const int ncb = DV / BVD;
     const int blk = blockIdx.x;
@@ -95,7 +101,7 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
         float e[RPT], kk[RPT], qq[RPT];
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
-            e[m] = __expf(gn[m]);
+            e[m] = GS ? decay_from_logit(gn[m]) : __expf(gn[m]);
             kk[m] = to_f32(kn[m]);
             qq[m] = to_f32(qn[m]);
         }
@@ -105,10 +111,12 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
 
         // pass 1: prediction with the decay folded in
         f32x4 p = {0.f, 0.f, 0.f, 0.f};
+        float s2 = 0.f;
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
             S[m] *= e[m];
             p += S[m] * kk[m];
+            if constexpr (KN) s2 = fmaf(kk[m], kk[m], s2);
         }
 #pragma unroll
         for (int off = NQ; off < 64; off <<= 1) {
@@ -116,13 +124,20 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
             p.y += __shfl_xor(p.y, off);
             p.z += __shfl_xor(p.z, off);
             p.w += __shfl_xor(p.w, off);
+            if constexpr (KN) s2 += __shfl_xor(s2, off);
         }
         // red_p is free: every thread read the previous token's sums before the previous
-        // token's second barrier
+        // token's second barrier (likewise red_k)
         if ((tid & 63) < NQ) red_p[wave][cq] = p;
+        if (KN && (tid & 63) == 0) red_k[wave] = s2;
         __syncthreads();
-        const f32x4 pred = red_p[0][cq] + red_p[1][cq] + red_p[2][cq] + red_p[3][cq];
-        const f32x4 d = (vv - pred) * bt;
+        f32x4 pred = red_p[0][cq] + red_p[1][cq] + red_p[2][cq] + red_p[3][cq];
+        float rn = 1.f;
+        if constexpr (KN) {
+            rn = inv_key_norm(red_k[0] + red_k[1] + red_k[2] + red_k[3]);
+            pred *= rn;
+        }
+        const f32x4 d = (vv - pred) * (bt * rn);  // d / |k|: the update then uses the raw key
 
         // pass 2: rank-one update of the (already decayed) state, output partial sums
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -161,7 +176,7 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
 // That keeps a thread within 64 registers, so eight waves fit per SIMD and every
 // workgroup of a decode step is resident at once: the whole state is requested in one
 // round instead of two.
-template <typename TIn, typename TG, int DK, int DV>
+template <typename TIn, typename TG, int DK, int DV, bool KN, bool GS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
                    const TG* __restrict__ g, const float* __restrict__ beta, const float* h0,
@@ -175,6 +190,7 @@ void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const T
     __shared__ float s_e[DK], s_k[DK], s_q[DK];
     __shared__ f32x4 red_p[4][NQ];
     __shared__ f32x4 red_o[4][NQ];
+    __shared__ float red_k[4];  // the key's sum of squares per staging wave (raw keys)
 
     const int ncb = DV / BVD;
     const int blk = blockIdx.x;
@@ -203,9 +219,19 @@ void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const T
     const size_t gb = ((size_t)b * HV + h) * DK;
     const size_t vb = ((size_t)b * HV + h) * DV + col;
     if (tid < DK) {
-        s_e[tid] = __expf(to_f32(g[gb + tid]));
+        const float gv = to_f32(g[gb + tid]);
+        s_e[tid] = GS ? decay_from_logit(gv) : __expf(gv);
         s_k[tid] = to_f32(k[kq + tid]);
         s_q[tid] = to_f32(q[kq + tid]);
+    }
+    if constexpr (KN) {  // the staging waves (threads < DK) reduce the key's sum of squares
+        if (tid < ((DK + 63) & ~63)) {
+            const float kx = tid < DK ? to_f32(k[kq + tid]) : 0.f;
+            float s2 = kx * kx;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) s2 += __shfl_xor(s2, off);
+            if ((tid & 63) == 0) red_k[wave] = s2;
+        }
     }
     const f32x4 vv = {to_f32(v[vb]), to_f32(v[vb + 1]), to_f32(v[vb + 2]), to_f32(v[vb + 3])};
     const float bt = beta[(size_t)b * HV + h];
@@ -227,8 +253,16 @@ void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const T
     }
     if ((tid & 63) < NQ) red_p[wave][cq] = p;
     __syncthreads();
-    const f32x4 pred = red_p[0][cq] + red_p[1][cq] + red_p[2][cq] + red_p[3][cq];
-    const f32x4 d = (vv - pred) * bt;
+    f32x4 pred = red_p[0][cq] + red_p[1][cq] + red_p[2][cq] + red_p[3][cq];
+    float rn = 1.f;
+    if constexpr (KN) {
+        float s2 = red_k[0];
+#pragma unroll
+        for (int w2 = 1; w2 < (DK + 63) / 64; ++w2) s2 += red_k[w2];
+        rn = inv_key_norm(s2);
+        pred *= rn;  // the prediction with the normalised key
+    }
+    const f32x4 d = (vv - pred) * (bt * rn);  // d / |k|: the update then uses the raw key
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -257,26 +291,26 @@ void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const T
     }
 }
 
-template <typename TIn, typename TG, int DK, int DV>
+template <typename TIn, typename TG, int DK, int DV, bool KN, bool GS>
 static hipError_t launch_tokens_t(const LaunchArgs& a) {
     constexpr int BVD = DV < 64 ? DV : 64;
     const long long nblk = (long long)a.B * a.HV * (DV / BVD);
     if (a.T == 1) {
-        hipLaunchKernelGGL((decode_kernel<TIn, TG, DK, DV>), dim3((unsigned)nblk), dim3(256), 0,
+        hipLaunchKernelGGL((decode_kernel<TIn, TG, DK, DV, KN, GS>), dim3((unsigned)nblk), dim3(256), 0,
                            (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
                            (const TG*)a.g, a.beta, a.h0, a.o, a.ht, a.HK, a.HV);
     } else {
-        hipLaunchKernelGGL((token_kernel<TIn, TG, DK, DV>), dim3((unsigned)nblk), dim3(256), 0,
+        hipLaunchKernelGGL((token_kernel<TIn, TG, DK, DV, KN, GS>), dim3((unsigned)nblk), dim3(256), 0,
                            (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
                            (const TG*)a.g, a.beta, a.h0, a.o, a.ht, a.T, a.HK, a.HV);
     }
     return hipGetLastError();
 }
 
-template <typename TIn, typename TG>
+template <typename TIn, typename TG, bool KN, bool GS>
 static hipError_t dispatch_dims(const LaunchArgs& a) {
 #define GDR_CASE(DK_, DV_) \
-    if (a.dk == DK_ && a.dv == DV_) return launch_tokens_t<TIn, TG, DK_, DV_>(a);
+    if (a.dk == DK_ && a.dv == DV_) return launch_tokens_t<TIn, TG, DK_, DV_, KN, GS>(a);
     GDR_CASE(32, 32) GDR_CASE(32, 64) GDR_CASE(32, 128)
     GDR_CASE(64, 32) GDR_CASE(64, 64) GDR_CASE(64, 128)
     GDR_CASE(128, 32) GDR_CASE(128, 64) GDR_CASE(128, 128)
@@ -285,9 +319,15 @@ static hipError_t dispatch_dims(const LaunchArgs& a) {
 }
 
 // Decode step and fused recurrent call: decode_kernel for T == 1, token_kernel otherwise.
+template <bool KN, bool GS>
+static hipError_t dispatch_types(const LaunchArgs& a) {
+    if (a.qkv_f32) return dispatch_dims<float, float, KN, GS>(a);
+    return a.g_bf16 ? dispatch_dims<bf16_t, bf16_t, KN, GS>(a) : dispatch_dims<bf16_t, float, KN, GS>(a);
+}
+
 hipError_t launch_tokens(const LaunchArgs& a) {
-    if (a.qkv_f32) return dispatch_dims<float, float>(a);
-    return a.g_bf16 ? dispatch_dims<bf16_t, bf16_t>(a) : dispatch_dims<bf16_t, float>(a);
+    if (a.k_l2norm) return a.g_softplus ? dispatch_types<true, true>(a) : dispatch_types<true, false>(a);
+    return a.g_softplus ? dispatch_types<false, true>(a) : dispatch_types<false, false>(a);
 }
 
 }  // namespace gdr

@@ -93,7 +93,7 @@ int validate(const gdr_dims* d, Path path, const void* q, const void* k, const v
     if (path == Path::decode && d->T != 1) return GDR_ERR_SHAPE;
     if (!supported_head_dim(d->dk) || !supported_head_dim(d->dv)) return GDR_ERR_UNSUPPORTED;
     if (d->qkv_dtype != GDR_BF16 && d->qkv_dtype != GDR_F32) return GDR_ERR_UNSUPPORTED;
-    if ((d->flags & ~GDR_G_BF16) != 0) return GDR_ERR_UNSUPPORTED;
+    if ((d->flags & ~(GDR_G_BF16 | GDR_K_L2NORM | GDR_G_SOFTPLUS)) != 0) return GDR_ERR_UNSUPPORTED;
     if ((d->flags & GDR_G_BF16) && d->qkv_dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
     if (path == Path::chunked && d->chunk != 16 && d->chunk != 32 && d->chunk != 64)
         return GDR_ERR_UNSUPPORTED;
@@ -134,6 +134,8 @@ gdr::LaunchArgs make_args(const gdr_dims* d, const void* q, const void* k, const
     a.chunk = d->chunk;
     a.qkv_f32 = d->qkv_dtype == GDR_F32;
     a.g_bf16 = (d->flags & GDR_G_BF16) != 0;
+    a.k_l2norm = (d->flags & GDR_K_L2NORM) != 0;
+    a.g_softplus = (d->flags & GDR_G_SOFTPLUS) != 0;
     a.q = q;
     a.k = k;
     a.v = v;

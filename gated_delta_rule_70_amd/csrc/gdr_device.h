@@ -111,6 +111,31 @@ __device__ __forceinline__ float max_xor32(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// x[l] + x[l ^ 16] + x[l ^ 32] + x[l ^ 48] in every lane: the four lane groups' sum
+__device__ __forceinline__ float sum_over_groups(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto u = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(u[0]) + __uint_as_float(u[1]);
+}
+
+// ---- fused input prologue ---------------------------------------------------------------
+// Keys given raw are used as k / max(|k|_2, 1e-12) (per token and key head); gate logits a
+// give the log-decay g = -softplus(a) = -log(1 + e^a).
+constexpr float kKeyNormEps = 1e-12f;
+__device__ __forceinline__ float inv_key_norm(float sum_sq) {
+    return 1.f / fmaxf(__builtin_sqrtf(sum_sq), kKeyNormEps);
+}
+// -softplus(a) in log2 units (g * log2(e)), stable for either sign of a
+__device__ __forceinline__ float neg_softplus_log2(float a) {
+    const float u = a * 1.4426950408889634f;
+    return -(fmaxf(u, 0.f) + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(u))));
+}
+// -softplus(a) in natural units: the log-decay g from a gate logit a
+__device__ __forceinline__ float neg_softplus(float a) { return neg_softplus_log2(a) * 0.6931471805599453f; }
+// exp(-softplus(a)) = 1 / (1 + e^a): the per-token decay factor from a gate logit
+__device__ __forceinline__ float decay_from_logit(float a) { return 1.f / (1.f + __expf(a)); }
+
 // Maximum over the four lanes l % 16 + 16 * g (g = 0..3): one column of an accumulator tile.
 __device__ __forceinline__ float max_over_groups(float x) { return max_xor32(max_xor16(x)); }
 // Maximum over the whole wave, in every lane.

@@ -11,7 +11,9 @@ namespace gdr {
 struct LaunchArgs {
     int B, T, HK, HV, dk, dv, chunk;
     bool qkv_f32;
-    bool g_bf16;  // g stored as bf16 (only with bf16 q/k/v)
+    bool g_bf16;      // g stored as bf16 (only with bf16 q/k/v)
+    bool k_l2norm;    // keys given raw: every kernel uses k / |k|_2 (fused prologue)
+    bool g_softplus;  // g given as gate logits a: every kernel uses -softplus(a)
     const void* q;
     const void* k;
     const void* v;

@@ -130,7 +130,9 @@ __device__ __forceinline__ f32x4 prefix_tile(unsigned long long bits, const floa
     return acc;
 }
 
-template <typename TIn, typename TG, int DK>
+// KN: keys given raw (each row used divided by its L2 norm); GS: g given as gate logits
+// (log-decay -softplus(a)).  The fused input prologue, applied where the rows are loaded.
+template <typename TIn, typename TG, int DK, bool KN, bool GS>
 __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int32_t* __restrict__ parent, const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const TG* __restrict__ g, const float* __restrict__ beta,
@@ -189,6 +191,10 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     for (int m = 0; m < NPASS; ++m) {
         const int t = min(tid / QPR + RPI * m, T - 1);
         gv[m] = load_g4(g, (((size_t)b * T + t) * HV + h) * DK + c4);
+        if constexpr (GS) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gv[m][e] = neg_softplus(gv[m][e]);
+        }
     }
     uint32_t kraw[NPASS][ELT], qraw[NPASS][ELT];
 #pragma unroll
@@ -324,8 +330,14 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
             kr[e] = t < T ? kraw[m][e] : 0u;
             qr[e] = t < T ? qraw[m][e] : 0u;
         }
-        const f32x4 kv = raw4(kr);
+        f32x4 kv = raw4(kr);
         const f32x4 qv = raw4(qr);
+        if constexpr (KN) {  // the row's dk entries sit in QPR consecutive lanes
+            float s2 = kv[0] * kv[0] + kv[1] * kv[1] + kv[2] * kv[2] + kv[3] * kv[3];
+#pragma unroll
+            for (int off = 1; off < QPR; off <<= 1) s2 += __shfl_xor(s2, off);
+            kv *= inv_key_norm(s2);
+        }
         f32x4 kt, kb, qt;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -526,29 +538,36 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     }
 }
 
-template <typename TIn, typename TG, int DK>
+template <typename TIn, typename TG, int DK, bool KN, bool GS>
 hipError_t launch_tree_t(const LaunchArgs& a, const int32_t* parent) {
     const long long nblk = (long long)a.B * a.HV * (a.dv / CB);
-    hipLaunchKernelGGL((tree_verify_kernel<TIn, TG, DK>), dim3((unsigned)nblk), dim3(256), 0,
+    hipLaunchKernelGGL((tree_verify_kernel<TIn, TG, DK, KN, GS>), dim3((unsigned)nblk), dim3(256), 0,
                        (hipStream_t)a.stream, parent, (const TIn*)a.q, (const TIn*)a.k,
                        (const TIn*)a.v, (const TG*)a.g, a.beta, a.h0, a.o, a.T, a.HK, a.HV, a.dv);
     return hipGetLastError();
 }
 
-template <typename TIn, typename TG>
+template <typename TIn, typename TG, bool KN, bool GS>
 hipError_t dispatch_tree(const LaunchArgs& a, const int32_t* parent) {
-    if (a.dk == 32) return launch_tree_t<TIn, TG, 32>(a, parent);
-    if (a.dk == 64) return launch_tree_t<TIn, TG, 64>(a, parent);
-    if (a.dk == 128) return launch_tree_t<TIn, TG, 128>(a, parent);
+    if (a.dk == 32) return launch_tree_t<TIn, TG, 32, KN, GS>(a, parent);
+    if (a.dk == 64) return launch_tree_t<TIn, TG, 64, KN, GS>(a, parent);
+    if (a.dk == 128) return launch_tree_t<TIn, TG, 128, KN, GS>(a, parent);
     return hipErrorInvalidValue;
+}
+
+template <bool KN, bool GS>
+hipError_t dispatch_tree_types(const LaunchArgs& a, const int32_t* parent) {
+    if (a.qkv_f32) return dispatch_tree<float, float, KN, GS>(a, parent);
+    return a.g_bf16 ? dispatch_tree<bf16_t, bf16_t, KN, GS>(a, parent) : dispatch_tree<bf16_t, float, KN, GS>(a, parent);
 }
 
 }  // namespace
 
 hipError_t launch_tree_verify(const LaunchArgs& a, const int32_t* parent) {
     if (a.T < 1 || a.T > TM || a.dv % CB != 0) return hipErrorInvalidValue;
-    if (a.qkv_f32) return dispatch_tree<float, float>(a, parent);
-    return a.g_bf16 ? dispatch_tree<bf16_t, bf16_t>(a, parent) : dispatch_tree<bf16_t, float>(a, parent);
+    if (a.k_l2norm)
+        return a.g_softplus ? dispatch_tree_types<true, true>(a, parent) : dispatch_tree_types<true, false>(a, parent);
+    return a.g_softplus ? dispatch_tree_types<false, true>(a, parent) : dispatch_tree_types<false, false>(a, parent);
 }
 
 }  // namespace gdr

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 4
+#define GDR_ABI_VERSION 5
 
 typedef enum {
     GDR_OK = 0,
@@ -85,15 +85,30 @@ typedef enum { GDR_BF16 = 0, GDR_F32 = 1 } gdr_dtype;
  *               per token and value head), and bf16 halves it.  The kernels widen each value
  *               exactly to fp32, so a call gives bitwise the result of the same call with an
  *               fp32 g holding the same (bf16-representable) values.  Requires bf16 q/k/v.
- * Any other bit, or GDR_G_BF16 with fp32 q/k/v, returns GDR_ERR_UNSUPPORTED.
  */
 #define GDR_G_BF16 0x1
+/*
+ * Fused input prologue (gdr_dims.flags), the follow-up work's I/O-lean mode on the
+ * pre-processing side: the real-scale input recipe of the uzu PR #576 review feeds the
+ * recurrence L2-normalised keys and a softplus decay, which a caller would otherwise
+ * compute in separate passes over k and g (each a read and a write of the tensor).
+ *   GDR_K_L2NORM  k holds raw keys; every kernel uses k_t / max(|k_t|_2, 1e-12), the norm
+ *                 taken per token and key head over dk.
+ *   GDR_G_SOFTPLUS g holds gate logits a (same layout and dtype rules as g); every kernel
+ *                 uses the log-decay g = -softplus(a) = -log(1 + exp(a)).
+ * Both apply to every entry point and combine freely with each other and with GDR_G_BF16.
+ * Results equal those of the same call with the pre-processed k and g given explicitly, up
+ * to fp32 rounding of the pre-processing.
+ * Any other bit, or GDR_G_BF16 with fp32 q/k/v, returns GDR_ERR_UNSUPPORTED.
+ */
+#define GDR_K_L2NORM 0x2
+#define GDR_G_SOFTPLUS 0x4
 
 typedef struct {
     int32_t B, T, HK, HV, dk, dv;
     int32_t chunk;      /* prefill chunk length C (ignored by the token-recurrence calls)  */
     int32_t qkv_dtype;  /* gdr_dtype of q, k and v                                         */
-    int32_t flags;      /* input-format flags (GDR_G_BF16); 0 for the defaults             */
+    int32_t flags;      /* input-format flags (GDR_G_BF16 | GDR_K_L2NORM | GDR_G_SOFTPLUS)    */
 } gdr_dims;
 
 /*

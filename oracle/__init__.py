@@ -15,6 +15,8 @@ Two routes to the same result, both in fp64 (see ``gdr_oracle.c`` for the arithm
 * :func:`tree` -- the same token step over a tree of tokens per batch element (every node
   continues from its parent's state), the setting of the tree-verify solve of uzu PR #576
   ("Support TreeUpdateSolve kernel").
+* :func:`l2_normalize_keys`, :func:`neg_softplus` -- the input pre-processing of that page's
+  real-scale recipe (normalised keys, softplus decay), which the library can fuse.
 
 Inputs may be numpy arrays or torch CPU tensors of any float dtype (bf16 values are
 upcast exactly).  Layouts: q, k ``[B,T,HK,dk]``; v ``[B,T,HV,dv]``; g ``[B,T,HV,dk]``;
@@ -180,6 +182,23 @@ def tree(q, k, v, g, beta, h0, parent, threads: int = 0, lib=None):
     if rc != 0:
         raise RuntimeError(f"oracle_gdr_tree failed ({rc})")
     return o
+
+
+def l2_normalize_keys(k, eps: float = 1e-12) -> np.ndarray:
+    """Raw keys [..., dk] -> k / max(|k|_2, eps) over the last axis, in fp64: the key
+    normalisation of the real-scale input recipe (uzu PR #576 review: normalised keys),
+    which the library's fused prologue (GDR_K_L2NORM) applies per token and key head."""
+    k = _f64(k)
+    n = np.sqrt(np.sum(k * k, axis=-1, keepdims=True))
+    return k / np.maximum(n, eps)
+
+
+def neg_softplus(a) -> np.ndarray:
+    """Gate logits a -> log-decay g = -softplus(a) = -log(1 + e^a), in fp64, in the form
+    -(max(a, 0) + log1p(e^-|a|)) that neither overflows nor cancels: the softplus decay of
+    the same input recipe, applied by the library's fused prologue (GDR_G_SOFTPLUS)."""
+    a = _f64(a)
+    return -(np.maximum(a, 0.0) + np.log1p(np.exp(-np.abs(a))))
 
 
 def num_threads() -> int:

@@ -276,9 +276,10 @@ def test_bench_carry_plan_matches_library(L):
 
 
 def test_input_format_flags(L):
-    """gdr_dims.flags: only GDR_G_BF16 is defined, and only with bf16 q/k/v; anything else is
-    refused before any HIP call on every entry point."""
-    for bad in (dict(flags=2), dict(flags=1 << 30), dict(flags=-1), dict(flags=1, qkv_dtype=1)):
+    """gdr_dims.flags: GDR_G_BF16 (bf16 q/k/v only), GDR_K_L2NORM and GDR_G_SOFTPLUS are
+    defined; anything else is refused before any HIP call on every entry point."""
+    for bad in (dict(flags=8), dict(flags=1 << 30), dict(flags=-1), dict(flags=1, qkv_dtype=1),
+                dict(flags=7, qkv_dtype=1)):
         assert prefill(L, dims(**bad)) == EUNSUP, bad
         assert decode(L, dims(T=1, **bad)) == EUNSUP, bad
         assert decode(L, dims(T=3, **bad), entry="gdr_fused_recurrent") == EUNSUP, bad
@@ -312,3 +313,11 @@ def test_header_is_plain_c_and_links(L, tmp_path):
     res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, res.stderr
     assert "c abi ok" in res.stdout
+
+
+@pytest.mark.parametrize("flags", [2, 4, 6, 7, 3, 5])
+def test_prologue_flags_pass_validation_without_a_gpu(L, flags):
+    """The fused-prologue flags (alone, together, and with bf16 g) are accepted: with no GPU
+    the call gets past every host check and fails only at the first HIP call."""
+    assert prefill(L, dims(flags=flags)) == EHIP
+    assert decode(L, dims(T=1, flags=flags)) == EHIP
