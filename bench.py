@@ -430,6 +430,52 @@ def bench_prologue(w, steps=10, warmup=2):
                     "the fused prologue reads the raw inputs where the kernels already read k and g"}
 
 
+GATE_HEAD_CASES = ((1, 64), (1, 128), (1, 256), (1, 512), (1, 1024), (1, 2048), (1, 4097), (1, 8192),
+                   (1, 16384), (8, 512))
+
+
+def bench_gate_heads(reps=20, warmup=3):
+    """A gate shared per key head (GDR_G_PER_KEY_HEAD) at HK=16 HV=32 dk=dv=128 C=64, bf16
+    q/k/v: the chunk-parallel stage in its fused form (a workgroup per value head, the gram
+    per value head) and its split form (a workgroup per key head, the gram once per group,
+    the solve per value head), timed alone with HIP events over back-to-back calls, for a
+    range of sequence lengths -- the crossover the uzu PR #576 review thread asks about --
+    and the library's own pick ("auto")."""
+    import torch
+
+    import gated_delta_rule_70_amd as gdr
+    from gdr_synth import make_inputs
+
+    HK, HV, dk, dv, C = 16, 32, 128, 128, 64
+    rows = []
+    for B, T in GATE_HEAD_CASES:
+        x = make_inputs(B, T, HK, HV, dk, dv, seed=T, gate_heads="key")
+        d = {k: (None if v is None else v.cuda()) for k, v in x.items()}
+        ws = torch.empty(gdr.workspace_bytes(B, T, HK, HV, dk, dv, C), dtype=torch.uint8, device="cuda")
+        o = torch.empty(B, T, HV, dv, device="cuda")
+        ht = torch.empty(B, HV, dk, dv, device="cuda")
+        row = {"B": B, "T": T}
+        for prep in ("fused", "split", "auto"):
+            def call():
+                gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk=C, o=o, ht=ht, workspace=ws,
+                                  stage="prep", prep=prep)
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            row[f"{prep}_prep_us"] = round(e0.elapsed_time(e1) / reps * 1e3, 2)
+        row["faster"] = "split" if row["split_prep_us"] < row["fused_prep_us"] else "fused"
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+        del d, ws, o, ht
+    return {"workload": "key-head gate, HK=16 HV=32 dk=dv=128 C=64, bf16 q/k/v", "rows": rows}
+
+
 OTHER_OUTPUTS = {}  # workload name -> (inputs, o, ht) of the last bench_other_prefills run
 
 
@@ -763,7 +809,7 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-util", metavar="UTIL_DIR")
     ap.add_argument("--summarize-stats", nargs=3, metavar=("DIR", "NAME", "COMMAND"))
-    ap.add_argument("--section", choices=("tree", "short_calls", "prologue"),
+    ap.add_argument("--section", choices=("tree", "short_calls", "prologue", "gate_heads"),
                     help="run only this part of the benchmark (tree-verify cases or short calls) "
                          "and print its JSON; for kernel traces of those kernels")
     ap.add_argument("--profile-name", default=HEADLINE_PROFILE,
@@ -801,6 +847,8 @@ def main():
         if args.section == "prologue":
             from gdr_synth import WORKLOADS
             res = bench_prologue(WORKLOADS[args.workload])
+        elif args.section == "gate_heads":
+            res = bench_gate_heads()
         else:
             res = bench_tree(DECODE) if args.section == "tree" else bench_short_calls(DECODE)
         print(json.dumps({"section": args.section, **res}), flush=True)

@@ -27,7 +27,7 @@ __all__ = ["decode_step", "fused_recurrent", "chunk_prefill", "chunk_prefill_noa
            "RECURRENT_MAX_T", "TREE_MAX_T"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so")
-ABI_VERSION = 5
+ABI_VERSION = 6
 NOALLOC_SCRATCH_BYTES = 64 << 20  # gdr_chunk_prefill_noalloc: the library's per-device scratch
 RECURRENT_MAX_T = 8  # gdr_forward: calls of at most this many tokens take the fused recurrence
 TREE_MAX_T = 64      # gdr_tree_verify: most nodes per tree
@@ -35,6 +35,10 @@ BF16, F32 = 0, 1
 G_BF16 = 0x1  # gdr_dims.flags: g stored as bf16
 K_L2NORM = 0x2  # keys given raw; the kernels normalise each key row (fused prologue)
 G_SOFTPLUS = 0x4  # g given as gate logits a; the kernels use -softplus(a)
+G_PER_KEY_HEAD = 0x8  # g is [B,T,HK,dk]: one gate per key head, shared by its value heads
+PREP_SPLIT = 0x10  # prefill prep: one workgroup per key head (gram once per GQA group)
+PREP_FUSED = 0x20  # prefill prep: one workgroup per value head
+PREP_SPLIT_MAX_GROUP = 8  # largest HV / HK the split prep serves
 
 
 class Dims(ctypes.Structure):
@@ -115,11 +119,19 @@ def _need(t: torch.Tensor, name: str, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
-def _dims(q, v, chunk, g=None, k_l2norm=False, g_softplus=False) -> Dims:
+def _dims(q, v, chunk, g=None, k_l2norm=False, g_softplus=False, prep="auto") -> Dims:
+    """gdr_dims for the call.  The gate layout follows g's shape: [B,T,HK,dk] with HK != HV
+    is a gate per key head (so is HK == HV with the split prep forced, where the two layouts
+    coincide).  ``prep`` ("auto", "fused", "split") picks the prefill's prep form."""
     B, T, HK, dk = q.shape
     HV, dv = v.shape[2], v.shape[3]
+    if prep not in ("auto", "fused", "split"):
+        raise ValueError(f"prep must be 'auto', 'fused' or 'split', got {prep!r}")
     flags = G_BF16 if g is not None and g.dtype == torch.bfloat16 else 0
     flags |= (K_L2NORM if k_l2norm else 0) | (G_SOFTPLUS if g_softplus else 0)
+    if g is not None and g.shape[2] == HK and (HK != HV or prep == "split"):
+        flags |= G_PER_KEY_HEAD
+    flags |= {"auto": 0, "fused": PREP_FUSED, "split": PREP_SPLIT}[prep]
     return Dims(B, T, HK, HV, dk, dv, int(chunk), _qkv_dtype(q), flags)
 
 
@@ -145,12 +157,17 @@ def _check_shapes(q, k, v, g, beta, h0=None, o=None, ht=None, parent=None):
     if v.dim() != 4 or _shape_of(v)[:2] != (B, T):
         raise ValueError(f"v must be [B,T,HV,dv] with B,T = {(B, T)}, got {_shape_of(v)}")
     HV, dv = _shape_of(v)[2], _shape_of(v)[3]
-    want = {"g": (g, (B, T, HV, dk)), "beta": (beta, (B, T, HV)),
+    if HK < 1 or HV % HK:
+        raise ValueError(f"value heads ({HV}) must be a multiple of key heads ({HK})")
+    # g per value head, or per key head (shared by the key head's value heads)
+    g_shape = (B, T, HK, dk) if g is not None and _shape_of(g) == (B, T, HK, dk) else (B, T, HV, dk)
+    want = {"g": (g, g_shape), "beta": (beta, (B, T, HV)),
             "h0": (h0, (B, HV, dk, dv)), "o": (o, (B, T, HV, dv)), "ht": (ht, (B, HV, dk, dv)),
             "parent": (parent, (B, T))}
     for name, (t, shape) in want.items():
         if t is not None and _shape_of(t) != shape:
-            raise ValueError(f"{name} must be {list(shape)}, got {list(_shape_of(t))}")
+            what = f"{list(shape)} or {[B, T, HK, dk]}" if name == "g" else f"{list(shape)}"
+            raise ValueError(f"{name} must be {what}, got {list(_shape_of(t))}")
     return B, T, HK, HV, dk, dv
 
 
@@ -193,13 +210,15 @@ def decode_step(q, k, v, g, beta, state, o=None, out_state=None, stream=None, k_
 
 def chunk_prefill(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
                   workspace=None, want_state: bool = True, stream=None, stage: str = "both",
-                  k_l2norm=False, g_softplus=False):
+                  k_l2norm=False, g_softplus=False, prep: str = "auto"):
     """Chunkwise WY/UT prefill over all T tokens.  Returns ``(o, ht)`` (``ht`` None if not wanted).
 
     ``workspace`` (optional) is a uint8 GPU tensor of at least ``workspace_bytes(...)``
     bytes; one is allocated if omitted.  ``ht`` may be ``h0`` itself (in-place carry).
     ``stage`` selects "both" (gdr_chunk_prefill), "prep" (gdr_chunk_prep) or "carry"
     (gdr_chunk_carry, which needs a workspace filled by "prep" for the same inputs).
+    g is ``[B,T,HV,dk]``, or ``[B,T,HK,dk]`` for a gate shared per key head; ``prep``
+    ("auto", "fused", "split") then picks the form of the chunk-parallel stage.
     """
     entry = {"both": "gdr_chunk_prefill", "prep": "gdr_chunk_prep", "carry": "gdr_chunk_carry"}[stage]
     B, T, HK, HV, dk, dv = _check_shapes(q, k, v, g, beta, h0=h0, o=o, ht=ht)
@@ -213,7 +232,7 @@ def chunk_prefill(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
         ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
     if ht is not None:
         _need(ht, "ht", torch.float32)
-    d = _dims(q, v, chunk, g, k_l2norm, g_softplus)
+    d = _dims(q, v, chunk, g, k_l2norm, g_softplus, prep)
     need = int(lib().gdr_chunk_prefill_workspace_bytes(ctypes.byref(d)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
@@ -225,7 +244,8 @@ def chunk_prefill(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
 
 
 def chunk_prefill_noalloc(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
-                          want_state: bool = True, stream=None, k_l2norm=False, g_softplus=False):
+                          want_state: bool = True, stream=None, k_l2norm=False, g_softplus=False,
+                          prep: str = "auto"):
     """gdr_chunk_prefill_noalloc: the chunked prefill with the library's own per-device
     scratch as workspace (no device allocation inside the call; pass ``o`` and ``ht`` to
     allocate nothing here either).  Returns ``(o, ht)``.  Calls needing more than
@@ -241,7 +261,7 @@ def chunk_prefill_noalloc(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht
         ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
     if ht is not None:
         _need(ht, "ht", torch.float32)
-    d = _dims(q, v, chunk, g, k_l2norm, g_softplus)
+    d = _dims(q, v, chunk, g, k_l2norm, g_softplus, prep)
     _check(lib().gdr_chunk_prefill_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                            _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht), _stream(stream)))
     return o, ht
@@ -270,7 +290,7 @@ def fused_recurrent(q, k, v, g, beta, h0=None, o=None, ht=None, want_state: bool
 
 
 def forward(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None, workspace=None,
-            want_state: bool = True, stream=None, k_l2norm=False, g_softplus=False):
+            want_state: bool = True, stream=None, k_l2norm=False, g_softplus=False, prep: str = "auto"):
     """Routed call (gdr_forward): the fused recurrence for T <= RECURRENT_MAX_T, the chunked
     prefill otherwise.  Returns ``(o, ht)``."""
     B, T, HK, HV, dk, dv = _check_shapes(q, k, v, g, beta, h0=h0, o=o, ht=ht)
@@ -284,7 +304,7 @@ def forward(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None, workspa
         ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
     if ht is not None:
         _need(ht, "ht", torch.float32)
-    d = _dims(q, v, chunk, g, k_l2norm, g_softplus)
+    d = _dims(q, v, chunk, g, k_l2norm, g_softplus, prep)
     if T > RECURRENT_MAX_T and workspace is None:
         need = int(lib().gdr_chunk_prefill_workspace_bytes(ctypes.byref(d)))
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
                                                     const TG* __restrict__ g,
                                                     const float* __restrict__ beta,
                                                     const float* h0, float* __restrict__ o,
-                                                    float* ht, int T, int HK, int HV) {
+                                                    float* ht, int T, int HK, int HV, int HG) {
     constexpr int BVD = DV < 64 ? DV : 64;   // columns per workgroup
     constexpr int NQ = BVD / 4;              // column quads per row
     constexpr int NRL = 256 / NQ;            // row lanes
@@ -73,10 +73,10 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
 
     // Token tok of this (batch, head): q/k row, g row, v/o columns, beta.
     const size_t kq0 = ((size_t)b * T * HK + kh) * DK;
-    const size_t gb0 = ((size_t)b * T * HV + h) * DK;
+    const size_t gb0 = ((size_t)b * T * HG + h / (HV / HG)) * DK;  // gate head of h
     const size_t vb0 = ((size_t)b * T * HV + h) * DV + col;
     const size_t bb0 = (size_t)b * T * HV + h;
-    const size_t kq_t = (size_t)HK * DK, gb_t = (size_t)HV * DK, vb_t = (size_t)HV * DV;
+    const size_t kq_t = (size_t)HK * DK, gb_t = (size_t)HG * DK, vb_t = (size_t)HV * DV;
 
     // raw inputs of the next token, requested one token ahead
     float gn[RPT];
@@ -180,7 +180,7 @@ template <typename TIn, typename TG, int DK, int DV, bool KN, bool GS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
                    const TG* __restrict__ g, const float* __restrict__ beta, const float* h0,
-                   float* __restrict__ o, float* ht, int HK, int HV) {
+                   float* __restrict__ o, float* ht, int HK, int HV, int HG) {
     constexpr int BVD = DV < 64 ? DV : 64;
     constexpr int NQ = BVD / 4;
     constexpr int NRL = 256 / NQ;
@@ -216,7 +216,7 @@ void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const T
         for (int m = 0; m < RPT; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const size_t kq = ((size_t)b * HK + kh) * DK;
-    const size_t gb = ((size_t)b * HV + h) * DK;
+    const size_t gb = ((size_t)b * HG + h / (HV / HG)) * DK;  // gate head of h
     const size_t vb = ((size_t)b * HV + h) * DV + col;
     if (tid < DK) {
         const float gv = to_f32(g[gb + tid]);
@@ -298,11 +298,11 @@ static hipError_t launch_tokens_t(const LaunchArgs& a) {
     if (a.T == 1) {
         hipLaunchKernelGGL((decode_kernel<TIn, TG, DK, DV, KN, GS>), dim3((unsigned)nblk), dim3(256), 0,
                            (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
-                           (const TG*)a.g, a.beta, a.h0, a.o, a.ht, a.HK, a.HV);
+                           (const TG*)a.g, a.beta, a.h0, a.o, a.ht, a.HK, a.HV, a.HG);
     } else {
         hipLaunchKernelGGL((token_kernel<TIn, TG, DK, DV, KN, GS>), dim3((unsigned)nblk), dim3(256), 0,
                            (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
-                           (const TG*)a.g, a.beta, a.h0, a.o, a.ht, a.T, a.HK, a.HV);
+                           (const TG*)a.g, a.beta, a.h0, a.o, a.ht, a.T, a.HK, a.HV, a.HG);
     }
     return hipGetLastError();
 }

@@ -11,6 +11,8 @@
 
 #include "gdr_launch.h"
 
+static_assert(gdr::kSplitMaxGroup == GDR_PREP_SPLIT_MAX_GROUP, "split prep group limit");
+
 // Workspace of the allocation-free prefill entry point (see gdr.h).  In host code `scratch`
 // is only a handle to the device array; its address on a device comes from
 // hipGetSymbolAddress, looked up once per device and cached.
@@ -70,7 +72,8 @@ bool tensor_sizes(const gdr_dims& d, size_t elt, Sizes* s) {
     if (!mul_ok(bt, (size_t)d.HK, &bth) || !mul_ok(bt, (size_t)d.HV, &btv)) return false;
     if (!mul_ok(bth, (size_t)d.dk, &x) || !mul_ok(x, elt, &s->q)) return false;
     if (!mul_ok(btv, (size_t)d.dv, &x) || !mul_ok(x, elt, &s->v)) return false;
-    if (!mul_ok(btv, (size_t)d.dk, &x) || !mul_ok(x, gelt, &s->g)) return false;
+    const size_t btg = (d.flags & GDR_G_PER_KEY_HEAD) ? bth : btv;  // g rows: key or value heads
+    if (!mul_ok(btg, (size_t)d.dk, &x) || !mul_ok(x, gelt, &s->g)) return false;
     if (!mul_ok(btv, 4, &s->beta)) return false;
     if (!mul_ok(btv, (size_t)d.dv, &x) || !mul_ok(x, 4, &s->o)) return false;
     size_t bh;
@@ -93,8 +96,14 @@ int validate(const gdr_dims* d, Path path, const void* q, const void* k, const v
     if (path == Path::decode && d->T != 1) return GDR_ERR_SHAPE;
     if (!supported_head_dim(d->dk) || !supported_head_dim(d->dv)) return GDR_ERR_UNSUPPORTED;
     if (d->qkv_dtype != GDR_BF16 && d->qkv_dtype != GDR_F32) return GDR_ERR_UNSUPPORTED;
-    if ((d->flags & ~(GDR_G_BF16 | GDR_K_L2NORM | GDR_G_SOFTPLUS)) != 0) return GDR_ERR_UNSUPPORTED;
+    constexpr int32_t known = GDR_G_BF16 | GDR_K_L2NORM | GDR_G_SOFTPLUS | GDR_G_PER_KEY_HEAD |
+                              GDR_PREP_SPLIT | GDR_PREP_FUSED;
+    if ((d->flags & ~known) != 0) return GDR_ERR_UNSUPPORTED;
     if ((d->flags & GDR_G_BF16) && d->qkv_dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
+    if ((d->flags & GDR_PREP_SPLIT) &&
+        ((d->flags & GDR_PREP_FUSED) || !(d->flags & GDR_G_PER_KEY_HEAD) ||
+         d->HV / d->HK > GDR_PREP_SPLIT_MAX_GROUP))
+        return GDR_ERR_UNSUPPORTED;
     if (path == Path::chunked && d->chunk != 16 && d->chunk != 32 && d->chunk != 64)
         return GDR_ERR_UNSUPPORTED;
     const size_t elt = d->qkv_dtype == GDR_F32 ? 4 : 2;
@@ -136,6 +145,16 @@ gdr::LaunchArgs make_args(const gdr_dims* d, const void* q, const void* k, const
     a.g_bf16 = (d->flags & GDR_G_BF16) != 0;
     a.k_l2norm = (d->flags & GDR_K_L2NORM) != 0;
     a.g_softplus = (d->flags & GDR_G_SOFTPLUS) != 0;
+    const bool gk = (d->flags & GDR_G_PER_KEY_HEAD) != 0;
+    a.HG = gk ? d->HK : d->HV;
+    const int G = d->HV / d->HK;
+    if (d->flags & GDR_PREP_SPLIT)
+        a.prep_split = true;
+    else if (d->flags & GDR_PREP_FUSED)
+        a.prep_split = false;
+    else
+        a.prep_split = gk && G > 1 && G <= GDR_PREP_SPLIT_MAX_GROUP &&
+                       gdr::split_prep_preferred(d->B, d->HK, d->T, d->chunk);
     a.q = q;
     a.k = k;
     a.v = v;

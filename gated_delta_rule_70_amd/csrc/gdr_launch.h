@@ -8,8 +8,13 @@
 
 namespace gdr {
 
+// Largest group G = HV / HK the split prep form serves (its beta staging holds G rows).
+constexpr int kSplitMaxGroup = 8;
+
 struct LaunchArgs {
     int B, T, HK, HV, dk, dv, chunk;
+    int HG;           // gate heads of g: HV (per value head) or HK (shared per key head)
+    bool prep_split;  // prefill prep in split form (gate per key head, one workgroup per key head)
     bool qkv_f32;
     bool g_bf16;      // g stored as bf16 (only with bf16 q/k/v)
     bool k_l2norm;    // keys given raw: every kernel uses k / |k|_2 (fused prologue)
@@ -120,9 +125,28 @@ inline CarryLayout carry_layout(int B, int HV, int T, int dk, int dv, int chunk)
     return L;
 }
 
+// Prep form for a gate shared per key head when the caller does not force one: the split
+// form (a workgroup per key head and chunk, the gram computed once per group) once there
+// are enough (batch, key head, chunk) triples to fill the chip with it.  Measured on an
+// MI355X at HK = 16, HV = 32, 128 x 128, chunk 64 (prep alone, fused / split): T = 512
+// 15.6 / 18.0 us, T = 1024 21.9 / 19.1 us, T = 4097 62.2 / 57.8 us, T = 16384 249 / 202 us,
+// B = 8 T = 512 58.2 / 49.9 us -- the split form wins from 256 triples.
+inline bool split_prep_preferred(int B, int HK, int T, int chunk) {
+    if (chunk <= 0) return false;  // the token-recurrence calls carry no chunk length
+    const long long triples = (long long)B * HK * ((T + (long long)chunk - 1) / chunk);
+    return triples >= 256;
+}
+
 // token recurrence over a.T tokens in one launch (the decode step is a.T == 1)
 hipError_t launch_tokens(const LaunchArgs& a);
-hipError_t launch_chunk_prep(const LaunchArgs& a);
+// The prep kernel in fused form (one workgroup per value head and chunk) or in split
+// form (one per key head and chunk, solving per value head; needs HG == HK and
+// HV / HK <= 8).
+hipError_t launch_prep_fused(const LaunchArgs& a);
+hipError_t launch_prep_split(const LaunchArgs& a);
+inline hipError_t launch_chunk_prep(const LaunchArgs& a) {
+    return a.prep_split ? launch_prep_split(a) : launch_prep_fused(a);
+}
 // the carry: whole-head segmented kernels where carry_layout says so, else the
 // column-split kernel (launch_carry_split)
 hipError_t launch_chunk_carry(const LaunchArgs& a);

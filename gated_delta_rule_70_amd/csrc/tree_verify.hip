@@ -136,7 +136,7 @@ template <typename TIn, typename TG, int DK, bool KN, bool GS>
 __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int32_t* __restrict__ parent, const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const TG* __restrict__ g, const float* __restrict__ beta,
-    const float* __restrict__ h0, float* __restrict__ o, int T, int HK, int HV, int DV) {
+    const float* __restrict__ h0, float* __restrict__ o, int T, int HK, int HV, int HG, int DV) {
     constexpr int KP = DK + 4;   // row pitch (floats) of the fp32 g rows and decay prefixes
     constexpr int AP = TM + 4;
     constexpr int UP = CB + 4;
@@ -163,6 +163,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int h = bh % HV;
     const int b = bh / HV;
     const int kh = h / (HV / HK);
+    const int hg = h / (HV / HG);  // gate head
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 #pragma unroll
     for (int m = 0; m < NPASS; ++m) {
         const int t = min(tid / QPR + RPI * m, T - 1);
-        gv[m] = load_g4(g, (((size_t)b * T + t) * HV + h) * DK + c4);
+        gv[m] = load_g4(g, (((size_t)b * T + t) * HG + hg) * DK + c4);
         if constexpr (GS) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) gv[m][e] = neg_softplus(gv[m][e]);
@@ -543,7 +544,7 @@ hipError_t launch_tree_t(const LaunchArgs& a, const int32_t* parent) {
     const long long nblk = (long long)a.B * a.HV * (a.dv / CB);
     hipLaunchKernelGGL((tree_verify_kernel<TIn, TG, DK, KN, GS>), dim3((unsigned)nblk), dim3(256), 0,
                        (hipStream_t)a.stream, parent, (const TIn*)a.q, (const TIn*)a.k,
-                       (const TIn*)a.v, (const TG*)a.g, a.beta, a.h0, a.o, a.T, a.HK, a.HV, a.dv);
+                       (const TIn*)a.v, (const TG*)a.g, a.beta, a.h0, a.o, a.T, a.HK, a.HV, a.HG, a.dv);
     return hipGetLastError();
 }
 

@@ -71,15 +71,20 @@ WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL_1x4097, PREFILL_8x512, PR
 
 def make_inputs(B: int, T: int, HK: int, HV: int, dk: int, dv: int, *,
                 dtype: torch.dtype = torch.bfloat16, seed: int = 0, h0: bool = False,
-                beta_mode: str = "sigmoid", g_scale: float = 1.0) -> dict:
-    """Draw one seeded input set on the CPU.  Returns a dict of CPU tensors."""
+                beta_mode: str = "sigmoid", g_scale: float = 1.0, gate_heads: str = "value") -> dict:
+    """Draw one seeded input set on the CPU.  Returns a dict of CPU tensors.
+
+    ``gate_heads`` "value" draws g ``[B,T,HV,dk]``; "key" draws one gate per key head,
+    ``[B,T,HK,dk]``, from the same distribution."""
+    if gate_heads not in ("value", "key"):
+        raise ValueError(f"unknown gate_heads {gate_heads!r}")
     gen = torch.Generator("cpu").manual_seed(int(seed))
     q = torch.randn(B, T, HK, dk, generator=gen) * dk ** -0.5
     n = torch.randn(B, T, HK, dk, generator=gen)
     k = n / n.norm(dim=-1, keepdim=True).clamp_min(1e-30)
     v = torch.randn(B, T, HV, dv, generator=gen)
     beta_logits = torch.randn(B, T, HV, generator=gen)
-    g_logits = torch.randn(B, T, HV, dk, generator=gen)
+    g_logits = torch.randn(B, T, HV if gate_heads == "value" else HK, dk, generator=gen)
     if beta_mode == "sigmoid":
         beta = torch.sigmoid(beta_logits)
     elif beta_mode == "uniform_half":
@@ -147,7 +152,7 @@ def head_group(inputs: dict, b: int, kh: int, G: int) -> dict:
         "q": inputs["q"][b:b + 1, :, kh:kh + 1],
         "k": inputs["k"][b:b + 1, :, kh:kh + 1],
         "v": inputs["v"][b:b + 1, :, hv],
-        "g": inputs["g"][b:b + 1, :, hv],
+        "g": inputs["g"][b:b + 1, :, hv if inputs["g"].shape[2] == inputs["v"].shape[2] else slice(kh, kh + 1)],
         "beta": inputs["beta"][b:b + 1, :, hv],
         "h0": None if inputs["h0"] is None else inputs["h0"][b:b + 1, hv],
     }

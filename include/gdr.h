@@ -15,7 +15,8 @@
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers to dense row-major arrays, 16-byte aligned:
  *       q, k  [B][T][HK][dk]   (qkv_dtype)      v     [B][T][HV][dv]  (qkv_dtype)
- *       g     [B][T][HV][dk]   log-decay, fp32 (bf16 with GDR_G_BF16)
+ *       g     [B][T][HV][dk]   log-decay, fp32 (bf16 with GDR_G_BF16; [B][T][HK][dk] with
+ *                              GDR_G_PER_KEY_HEAD)
  *       beta  [B][T][HV]       fp32
  *       h0,ht [B][HV][dk][dv]  fp32 state       o     [B][T][HV][dv]  fp32
  *     value head h reads key head h / (HV/HK) (contiguous GQA groups).
@@ -60,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 5
+#define GDR_ABI_VERSION 6
 
 typedef enum {
     GDR_OK = 0,
@@ -99,16 +100,41 @@ typedef enum { GDR_BF16 = 0, GDR_F32 = 1 } gdr_dtype;
  * Both apply to every entry point and combine freely with each other and with GDR_G_BF16.
  * Results equal those of the same call with the pre-processed k and g given explicitly, up
  * to fp32 rounding of the pre-processing.
- * Any other bit, or GDR_G_BF16 with fp32 q/k/v, returns GDR_ERR_UNSUPPORTED.
  */
 #define GDR_K_L2NORM 0x2
 #define GDR_G_SOFTPLUS 0x4
+/*
+ * Gate shared per key head (gdr_dims.flags).
+ *   GDR_G_PER_KEY_HEAD  g is [B][T][HK][dk] (dtype and prologue rules unchanged): every value
+ *                 head of a GQA group decays with its key head's gate, value head h using
+ *                 g row h / (HV/HK).  beta stays per value head.  Every entry point takes it.
+ * With a shared gate the prefill's unscaled gram sum_c k_rc k_sc exp(gam_rc - gam_sc) is the
+ * same for the G value heads of a group; only beta, a row scaling of it, differs.  The
+ * uzu PR #576 review thread on the per-value-head gram weighs a gram per value head fused
+ * with the rest against a gram per key head with the solve split off.  The prefill has both
+ * forms of its chunk-parallel stage:
+ *   fused  one workgroup per (batch, value head, chunk), as for a gate per value head;
+ *   split  one workgroup per (batch, key head, chunk): the gram, causal terms and decayed
+ *          operands once, then the solve and the pseudo-keys for each of the G value heads
+ *          (G <= GDR_PREP_SPLIT_MAX_GROUP).
+ * Both give bitwise the same results.  The library picks the split form when the call has
+ * enough (batch, key head, chunk) triples to fill the GPU with it, the fused form
+ * otherwise; GDR_PREP_SPLIT or GDR_PREP_FUSED forces one (the other entry points ignore
+ * both).  GDR_PREP_SPLIT without GDR_G_PER_KEY_HEAD, with HV/HK above the limit, or with
+ * GDR_PREP_FUSED returns GDR_ERR_UNSUPPORTED.
+ * Any other bit, or GDR_G_BF16 with fp32 q/k/v, returns GDR_ERR_UNSUPPORTED.
+ */
+#define GDR_G_PER_KEY_HEAD 0x8
+#define GDR_PREP_SPLIT 0x10
+#define GDR_PREP_FUSED 0x20
+#define GDR_PREP_SPLIT_MAX_GROUP 8
 
 typedef struct {
     int32_t B, T, HK, HV, dk, dv;
     int32_t chunk;      /* prefill chunk length C (ignored by the token-recurrence calls)  */
     int32_t qkv_dtype;  /* gdr_dtype of q, k and v                                         */
-    int32_t flags;      /* input-format flags (GDR_G_BF16 | GDR_K_L2NORM | GDR_G_SOFTPLUS)    */
+    int32_t flags;      /* GDR_G_BF16 | GDR_K_L2NORM | GDR_G_SOFTPLUS | GDR_G_PER_KEY_HEAD,
+                           GDR_PREP_SPLIT or GDR_PREP_FUSED                                  */
 } gdr_dims;
 
 /*

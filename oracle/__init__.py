@@ -17,9 +17,13 @@ Two routes to the same result, both in fp64 (see ``gdr_oracle.c`` for the arithm
   ("Support TreeUpdateSolve kernel").
 * :func:`l2_normalize_keys`, :func:`neg_softplus` -- the input pre-processing of that page's
   real-scale recipe (normalised keys, softplus decay), which the library can fuse.
+* :func:`gate_per_value_head` -- a gate given per key head, as every value head of the GQA
+  group sees it (the per-key-head layout that the uzu PR #576 review thread on the
+  per-value-head gram is about).
 
 Inputs may be numpy arrays or torch CPU tensors of any float dtype (bf16 values are
-upcast exactly).  Layouts: q, k ``[B,T,HK,dk]``; v ``[B,T,HV,dv]``; g ``[B,T,HV,dk]``;
+upcast exactly).  Layouts: q, k ``[B,T,HK,dk]``; v ``[B,T,HV,dv]``; g ``[B,T,HV,dk]``, or
+``[B,T,HK,dk]`` for a gate shared per key head (expanded by :func:`gate_per_value_head`);
 beta ``[B,T,HV]``; h0 ``[B,HV,dk,dv]`` or None.  Results are fp64 numpy arrays.
 
 Parity is pinned by the ``-m "not gpu"`` tests (closed forms, hand-worked example,
@@ -98,6 +102,25 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(_DP)
 
 
+def gate_per_value_head(g, HV: int) -> np.ndarray:
+    """A gate ``[B,T,HK,dk]`` given once per key head -> ``[B,T,HV,dk]``: value head h of a
+    GQA group of G = HV / HK contiguous value heads decays with the gate of its key head
+    h // G, the same head map as for q and k."""
+    g = _f64(g)
+    HK = g.shape[2]
+    if HV % HK:
+        raise ValueError("value heads must be a multiple of key heads")
+    return np.repeat(g, HV // HK, axis=2)
+
+
+def _gate(g, q, v):
+    """g as given, or expanded to one row per value head if given per key head."""
+    HK, HV = q.shape[2], v.shape[2]
+    if g.shape[2] == HK and HK != HV:
+        return gate_per_value_head(g, HV)
+    return g
+
+
 def _dims(q, k, v, g, beta, h0):
     B, T, HK, dk = q.shape
     if k.shape != q.shape:
@@ -120,6 +143,7 @@ def sequential(q, k, v, g, beta, h0=None, threads: int = 0, lib=None):
     """Token-by-token recurrence in fp64.  Returns ``(o, ht)``."""
     lib = lib or load()
     q, k, v, g, beta, h0 = (_f64(x) for x in (q, k, v, g, beta, h0))
+    g = _gate(g, q, v)
     B, T, HK, HV, dk, dv = _dims(q, k, v, g, beta, h0)
     o = np.empty((B, T, HV, dv), np.float64)
     ht = np.empty((B, HV, dk, dv), np.float64)
@@ -140,6 +164,7 @@ def chunked(q, k, v, g, beta, h0=None, chunk: int = 64, threads: int = 0,
     """
     lib = lib or load()
     q, k, v, g, beta, h0 = (_f64(x) for x in (q, k, v, g, beta, h0))
+    g = _gate(g, q, v)
     B, T, HK, HV, dk, dv = _dims(q, k, v, g, beta, h0)
     C = int(chunk)
     NC = (T + C - 1) // C
@@ -171,6 +196,7 @@ def tree(q, k, v, g, beta, h0, parent, threads: int = 0, lib=None):
     ``o`` ``[B,T,HV,dv]``: each node's output from the state at the end of its path."""
     lib = lib or load()
     q, k, v, g, beta, h0 = (_f64(x) for x in (q, k, v, g, beta, h0))
+    g = _gate(g, q, v)
     B, T, HK, HV, dk, dv = _dims(q, k, v, g, beta, h0)
     par = np.ascontiguousarray(np.asarray(parent), dtype=np.int32)
     if par.shape != (B, T):

@@ -276,10 +276,15 @@ def test_bench_carry_plan_matches_library(L):
 
 
 def test_input_format_flags(L):
-    """gdr_dims.flags: GDR_G_BF16 (bf16 q/k/v only), GDR_K_L2NORM and GDR_G_SOFTPLUS are
-    defined; anything else is refused before any HIP call on every entry point."""
-    for bad in (dict(flags=8), dict(flags=1 << 30), dict(flags=-1), dict(flags=1, qkv_dtype=1),
-                dict(flags=7, qkv_dtype=1)):
+    """gdr_dims.flags: GDR_G_BF16 (bf16 q/k/v only), GDR_K_L2NORM, GDR_G_SOFTPLUS,
+    GDR_G_PER_KEY_HEAD and one of GDR_PREP_SPLIT (needs a per-key-head gate and HV/HK <= 8)
+    or GDR_PREP_FUSED are defined; anything else is refused before any HIP call on every
+    entry point."""
+    for bad in (dict(flags=0x40), dict(flags=1 << 30), dict(flags=-1), dict(flags=1, qkv_dtype=1),
+                dict(flags=7, qkv_dtype=1),
+                dict(flags=0x10),                  # split prep without a per-key-head gate
+                dict(flags=0x38),                  # split and fused both forced
+                dict(flags=0x18, HK=1, HV=16)):    # split prep past its largest group (8)
         assert prefill(L, dims(**bad)) == EUNSUP, bad
         assert decode(L, dims(T=1, **bad)) == EUNSUP, bad
         assert decode(L, dims(T=3, **bad), entry="gdr_fused_recurrent") == EUNSUP, bad
@@ -315,9 +320,31 @@ def test_header_is_plain_c_and_links(L, tmp_path):
     assert "c abi ok" in res.stdout
 
 
+@pytest.mark.skipif("_gpu_visible()", reason="valid fake pointers would reach a real GPU")
 @pytest.mark.parametrize("flags", [2, 4, 6, 7, 3, 5])
 def test_prologue_flags_pass_validation_without_a_gpu(L, flags):
     """The fused-prologue flags (alone, together, and with bf16 g) are accepted: with no GPU
     the call gets past every host check and fails only at the first HIP call."""
     assert prefill(L, dims(flags=flags)) == EHIP
     assert decode(L, dims(T=1, flags=flags)) == EHIP
+
+
+@pytest.mark.skipif("_gpu_visible()", reason="valid fake pointers would reach a real GPU")
+@pytest.mark.parametrize("flags", [0x8, 0x18, 0x28, 0x20, 0xF, 0x1F, 0x2F])
+def test_gate_head_flags_pass_validation_without_a_gpu(L, flags):
+    """A per-key-head gate and the prep-form flags are accepted on every entry point: with no
+    GPU the call gets past every host check and fails only at the first HIP call."""
+    assert prefill(L, dims(flags=flags)) == EHIP
+    assert decode(L, dims(T=1, flags=flags)) == EHIP
+    assert decode(L, dims(T=3, flags=flags), entry="gdr_fused_recurrent") == EHIP
+    # the token-recurrence calls ignore the chunk length, zero included
+    assert decode(L, dims(T=1, chunk=0, flags=flags)) == EHIP
+    assert decode(L, dims(T=3, chunk=0, flags=flags), entry="gdr_fused_recurrent") == EHIP
+
+
+def test_key_head_gate_extent_in_alias_checks(L):
+    """With GDR_G_PER_KEY_HEAD, g spans B*T*HK*dk*4 bytes (half of the per-value-head extent
+    at HV = 2 HK): o over its last 16 bytes overlaps it, o just past it does not."""
+    gbytes = 2 * 5 * 2 * 64 * 4
+    assert prefill(L, dims(flags=8), o=addr(3, gbytes - 16)) == EALIAS
+    assert prefill(L, dims(flags=0), o=addr(3, gbytes + 16)) == EALIAS

@@ -18,7 +18,7 @@ def good():
 BAD = {
     "k": torch.zeros(B, T, HK, DK + 1),
     "v": torch.zeros(B, T - 1, HV, DV),
-    "g_per_key_head": torch.zeros(B, T, HK, DK),
+    "g_wrong_heads": torch.zeros(B, T, HK + 1, DK),
     "beta_per_key_head": torch.zeros(B, T, HK),
 }
 
@@ -75,3 +75,12 @@ def test_well_shaped_cpu_tensors_fail_only_on_device():
     # the shape check passes; the next check (device) is what rejects CPU tensors
     with pytest.raises(ValueError, match="GPU tensor"):
         gdr.chunk_prefill(**good(), h0=torch.zeros(B, HV, DK, DV))
+
+
+def test_key_head_gate_shape_is_accepted():
+    # g [B,T,HK,dk] (a gate per key head) passes the shape check on every entry point
+    x = good()
+    x["g"] = torch.zeros(B, T, HK, DK)
+    for entry in ("chunk_prefill", "fused_recurrent", "forward"):
+        with pytest.raises(ValueError, match="GPU tensor"):
+            getattr(gdr, entry)(**x)
