@@ -476,6 +476,84 @@ def bench_gate_heads(reps=20, warmup=3):
     return {"workload": "key-head gate, HK=16 HV=32 dk=dv=128 C=64, bf16 q/k/v", "rows": rows}
 
 
+def varlen_lengths(n=32, seed=9, lo=1, hi=4097):
+    """A seeded mix of sequence lengths, log-uniform on [lo, hi] (many short, a few long)."""
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    return [int(round(float(x))) for x in np.exp(rng.uniform(np.log(lo), np.log(hi), n))]
+
+
+def bench_varlen(reps=10, warmup=2):
+    """A packed batch of 32 sequences with a log-uniform length mix (1 .. 4097 rows) at
+    HK=16 HV=32 128/128 C=64, bf16: one gdr_chunk_prefill_varlen call, against one
+    gdr_chunk_prefill per sequence and against one dense call padded to the longest
+    sequence (padding rows with beta = 0, whose outputs are discarded).  Wall time per batch,
+    CUDA events on the launch stream."""
+    import torch
+
+    import gated_delta_rule_70_amd as gdr
+    from gdr_synth import make_inputs
+
+    HK, HV, dk, dv, C = 16, 32, 128, 128, 64
+    lengths = varlen_lengths()
+    N, T = len(lengths), sum(lengths)
+    x = make_inputs(1, T, HK, HV, dk, dv, seed=17, h0=False)
+    d = {n: t[0].cuda() for n, t in x.items() if t is not None}
+    cu_host = [0]
+    for L in lengths:
+        cu_host.append(cu_host[-1] + L)
+    cu = torch.tensor(cu_host, dtype=torch.int32, device="cuda")
+    ws = torch.empty(gdr.workspace_bytes_varlen(N, T, HK, HV, dk, dv, C), dtype=torch.uint8, device="cuda")
+    o = torch.empty(T, HV, dv, device="cuda")
+    ht = torch.empty(N, HV, dk, dv, device="cuda")
+
+    def packed():
+        gdr.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, chunk=C, o=o, ht=ht, workspace=ws)
+
+    seqs = []
+    for i in range(N):
+        a, b = cu_host[i], cu_host[i + 1]
+        sl = {n: d[n][a:b].unsqueeze(0) for n in ("q", "k", "v", "g", "beta")}
+        wsi = torch.empty(gdr.workspace_bytes(1, b - a, HK, HV, dk, dv, C), dtype=torch.uint8, device="cuda")
+        seqs.append((sl, wsi, o[a:b].unsqueeze(0), ht[i:i + 1]))
+
+    def per_sequence():
+        for sl, wsi, oi, hi in seqs:
+            gdr.chunk_prefill(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], chunk=C, o=oi, ht=hi, workspace=wsi)
+
+    Lmax = max(lengths)
+    pad = {n: torch.zeros((N, Lmax) + tuple(d[n].shape[1:]), dtype=d[n].dtype, device="cuda")
+           for n in ("q", "k", "v", "g", "beta")}
+    for i in range(N):
+        for n in pad:
+            pad[n][i, :lengths[i]] = d[n][cu_host[i]:cu_host[i + 1]]
+    wsp = torch.empty(gdr.workspace_bytes(N, Lmax, HK, HV, dk, dv, C), dtype=torch.uint8, device="cuda")
+    op = torch.empty(N, Lmax, HV, dv, device="cuda")
+
+    def padded():
+        gdr.chunk_prefill(pad["q"], pad["k"], pad["v"], pad["g"], pad["beta"], chunk=C, o=op, ht=ht, workspace=wsp)
+
+    res = {}
+    for name, fn in (("packed", packed), ("per_sequence", per_sequence), ("padded", padded)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) / reps, 4)
+    # the padded batch carries its states past each sequence's end (beta = 0 rows still
+    # decay), so only its time is comparable, not its final states
+    return {"workload": f"{N} sequences, log-uniform lengths 1..4097 ({T} rows, longest {Lmax}), "
+                        "HK=16 HV=32 dk=dv=128 C=64, bf16",
+            "ms_per_batch": res, "tokens_per_s_packed": round(T / (res["packed"] * 1e-3), 1),
+            "lengths": lengths}
+
+
 OTHER_OUTPUTS = {}  # workload name -> (inputs, o, ht) of the last bench_other_prefills run
 
 
@@ -809,7 +887,7 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-util", metavar="UTIL_DIR")
     ap.add_argument("--summarize-stats", nargs=3, metavar=("DIR", "NAME", "COMMAND"))
-    ap.add_argument("--section", choices=("tree", "short_calls", "prologue", "gate_heads"),
+    ap.add_argument("--section", choices=("tree", "short_calls", "prologue", "gate_heads", "varlen"),
                     help="run only this part of the benchmark (tree-verify cases or short calls) "
                          "and print its JSON; for kernel traces of those kernels")
     ap.add_argument("--profile-name", default=HEADLINE_PROFILE,
@@ -849,6 +927,8 @@ def main():
             res = bench_prologue(WORKLOADS[args.workload])
         elif args.section == "gate_heads":
             res = bench_gate_heads()
+        elif args.section == "varlen":
+            res = bench_varlen()
         else:
             res = bench_tree(DECODE) if args.section == "tree" else bench_short_calls(DECODE)
         print(json.dumps({"section": args.section, **res}), flush=True)

@@ -22,12 +22,13 @@ import os
 import torch
 
 __all__ = ["decode_step", "fused_recurrent", "chunk_prefill", "chunk_prefill_noalloc", "forward",
-           "tree_verify", "NOALLOC_SCRATCH_BYTES",
+           "tree_verify", "chunk_prefill_varlen", "fused_recurrent_varlen", "workspace_bytes_varlen",
+           "NOALLOC_SCRATCH_BYTES", "VARLEN_MAX_SEQS",
            "workspace_bytes", "GdrError", "lib", "Dims", "LIB_PATH", "ABI_VERSION",
            "RECURRENT_MAX_T", "TREE_MAX_T"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so")
-ABI_VERSION = 6
+ABI_VERSION = 7
 NOALLOC_SCRATCH_BYTES = 64 << 20  # gdr_chunk_prefill_noalloc: the library's per-device scratch
 RECURRENT_MAX_T = 8  # gdr_forward: calls of at most this many tokens take the fused recurrence
 TREE_MAX_T = 64      # gdr_tree_verify: most nodes per tree
@@ -39,6 +40,7 @@ G_PER_KEY_HEAD = 0x8  # g is [B,T,HK,dk]: one gate per key head, shared by its v
 PREP_SPLIT = 0x10  # prefill prep: one workgroup per key head (gram once per GQA group)
 PREP_FUSED = 0x20  # prefill prep: one workgroup per value head
 PREP_SPLIT_MAX_GROUP = 8  # largest HV / HK the split prep serves
+VARLEN_MAX_SEQS = 4096  # most sequences in one packed variable-length call
 
 
 class Dims(ctypes.Structure):
@@ -87,6 +89,12 @@ def lib():
         fn = getattr(L, name)
         fn.restype = ctypes.c_int
         fn.argtypes = L.gdr_chunk_prefill.argtypes
+    L.gdr_chunk_prefill_varlen_workspace_bytes.restype = ctypes.c_size_t
+    L.gdr_chunk_prefill_varlen_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
+    L.gdr_chunk_prefill_varlen.restype = ctypes.c_int
+    L.gdr_chunk_prefill_varlen.argtypes = [ctypes.POINTER(Dims)] + [_VP] * 10 + [ctypes.c_size_t, _VP]
+    L.gdr_fused_recurrent_varlen.restype = ctypes.c_int
+    L.gdr_fused_recurrent_varlen.argtypes = [ctypes.POINTER(Dims)] + [_VP] * 10
     if L.gdr_abi_version() != ABI_VERSION:
         raise RuntimeError("libgdr.so ABI version mismatch; rebuild it")
     _lib = L
@@ -314,6 +322,96 @@ def forward(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None, workspa
                              _ptr(h0), _ptr(o), _ptr(ht), _ptr(workspace),
                              ctypes.c_size_t(0 if workspace is None else workspace.numel()),
                              _stream(stream)))
+    return o, ht
+
+
+def workspace_bytes_varlen(N, T, HK, HV, dk, dv, chunk=64, dtype=torch.bfloat16) -> int:
+    """Workspace of a packed prefill of N sequences in T rows (any split of the rows)."""
+    d = Dims(N, T, HK, HV, dk, dv, chunk, BF16 if dtype == torch.bfloat16 else F32)
+    return int(lib().gdr_chunk_prefill_varlen_workspace_bytes(ctypes.byref(d)))
+
+
+def _packed(q, k, v, g, beta, cu_seqlens, h0, o, ht):
+    """Shapes of a packed batch: token tensors [T, H, d] (or with a leading 1), cu_seqlens
+    [N+1] int32, states [N, HV, dk, dv].  Returns 4-D views of the token tensors, the o
+    shape in the caller's rank, and (N, T, HK, HV, dk, dv)."""
+    if q.dim() not in (3, 4) or (q.dim() == 4 and q.shape[0] != 1):
+        raise ValueError(f"q must be [T,HK,dk] (or [1,T,HK,dk]) for a packed batch, got {_shape_of(q)}")
+    lead = q.dim() == 4
+
+    def as4(t, name, r):
+        if t is None:
+            return None
+        if t.dim() == r + (1 if lead else 0) and (not lead or t.shape[0] == 1):
+            return t if lead else t.unsqueeze(0)
+        raise ValueError(f"{name} must have q's leading layout, got {_shape_of(t)}")
+
+    q4, k4, v4, g4 = (as4(t, n, 3) for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g")))
+    b4 = as4(beta, "beta", 2)
+    if cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 2:
+        raise ValueError(f"cu_seqlens must be [N+1] with N >= 1, got {_shape_of(cu_seqlens)}")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError(f"cu_seqlens must be int32, got {cu_seqlens.dtype}")
+    N = cu_seqlens.shape[0] - 1
+    _, T, HK, HV, dk, dv = _check_shapes(q4, k4, v4, g4, b4, o=as4(o, "o", 3))
+    for name, t in (("h0", h0), ("ht", ht)):
+        if t is not None and _shape_of(t) != (N, HV, dk, dv):
+            raise ValueError(f"{name} must be {[N, HV, dk, dv]}, got {list(_shape_of(t))}")
+    o_shape = (1, T, HV, dv) if lead else (T, HV, dv)
+    return q4, k4, v4, g4, b4, o_shape, (N, T, HK, HV, dk, dv)
+
+
+def chunk_prefill_varlen(q, k, v, g, beta, cu_seqlens, h0=None, chunk: int = 64, o=None, ht=None,
+                         workspace=None, want_state: bool = True, stream=None, k_l2norm=False,
+                         g_softplus=False, prep: str = "auto"):
+    """Chunked prefill of a packed batch (gdr_chunk_prefill_varlen): N sequences laid end
+    to end in T rows, sequence i on rows ``[cu_seqlens[i], cu_seqlens[i+1])`` (an int32 GPU
+    tensor), each run from its own ``h0[i]``.  Token tensors are ``[T, H, d]`` (or with a
+    leading 1); states ``[N, HV, dk, dv]``.  Returns ``(o, ht)``."""
+    q4, k4, v4, g4, b4, o_shape, (N, T, HK, HV, dk, dv) = _packed(q, k, v, g, beta, cu_seqlens, h0, o, ht)
+    _check_inputs(q4, k4, v4, g4, b4)
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    if o is None:
+        o = torch.empty(o_shape, device=q.device, dtype=torch.float32)
+    _need(o, "o", torch.float32)
+    if ht is None and want_state:
+        ht = torch.empty(N, HV, dk, dv, device=q.device, dtype=torch.float32)
+    if ht is not None:
+        _need(ht, "ht", torch.float32)
+    d = _dims(q4, v4, chunk, g4, k_l2norm, g_softplus, prep)
+    d.B = N
+    need = int(lib().gdr_chunk_prefill_varlen_workspace_bytes(ctypes.byref(d)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    _need(workspace, "workspace", torch.uint8)
+    _check(lib().gdr_chunk_prefill_varlen(ctypes.byref(d), _ptr(cu_seqlens), _ptr(q4), _ptr(k4), _ptr(v4),
+                                          _ptr(g4), _ptr(b4), _ptr(h0), _ptr(o), _ptr(ht), _ptr(workspace),
+                                          ctypes.c_size_t(workspace.numel()), _stream(stream)))
+    return o, ht
+
+
+def fused_recurrent_varlen(q, k, v, g, beta, cu_seqlens, h0=None, o=None, ht=None, want_state: bool = True,
+                           stream=None, k_l2norm=False, g_softplus=False):
+    """The fused token recurrence over a packed batch (gdr_fused_recurrent_varlen); layouts
+    as for :func:`chunk_prefill_varlen`.  Returns ``(o, ht)``."""
+    q4, k4, v4, g4, b4, o_shape, (N, T, HK, HV, dk, dv) = _packed(q, k, v, g, beta, cu_seqlens, h0, o, ht)
+    _check_inputs(q4, k4, v4, g4, b4)
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    if o is None:
+        o = torch.empty(o_shape, device=q.device, dtype=torch.float32)
+    _need(o, "o", torch.float32)
+    if ht is None and want_state:
+        ht = torch.empty(N, HV, dk, dv, device=q.device, dtype=torch.float32)
+    if ht is not None:
+        _need(ht, "ht", torch.float32)
+    d = _dims(q4, v4, 0, g4, k_l2norm, g_softplus)
+    d.B = N
+    _check(lib().gdr_fused_recurrent_varlen(ctypes.byref(d), _ptr(cu_seqlens), _ptr(q4), _ptr(k4), _ptr(v4),
+                                            _ptr(g4), _ptr(b4), _ptr(h0), _ptr(o), _ptr(ht), _stream(stream)))
     return o, ht
 
 

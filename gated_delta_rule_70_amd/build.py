@@ -22,7 +22,7 @@ OBJ_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdr.so")
 
 SOURCES = ["gdr_api.cpp", "decode.hip", "chunk_prep.hip", "chunk_prep_split.hip", "chunk_carry.hip",
-           "chunk_carry_wide.hip", "tree_verify.hip"]
+           "chunk_carry_wide.hip", "tree_verify.hip", "varlen_plan.hip"]
 ARCH = os.environ.get("GDR_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU forms are kept out of the device code (plain fp32 FMAs only).

@@ -94,7 +94,7 @@ __device__ __forceinline__ float raw_absmax(uint32_t x) {
 template <typename TIn, int DK, int DV, int C, int NT>
 __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
     const TIn* __restrict__ v, const float* h0, float* __restrict__ o, float* ht,
-    const unsigned char* __restrict__ ws, int B, int T, int HV, int NC) {
+    const unsigned char* __restrict__ ws, int B, int T, int HV, int NC, const int32_t* __restrict__ plan) {
     constexpr int NB = C / 16;
     constexpr int NW = NB;                    // one wave per 16-row tile of the chunk
     constexpr int NQS = (C + 31) / 32;
@@ -120,6 +120,8 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
     const int cg = blk / NH;
     const int h = bh % HV;
     const int b = bh / HV;
+    // this batch element's (or packed sequence's) rows, chunks and first chunk slot
+    const SeqSpan sp = seq_span(plan, b, B, T, NC);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // row tile of this wave
     __builtin_assume(w >= 0 && w < NW);  // lets the compiler drop the per-tile guards
     const int lane = threadIdx.x & 63;
@@ -150,12 +152,12 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
     // Buffer resources: this head's records, and this batch element's v and o rows (the
     // host guarantees each fits a 31-bit byte offset).  Wave-uniform offsets (fragment
     // index, row within a chunk) go to SGPRs; one per-lane offset is built per chunk.
-    const unsigned char* rec0 = ws + (size_t)bh * NC * R.bytes;
+    const unsigned char* rec0 = ws + ((size_t)sp.c0 * HV + (size_t)h * sp.nc) * R.bytes;
     const int rowv = HV * DV * ELT;  // bytes between consecutive tokens of v
     const int rowo = HV * DV * 4;    // ... of o
-    const rsrc_t rs_rec = make_rsrc(rec0, (uint32_t)NC * R.bytes);
-    const rsrc_t rs_v = make_rsrc(v + (size_t)b * T * HV * DV, (uint32_t)T * rowv);
-    const rsrc_t rs_o = make_rsrc(o + (size_t)b * T * HV * DV, (uint32_t)T * rowo);
+    const rsrc_t rs_rec = make_rsrc(rec0, (uint32_t)sp.nc * R.bytes);
+    const rsrc_t rs_v = make_rsrc(v + (size_t)sp.row0 * HV * DV, (uint32_t)sp.T * rowv);
+    const rsrc_t rs_o = make_rsrc(o + (size_t)sp.row0 * HV * DV, (uint32_t)sp.T * rowo);
 
     // v rows of a chunk.  Wave w loads rows 16w .. 16w+15 of its workgroup's 16*NT columns
     // with one vector load per 16-column tile (lane l: row l/4, four columns 4(l%4)..),
@@ -453,21 +455,25 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
         }
     };
 
-    Frags FA, FB, FC;
-    load_all(FA, 0);
-    load_all(FB, min(1, NC - 1));
-    // Three steps per iteration (register set and exchange copy fixed per position), then
-    // up to two more; the requested chunk is clamped to the last one, whose operands then
-    // simply arrive twice.
-    int n = 0;
-    for (; n + 3 <= NC; n += 3) {
-        step(FA, FC, n, min(n + 2, NC - 1), 0);
-        step(FB, FA, n + 1, min(n + 3, NC - 1), 1);
-        step(FC, FB, n + 2, min(n + 4, NC - 1), 2);
+    // A sequence with no rows (packed batches) passes its initial state through.
+    const int nc = sp.nc;
+    if (nc > 0) {
+        Frags FA, FB, FC;
+        load_all(FA, 0);
+        load_all(FB, min(1, nc - 1));
+        // Three steps per iteration (register set and exchange copy fixed per position), then
+        // up to two more; the requested chunk is clamped to the last one, whose operands then
+        // simply arrive twice.
+        int n = 0;
+        for (; n + 3 <= nc; n += 3) {
+            step(FA, FC, n, min(n + 2, nc - 1), 0);
+            step(FB, FA, n + 1, min(n + 3, nc - 1), 1);
+            step(FC, FB, n + 2, min(n + 4, nc - 1), 2);
+        }
+        if (n < nc) step(FA, FC, n, min(n + 2, nc - 1), 0);
+        if (n + 1 < nc) step(FB, FA, n + 1, min(n + 3, nc - 1), 1);
+        store_o(nc - 1, Op);
     }
-    if (n < NC) step(FA, FC, n, min(n + 2, NC - 1), 0);
-    if (n + 1 < NC) step(FB, FA, n + 1, min(n + 3, NC - 1), 1);
-    store_o(NC - 1, Op);
 
     if (ht) {
 #pragma unroll
@@ -486,11 +492,11 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
 
 template <typename TIn, int DK, int DV, int C, int NT>
 static hipError_t launch_carry_t(const LaunchArgs& a) {
-    const int NC = (a.T + C - 1) / C;
+    const int NC = a.plan ? 0 : (a.T + C - 1) / C;  // packed batches: per sequence, from the plan
     const long long nblk = (long long)a.B * a.HV * (DV / (16 * NT));
     hipLaunchKernelGGL((chunk_carry_kernel<TIn, DK, DV, C, NT>), dim3((unsigned)nblk),
                        dim3(64 * (C / 16)), 0, (hipStream_t)a.stream, (const TIn*)a.v, a.h0, a.o,
-                       a.ht, (const unsigned char*)a.workspace, a.B, a.T, a.HV, NC);
+                       a.ht, (const unsigned char*)a.workspace, a.B, a.T, a.HV, NC, a.plan);
     return hipGetLastError();
 }
 

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(SUM ? 512 : 256) __attribute__((amdgpu_waves_per_eu
 void carry_wide_kernel(
     const TIn* __restrict__ v, const float* h0, float* __restrict__ o, float* ht,
     const unsigned char* __restrict__ ws, float* xsum, const float* sstart, int B, int T,
-    int HV, int NC, int NSEG) {
+    int HV, int NCD, int NSEG, const int32_t* __restrict__ plan) {
     using ST = Stage<C, D, SUM>;
     constexpr ChunkRecord R = ST::R;
     constexpr int NB = ST::NB, NQS = ST::NQS, KC = ST::KC, DKT = ST::DKT;
@@ -123,6 +123,10 @@ void carry_wide_kernel(
     const int seg = blockIdx.x / NH;
     const int h = bh % HV;
     const int b = bh / HV;
+    // this batch element's (or packed sequence's) rows, chunks and first chunk slot; a packed
+    // batch runs as one segment (NSEG = 1)
+    const SeqSpan sp = seq_span(plan, b, B, T, NCD);
+    const int NC = sp.nc;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int li = lane & 15;
@@ -184,12 +188,12 @@ void carry_wide_kernel(
         }
     }
 
-    const unsigned char* rec0 = ws + (size_t)bh * NC * R.bytes;
+    const unsigned char* rec0 = ws + ((size_t)sp.c0 * HV + (size_t)h * NC) * R.bytes;
     const rsrc_t rs_rec = make_rsrc(rec0, (uint32_t)NC * R.bytes);
     const int rowv = HV * D * ELT;
     const int rowo = HV * D * 4;
-    const rsrc_t rs_v = make_rsrc(v + (size_t)b * T * HV * D, (uint32_t)T * rowv);
-    const rsrc_t rs_o = make_rsrc(o + (size_t)b * T * HV * D, (uint32_t)T * rowo);
+    const rsrc_t rs_v = make_rsrc(v + (size_t)sp.row0 * HV * D, (uint32_t)sp.T * rowv);
+    const rsrc_t rs_o = make_rsrc(o + (size_t)sp.row0 * HV * D, (uint32_t)sp.T * rowo);
 
     // Record staging: each wave copies its share of the copy list straight from memory into
     // the LDS buffer with LDS-DMA loads (16 bytes per lane, no registers); the copy of chunk
@@ -421,12 +425,14 @@ void carry_wide_kernel(
         wait_vm();
     };
 
-    issue_v(VR, c0);
-    issue_rec(c0, 0);
-    wait_vm();
+    if (c1 > c0) {  // a packed sequence with no rows passes its initial state through
+        issue_v(VR, c0);
+        issue_rec(c0, 0);
+        wait_vm();
 #pragma nounroll
-    for (int n = c0; n < c1; ++n) step(n, (n - c0) & 1);
-    store_o(c1 - 1, true);
+        for (int n = c0; n < c1; ++n) step(n, (n - c0) & 1);
+        store_o(c1 - 1, true);
+    }
 
     float* dst = nullptr;
     if (SUM) dst = xsum + ((size_t)(bh * (NSEG - 1) + seg) * 2 + part) * D * D;
@@ -591,19 +597,19 @@ hipError_t launch_wide_t(const LaunchArgs& a, int NC, int NSEG) {
     const int NH = a.B * a.HV;
     hipStream_t st = (hipStream_t)a.stream;
     const unsigned char* ws = (const unsigned char*)a.workspace;
-    const CarryLayout L = carry_layout(a.B, a.HV, a.T, a.dk, a.dv, a.chunk);
+    const CarryLayout L = carry_layout(a.B, a.HV, a.T, a.dk, a.dv, a.chunk, a.plan != nullptr);
     float* xsum = (float*)((unsigned char*)a.workspace + L.xsum_off);
     float* sstart = (float*)((unsigned char*)a.workspace + L.sstart_off);
     if (NSEG > 1) {
         hipLaunchKernelGGL((carry_wide_kernel<TIn, D, C, true>), dim3((unsigned)(NH * (NSEG - 1))), dim3(512),
                            0, st, (const TIn*)a.v, nullptr, nullptr, nullptr, ws, xsum, nullptr, a.B,
-                           a.T, a.HV, NC, NSEG);
+                           a.T, a.HV, NC, NSEG, a.plan);
         hipLaunchKernelGGL((carry_combine_kernel<D>), dim3((unsigned)(NH * 2)), dim3(2 * D), 0, st,
                            a.h0, (const float*)xsum, sstart, NH, NSEG);
     }
     hipLaunchKernelGGL((carry_wide_kernel<TIn, D, C, false>), dim3((unsigned)(NH * NSEG)), dim3(256), 0,
                        st, (const TIn*)a.v, a.h0, a.o, a.ht, ws, nullptr, (const float*)sstart, a.B,
-                       a.T, a.HV, NC, NSEG);
+                       a.T, a.HV, NC, NSEG, a.plan);
     return hipGetLastError();
 }
 
@@ -625,9 +631,9 @@ hipError_t launch_wide(const LaunchArgs& a, int NC, int NSEG) {
 }  // namespace
 
 hipError_t launch_chunk_carry(const LaunchArgs& a) {
-    const CarryLayout L = carry_layout(a.B, a.HV, a.T, a.dk, a.dv, a.chunk);
+    const CarryLayout L = carry_layout(a.B, a.HV, a.T, a.dk, a.dv, a.chunk, a.plan != nullptr);
     if (!L.wide) return launch_carry_split(a);
-    const int NC = (a.T + a.chunk - 1) / a.chunk;
+    const int NC = a.plan ? 0 : (a.T + a.chunk - 1) / a.chunk;  // packed: per sequence
     return a.qkv_f32 ? launch_wide<float>(a, NC, L.nseg) : launch_wide<bf16_t>(a, NC, L.nseg);
 }
 

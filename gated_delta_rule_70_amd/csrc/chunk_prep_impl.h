@@ -247,9 +247,9 @@ struct PrepCtx {
 template <typename TIn, typename TG, int DK, int C, int I, bool KN, bool GS, bool SP>
 __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restrict__ q,
                                           const TIn* __restrict__ k, const TG* __restrict__ g,
-                                          const float* __restrict__ beta, unsigned char* rec, int b,
-                                          int T, int HK, int HV, int HG, int h, int kh, int t0, int L,
-                                          size_t hstride) {
+                                          const float* __restrict__ beta, unsigned char* rec,
+                                          long long row0, int T, int HK, int HV, int HG, int h, int kh,
+                                          int t0, int L, size_t hstride) {
     constexpr int NB = C / 16;
     constexpr int KC = DK / 32;
     constexpr int DKT = DK / 16;
@@ -276,15 +276,15 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
     };
 
     // ---- 1. loads, g -> log2 units, 16-row inclusive scan ---------------------------------
-    // Buffer resources over this batch element's rows: a row past the sequence end lies
-    // beyond the range and reads as zero, which is exactly the zero padding of the ragged
-    // last chunk (g = 0, k = q = 0, beta = 0).  The host keeps every offset below 2^31.
+    // Buffer resources over this sequence's T rows (from row0): a row past the sequence end
+    // lies beyond the range and reads as zero, which is exactly the zero padding of the
+    // ragged last chunk (g = 0, k = q = 0, beta = 0).  The host keeps every offset below 2^31.
     constexpr int GE = sizeof(TG);  // bytes per g element (fp32 or bf16)
     const int hg = h / (HV / HG);  // gate head
-    const rsrc_t rs_g = make_rsrc(g + (size_t)b * T * HG * DK, (uint32_t)T * HG * DK * GE);
-    const rsrc_t rs_k = make_rsrc(k + (size_t)b * T * HK * DK, (uint32_t)T * HK * DK * ELT);
-    const rsrc_t rs_q = make_rsrc(q + (size_t)b * T * HK * DK, (uint32_t)T * HK * DK * ELT);
-    const rsrc_t rs_b = make_rsrc(beta + (size_t)b * T * HV, (uint32_t)T * HV * 4);
+    const rsrc_t rs_g = make_rsrc(g + (size_t)row0 * HG * DK, (uint32_t)T * HG * DK * GE);
+    const rsrc_t rs_k = make_rsrc(k + (size_t)row0 * HK * DK, (uint32_t)T * HK * DK * ELT);
+    const rsrc_t rs_q = make_rsrc(q + (size_t)row0 * HK * DK, (uint32_t)T * HK * DK * ELT);
+    const rsrc_t rs_b = make_rsrc(beta + (size_t)row0 * HV, (uint32_t)T * HV * 4);
     const int tr = t0 + r;  // token row within this batch element
     float x[KC][8];
     In4<TIn> kin[KC][2], qin[KC][2];
@@ -669,7 +669,7 @@ template <typename TIn, typename TG, int DK, int C, bool KN, bool GS, bool SP>
 __global__ __launch_bounds__(C * 4, (KN || SP) ? 2 : 3) void chunk_prep_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TG* __restrict__ g,
     const float* __restrict__ beta, unsigned char* __restrict__ ws, int B, int T, int HK, int HV,
-    int HG, int NC) {
+    int HG, int NC, const int32_t* __restrict__ plan) {
     using Lds = PrepLds<DK, C>;
     constexpr int NB = C / 16;
     constexpr ChunkRecord R = ChunkRecord::make(C, DK);
@@ -687,40 +687,54 @@ __global__ __launch_bounds__(C * 4, (KN || SP) ? 2 : 3) void chunk_prep_kernel(
     s.sConE = sConE;
     s.sBeta = sBeta;
 
+    // Items are (batch element, key head, chunk) triples, chunk fastest -- or, for a packed
+    // variable-length batch (plan != nullptr), (key head, chunk slot) pairs, the slot's
+    // sequence read from the plan; NC is then the number of chunk slots.
     const int G = HV / HK;
     const int blk = blockIdx.x;
-    int pair, h;
+    const long long items = plan ? (long long)HK * NC : (long long)B * HK * NC;
+    int pair, sub;
     if constexpr (SP) {
-        // one (batch, key head, chunk) triple per block, serving value heads kh*G .. kh*G+G-1
+        // one item per block, serving value heads kh*G .. kh*G+G-1
         pair = blk;
-        if (pair >= B * HK * NC) return;
-        h = (pair / NC) % HK * G;
+        sub = 0;
     } else {
         // Block -> item: the G value heads that share a key head (and so read the same q and
         // k rows) get blocks 8 apart, i.e. the same XCD (blocks are dealt round-robin to the
         // 8 XCDs) at about the same time, so all but the first read of each q/k row hit that
-        // XCD's L2.  Runs of 8G blocks cover 8 (batch, key head, chunk) triples; the last
-        // run's unused blocks return at once.
+        // XCD's L2.  Runs of 8G blocks cover 8 items; the last run's unused blocks return
+        // at once.
         const int within = blk % (8 * G);
         pair = (blk / (8 * G)) * 8 + within % 8;
-        if (pair >= B * HK * NC) return;
-        h = (pair / NC) % HK * G + within / 8;
+        sub = within / 8;
     }
-    const int n = pair % NC;
-    const int bk = pair / NC;
-    const int kh = bk % HK;
-    const int b = bk / HK;
-    const int bh = b * HV + h;
+    if (pair >= items) return;
+    int b, kh, n;
+    SeqSpan sp;
+    if (plan) {
+        const int slot = pair % NC;
+        if (slot >= plan[VarlenPlan::first(B) + B]) return;  // past the last sequence's chunks
+        kh = pair / NC;
+        b = plan[VarlenPlan::chunk_seq(B) + slot];
+        sp = seq_span(plan, b, B, T, NC);
+        n = slot - sp.c0;
+    } else {
+        n = pair % NC;
+        kh = (pair / NC) % HK;
+        b = pair / NC / HK;
+        sp = seq_span(nullptr, b, B, T, NC);
+    }
+    const int h = kh * G + sub;
     const int t0 = n * C;
-    const int L = min(C, T - t0);
-    const size_t hstride = (size_t)NC * R.bytes;  // between the records of heads h and h + 1
-    unsigned char* rec = ws + ((size_t)bh * NC + n) * R.bytes;
+    const int L = min(C, sp.T - t0);
+    const size_t hstride = (size_t)sp.nc * R.bytes;  // between the records of heads h and h + 1
+    unsigned char* rec = ws + ((size_t)sp.c0 * HV + (size_t)h * sp.nc + n) * R.bytes;
     const int I = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #define GDR_WAVE(I_)                                                                            \
     if (I == I_) {                                                                              \
         if constexpr (I_ < NB)                                                                  \
-            prep_wave<TIn, TG, DK, C, I_, KN, GS, SP>(s, q, k, g, beta, rec, b, T, HK, HV, HG, h, \
-                                                      kh, t0, L, hstride);                      \
+            prep_wave<TIn, TG, DK, C, I_, KN, GS, SP>(s, q, k, g, beta, rec, sp.row0, sp.T, HK, HV, \
+                                                      HG, h, kh, t0, L, hstride);               \
         return;                                                                                 \
     }
     GDR_WAVE(0) GDR_WAVE(1) GDR_WAVE(2) GDR_WAVE(3)
@@ -730,12 +744,13 @@ __global__ __launch_bounds__(C * 4, (KN || SP) ? 2 : 3) void chunk_prep_kernel(
 // Launch of the prep kernel for one instantiation: blocks as the kernel maps them.
 template <typename TIn, typename TG, int DK, int C, bool KN, bool GS, bool SP>
 hipError_t launch_prep_t(const LaunchArgs& a) {
-    const int NC = (a.T + C - 1) / C;
-    const long long triples = (long long)a.B * a.HK * NC;  // (batch, key head, chunk)
-    const long long blocks = SP ? triples : (triples + 7) / 8 * 8 * (a.HV / a.HK);
+    // dense: chunks per batch element; packed: chunk slots
+    const int NC = a.plan ? a.nct : (a.T + C - 1) / C;
+    const long long items = (long long)(a.plan ? 1 : a.B) * a.HK * NC;
+    const long long blocks = SP ? items : (items + 7) / 8 * 8 * (a.HV / a.HK);
     hipLaunchKernelGGL((chunk_prep_kernel<TIn, TG, DK, C, KN, GS, SP>), dim3((unsigned)blocks), dim3(C * 4), 0,
                        (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TG*)a.g, a.beta,
-                       (unsigned char*)a.workspace, a.B, a.T, a.HK, a.HV, a.HG, NC);
+                       (unsigned char*)a.workspace, a.B, a.T, a.HK, a.HV, a.HG, NC, a.plan);
     return hipGetLastError();
 }
 

@@ -36,7 +36,8 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
                                                     const TG* __restrict__ g,
                                                     const float* __restrict__ beta,
                                                     const float* h0, float* __restrict__ o,
-                                                    float* ht, int T, int HK, int HV, int HG) {
+                                                    float* ht, int T, int HK, int HV, int HG,
+                                                    const int32_t* __restrict__ cu) {
     constexpr int BVD = DV < 64 ? DV : 64;   // columns per workgroup
     constexpr int NQ = BVD / 4;              // column quads per row
     constexpr int NRL = 256 / NQ;            // row lanes
@@ -71,11 +72,21 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
         for (int m = 0; m < RPT; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    // Rows of this batch element, or of packed sequence b (cu != nullptr: rows
+    // [cu[b], cu[b + 1]), both clamped to [0, T] so that no access leaves the tensors).
+    size_t row0 = (size_t)b * T;
+    int nt = T;
+    if (cu != nullptr) {
+        const int r0 = min(max(cu[b], 0), T);
+        const int r1 = min(max(cu[b + 1], r0), T);
+        row0 = (size_t)r0;
+        nt = r1 - r0;
+    }
     // Token tok of this (batch, head): q/k row, g row, v/o columns, beta.
-    const size_t kq0 = ((size_t)b * T * HK + kh) * DK;
-    const size_t gb0 = ((size_t)b * T * HG + h / (HV / HG)) * DK;  // gate head of h
-    const size_t vb0 = ((size_t)b * T * HV + h) * DV + col;
-    const size_t bb0 = (size_t)b * T * HV + h;
+    const size_t kq0 = (row0 * HK + kh) * DK;
+    const size_t gb0 = (row0 * HG + h / (HV / HG)) * DK;  // gate head of h
+    const size_t vb0 = (row0 * HV + h) * DV + col;
+    const size_t bb0 = row0 * HV + h;
     const size_t kq_t = (size_t)HK * DK, gb_t = (size_t)HG * DK, vb_t = (size_t)HV * DV;
 
     // raw inputs of the next token, requested one token ahead
@@ -95,9 +106,9 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
         for (int c = 0; c < 4; ++c) vn[c] = v[vb + c];
         btn = beta[bb0 + tok * HV];
     };
-    request(0);
+    if (nt > 0) request(0);
 
-    for (int tok = 0; tok < T; ++tok) {
+    for (int tok = 0; tok < nt; ++tok) {
         float e[RPT], kk[RPT], qq[RPT];
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
@@ -107,7 +118,7 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
         }
         const f32x4 vv = {to_f32(vn[0]), to_f32(vn[1]), to_f32(vn[2]), to_f32(vn[3])};
         const float bt = btn;
-        if (tok + 1 < T) request(tok + 1);
+        if (tok + 1 < nt) request(tok + 1);
 
         // pass 1: prediction with the decay folded in
         f32x4 p = {0.f, 0.f, 0.f, 0.f};
@@ -295,14 +306,14 @@ template <typename TIn, typename TG, int DK, int DV, bool KN, bool GS>
 static hipError_t launch_tokens_t(const LaunchArgs& a) {
     constexpr int BVD = DV < 64 ? DV : 64;
     const long long nblk = (long long)a.B * a.HV * (DV / BVD);
-    if (a.T == 1) {
+    if (a.T == 1 && a.cu_seqlens == nullptr) {
         hipLaunchKernelGGL((decode_kernel<TIn, TG, DK, DV, KN, GS>), dim3((unsigned)nblk), dim3(256), 0,
                            (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
                            (const TG*)a.g, a.beta, a.h0, a.o, a.ht, a.HK, a.HV, a.HG);
     } else {
         hipLaunchKernelGGL((token_kernel<TIn, TG, DK, DV, KN, GS>), dim3((unsigned)nblk), dim3(256), 0,
                            (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
-                           (const TG*)a.g, a.beta, a.h0, a.o, a.ht, a.T, a.HK, a.HV, a.HG);
+                           (const TG*)a.g, a.beta, a.h0, a.o, a.ht, a.T, a.HK, a.HV, a.HG, a.cu_seqlens);
     }
     return hipGetLastError();
 }

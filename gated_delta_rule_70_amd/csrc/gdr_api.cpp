@@ -12,6 +12,7 @@
 #include "gdr_launch.h"
 
 static_assert(gdr::kSplitMaxGroup == GDR_PREP_SPLIT_MAX_GROUP, "split prep group limit");
+static_assert(gdr::kVarlenMaxSeqs == GDR_VARLEN_MAX_SEQS, "packed batch sequence limit");
 
 // Workspace of the allocation-free prefill entry point (see gdr.h).  In host code `scratch`
 // is only a handle to the device array; its address on a device comes from
@@ -65,10 +66,12 @@ bool mul_ok(size_t a, size_t b, size_t* out) {
     return true;
 }
 
-bool tensor_sizes(const gdr_dims& d, size_t elt, Sizes* s) {
+// A packed variable-length batch (varlen) has its d.B sequences laid end to end in d.T token
+// rows; the states are still one per sequence.
+bool tensor_sizes(const gdr_dims& d, size_t elt, Sizes* s, bool varlen) {
     const size_t gelt = (d.flags & GDR_G_BF16) ? 2 : 4;
     size_t bt, bth, btv, x;
-    if (!mul_ok((size_t)d.B, (size_t)d.T, &bt)) return false;
+    if (!mul_ok(varlen ? 1 : (size_t)d.B, (size_t)d.T, &bt)) return false;
     if (!mul_ok(bt, (size_t)d.HK, &bth) || !mul_ok(bt, (size_t)d.HV, &btv)) return false;
     if (!mul_ok(bth, (size_t)d.dk, &x) || !mul_ok(x, elt, &s->q)) return false;
     if (!mul_ok(btv, (size_t)d.dv, &x) || !mul_ok(x, elt, &s->v)) return false;
@@ -87,12 +90,14 @@ bool tensor_sizes(const gdr_dims& d, size_t elt, Sizes* s) {
 // (any T, chunk ignored) or the chunked prefill (chunk checked).
 enum class Path { decode, tokens, chunked };
 
-// Shared validation of dims, pointers, alignment and aliasing.
+// Shared validation of dims, pointers, alignment and aliasing.  `cu` is the sequence
+// boundary array of a packed variable-length call (nullptr otherwise).
 int validate(const gdr_dims* d, Path path, const void* q, const void* k, const void* v,
              const void* g, const float* beta, const float* h0, const float* o,
-             const float* ht, Sizes* sizes) {
-    if (!d || !q || !k || !v || !g || !beta || !o) return GDR_ERR_NULL;
+             const float* ht, Sizes* sizes, const int32_t* cu = nullptr, bool varlen = false) {
+    if (!d || !q || !k || !v || !g || !beta || !o || (varlen && !cu)) return GDR_ERR_NULL;
     if (d->B < 1 || d->T < 1 || d->HK < 1 || d->HV < 1 || d->HV % d->HK != 0) return GDR_ERR_SHAPE;
+    if (varlen && d->B > GDR_VARLEN_MAX_SEQS) return GDR_ERR_SHAPE;
     if (path == Path::decode && d->T != 1) return GDR_ERR_SHAPE;
     if (!supported_head_dim(d->dk) || !supported_head_dim(d->dv)) return GDR_ERR_UNSUPPORTED;
     if (d->qkv_dtype != GDR_BF16 && d->qkv_dtype != GDR_F32) return GDR_ERR_UNSUPPORTED;
@@ -107,15 +112,18 @@ int validate(const gdr_dims* d, Path path, const void* q, const void* k, const v
     if (path == Path::chunked && d->chunk != 16 && d->chunk != 32 && d->chunk != 64)
         return GDR_ERR_UNSUPPORTED;
     const size_t elt = d->qkv_dtype == GDR_F32 ? 4 : 2;
-    if (!tensor_sizes(*d, elt, sizes)) return GDR_ERR_SHAPE;
-    // Grid sizes must fit the launch limits: (B*HV) heads times chunks or column tiles.
+    if (!tensor_sizes(*d, elt, sizes, varlen)) return GDR_ERR_SHAPE;
+    // Grid sizes must fit the launch limits: (B*HV) heads times chunks or column tiles; a
+    // packed batch's prep covers its chunk slots per value head (plus a partial run of 8).
     const long long heads = (long long)d->B * d->HV;
-    const long long nchunk = path == Path::chunked ? (d->T + d->chunk - 1) / d->chunk : 1;
-    if (heads * nchunk >= (1LL << 31) || heads * (d->dv / 16) >= (1LL << 31)) return GDR_ERR_SHAPE;
+    long long grid = heads * (path == Path::chunked && !varlen ? (d->T + d->chunk - 1) / d->chunk : 1);
+    if (path == Path::chunked && varlen) grid = (gdr::varlen_chunk_slots(d->B, d->T, d->chunk) + 8) * d->HV;
+    if (grid >= (1LL << 31) || heads * (d->dv / 16) >= (1LL << 31)) return GDR_ERR_SHAPE;
 
     const void* ptrs[] = {q, k, v, g, beta, h0, o, ht};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDR_ERR_ALIGN;
+    if (cu && (reinterpret_cast<uintptr_t>(cu) & 3u) != 0) return GDR_ERR_ALIGN;
 
     const Range rq = range_of(q, sizes->q), rk = range_of(k, sizes->q), rv = range_of(v, sizes->v),
                 rg = range_of(g, sizes->g), rb = range_of(beta, sizes->beta),
@@ -127,13 +135,17 @@ int validate(const gdr_dims* d, Path path, const void* q, const void* k, const v
     }
     if (overlap(ro, rh0) || overlap(ro, rht)) return GDR_ERR_ALIAS;
     if (overlap(rht, rh0) && rht.lo != rh0.lo) return GDR_ERR_ALIAS;
+    if (cu) {
+        const Range rc = range_of(cu, ((size_t)d->B + 1) * 4);
+        if (overlap(ro, rc) || overlap(rht, rc)) return GDR_ERR_ALIAS;
+    }
     return GDR_OK;
 }
 
 gdr::LaunchArgs make_args(const gdr_dims* d, const void* q, const void* k, const void* v,
                           const void* g, const float* beta, const float* h0, float* o, float* ht,
-                          void* workspace, void* stream) {
-    gdr::LaunchArgs a;
+                          void* workspace, void* stream, const int32_t* cu = nullptr) {
+    gdr::LaunchArgs a{};
     a.B = d->B;
     a.T = d->T;
     a.HK = d->HK;
@@ -152,9 +164,12 @@ gdr::LaunchArgs make_args(const gdr_dims* d, const void* q, const void* k, const
         a.prep_split = true;
     else if (d->flags & GDR_PREP_FUSED)
         a.prep_split = false;
-    else
-        a.prep_split = gk && G > 1 && G <= GDR_PREP_SPLIT_MAX_GROUP &&
-                       gdr::split_prep_preferred(d->B, d->HK, d->T, d->chunk);
+    else if (gk && G > 1 && G <= GDR_PREP_SPLIT_MAX_GROUP && d->chunk > 0) {
+        // (batch element or sequence, key head, chunk) items of the prep
+        const long long chunks = cu ? gdr::varlen_chunk_slots(d->B, d->T, d->chunk)
+                                    : (long long)d->B * ((d->T + (long long)d->chunk - 1) / d->chunk);
+        a.prep_split = gdr::split_prep_preferred(chunks * d->HK);
+    }
     a.q = q;
     a.k = k;
     a.v = v;
@@ -165,17 +180,25 @@ gdr::LaunchArgs make_args(const gdr_dims* d, const void* q, const void* k, const
     a.ht = ht;
     a.workspace = workspace;
     a.stream = stream;
+    a.cu_seqlens = cu;
     return a;
 }
 
-size_t workspace_bytes_unchecked(const gdr_dims* d) {
+size_t workspace_bytes_unchecked(const gdr_dims* d, bool varlen = false) {
     const gdr::ChunkRecord rec = gdr::ChunkRecord::make(d->chunk, d->dk);
-    const size_t nchunk = (size_t)((d->T + d->chunk - 1) / d->chunk);
+    const size_t nchunk = varlen ? (size_t)gdr::varlen_chunk_slots(d->B, d->T, d->chunk)
+                                 : (size_t)d->B * (size_t)((d->T + d->chunk - 1) / d->chunk);
     size_t x;
-    if (!mul_ok((size_t)d->B * (size_t)d->HV, nchunk, &x) || !mul_ok(x, rec.bytes, &x)) return 0;
+    if (!mul_ok((size_t)d->HV, nchunk, &x) || !mul_ok(x, rec.bytes, &x)) return 0;
     // the carry's segment summaries and start states (at most 256 heads x segments of
-    // dk x dk fp32 matrices each) follow the records
-    return gdr::carry_layout(d->B, d->HV, d->T, d->dk, d->dv, d->chunk).total;
+    // dk x dk fp32 matrices each), or a packed batch's plan, follow the records
+    return gdr::carry_layout(d->B, d->HV, d->T, d->dk, d->dv, d->chunk, varlen).total;
+}
+
+bool prefill_dims_ok(const gdr_dims* dims) {
+    return dims && dims->B >= 1 && dims->T >= 1 && dims->HK >= 1 && dims->HV >= 1 &&
+           dims->HV % dims->HK == 0 && supported_head_dim(dims->dk) && supported_head_dim(dims->dv) &&
+           (dims->chunk == 16 || dims->chunk == 32 || dims->chunk == 64);
 }
 
 }  // namespace
@@ -220,22 +243,24 @@ int gdr_fused_recurrent(const gdr_dims* dims, const void* q, const void* k, cons
 }
 
 size_t gdr_chunk_prefill_workspace_bytes(const gdr_dims* dims) {
-    if (!dims || dims->B < 1 || dims->T < 1 || dims->HK < 1 || dims->HV < 1 ||
-        dims->HV % dims->HK != 0 || !supported_head_dim(dims->dk) ||
-        !supported_head_dim(dims->dv) ||
-        (dims->chunk != 16 && dims->chunk != 32 && dims->chunk != 64))
-        return 0;
+    if (!prefill_dims_ok(dims)) return 0;
     return workspace_bytes_unchecked(dims);
+}
+
+size_t gdr_chunk_prefill_varlen_workspace_bytes(const gdr_dims* dims) {
+    if (!prefill_dims_ok(dims) || dims->B > GDR_VARLEN_MAX_SEQS) return 0;
+    return workspace_bytes_unchecked(dims, true);
 }
 
 static int prefill_stages(const gdr_dims* dims, const void* q, const void* k, const void* v,
                           const void* g, const float* beta, const float* h0, float* o, float* ht,
                           void* workspace, size_t workspace_bytes, void* stream, bool prep,
-                          bool carry) {
+                          bool carry, const int32_t* cu = nullptr) {
     Sizes s;
-    const int st = validate(dims, Path::chunked, q, k, v, g, beta, h0, o, ht, &s);
+    const bool varlen = cu != nullptr;
+    const int st = validate(dims, Path::chunked, q, k, v, g, beta, h0, o, ht, &s, cu, varlen);
     if (st != GDR_OK) return st;
-    const size_t need = workspace_bytes_unchecked(dims);
+    const size_t need = workspace_bytes_unchecked(dims, varlen);
     if (need == 0) return GDR_ERR_SHAPE;
     // The kernels address one batch element's g/q/k/v/o rows (including the padding rows of
     // the last chunk, which lie past the end and read as zero) and one head's chunk records
@@ -251,10 +276,17 @@ static int prefill_stages(const gdr_dims* dims, const void* q, const void* k, co
     const Range rw = range_of(workspace, need);
     const Range others[] = {range_of(q, s.q), range_of(k, s.q), range_of(v, s.v), range_of(g, s.g),
                             range_of(beta, s.beta), range_of(h0, s.state), range_of(o, s.o),
-                            range_of(ht, s.state)};
+                            range_of(ht, s.state), range_of(cu, ((size_t)dims->B + 1) * 4)};
     for (const Range& r : others)
         if (overlap(rw, r)) return GDR_ERR_ALIAS;
-    const gdr::LaunchArgs a = make_args(dims, q, k, v, g, beta, h0, o, ht, workspace, stream);
+    gdr::LaunchArgs a = make_args(dims, q, k, v, g, beta, h0, o, ht, workspace, stream, cu);
+    if (varlen) {
+        const gdr::CarryLayout L = gdr::carry_layout(dims->B, dims->HV, dims->T, dims->dk, dims->dv,
+                                                     dims->chunk, true);
+        a.plan = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) + L.plan_off);
+        a.nct = (int)gdr::varlen_chunk_slots(dims->B, dims->T, dims->chunk);
+        if (prep && gdr::launch_varlen_plan(a) != hipSuccess) return GDR_ERR_HIP;
+    }
     if (prep && gdr::launch_chunk_prep(a) != hipSuccess) return GDR_ERR_HIP;
     if (carry && gdr::launch_chunk_carry(a) != hipSuccess) return GDR_ERR_HIP;
     return GDR_OK;
@@ -294,6 +326,25 @@ int gdr_chunk_carry(const gdr_dims* dims, const void* q, const void* k, const vo
                     void* workspace, size_t workspace_bytes, void* stream) {
     return prefill_stages(dims, q, k, v, g, beta, h0, o, ht, workspace, workspace_bytes, stream,
                           false, true);
+}
+
+int gdr_chunk_prefill_varlen(const gdr_dims* dims, const int32_t* cu_seqlens, const void* q,
+                             const void* k, const void* v, const void* g, const float* beta,
+                             const float* h0, float* o, float* ht, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    if (!cu_seqlens) return GDR_ERR_NULL;
+    return prefill_stages(dims, q, k, v, g, beta, h0, o, ht, workspace, workspace_bytes, stream,
+                          true, true, cu_seqlens);
+}
+
+int gdr_fused_recurrent_varlen(const gdr_dims* dims, const int32_t* cu_seqlens, const void* q,
+                               const void* k, const void* v, const void* g, const float* beta,
+                               const float* h0, float* o, float* ht, void* stream) {
+    Sizes s;
+    const int st = validate(dims, Path::tokens, q, k, v, g, beta, h0, o, ht, &s, cu_seqlens, true);
+    if (st != GDR_OK) return st;
+    const gdr::LaunchArgs a = make_args(dims, q, k, v, g, beta, h0, o, ht, nullptr, stream, cu_seqlens);
+    return gdr::launch_tokens(a) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
 int gdr_tree_verify(const gdr_dims* dims, const int32_t* parent, const void* q, const void* k,

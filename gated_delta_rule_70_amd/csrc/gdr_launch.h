@@ -29,7 +29,52 @@ struct LaunchArgs {
     float* ht;
     void* workspace;
     void* stream;
+    // Packed variable-length batch (nullptr / 0 for a dense [B][T] batch): B sequences laid
+    // end to end in T rows, sequence b on rows [cu_seqlens[b], cu_seqlens[b + 1]).
+    const int32_t* cu_seqlens;  // [B + 1], on the device
+    int32_t* plan;              // prefill: the sequence plan in the workspace (VarlenPlan)
+    int nct;                    // prefill: chunk slots, an upper bound on the sum of the
+                                // sequences' chunk counts (varlen_chunk_slots)
 };
+
+// Largest number of sequences in one packed variable-length call (the plan kernel holds
+// two entries per sequence in LDS).
+constexpr int kVarlenMaxSeqs = 4096;
+
+// Upper bound on sum_b ceil(len_b / C) over B sequences of T rows in all:
+// ceil(len / C) <= (len + C - 1) / C, summed.
+inline long long varlen_chunk_slots(long long B, long long T, int chunk) {
+    return (T + B * (chunk - 1)) / chunk;
+}
+
+// The plan of a packed variable-length prefill, int32 in the workspace after the records:
+//   [0, B]              sequence starts, sanitised: clamped to [0, T] and made
+//                       non-decreasing (running maximum), so sequences never overlap
+//   [B + 1, 2B + 1]     first chunk slot of each sequence (exclusive prefix of
+//                       ceil(len / C)); entry 2B + 1 is the number of chunks in all
+//   [2B + 2, 2B + 2 + nct)  the sequence of each chunk slot
+// Chunk records are stored per sequence, then head, then chunk: sequence b's record of head
+// h and chunk n sits at slot (first_b * HV + h * nchunks_b + n), which for a dense batch
+// (first_b = b * NC, nchunks_b = NC) is the dense layout ((b * HV + h) * NC + n).
+struct VarlenPlan {
+    __host__ __device__ static constexpr long long ints(long long B, long long nct) { return 2 * (B + 1) + nct; }
+    __host__ __device__ static constexpr int starts(int) { return 0; }
+    __host__ __device__ static constexpr int first(int B) { return B + 1; }
+    __host__ __device__ static constexpr int chunk_seq(int B) { return 2 * B + 2; }
+};
+
+// Rows and chunk records of batch element (dense) or sequence (packed) b: first row, rows,
+// chunks, first chunk slot.
+struct SeqSpan {
+    long long row0;
+    int T, nc, c0;
+};
+__device__ __forceinline__ SeqSpan seq_span(const int32_t* plan, int b, int B, int T, int NC) {
+    if (plan == nullptr) return SeqSpan{(long long)b * T, T, NC, b * NC};
+    const int r0 = plan[b], r1 = plan[b + 1];
+    const int k0 = plan[VarlenPlan::first(B) + b], k1 = plan[VarlenPlan::first(B) + b + 1];
+    return SeqSpan{r0, r1 - r0, k1 - k0, k0};
+}
 
 // Per-(batch, head, chunk) record that the chunk-parallel kernel writes and the
 // sequential carry kernel reads: fp16 MFMA operand fragments (1 KiB each: 64 lanes x 8
@@ -92,25 +137,28 @@ struct ChunkRecord {
 // workspace also holds each segment's summary [S_loc | M] (fp32, [heads][nseg - 1][2][dk]
 // [dk]) and start state (fp32, [heads][nseg][dk][dv]).  A pure function of the dims, so
 // the size query and the launch agree.
+// A packed variable-length batch (varlen) never takes the time segments: its records are
+// cnt slots per head (varlen_chunk_slots), followed by the plan (VarlenPlan).
 struct CarryLayout {
     bool wide;
     int nseg;
-    size_t rec_bytes, xsum_off, sstart_off, total;
+    size_t rec_bytes, xsum_off, sstart_off, plan_off, total;
 };
 
-inline CarryLayout carry_layout(int B, int HV, int T, int dk, int dv, int chunk) {
+inline CarryLayout carry_layout(int B, int HV, int T, int dk, int dv, int chunk, bool varlen = false) {
     CarryLayout L{};
     const ChunkRecord R = ChunkRecord::make(chunk, dk);
     const long long NC = (T + (long long)chunk - 1) / chunk;
     const long long NH = (long long)B * HV;
-    L.rec_bytes = (size_t)NH * (size_t)NC * (size_t)R.bytes;
+    const long long slots = varlen ? varlen_chunk_slots(B, T, chunk) * HV : NH * NC;
+    L.rec_bytes = (size_t)slots * (size_t)R.bytes;
     const bool dims_ok = dk == dv && (dk == 64 || dk == 128);
     L.nseg = 1;
     L.wide = false;
     if (dims_ok) {
         if (NH > 128) {
             L.wide = true;
-        } else {
+        } else if (!varlen) {
             const long long want = 256 / NH;  // >= 2
             if (NC >= 16 * want) {
                 L.wide = true;
@@ -121,23 +169,24 @@ inline CarryLayout carry_layout(int B, int HV, int T, int dk, int dv, int chunk)
     const size_t mat = (size_t)dk * dk * 4;
     L.xsum_off = L.rec_bytes;
     L.sstart_off = L.xsum_off + (L.nseg > 1 ? (size_t)NH * (L.nseg - 1) * 2 * mat : 0);
-    L.total = L.sstart_off + (L.nseg > 1 ? (size_t)NH * L.nseg * mat : 0);
+    L.plan_off = L.sstart_off + (L.nseg > 1 ? (size_t)NH * L.nseg * mat : 0);
+    L.total = L.plan_off +
+              (varlen ? (size_t)VarlenPlan::ints(B, varlen_chunk_slots(B, T, chunk)) * 4 : 0);
     return L;
 }
 
 // Prep form for a gate shared per key head when the caller does not force one: the split
 // form (a workgroup per key head and chunk, the gram computed once per group) once there
-// are enough (batch, key head, chunk) triples to fill the chip with it.  Measured on an
+// are enough (batch element or sequence, key head, chunk) triples to fill the chip with it.  Measured on an
 // MI355X at HK = 16, HV = 32, 128 x 128, chunk 64 (prep alone, fused / split): T = 512
 // 15.6 / 18.0 us, T = 1024 21.9 / 19.1 us, T = 4097 62.2 / 57.8 us, T = 16384 249 / 202 us,
 // B = 8 T = 512 58.2 / 49.9 us -- the split form wins from 256 triples.
-inline bool split_prep_preferred(int B, int HK, int T, int chunk) {
-    if (chunk <= 0) return false;  // the token-recurrence calls carry no chunk length
-    const long long triples = (long long)B * HK * ((T + (long long)chunk - 1) / chunk);
-    return triples >= 256;
-}
+inline bool split_prep_preferred(long long triples) { return triples >= 256; }
 
-// token recurrence over a.T tokens in one launch (the decode step is a.T == 1)
+// packed variable-length prefill: sanitised starts and chunk plan into a.plan
+hipError_t launch_varlen_plan(const LaunchArgs& a);
+// token recurrence over a.T tokens in one launch (the decode step is a.T == 1; with
+// a.cu_seqlens, over each packed sequence)
 hipError_t launch_tokens(const LaunchArgs& a);
 // The prep kernel in fused form (one workgroup per value head and chunk) or in split
 // form (one per key head and chunk, solving per value head; needs HG == HK and

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 6
+#define GDR_ABI_VERSION 7
 
 typedef enum {
     GDR_OK = 0,
@@ -225,6 +225,51 @@ int gdr_chunk_carry(const gdr_dims* dims, const void* q, const void* k, const vo
 int gdr_forward(const gdr_dims* dims, const void* q, const void* k, const void* v,
                 const void* g, const float* beta, const float* h0, float* o, float* ht,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Packed variable-length batches.  The pages route work by sequence length (ExecuTorch PR
+ * #21021, second commit summary) and batch speculative chains of different lengths (uzu PR
+ * #576 review: dispatch cost at small T); a batch of sequences of different lengths is laid
+ * end to end instead of padded:
+ *   dims->B     number of sequences N (1 .. GDR_VARLEN_MAX_SEQS)
+ *   dims->T     rows in all, the packed length
+ *   cu_seqlens  device array [N + 1] of int32, 4-byte aligned: sequence i is on rows
+ *               [cu_seqlens[i], cu_seqlens[i + 1]); expected non-decreasing from 0 to T.
+ *   q, k        [T][HK][dk]         v, o  [T][HV][dv]       beta  [T][HV]
+ *   g           [T][HV][dk] (or [T][HK][dk] with GDR_G_PER_KEY_HEAD)
+ *   h0, ht      [N][HV][dk][dv]: one state per sequence
+ * i.e. the dense layouts with B = 1 for the token tensors and B = N for the states.  Every
+ * sequence runs the recurrence from its own h0 (zero if h0 is NULL) and ends in its own ht;
+ * a sequence with no rows passes h0 to ht.  Flags and other rules are those of the dense
+ * calls.  The library reads cu_seqlens on the device only: entries are clamped to [0, T]
+ * and to the running maximum of the entries before them, so no access leaves the tensors
+ * whatever they hold, but results are defined only for non-decreasing entries from 0 to T
+ * (rows outside [cu_seqlens[0], cu_seqlens[N]) are then not written).
+ */
+#define GDR_VARLEN_MAX_SEQS 4096
+
+/*
+ * Chunkwise prefill of a packed batch: each sequence chunked from its own first row (its
+ * last chunk ragged), the chunk-parallel stage over every sequence's chunks at once, the
+ * carry per (sequence, head).  A first small kernel turns cu_seqlens into the plan the
+ * others read (kept in the workspace).  Equal to one gdr_chunk_prefill call per sequence.
+ * `workspace` as for gdr_chunk_prefill, of at least
+ * gdr_chunk_prefill_varlen_workspace_bytes(dims) bytes (a bound that holds for any split of
+ * T rows into N sequences).
+ */
+size_t gdr_chunk_prefill_varlen_workspace_bytes(const gdr_dims* dims);
+int gdr_chunk_prefill_varlen(const gdr_dims* dims, const int32_t* cu_seqlens, const void* q,
+                             const void* k, const void* v, const void* g, const float* beta,
+                             const float* h0, float* o, float* ht, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * The fused token recurrence (gdr_fused_recurrent) over a packed batch: one workgroup per
+ * (sequence, value head, column block) runs that sequence's rows.  Uses no workspace.
+ */
+int gdr_fused_recurrent_varlen(const gdr_dims* dims, const int32_t* cu_seqlens, const void* q,
+                               const void* k, const void* v, const void* g, const float* beta,
+                               const float* h0, float* o, float* ht, void* stream);
 
 /*
  * Tree-verify solve (uzu PR #576, "Support TreeUpdateSolve kernel": a gram over a

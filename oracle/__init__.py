@@ -17,6 +17,8 @@ Two routes to the same result, both in fp64 (see ``gdr_oracle.c`` for the arithm
   ("Support TreeUpdateSolve kernel").
 * :func:`l2_normalize_keys`, :func:`neg_softplus` -- the input pre-processing of that page's
   real-scale recipe (normalised keys, softplus decay), which the library can fuse.
+* :func:`varlen` -- a packed batch of sequences of different lengths, laid end to end: each
+  sequence run through one of the routes above on its own, from its own initial state.
 * :func:`gate_per_value_head` -- a gate given per key head, as every value head of the GQA
   group sees it (the per-key-head layout that the uzu PR #576 review thread on the
   per-value-head gram is about).
@@ -225,6 +227,35 @@ def neg_softplus(a) -> np.ndarray:
     the same input recipe, applied by the library's fused prologue (GDR_G_SOFTPLUS)."""
     a = _f64(a)
     return -(np.maximum(a, 0.0) + np.log1p(np.exp(-np.abs(a))))
+
+
+def varlen(route, q, k, v, g, beta, cu_seqlens, h0=None, **kw):
+    """A packed batch: token tensors ``[T, H, d]`` (or ``[1, T, H, d]``), ``cu_seqlens``
+    ``[N+1]`` with sequence i on rows ``[cu[i], cu[i+1])``, h0 ``[N,HV,dk,dv]`` or None.  Each
+    sequence is passed to ``route`` (:func:`sequential` or :func:`chunked`, extra keywords
+    forwarded) as a batch of one with its own h0 row.  Returns ``(o [T,HV,dv], ht
+    [N,HV,dk,dv])``; rows outside every sequence stay zero."""
+    q, k, v, g, beta, h0 = (_f64(x) for x in (q, k, v, g, beta, h0))
+    q, k, v, g, beta = (x[0] if x.ndim == (3 if n == "beta" else 4) else x
+                        for n, x in zip(("q", "k", "v", "g", "beta"), (q, k, v, g, beta)))
+    cu = [int(c) for c in np.asarray(cu_seqlens).reshape(-1)]
+    N = len(cu) - 1
+    T, HV, dv = v.shape
+    dk = q.shape[2]
+    if any(b < a for a, b in zip(cu, cu[1:])) or cu[0] < 0 or cu[-1] > T:
+        raise ValueError("cu_seqlens must be non-decreasing within [0, T]")
+    o = np.zeros((T, HV, dv))
+    ht = np.zeros((N, HV, dk, dv))
+    for i in range(N):
+        a, b = cu[i], cu[i + 1]
+        hi = None if h0 is None else h0[i:i + 1]
+        if b == a:  # no rows: the state passes through
+            ht[i] = 0.0 if hi is None else hi[0]
+            continue
+        oi, hti = route(q[None, a:b], k[None, a:b], v[None, a:b], g[None, a:b], beta[None, a:b], hi, **kw)
+        o[a:b] = oi[0]
+        ht[i] = hti[0]
+    return o, ht
 
 
 def num_threads() -> int:

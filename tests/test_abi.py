@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "gdr_abi_version", "gdr_chunk_carry", "gdr_chunk_prefill", "gdr_chunk_prefill_workspace_bytes",
         "gdr_chunk_prefill_noalloc", "gdr_chunk_prep", "gdr_decode_step", "gdr_forward",
-        "gdr_fused_recurrent", "gdr_status_str", "gdr_tree_verify"])
+        "gdr_fused_recurrent", "gdr_status_str", "gdr_tree_verify", "gdr_chunk_prefill_varlen",
+        "gdr_chunk_prefill_varlen_workspace_bytes", "gdr_fused_recurrent_varlen"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -348,3 +349,47 @@ def test_key_head_gate_extent_in_alias_checks(L):
     gbytes = 2 * 5 * 2 * 64 * 4
     assert prefill(L, dims(flags=8), o=addr(3, gbytes - 16)) == EALIAS
     assert prefill(L, dims(flags=0), o=addr(3, gbytes + 16)) == EALIAS
+
+
+def varlen_call(L, d, entry="gdr_chunk_prefill_varlen", ws_bytes=None, **ptrs):
+    p = {n: addr(i) for i, n in enumerate(["cu", "q", "k", "v", "g", "beta", "h0", "o", "ht", "ws"])}
+    p.update(ptrs)
+    args = [p[n] for n in ("cu", "q", "k", "v", "g", "beta", "h0", "o", "ht")]
+    if entry == "gdr_fused_recurrent_varlen":
+        return L.gdr_fused_recurrent_varlen(ctypes.byref(d), *args, None)
+    if ws_bytes is None:
+        ws_bytes = L.gdr_chunk_prefill_varlen_workspace_bytes(ctypes.byref(d))
+    return L.gdr_chunk_prefill_varlen(ctypes.byref(d), *args, p["ws"], ctypes.c_size_t(ws_bytes), None)
+
+
+def test_varlen_workspace_bound(L):
+    """Records for every chunk slot (T + N (C - 1)) / C per value head, then the plan
+    (2 (N + 1) + slots int32)."""
+    for N, T, C, dk in ((1, 1, 64, 128), (7, 4405, 64, 128), (4096, 4096, 16, 32), (3, 200, 32, 64)):
+        d = dims(B=N, T=T, HK=2, HV=4, dk=dk, dv=dk, chunk=C)
+        slots = (T + N * (C - 1)) // C
+        rec = ((C // 16) * (dk // 32) * 2 + (dk // 16) * ((C + 31) // 32) + 2 * (C // 16) * ((C + 31) // 32) + 1) * 1024
+        assert L.gdr_chunk_prefill_varlen_workspace_bytes(ctypes.byref(d)) == slots * 4 * rec + (2 * (N + 1) + slots) * 4
+    assert L.gdr_chunk_prefill_varlen_workspace_bytes(ctypes.byref(dims(B=4097, T=5000))) == 0
+
+
+def test_varlen_checks(L):
+    for entry in ("gdr_chunk_prefill_varlen", "gdr_fused_recurrent_varlen"):
+        assert varlen_call(L, dims(), entry, cu=None) == ENULL
+        assert varlen_call(L, dims(), entry, cu=addr(0, 2)) == EALIGN
+        assert varlen_call(L, dims(B=4097, T=5000), entry) == ESHAPE
+        # o over the boundary array
+        assert varlen_call(L, dims(), entry, o=addr(0, 0)) == EALIAS
+    # the workspace must hold the plan too
+    d = dims()
+    need = L.gdr_chunk_prefill_varlen_workspace_bytes(ctypes.byref(d))
+    assert varlen_call(L, d, ws_bytes=need - 4) == EWS
+
+
+@pytest.mark.skipif("_gpu_visible()", reason="valid fake pointers would reach a real GPU")
+def test_varlen_valid_arguments_reach_the_runtime_without_a_gpu(L):
+    """States are [N][HV][dk][dv] and token tensors [T][..]: with N = 2, T = 5 every check
+    passes and the call fails only at the first HIP call."""
+    for entry in ("gdr_chunk_prefill_varlen", "gdr_fused_recurrent_varlen"):
+        assert varlen_call(L, dims(), entry) == EHIP
+        assert varlen_call(L, dims(flags=0x18), entry) == EHIP
