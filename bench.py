@@ -710,6 +710,42 @@ def bench_decode(w, steps, warmup):
     gb.record()
     torch.cuda.synchronize()
     graph_ms = ga.elapsed_time(gb) / nstep
+    del graph
+
+    # The same steps cycling over the 8 states (512 MiB, more than the 256 MB last-level
+    # cache), replayed from a graph: the HBM-resident decode rate without host launch gaps.
+    rgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(rgraph):
+        cs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for t in range(nstep):
+            q, k, v, g, b, o = args[t]
+            s = ptr(rot[t % len(rot)])
+            st = L.gdr_decode_step(ctypes.byref(dims), q, k, v, g, b, s, o, s, cs)
+            if st != 0:
+                raise RuntimeError(f"gdr_decode_step failed under capture: {st}")
+    rgraph.replay()
+    torch.cuda.synchronize()
+    ga.record()
+    rgraph.replay()
+    gb.record()
+    torch.cuda.synchronize()
+    graph_rot_ms = ga.elapsed_time(gb) / nstep
+    del rgraph
+
+    # Attainable HBM rate: one 1 GiB device copy (1 GiB read + 1 GiB written), far larger
+    # than the last-level cache.
+    big = 1 << 28
+    bsrc = torch.ones(big, device="cuda")
+    bdst = torch.empty_like(bsrc)
+    bdst.copy_(bsrc)
+    torch.cuda.synchronize()
+    ga.record()
+    for _ in range(5):
+        bdst.copy_(bsrc)
+    gb.record()
+    torch.cuda.synchronize()
+    copy_1g_ms = ga.elapsed_time(gb) / 5
+    del bsrc, bdst
 
     # A plain device copy of the state's size (read + write the same bytes as one step's
     # state stream), cycling over 8 buffer pairs like the rotating decode run.
@@ -732,7 +768,8 @@ def bench_decode(w, steps, warmup):
         "nstep": nstep,
         "carried": {"wall_s": wall_c, "mean_ms": _mean(per_c), "median_ms": per_c[len(per_c) // 2]},
         "rotating8": {"wall_s": wall_r, "mean_ms": _mean(per_r), "median_ms": per_r[len(per_r) // 2]},
-        "graph_ms_per_step": graph_ms, "copy_ms": copy_ms,
+        "graph_ms_per_step": graph_ms, "graph_rot_ms_per_step": graph_rot_ms, "copy_ms": copy_ms,
+        "copy_1g_ms": copy_1g_ms,
         "inputs": x, "obuf": obuf, "state": state,
     }
 
@@ -1005,10 +1042,21 @@ def main():
         gms = dres["graph_ms_per_step"]
         dec["graph_replay"] = {"ms_per_step": round(gms, 5), "total_GBps": round(dbytes / (gms * 1e-3) / 1e9, 1),
                                "hbm_frac": round(dbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        grms = dres["graph_rot_ms_per_step"]
+        dec["graph_replay_rotating8"] = {
+            "what": "the steps cycling over 8 states (512 MiB, HBM-resident), replayed from one graph",
+            "ms_per_step": round(grms, 5), "total_GBps": round(dbytes / (grms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(dbytes / (grms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         cms = dres["copy_ms"]
         dec["copy_reference"] = {"what": f"device copy of {sbytes // 2} B (state-sized read + write), 8 rotating buffers",
                                  "ms": round(cms, 5), "GBps": round(sbytes / (cms * 1e-3) / 1e9, 1),
                                  "decode_rotating8_frac_of_copy": round(cms / dres["rotating8"]["mean_ms"], 4)}
+        c1 = dres["copy_1g_ms"]
+        copy_gbs = 2 * (1 << 30) / (c1 * 1e-3) / 1e9
+        dec["copy_1GiB"] = {"what": "one 1 GiB device copy (read + write 2 GiB): the attainable HBM rate",
+                            "ms": round(c1, 4), "GBps": round(copy_gbs, 1), "hbm_frac": round(copy_gbs / HBM_PEAK_GBS, 4),
+                            "decode_graph_rotating8_frac_of_copy":
+                                round(dbytes / (grms * 1e-3) / 1e9 / copy_gbs, 4)}
         line["decode"] = dec
 
     if not args.no_short_calls and not args.profile_run:

@@ -116,7 +116,7 @@ int validate(const gdr_dims* d, Path path, const void* q, const void* k, const v
     // Grid sizes must fit the launch limits: (B*HV) heads times chunks or column tiles; a
     // packed batch's prep covers its chunk slots per value head (plus a partial run of 8).
     const long long heads = (long long)d->B * d->HV;
-    long long grid = heads * (path == Path::chunked && !varlen ? (d->T + d->chunk - 1) / d->chunk : 1);
+    long long grid = heads * (path == Path::chunked && !varlen ? ((long long)d->T + d->chunk - 1) / d->chunk : 1);
     if (path == Path::chunked && varlen) grid = (gdr::varlen_chunk_slots(d->B, d->T, d->chunk) + 8) * d->HV;
     if (grid >= (1LL << 31) || heads * (d->dv / 16) >= (1LL << 31)) return GDR_ERR_SHAPE;
 
@@ -187,7 +187,7 @@ gdr::LaunchArgs make_args(const gdr_dims* d, const void* q, const void* k, const
 size_t workspace_bytes_unchecked(const gdr_dims* d, bool varlen = false) {
     const gdr::ChunkRecord rec = gdr::ChunkRecord::make(d->chunk, d->dk);
     const size_t nchunk = varlen ? (size_t)gdr::varlen_chunk_slots(d->B, d->T, d->chunk)
-                                 : (size_t)d->B * (size_t)((d->T + d->chunk - 1) / d->chunk);
+                                 : (size_t)d->B * (((size_t)d->T + d->chunk - 1) / d->chunk);
     size_t x;
     if (!mul_ok((size_t)d->HV, nchunk, &x) || !mul_ok(x, rec.bytes, &x)) return 0;
     // the carry's segment summaries and start states (at most 256 heads x segments of
@@ -266,9 +266,9 @@ static int prefill_stages(const gdr_dims* dims, const void* q, const void* k, co
     // the last chunk, which lie past the end and read as zero) and one head's chunk records
     // with 31-bit buffer offsets.
     const gdr::ChunkRecord rec = gdr::ChunkRecord::make(dims->chunk, dims->dk);
-    const size_t nchunk = (size_t)((dims->T + dims->chunk - 1) / dims->chunk);
+    const size_t nchunk = ((size_t)dims->T + dims->chunk - 1) / dims->chunk;
     const size_t dmax = (size_t)(dims->dk > dims->dv ? dims->dk : dims->dv);
-    if ((size_t)(dims->T + dims->chunk) * dims->HV * dmax * 4 >= (size_t(1) << 31) ||
+    if (((size_t)dims->T + dims->chunk) * dims->HV * dmax * 4 >= (size_t(1) << 31) ||
         nchunk * (size_t)rec.bytes >= (size_t(1) << 31))
         return GDR_ERR_SHAPE;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)

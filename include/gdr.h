@@ -294,7 +294,7 @@ int gdr_tree_verify(const gdr_dims* dims, const int32_t* parent, const void* q, 
  * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation.  Same arguments, checks and results as gdr_chunk_prefill, minus the
  * workspace: the library uses its own per-device scratch array of GDR_NOALLOC_SCRATCH_BYTES
- * (64 MiB: the chunk records of a 2048-token prefill at HV = 32, dk = 128, chunk 64), which
+ * (64 MiB: the chunk records of a prefill of up to 1984 tokens at HV = 32, dk = 128, chunk 64), which
  * each GPU the library runs on holds until the process ends.  Calls whose workspace
  * (gdr_chunk_prefill_workspace_bytes) exceeds it return GDR_ERR_SCRATCH before any HIP
  * call.  It calls no allocating routine (the array's device address is looked up once per
