@@ -215,7 +215,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
     auto store_o = [&](int n, const f32x4 (&O)[NT]) {
         const int obase = ((n * C + 16 * w + li) * HV + h) * DV * 4 + (16 * cg * NT + 4 * gq) * 4;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) buf_store_f32x4(O[nt], rs_o, obase, nt * 64);
+        for (int nt = 0; nt < NT; ++nt) buf_store_f32x4_stream(O[nt], rs_o, obase, nt * 64);
     };
 
     // This wave's operand fragments, in registers, in a ring of three sets (the empty asm

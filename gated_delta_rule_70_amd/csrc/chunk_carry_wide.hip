@@ -263,7 +263,7 @@ void carry_wide_kernel(
                 const int obase = on ? ((n * C + 16 * r + li) * HV + h) * D * 4 + (col0 + 4 * gq) * 4
                                      : (int)0xFFFFFF00u;
 #pragma unroll
-                for (int ct = 0; ct < CTW; ++ct) buf_store_f32x4(Oq[r][ct], rs_o, obase, ct * 64);
+                for (int ct = 0; ct < CTW; ++ct) buf_store_f32x4_stream(Oq[r][ct], rs_o, obase, ct * 64);
             }
         }
     };

@@ -20,6 +20,14 @@
 // barriers per token; the two reduction buffers alternate so no third one is needed).
 // The next token's inputs are requested while the current one is processed.
 //
+// The state is loaded and stored with non-temporal hints: each element is touched once per
+// call, and between decode steps of a real model the state of every other layer passes
+// through the caches, so keeping it cached buys nothing.  Measured at B = 32, HV = 32,
+// 128 x 128, steps cycling over 8 states (512 MiB, HBM-resident) replayed from a graph:
+// 23.5 us per step (72 % of the 8 TB/s peak) against 29.1 us with ordinary accesses; a
+// single state replayed in place (then held in the 256 MB last-level cache) goes from 20.8
+// to 22.9 us.
+//
 // Fused input prologue (template flags KN, GS): with raw keys (KN) the prediction is formed
 // with the raw key and scaled by 1 / |k|_2 after its reduction (it is linear in k), the
 // sum of squares riding along in the same reduction, and the update uses d / |k|_2; with gate
@@ -66,7 +74,7 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
     if (h0 != nullptr) {
 #pragma unroll
         for (int m = 0; m < RPT; ++m)
-            S[m] = *reinterpret_cast<const f32x4*>(h0 + sbase + (size_t)(rl + NRL * m) * DV);
+            S[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(h0 + sbase + (size_t)(rl + NRL * m) * DV));
     } else {
 #pragma unroll
         for (int m = 0; m < RPT; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -176,7 +184,7 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
     if (ht != nullptr) {
 #pragma unroll
         for (int m = 0; m < RPT; ++m)
-            *reinterpret_cast<f32x4*>(ht + sbase + (size_t)(rl + NRL * m) * DV) = S[m];
+            __builtin_nontemporal_store(S[m], reinterpret_cast<f32x4*>(ht + sbase + (size_t)(rl + NRL * m) * DV));
     }
 }
 
@@ -221,7 +229,7 @@ void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const T
     if (h0 != nullptr) {
 #pragma unroll
         for (int m = 0; m < RPT; ++m)
-            S[m] = *reinterpret_cast<const f32x4*>(h0 + sbase + (size_t)(rl + NRL * m) * DV);
+            S[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(h0 + sbase + (size_t)(rl + NRL * m) * DV));
     } else {
 #pragma unroll
         for (int m = 0; m < RPT; ++m) S[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -298,7 +306,7 @@ void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const T
     if (ht != nullptr) {
 #pragma unroll
         for (int m = 0; m < RPT; ++m)
-            *reinterpret_cast<f32x4*>(ht + sbase + (size_t)(rl + NRL * m) * DV) = S[m];
+            __builtin_nontemporal_store(S[m], reinterpret_cast<f32x4*>(ht + sbase + (size_t)(rl + NRL * m) * DV));
     }
 }
 

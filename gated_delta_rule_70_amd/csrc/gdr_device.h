@@ -82,6 +82,18 @@ __device__ __forceinline__ void buf_store_f32(float x, rsrc_t r, int voff, int s
 __device__ __forceinline__ void buf_store_f32x4(f32x4 x, rsrc_t r, int voff, int soff) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, voff, soff, 0);
 }
+// Cache-policy operand of stores whose data is not read again by the kernels that follow
+// (the gfx950 non-temporal bit): the prefill's outputs o.  Written that way they do not
+// displace the chunk records, which the carry reads right after the prep wrote them.
+// Measured at HV = 32, 128 x 128, C = 64: the carry takes 84.5 instead of 94 us at B = 1,
+// T = 4097, 57.6 instead of 64 us at B = 8, T = 512, 702 us either way at B = 1, T = 32768.
+// Streaming loads as well was measured and dropped: the log-decays in the prep (the prep
+// 4-16 us slower) and v in the whole-head carry (up to 30 % slower) lose by it, v in the
+// column-split carry gains nothing.
+constexpr int kStream = 2;
+__device__ __forceinline__ void buf_store_f32x4_stream(f32x4 x, rsrc_t r, int voff, int soff) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, voff, soff, kStream);
+}
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
 // (lgkmcnt(0)), then s_barrier.  Unlike __syncthreads() it does not wait for outstanding
