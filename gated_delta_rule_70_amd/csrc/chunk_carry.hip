@@ -290,9 +290,35 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
     };
 
     f32x4 Op[NT];  // outputs of the previous chunk (true scale), stored one step late
+
+    // This wave's scale exponents for the next chunk step: largest magnitudes of its state
+    // tiles and of that chunk's v rows.  Each step computes them for the following one right
+    // after its state update, where the reductions overlap the step's output products rather
+    // than delay the next step's first exchange.
+    int es, ev;
+    auto state_exponent = [&]() {
+        float ms = 0.f;
+#pragma unroll
+        for (int j = 0; j < OWN; ++j)
+            if (w + NW * j < DKT)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ms = fmaxf(ms, fabsf(S[j][nt][i]));
+        return scale_exponent(wave_max(ms));
+    };
+    auto v_exponent = [&](const Frags& F) {
+        float mv = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int e = 0; e < ELT; ++e) mv = fmaxf(mv, raw_absmax<TIn>(F.v[nt][e]));
+        return scale_exponent(wave_max(mv));
+    };
+
     // One chunk: request chunk nn's operands into set Fn, consume set F (chunk n), using
-    // exchange-buffer copy `par`.
-    auto step = [&](Frags& F, Frags& Fn, int n, int nn, int par) {
+    // exchange-buffer copy `par`; Fx holds the next chunk's operands.
+    auto step = [&](Frags& F, Frags& Fn, Frags& Fx, int n, int nn, int par) {
         ld_g1(Fn, nn);
         // The empty asm fixes where the raw v bits are consumed: the compiler would otherwise
         // convert them a step early, while their load may still be in flight.
@@ -301,24 +327,6 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
 #pragma unroll
             for (int e = 0; e < ELT; ++e) asm volatile("" : "+v"(F.v[nt][e]));
 
-        // 0. this wave's scale exponents: largest magnitudes of its state tiles and v rows
-        int es, ev;
-        {
-            float ms = 0.f, mv = 0.f;
-#pragma unroll
-            for (int j = 0; j < OWN; ++j)
-                if (w + NW * j < DKT)
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) ms = fmaxf(ms, fabsf(S[j][nt][i]));
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int e = 0; e < ELT; ++e) mv = fmaxf(mv, raw_absmax<TIn>(F.v[nt][e]));
-            es = scale_exponent(wave_max(ms));
-            ev = scale_exponent(wave_max(mv));
-        }
         publish_v(F.v, sV[par], ev);
 
         // 1. publish this wave's state tiles (times 2^-es) as halves of the state B fragments
@@ -443,6 +451,13 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
                 }
             }
         }
+        // 0'. the next step's exponents (Fx's v loads were issued a step earlier)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int e = 0; e < ELT; ++e) asm volatile("" : "+v"(Fx.v[nt][e]));
+        es = state_exponent();
+        ev = v_exponent(Fx);
         // 6. O_w^T = qs 2^E_S S^T Qt^T + ps 2^E_U U^T P^T, the query rows' multipliers per lane
         const float fq = F.qs * ldexp2(1.f, ES), fp = F.ps * su;
 #pragma unroll
@@ -461,17 +476,19 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
         Frags FA, FB, FC;
         load_all(FA, 0);
         load_all(FB, min(1, nc - 1));
+        es = state_exponent();
+        ev = v_exponent(FA);
         // Three steps per iteration (register set and exchange copy fixed per position), then
         // up to two more; the requested chunk is clamped to the last one, whose operands then
         // simply arrive twice.
         int n = 0;
         for (; n + 3 <= nc; n += 3) {
-            step(FA, FC, n, min(n + 2, nc - 1), 0);
-            step(FB, FA, n + 1, min(n + 3, nc - 1), 1);
-            step(FC, FB, n + 2, min(n + 4, nc - 1), 2);
+            step(FA, FC, FB, n, min(n + 2, nc - 1), 0);
+            step(FB, FA, FC, n + 1, min(n + 3, nc - 1), 1);
+            step(FC, FB, FA, n + 2, min(n + 4, nc - 1), 2);
         }
-        if (n < nc) step(FA, FC, n, min(n + 2, nc - 1), 0);
-        if (n + 1 < nc) step(FB, FA, n + 1, min(n + 3, nc - 1), 1);
+        if (n < nc) step(FA, FC, FB, n, min(n + 2, nc - 1), 0);
+        if (n + 1 < nc) step(FB, FA, FC, n + 1, min(n + 3, nc - 1), 1);
         store_o(nc - 1, Op);
     }
 
