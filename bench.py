@@ -59,11 +59,11 @@ VALU_F32_OPS_PEAK = 256 * 64 * 2.4e9
 
 CSRC = os.path.join(ROOT, "gated_delta_rule_70_amd", "csrc")
 KERNEL_SOURCES = {  # kernel -> the sources its machine code is built from
-    "chunk_prep": ["chunk_prep.hip", "gdr_device.h", "gdr_launch.h"],
+    "chunk_prep": ["chunk_prep.hip", "chunk_prep_impl.h", "gdr_device.h", "gdr_launch.h"],
     "chunk_carry": ["chunk_carry.hip", "gdr_device.h", "gdr_launch.h"],
-    "carry_full": ["chunk_carry_wide.hip", "gdr_device.h", "gdr_launch.h"],
-    "carry_sum": ["chunk_carry_wide.hip", "gdr_device.h", "gdr_launch.h"],
-    "carry_combine": ["chunk_carry_wide.hip", "gdr_device.h", "gdr_launch.h"],
+    "carry_full": ["chunk_carry_wide.hip", "gdr_stage.h", "gdr_device.h", "gdr_launch.h"],
+    "carry_sum": ["chunk_carry_wide.hip", "gdr_stage.h", "gdr_device.h", "gdr_launch.h"],
+    "carry_combine": ["chunk_carry_wide.hip", "gdr_stage.h", "gdr_device.h", "gdr_launch.h"],
     "decode": ["decode.hip", "gdr_device.h", "gdr_launch.h"],
     "fused_recurrent": ["decode.hip", "gdr_device.h", "gdr_launch.h"],
     "tree_verify": ["tree_verify.hip", "gdr_device.h", "gdr_launch.h"],
