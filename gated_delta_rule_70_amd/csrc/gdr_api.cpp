@@ -184,8 +184,47 @@ gdr::LaunchArgs make_args(const gdr_dims* d, const void* q, const void* k, const
     return a;
 }
 
+// Rows one prefill launch can address: the kernels reach one batch element's g/q/k/v/o rows
+// (the padding rows of its last chunk included, which lie past the end and read as zero)
+// and one head's chunk records with 31-bit buffer offsets.  The largest multiple of the
+// chunk length W with (W + C) rows of HV heads x max(dk, dv) fp32 values and ceil(W / C)
+// records each below 2^31 bytes (0 if not even one chunk fits).  Longer dense calls run as a
+// chain of windows of W rows (see prefill_stages).
+long long window_rows(const gdr_dims* d) {
+    const long long C = d->chunk;
+    const long long dmax = d->dk > d->dv ? d->dk : d->dv;
+    const long long lim = (1LL << 31) - 1;
+    long long w = lim / ((long long)d->HV * dmax * 4) - C;  // (w + C) rows < 2^31 bytes
+    const gdr::ChunkRecord rec = gdr::ChunkRecord::make(d->chunk, d->dk);
+    const long long wr = lim / rec.bytes * C;               // ceil(w / C) records < 2^31 bytes
+    if (wr < w) w = wr;
+    return w < C ? 0 : w / C * C;
+}
+
+size_t state_bytes(const gdr_dims* d) { return (size_t)d->HV * d->dk * d->dv * 4; }
+
+// Whether T rows per batch element fit one launch: (T + C) rows of g and o and the records of
+// ceil(T / C) chunks below 2^31 bytes (the padding rows of a ragged last chunk lie past the
+// end but inside the range the offsets must cover).
+bool fits_one_launch(const gdr_dims* d) {
+    const size_t dmax = (size_t)(d->dk > d->dv ? d->dk : d->dv);
+    const gdr::ChunkRecord rec = gdr::ChunkRecord::make(d->chunk, d->dk);
+    const size_t nchunk = ((size_t)d->T + d->chunk - 1) / d->chunk;
+    return ((size_t)d->T + d->chunk) * d->HV * dmax * 4 < (size_t(1) << 31) &&
+           nchunk * (size_t)rec.bytes < (size_t(1) << 31);
+}
+
 size_t workspace_bytes_unchecked(const gdr_dims* d, bool varlen = false) {
     const gdr::ChunkRecord rec = gdr::ChunkRecord::make(d->chunk, d->dk);
+    const long long W = window_rows(d);
+    if (!varlen && W > 0 && !fits_one_launch(d)) {
+        // a chain of windows of W rows, one batch element at a time: one window's records and
+        // carry scratch, then one head group's state between windows
+        size_t x;
+        if (!mul_ok((size_t)d->HV, (size_t)(W / d->chunk), &x) || !mul_ok(x, rec.bytes, &x)) return 0;
+        const size_t win = (gdr::carry_layout(1, d->HV, (int)W, d->dk, d->dv, d->chunk).total + 255) / 256 * 256;
+        return win + state_bytes(d);
+    }
     const size_t nchunk = varlen ? (size_t)gdr::varlen_chunk_slots(d->B, d->T, d->chunk)
                                  : (size_t)d->B * (((size_t)d->T + d->chunk - 1) / d->chunk);
     size_t x;
@@ -252,6 +291,42 @@ size_t gdr_chunk_prefill_varlen_workspace_bytes(const gdr_dims* dims) {
     return workspace_bytes_unchecked(dims, true);
 }
 
+// A dense prefill longer than W rows, as a chain of windows of W rows (a multiple of the chunk
+// length, so the chunk grid is the one-call grid) per batch element: prep and carry of each
+// window in order on the stream, the state handed from window to window through ht (in place)
+// or, without ht, through a state slot after the window's records in the workspace.
+static int prefill_windows(const gdr_dims* dims, long long W, const void* q, const void* k,
+                           const void* v, const void* g, const float* beta, const float* h0,
+                           float* o, float* ht, void* workspace, void* stream) {
+    const size_t elt = dims->qkv_dtype == GDR_F32 ? 4 : 2;
+    const size_t gelt = (dims->flags & GDR_G_BF16) ? 2 : 4;
+    const size_t HG = (dims->flags & GDR_G_PER_KEY_HEAD) ? dims->HK : dims->HV;
+    const size_t HK = dims->HK, HV = dims->HV, dk = dims->dk, dv = dims->dv;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    const size_t win = (gdr::carry_layout(1, dims->HV, (int)W, dims->dk, dims->dv, dims->chunk).total + 255) / 256 * 256;
+    float* tmp = reinterpret_cast<float*>(ws + win);
+    for (int b = 0; b < dims->B; ++b) {
+        float* state = ht ? ht + (size_t)b * HV * dk * dv : tmp;
+        for (long long t0 = 0; t0 < dims->T; t0 += W) {
+            const long long t1 = t0 + W < dims->T ? t0 + W : dims->T;
+            const size_t row = (size_t)b * dims->T + (size_t)t0;  // first row of the window
+            gdr_dims dw = *dims;
+            dw.B = 1;
+            dw.T = (int32_t)(t1 - t0);
+            const float* hin = t0 == 0 ? (h0 ? h0 + (size_t)b * HV * dk * dv : nullptr) : state;
+            float* hout = (t1 == dims->T && !ht) ? nullptr : state;
+            gdr::LaunchArgs a = make_args(&dw, static_cast<const unsigned char*>(q) + row * HK * dk * elt,
+                                          static_cast<const unsigned char*>(k) + row * HK * dk * elt,
+                                          static_cast<const unsigned char*>(v) + row * HV * dv * elt,
+                                          static_cast<const unsigned char*>(g) + row * HG * dk * gelt,
+                                          beta + row * HV, hin, o + row * HV * dv, hout, ws, stream);
+            if (gdr::launch_chunk_prep(a) != hipSuccess || gdr::launch_chunk_carry(a) != hipSuccess)
+                return GDR_ERR_HIP;
+        }
+    }
+    return GDR_OK;
+}
+
 static int prefill_stages(const gdr_dims* dims, const void* q, const void* k, const void* v,
                           const void* g, const float* beta, const float* h0, float* o, float* ht,
                           void* workspace, size_t workspace_bytes, void* stream, bool prep,
@@ -262,15 +337,11 @@ static int prefill_stages(const gdr_dims* dims, const void* q, const void* k, co
     if (st != GDR_OK) return st;
     const size_t need = workspace_bytes_unchecked(dims, varlen);
     if (need == 0) return GDR_ERR_SHAPE;
-    // The kernels address one batch element's g/q/k/v/o rows (including the padding rows of
-    // the last chunk, which lie past the end and read as zero) and one head's chunk records
-    // with 31-bit buffer offsets.
-    const gdr::ChunkRecord rec = gdr::ChunkRecord::make(dims->chunk, dims->dk);
-    const size_t nchunk = ((size_t)dims->T + dims->chunk - 1) / dims->chunk;
-    const size_t dmax = (size_t)(dims->dk > dims->dv ? dims->dk : dims->dv);
-    if (((size_t)dims->T + dims->chunk) * dims->HV * dmax * 4 >= (size_t(1) << 31) ||
-        nchunk * (size_t)rec.bytes >= (size_t(1) << 31))
-        return GDR_ERR_SHAPE;
+    // Beyond the rows one launch can address (window_rows), a dense call runs as a chain of
+    // windows; packed batches and the separate stage entry points do not chain.
+    const long long W = window_rows(dims);
+    const bool windowed = !fits_one_launch(dims);
+    if (windowed && (W <= 0 || varlen || !prep || !carry)) return GDR_ERR_SHAPE;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
         return GDR_ERR_WORKSPACE;
     const Range rw = range_of(workspace, need);
@@ -279,6 +350,7 @@ static int prefill_stages(const gdr_dims* dims, const void* q, const void* k, co
                             range_of(ht, s.state), range_of(cu, ((size_t)dims->B + 1) * 4)};
     for (const Range& r : others)
         if (overlap(rw, r)) return GDR_ERR_ALIAS;
+    if (windowed) return prefill_windows(dims, W, q, k, v, g, beta, h0, o, ht, workspace, stream);
     gdr::LaunchArgs a = make_args(dims, q, k, v, g, beta, h0, o, ht, workspace, stream, cu);
     if (varlen) {
         const gdr::CarryLayout L = gdr::carry_layout(dims->B, dims->HV, dims->T, dims->dk, dims->dv,

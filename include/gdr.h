@@ -32,10 +32,17 @@
  *     GDR_ERR_HIP.  The library never aborts or prints.  NaN/Inf inputs are not checked
  *     and propagate.
  *   - Supported: dk, dv in {32, 64, 128}; chunk in {16, 32, 64}; HV % HK == 0; B, T >= 1;
- *     q/k/v in bf16 or fp32.  Prefill also needs (T + chunk)*HV*max(dk, dv)*4 < 2^31
- *     (one batch element's g and o rows, padding rows of the last chunk included) and
- *     ceil(T/chunk) * (workspace bytes per chunk) < 2^31 (one head's chunk records); about
- *     130K tokens at HV = 32, dk = dv = 128.  Decay values are expected to satisfy g <= 0 with the total
+ *     q/k/v in bf16 or fp32.  One prefill launch takes a batch element of T tokens while
+ *     (T + chunk)*HV*max(dk, dv)*4 < 2^31 (its g and o rows, padding rows of the last chunk
+ *     included) and ceil(T/chunk) * (workspace bytes per chunk) < 2^31 (one head's chunk
+ *     records): up to 131007 tokens at HV = 32, dk = dv = 128, chunk 64.  gdr_chunk_prefill
+ *     (and gdr_forward) runs longer sequences as a chain of windows of W tokens, W the
+ *     largest multiple of the chunk length within that limit (130944 in the same case), one
+ *     batch element at a time, handing the state on through ht or a slot in the workspace
+ *     (gdr_chunk_prefill_workspace_bytes sizes it); the chunk grid is that of one call.
+ *     gdr_chunk_prep, gdr_chunk_carry and the packed-batch calls take only what one launch
+ *     takes (GDR_ERR_SHAPE beyond).
+ *     Decay values are expected to satisfy g <= 0 with the total
  *     decay over any 8 consecutive tokens below 80 in every channel (exp(g) >= ~5e-5 per
  *     token); outside that range the prefill path's intra-chunk decay factors can
  *     overflow fp32.  The decode and fused recurrent paths have no such limit.

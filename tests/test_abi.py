@@ -192,11 +192,39 @@ def test_workspace_checks(L):
 
 
 def test_31_bit_offset_limit(L):
-    # (T + chunk) * HV * max(dk, dv) * 4 must stay below 2^31 (rows of one batch element,
-    # padding rows of the last chunk included): T = 131008 is the first length refused
+    # One launch takes T rows per batch element while (T + chunk) * HV * max(dk, dv) * 4 <
+    # 2^31: up to T = 131007 at HV=32, 128x128, chunk 64.  Longer dense prefills run as a
+    # chain of windows of W = 130944 rows (the largest multiple of the chunk that fits); the
+    # stage entry points and packed batches refuse them.
     d = dict(B=1, HK=16, HV=32, dk=128, dv=128, chunk=64)
-    assert prefill(L, dims(T=131008, **d)) == ESHAPE
-    assert prefill(L, dims(T=131007, **d), ws_bytes=1) == EWS  # passes the limit, fails later
+    for entry in ("gdr_chunk_prep", "gdr_chunk_carry"):
+        assert prefill(L, dims(T=131008, **d), entry=entry) == ESHAPE
+        assert prefill(L, dims(T=131007, **d), entry=entry, ws_bytes=1) == EWS  # within the limit
+    assert varlen_call(L, dims(T=131008, **d)) == ESHAPE
+    assert prefill(L, dims(T=131008, **d), ws_bytes=1) == EWS  # chained: passes, then needs workspace
+    one = L.gdr_chunk_prefill_workspace_bytes(ctypes.byref(dims(T=131007, **d)))
+    assert one >= _records(1, 131007, 32, 128, 64)  # one launch: every record of the call
+
+
+def test_windowed_workspace(L):
+    """A chained prefill needs one window's records and carry scratch (the window's own carry
+    plan), rounded to 256 bytes, plus one head group's state; independent of T and B."""
+    d = dict(HK=16, HV=32, dk=128, dv=128, chunk=64)
+    W = 130944
+    one = L.gdr_chunk_prefill_workspace_bytes(ctypes.byref(dims(B=1, T=W, **d)))
+    for B, T in ((1, 131008), (1, 10 * W + 5), (3, 2 * W)):
+        got = L.gdr_chunk_prefill_workspace_bytes(ctypes.byref(dims(B=B, T=T, **d)))
+        assert got == (one + 255) // 256 * 256 + 32 * 128 * 128 * 4, (B, T)
+
+
+@pytest.mark.skipif("_gpu_visible()", reason="valid fake pointers would reach a real GPU")
+def test_windowed_prefill_reaches_the_runtime_without_a_gpu(L):
+    # tensors of several GiB: fake addresses 256 GiB apart so that none overlaps another
+    far = {n: ctypes.c_void_p((1 << 44) + i * (1 << 38))
+           for i, n in enumerate(["q", "k", "v", "g", "beta", "h0", "o", "ht", "ws"])}
+    d = dict(B=2, T=300000, HK=16, HV=32, dk=128, dv=128, chunk=64)
+    assert prefill(L, dims(**d), **far) == EHIP
+    assert prefill(L, dims(**d), **dict(far, ht=None)) == EHIP
 
 
 def test_workspace_size_formula(L):

@@ -220,12 +220,12 @@ def test_segmented_carry_fp32_inputs(dk):
 
 
 def test_maximum_length_prefill():
-    """The longest sequence the prefill accepts at HV=32, 128x128, chunk 64 (T = 131007:
+    """The longest sequence one prefill launch takes at HV=32, 128x128, chunk 64 (T = 131007:
     one batch element's g and o rows, padding included, just under 2^31 bytes), so every
     31-bit buffer offset in the kernels is exercised near its limit; the carry runs in 8
     segments of 256 chunks.  One key-head group against the oracle."""
     B, T, HK, HV, dk = 1, 131007, 16, 32, 128
-    assert (T + 64) * HV * dk * 4 < 2 ** 31 <= (T + 1 + 64) * HV * dk * 4  # T + 1 is refused
+    assert (T + 64) * HV * dk * 4 < 2 ** 31 <= (T + 1 + 64) * HV * dk * 4  # T + 1 runs in windows
     x = small_inputs(B, T, HK, HV, dk, dk, seed=101)
     note(f"maximum-length prefill T={T}")
     d = dev(x)
@@ -238,6 +238,45 @@ def test_maximum_length_prefill():
     o_r, ht_r = ref[(0, kh)]
     hv = slice(kh * G, (kh + 1) * G)
     eo, es = err(o[0, :, hv].cpu(), o_r), err(ht[0, hv].cpu(), ht_r)
+    assert eo < TOL and es < TOL, f"o {eo:.2e} state {es:.2e}"
+
+
+def test_windowed_prefill_equals_chained_calls():
+    """Past what one launch addresses, the prefill runs as a chain of windows of W = 130944
+    tokens (HV=32, 128x128, chunk 64), one batch element at a time.  Two elements of 131100
+    tokens: bitwise the same outputs and final state as separate calls on each window with
+    the state handed on by hand; the stateless and in-place forms give the same outputs; the
+    last key-head group of the second element against the oracle."""
+    B, T, HK, HV, dk, W = 2, 131100, 16, 32, 128, 130944
+    assert (T + 64) * HV * dk * 4 >= 2 ** 31 > (W + 64) * HV * dk * 4
+    x = small_inputs(B, T, HK, HV, dk, dk, seed=103)
+    note(f"windowed prefill B={B} T={T}")
+    d = dev(x)
+    o, ht = run_prefill(d, 64)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(ht).all()
+    for b in range(B):
+        h = d["h0"][b:b + 1]
+        for t0, t1 in ((0, W), (W, T)):
+            part = {n: d[n][b:b + 1, t0:t1].contiguous() for n in ("q", "k", "v", "g", "beta")}
+            oc, h = gdr.chunk_prefill(part["q"], part["k"], part["v"], part["g"], part["beta"], h0=h, chunk=64)
+            assert torch.equal(o[b:b + 1, t0:t1], oc), (b, t0)
+            del part, oc
+        assert torch.equal(ht[b:b + 1], h), b
+    o_ref = o.clone()
+    o2, none = run_prefill(d, 64, o=o, want_state=False)
+    assert none is None and torch.equal(o2, o_ref)
+    st = d["h0"].clone()
+    run_prefill(d, 64, o=o, h0=False, want_state=False)  # o holds another result first
+    gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=st, ht=st, o=o, chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(st, ht)
+    G = HV // HK
+    kh = HK - 1
+    ref = oracle_on_groups(x, [(1, kh)], G)
+    o_r, ht_r = ref[(1, kh)]
+    hv = slice(kh * G, (kh + 1) * G)
+    eo, es = err(o[1, :, hv].cpu(), o_r), err(ht[1, hv].cpu(), ht_r)
     assert eo < TOL and es < TOL, f"o {eo:.2e} state {es:.2e}"
 
 
