@@ -69,10 +69,11 @@ KERNEL_SOURCES = {  # kernel -> the sources its machine code is built from
     "tree_verify": ["tree_verify.hip", "gdr_device.h", "gdr_launch.h"],
 }
 # kernel -> substrings that all appear in its (demangled) name in profiler output; the
-# column-split carry is chunk_carry_kernel, the whole-head carry's full and summary passes
+# column-split carry is chunk_carry_roles_kernel (one column tile per workgroup) or
+# chunk_carry_kernel (several), the whole-head carry's full and summary passes
 # are carry_wide_kernel<..., false> and <..., true>; the decode step is decode_kernel and a
 # multi-token fused recurrence token_kernel
-KERNEL_SYMBOL = {"chunk_prep": ("chunk_prep_kernel",), "chunk_carry": ("chunk_carry_kernel",),
+KERNEL_SYMBOL = {"chunk_prep": ("chunk_prep_kernel",), "chunk_carry": ("chunk_carry_",),
                  "carry_full": ("carry_wide_kernel", "false>"), "carry_sum": ("carry_wide_kernel", "true>"),
                  "carry_combine": ("carry_combine_kernel",),
                  "decode": ("decode_kernel",), "fused_recurrent": ("token_kernel",),

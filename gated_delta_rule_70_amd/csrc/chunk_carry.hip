@@ -507,6 +507,364 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
     }
 }
 
+// The same chunk step for one 16-column tile per workgroup, split over two wave roles
+// (2 * C/16 waves, two per SIMD).  Chain waves (row tile w) carry the state: they publish S,
+// form U_w = Tb_w V - W_w S, publish U_w and update their state tiles
+// S' = diag(exp(gam_last)) S + Kb^T U, then take the next step's state exponent.  Output
+// waves (row tile w) load, scale and publish the chunk's v rows with their exponent before
+// the first barrier, and form the outputs from the two exchanges: O_w^T = S^T Qt_w^T after
+// the first barrier and + U^T P_w^T after the second, then store them.  The v stream, the
+// output operands, products and stores thus stay out of the chain waves' instruction stream
+// and vector-memory counter (B=1 T=4097, HV=32, 128x128, the carry right after the prep
+// kernel: 80 against 82 us for the one-role kernel, bitwise the same results).  Each role
+// keeps its own ring of three operand sets, loaded two chunks ahead as above.
+template <typename TIn, int DK, int DV, int C>
+__global__ __launch_bounds__(128 * (C / 16)) void chunk_carry_roles_kernel(
+    const TIn* __restrict__ v, const float* h0, float* __restrict__ o, float* ht,
+    const unsigned char* __restrict__ ws, int B, int T, int HV, int NC, const int32_t* __restrict__ plan) {
+    constexpr int NT = 1;
+    constexpr int NB = C / 16;
+    constexpr int NW = NB;
+    constexpr int NQS = (C + 31) / 32;
+    constexpr int KC = DK / 32;
+    constexpr int DKT = DK / 16;
+    constexpr int OWN = (DKT + NW - 1) / NW;
+    constexpr ChunkRecord R = ChunkRecord::make(C, DK);
+    constexpr int ELT = sizeof(TIn);
+    constexpr int VP = C + 4;
+    // exchange buffers as in chunk_carry_kernel (three copies, chunk index mod 3): the chain
+    // waves write the state fragments, U and the state exponents, the output waves v and
+    // its exponents
+    __shared__ half8 sSB[3][KC * 64];
+    __shared__ half8 sUB[3][NQS * 64];
+    __shared__ __attribute__((aligned(16))) _Float16 sV[3][16 * VP];
+    __shared__ int sE[3][8];
+
+    const int NH = B * HV;
+    const int blk = blockIdx.x;
+    const int bh = blk % NH;
+    const int cg = blk / NH;
+    const int h = bh % HV;
+    const int b = bh / HV;
+    const SeqSpan sp = seq_span(plan, b, B, T, NC);
+    const int nc = sp.nc;
+    // waves 0 .. NW-1 carry the state, NW .. 2NW-1 form the outputs; both own row tile w
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool outw = wv >= NW;
+    const int w = outw ? wv - NW : wv;  // row tile
+    __builtin_assume(w >= 0 && w < NW);
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 15;
+    const int gq = lane >> 4;
+    const int jcol = 16 * cg + li;
+    const unsigned char* rec0 = ws + ((size_t)sp.c0 * HV + (size_t)h * sp.nc) * R.bytes;
+    const rsrc_t rs_rec = make_rsrc(rec0, (uint32_t)sp.nc * R.bytes);
+    constexpr int kBeyond = (int)0xFFFFFF00u;
+    auto ld = [&](half8& dst, int vrec, int f) {
+        dst = buf_load_half8(rs_rec, vrec, f * 1024);
+        asm volatile("" ::: "memory");
+    };
+    // common exponents of exchange copy `par` and the factors that align each wave's halves
+    struct Exps {
+        int ES, EV, EU;
+        _Float16 fs[NW], fv[NW];
+    };
+    auto read_exps = [&](int par) {
+        Exps x;
+        int esw[NW], evw[NW];
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            esw[ww] = sE[par][ww];
+            evw[ww] = sE[par][4 + ww];
+        }
+        x.ES = esw[0];
+        x.EV = evw[0];
+#pragma unroll
+        for (int ww = 1; ww < NW; ++ww) {
+            x.ES = max(x.ES, esw[ww]);
+            x.EV = max(x.EV, evw[ww]);
+        }
+        x.EU = max(x.ES, x.EV);
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            x.fs[ww] = half_pow2(esw[ww] - x.ES);
+            x.fv[ww] = half_pow2(evw[ww] - x.EV);
+        }
+        return x;
+    };
+    auto align = [&](half8 x, const _Float16 (&f)[NW], int wa, int wb) {
+        const _Float16 a = f[wa % NW], bb = f[wb % NW];
+        return x * half8{a, a, a, a, bb, bb, bb, bb};
+    };
+    auto read_sb = [&](half8 (&SB)[KC], int par, const Exps& x) {
+#pragma unroll
+        for (int p = 0; p < KC; ++p) SB[p] = align(sSB[par][p * 64 + lane], x.fs, 2 * p, 2 * p + 1);
+    };
+    auto read_ub = [&](half8 (&UB)[NQS], int par) {
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs) {
+            half8 x = sUB[par][qs * 64 + lane];
+            if (2 * qs + 1 >= NB) {
+#pragma unroll
+                for (int jj = 4; jj < 8; ++jj) x[jj] = static_cast<_Float16>(0.f);
+            }
+            UB[qs] = x;
+        }
+    };
+
+    const int rowv = HV * DV * ELT;
+    const rsrc_t rs_v = make_rsrc(v + (size_t)sp.row0 * HV * DV, (uint32_t)sp.T * rowv);
+    typedef uint32_t VRaw[ELT];
+    auto load_v = [&](int n, VRaw& V) {
+        const int row = n * C + 16 * w + (lane >> 2);
+        const int off = (row * HV + h) * DV * ELT + (16 * cg + 4 * (lane & 3)) * ELT;
+        if constexpr (ELT == 2) {
+            const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs_v, off, 0, 0);
+            V[0] = x[0];
+            V[1] = x[1];
+        } else {
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs_v, off, 0, 0);
+            V[0] = x[0];
+            V[1] = x[1];
+            V[2] = x[2];
+            V[3] = x[3];
+        }
+    };
+    auto publish_v = [&](const VRaw& V, _Float16* dst, int ew) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float x;
+            if constexpr (ELT == 2) x = __uint_as_float((e & 1) ? (V[e >> 1] & 0xFFFF0000u) : (V[e >> 1] << 16));
+            else x = __uint_as_float(V[e]);
+            dst[(4 * (lane & 3) + e) * VP + 16 * w + (lane >> 2)] = static_cast<_Float16>(ldexp2(x, -ew));
+        }
+    };
+    auto read_v = [&](half8 (&V)[NQS], const _Float16* src) {
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs) {
+            const _Float16* col = &src[li * VP + 32 * qs + 4 * gq];
+            const half4 lo = *reinterpret_cast<const half4*>(col);
+            half4 hi = {static_cast<_Float16>(0.f), static_cast<_Float16>(0.f), static_cast<_Float16>(0.f),
+                        static_cast<_Float16>(0.f)};
+            if (32 * qs + 16 < C) hi = *reinterpret_cast<const half4*>(col + 16);
+            V[qs] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+    };
+    // Both roles pass the same barriers: B0, then B1(n) and B2(n) for every chunk n.
+    if (outw) {
+        // ---- output waves: v rows, Qt and P fragments of row tile w and the row multipliers,
+        // two chunks ahead; outputs stored as soon as they are formed ----
+        const int rowo = HV * DV * 4;
+        const rsrc_t rs_o = make_rsrc(o + (size_t)sp.row0 * HV * DV, (uint32_t)sp.T * rowo);
+        struct OFr {
+            half8 q[KC], p[NQS];
+            float qs, ps;
+            uint32_t v[ELT];
+        };
+        auto load_o = [&](OFr& F, int n) {
+            const int vrec = n * R.bytes + lane * 16;
+            load_v(n, F.v);
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int qs = 0; qs < NQS; ++qs) ld(F.p[qs], 2 * qs > w ? kBeyond : vrec, R.off_p + w * NQS + qs);
+#pragma unroll
+            for (int p = 0; p < KC; ++p) ld(F.q[p], vrec, R.off_qt + w * KC + p);
+            const int rs = n * R.bytes + (16 * w + li) * 4;
+            F.qs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_rec, rs, R.nfrag * 1024 + R.qsc * 4, 0));
+            F.ps = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_rec, rs, R.nfrag * 1024 + R.psc * 4, 0));
+        };
+        auto ostep = [&](OFr& F, OFr& Fn, int n, int nn, int par) {
+            load_o(Fn, nn);
+#pragma unroll
+            for (int e = 0; e < ELT; ++e) asm volatile("" : "+v"(F.v[e]));
+            {  // this row tile's v rows of chunk n, times 2^-ev, and their exponent
+                float mv = 0.f;
+#pragma unroll
+                for (int e = 0; e < ELT; ++e) mv = fmaxf(mv, raw_absmax<TIn>(F.v[e]));
+                const int evn = scale_exponent(wave_max(mv));
+                publish_v(F.v, sV[par], evn);
+                if (lane == 0) sE[par][4 + w] = evn;
+            }
+            lds_barrier();  // B1(n)
+            const Exps x = read_exps(par);
+            half8 SB[KC];
+            read_sb(SB, par, x);
+            f32x4 OQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < KC; ++p) OQ = mfma_f16(SB[p], F.q[p], OQ);
+            lds_barrier();  // B2(n)
+            half8 UB[NQS];
+            read_ub(UB, par);
+            f32x4 OP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int qs = 0; qs < NQS; ++qs) OP = mfma_f16(UB[qs], F.p[qs], OP);
+            const float fq = F.qs * ldexp2(1.f, x.ES), fp = F.ps * ldexp2(1.f, x.EU);
+            f32x4 Ov;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Ov[i] = fmaf(OP[i], fp, OQ[i] * fq);
+            const int obase = ((n * C + 16 * w + li) * HV + h) * DV * 4 + (16 * cg + 4 * gq) * 4;
+            buf_store_f32x4_stream(Ov, rs_o, obase, 0);
+        };
+        lds_barrier();  // B0
+        if (nc > 0) {
+            OFr FA, FB, FC;
+            load_o(FA, 0);
+            load_o(FB, min(1, nc - 1));
+            int n = 0;
+            for (; n + 3 <= nc; n += 3) {
+                ostep(FA, FC, n, min(n + 2, nc - 1), 0);
+                ostep(FB, FA, n + 1, min(n + 3, nc - 1), 1);
+                ostep(FC, FB, n + 2, min(n + 4, nc - 1), 2);
+            }
+            if (n < nc) ostep(FA, FC, n, min(n + 2, nc - 1), 0);
+            if (n + 1 < nc) ostep(FB, FA, n + 1, min(n + 3, nc - 1), 1);
+        }
+        return;
+    }
+
+    // ---- chain waves: the state tiles and the Tb, W, Kb fragments of row tile w ----
+    f32x4 S[OWN];
+    const size_t sb = (size_t)bh * DK * DV;
+#pragma unroll
+    for (int j = 0; j < OWN; ++j) {
+        const int ct = w + NW * j;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (h0 != nullptr && ct < DKT) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = h0[sb + (size_t)(16 * ct + 4 * gq + i) * DV + jcol];
+        }
+        S[j] = x;
+    }
+    struct Frags {
+        half8 tb[NQS], w[KC], kb[OWN][NQS];
+        f32x4 e;
+    };
+    auto ld_egl = [&](int n) {
+        const int ct = w + NW * li;
+        const bool on = li < OWN && ct < DKT;
+        return buf_load_f32x4(rs_rec, on ? n * R.bytes + ct * 64 + gq * 16 : kBeyond, R.nfrag * 1024);
+    };
+    auto ld_g1 = [&](Frags& F, int n) {
+        const int vrec = n * R.bytes + lane * 16;
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs) ld(F.tb[qs], 2 * qs > w ? kBeyond : vrec, R.off_tb + w * NQS + qs);
+    };
+    auto ld_g2 = [&](Frags& F, int n) {
+        const int vrec = n * R.bytes + lane * 16;
+#pragma unroll
+        for (int p = 0; p < KC; ++p) ld(F.w[p], vrec, R.off_w + w * KC + p);
+    };
+    auto ld_g4 = [&](Frags& F, int n) {
+        const int vrec = n * R.bytes + lane * 16;
+#pragma unroll
+        for (int j = 0; j < OWN; ++j) {
+            const int ct = w + NW * j;
+            if (ct < DKT) {
+#pragma unroll
+                for (int qs = 0; qs < NQS; ++qs) ld(F.kb[j][qs], vrec, R.off_kb + ct * NQS + qs);
+            }
+        }
+        F.e = ld_egl(n);
+    };
+    auto load_all = [&](Frags& F, int n) {
+        ld_g1(F, n);
+        ld_g2(F, n);
+        ld_g4(F, n);
+    };
+    int es;
+    auto state_exponent = [&]() {
+        float ms = 0.f;
+#pragma unroll
+        for (int j = 0; j < OWN; ++j)
+            if (w + NW * j < DKT)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ms = fmaxf(ms, fabsf(S[j][i]));
+        return scale_exponent(wave_max(ms));
+    };
+    auto step = [&](Frags& F, Frags& Fn, Frags& Fx, int n, int nn, int par) {
+        ld_g1(Fn, nn);
+#pragma unroll
+        for (int j = 0; j < OWN; ++j) {
+            const int ct = w + NW * j;
+            if (ct < DKT)
+                *(reinterpret_cast<half4*>(&sSB[par][(ct >> 1) * 64 + lane]) + (ct & 1)) = to_half4_scaled(S[j], -es);
+        }
+        if (lane == 0) sE[par][w] = es;
+        lds_barrier();  // B1(n)
+        const Exps x = read_exps(par);
+        half8 SB[KC];
+        read_sb(SB, par, x);
+        half8 Vc[NQS];
+        read_v(Vc, sV[par]);
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs) Vc[qs] = align(Vc[qs], x.fv, 2 * qs, 2 * qs + 1 < NW ? 2 * qs + 1 : 2 * qs);
+        ld_g2(Fn, nn);
+        f32x4 U = {0.f, 0.f, 0.f, 0.f}, US = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs) U = mfma_f16(F.tb[qs], Vc[qs], U);
+#pragma unroll
+        for (int p = 0; p < KC; ++p) US = mfma_f16(F.w[p], SB[p], US);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) U[i] = ldexp2(U[i], x.EV - x.EU) + ldexp2(US[i], x.ES - x.EU);
+        *(reinterpret_cast<half4*>(&sUB[par][(w >> 1) * 64 + lane]) + (w & 1)) = to_half4(U);
+        lds_barrier();  // B2(n)
+        half8 UB[NQS];
+        read_ub(UB, par);
+        ld_g4(Fn, nn);
+        const float su = ldexp2(1.f, x.EU);
+#pragma unroll
+        for (int j = 0; j < OWN; ++j) {
+            const int ct = w + NW * j;
+            if (ct < DKT) {
+                f32x4 ej;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ej[i] = row_lane(F.e[i], j);
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int qs = 0; qs < NQS; ++qs) a = mfma_f16(F.kb[j][qs], UB[qs], a);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[j][i] = fmaf(a[i], su, S[j][i] * ej[i]);
+            }
+        }
+        es = state_exponent();
+    };
+    lds_barrier();  // B0
+    if (nc > 0) {
+        Frags FA, FB, FC;
+        load_all(FA, 0);
+        load_all(FB, min(1, nc - 1));
+        es = state_exponent();
+        int n = 0;
+        for (; n + 3 <= nc; n += 3) {
+            step(FA, FC, FB, n, min(n + 2, nc - 1), 0);
+            step(FB, FA, FC, n + 1, min(n + 3, nc - 1), 1);
+            step(FC, FB, FA, n + 2, min(n + 4, nc - 1), 2);
+        }
+        if (n < nc) step(FA, FC, FB, n, min(n + 2, nc - 1), 0);
+        if (n + 1 < nc) step(FB, FA, FC, n + 1, min(n + 3, nc - 1), 1);
+    }
+    if (ht) {
+#pragma unroll
+        for (int j = 0; j < OWN; ++j) {
+            const int ct = w + NW * j;
+            if (ct < DKT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ht[sb + (size_t)(16 * ct + 4 * gq + i) * DV + jcol] = S[j][i];
+            }
+        }
+    }
+}
+
+template <typename TIn, int DK, int DV, int C>
+static hipError_t launch_carry_roles(const LaunchArgs& a) {
+    const int NC = a.plan ? 0 : (a.T + C - 1) / C;
+    const long long nblk = (long long)a.B * a.HV * (DV / 16);
+    hipLaunchKernelGGL((chunk_carry_roles_kernel<TIn, DK, DV, C>), dim3((unsigned)nblk), dim3(128 * (C / 16)), 0,
+                       (hipStream_t)a.stream, (const TIn*)a.v, a.h0, a.o, a.ht, (const unsigned char*)a.workspace, a.B,
+                       a.T, a.HV, NC, a.plan);
+    return hipGetLastError();
+}
+
 template <typename TIn, int DK, int DV, int C, int NT>
 static hipError_t launch_carry_t(const LaunchArgs& a) {
     const int NC = a.plan ? 0 : (a.T + C - 1) / C;  // packed batches: per sequence, from the plan
@@ -518,8 +876,9 @@ static hipError_t launch_carry_t(const LaunchArgs& a) {
 }
 
 // Column split: with few heads every 16-column tile gets its own workgroup (the most
-// parallel carry, for B*HV too small to fill 256 CUs otherwise); with many heads a
-// workgroup covers several tiles so each head's records are read from L2 fewer times.
+// parallel carry, for B*HV too small to fill 256 CUs otherwise; the two-role kernel); with
+// many heads a workgroup covers several tiles so each head's records are read from L2 fewer
+// times.
 template <typename TIn, int DK, int DV, int C>
 static hipError_t dispatch_split(const LaunchArgs& a) {
     constexpr int CT = DV / 16;
@@ -530,7 +889,7 @@ static hipError_t dispatch_split(const LaunchArgs& a) {
     if constexpr (CT >= 2) {
         if (tiles > 1024) return launch_carry_t<TIn, DK, DV, C, 2>(a);
     }
-    return launch_carry_t<TIn, DK, DV, C, 1>(a);
+    return launch_carry_roles<TIn, DK, DV, C>(a);
 }
 
 template <typename TIn, int DK, int DV>
