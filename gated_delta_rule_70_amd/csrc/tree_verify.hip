@@ -16,8 +16,11 @@
 // Kh = exp(-gam) k; every term that survives the ancestry mask is bounded by 1, the
 // masked ones are finite while the path decay stays above -80 in every channel.
 //
-// One 256-thread workgroup per (batch, value head, 32-column block of v), all of a tree's
-// rows in LDS.  Every phase is parallel across nodes:
+// One 256-thread workgroup per (batch, value head, group of 32-column blocks of v), all of
+// a tree's rows in LDS; with enough heads a group holds 2 or 4 blocks, which share the
+// decayed rows, A, P and the diagonal inverses (phases 1, 3 and the inversion of 4 run once
+// per group, phases 2, 4 and 5 once per block; B=8 T=64 at 128x128: 28 against 63 us with
+// one block per workgroup, bitwise the same outputs).  Every phase is parallel across nodes:
 //   0. all global reads issued at once (parents, beta, g, k, q rows, the block's columns
 //      of h0 and v);
 //   1. ancestor masks by pointer doubling in one wave's registers (6 rounds cover any depth
@@ -136,7 +139,7 @@ template <typename TIn, typename TG, int DK, bool KN, bool GS>
 __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int32_t* __restrict__ parent, const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const TG* __restrict__ g, const float* __restrict__ beta,
-    const float* __restrict__ h0, float* __restrict__ o, int T, int HK, int HV, int HG, int DV) {
+    const float* __restrict__ h0, float* __restrict__ o, int T, int HK, int HV, int HG, int DV, int ncbw) {
     constexpr int KP = DK + 4;   // row pitch (floats) of the fp32 g rows and decay prefixes
     constexpr int AP = TM + 4;
     constexpr int UP = CB + 4;
@@ -157,9 +160,10 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     __shared__ unsigned long long sAnc[TM];
     __shared__ float sBeta[TM];
 
-    const int ncb = DV / CB;
-    const int cb = blockIdx.x % ncb;
-    const int bh = blockIdx.x / ncb;
+    // blocks: (batch, value head, group of ncbw column blocks of CB v columns)
+    const int ngrp = DV / CB / ncbw;
+    const int grp = blockIdx.x % ngrp;
+    const int bh = blockIdx.x / ngrp;
     const int h = bh % HV;
     const int b = bh / HV;
     const int kh = h / (HV / HK);
@@ -171,7 +175,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int gq = lane >> 4;
     const int T16 = (T + 15) & ~15;
     const int NB = T16 / 16;
-    const int col0 = cb * CB;
+    const int col0 = grp * ncbw * CB;  // the first block's columns
 
     // ---- 0. global reads, all requested before any is used --------------------------------
     // Issued in the order they are needed: parents and beta, then g (the decay prefixes need
@@ -358,52 +362,182 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         *reinterpret_cast<bf16x4*>(sQt + i) = hi;
         *reinterpret_cast<bf16x4*>(sQt + LO + i) = lo;
     }
-    // h0 columns (transposed, bf16 high/low pairs: high [CB][BP] then low [CB][BP], in sA's
-    // memory) and the v tile (transposed, fp32, in sP's)
-    __bf16* sH = reinterpret_cast<__bf16*>(sA);
+    // Per column block: stage its h0 columns (transposed, bf16 high/low pairs: high [CB][BP]
+    // then low [CB][BP]) and its v tile (transposed, fp32 [CB][TM + 4]) from registers
+    auto stage = [&](const f32x4 (&hvv)[HPASS], const uint32_t (&vr)[2][ELT], __bf16* sH, float* sVt) {
 #pragma unroll
-    for (int m = 0; m < HPASS; ++m) {  // sH[j * BP + c]
-        const int c = tid / 8 + 32 * m;
-        bf16x4 hi, lo;
-        split4(hv[m], hi, lo);
+        for (int m = 0; m < HPASS; ++m) {  // sH[j * BP + c]
+            const int c = tid / 8 + 32 * m;
+            bf16x4 hi, lo;
+            split4(hvv[m], hi, lo);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sH[(4 * (tid % 8) + e) * BP + c] = hi[e];
-            sH[CB * BP + (4 * (tid % 8) + e) * BP + c] = lo[e];
-        }
-    }
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {  // sP[j * (TM + 4) + t]
-        const int t = tid / 8 + 32 * m;
-        const f32x4 x = raw4(vraw[m]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sP[(4 * (tid % 8) + e) * (TM + 4) + t] = t < T ? x[e] : 0.f;
-    }
-    __syncthreads();  // decayed rows, h0 columns and v tile (read across threads below)
-
-    // ---- 2. Kt h0, Qt h0 and the right-hand side beta (v - Kt h0) -------------------------
-    // tile (I, N): rows 16I.., columns 16N.. of this block; wave w owns tiles w and w + 4 and
-    // keeps its Qt h0 tiles for the output
-    f32x4 qh[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int tile = wave + 4 * u;
-        f32x4 kacc = {0.f, 0.f, 0.f, 0.f}, qacc = {0.f, 0.f, 0.f, 0.f};
-        if (tile < 2 * NB) {
-            const int I = tile >> 1, N = tile & 1;
-            const int cq = 8 * gq;
-            const __bf16* hb = sH + (16 * N + li) * BP + cq;
-            kacc = tile_dot_split<DK>(sKt + (16 * I + li) * BP + cq, LO, hb, CB * BP);
-            qacc = tile_dot_split<DK>(sQt + (16 * I + li) * BP + cq, LO, hb, CB * BP);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * I + 4 * gq + i;
-                sU[r * UP + 16 * N + li] = sBeta[r] * (sP[(16 * N + li) * (TM + 4) + r] - kacc[i]);
+            for (int e = 0; e < 4; ++e) {
+                sH[(4 * (tid % 8) + e) * BP + c] = hi[e];
+                sH[CB * BP + (4 * (tid % 8) + e) * BP + c] = lo[e];
             }
         }
-        qh[u] = qacc;
-    }
-    __syncthreads();
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {  // sVt[j * (TM + 4) + t]
+            const int t = tid / 8 + 32 * m;
+            const f32x4 x = raw4(vr[m]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sVt[(4 * (tid % 8) + e) * (TM + 4) + t] = t < T ? x[e] : 0.f;
+        }
+    };
+    // the global reads of the column block starting at column colb (h0 columns, v tile)
+    auto load_block = [&](int colb, f32x4 (&hvv)[HPASS], uint32_t (&vr)[2][ELT]) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int t = min(tid / 8 + 32 * m, T - 1);
+            const size_t vo = (((size_t)b * T + t) * HV + h) * DV + colb + 4 * (tid % 8);
+            if constexpr (ELT == 2) {
+                const uint2 x = *reinterpret_cast<const uint2*>(v + vo);
+                vr[m][0] = x.x; vr[m][1] = x.y;
+            } else {
+                const uint4 x = *reinterpret_cast<const uint4*>(v + vo);
+                vr[m][0] = x.x; vr[m][1] = x.y; vr[m][2] = x.z; vr[m][3] = x.w;
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < HPASS; ++m)
+            hvv[m] = buf_load_f32x4(rs_h0, ((tid / 8 + 32 * m) * DV + colb + 4 * (tid % 8)) * 4, 0);
+    };
+
+    // ---- 2. Kt h0, Qt h0 and the right-hand side beta (v - Kt h0) -------------------------
+    // tile (I, N): rows 16I.., columns 16N.. of the block; wave w owns tiles w and w + 4 and
+    // keeps its Qt h0 tiles for the output
+    auto rhs = [&](const __bf16* sH, const float* sVt, f32x4 (&qh)[2]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tile = wave + 4 * u;
+            f32x4 kacc = {0.f, 0.f, 0.f, 0.f}, qacc = {0.f, 0.f, 0.f, 0.f};
+            if (tile < 2 * NB) {
+                const int I = tile >> 1, N = tile & 1;
+                const int cq = 8 * gq;
+                const __bf16* hb = sH + (16 * N + li) * BP + cq;
+                kacc = tile_dot_split<DK>(sKt + (16 * I + li) * BP + cq, LO, hb, CB * BP);
+                qacc = tile_dot_split<DK>(sQt + (16 * I + li) * BP + cq, LO, hb, CB * BP);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * I + 4 * gq + i;
+                    sU[r * UP + 16 * N + li] = sBeta[r] * (sVt[(16 * N + li) * (TM + 4) + r] - kacc[i]);
+                }
+            }
+            qh[u] = qacc;
+        }
+    };
+
+    // ---- 4. (I + A) U = rhs by 16-row blocks ----------------------------------------------
+    // A_rs is nonzero only for s an ancestor of r, so s < r: I + A is unit lower triangular
+    // and so is each diagonal block D_I.  Lane (block gq, column li) runs forward
+    // substitution down column li of inv(D_gq) in registers; then block by block
+    //   U_I = inv(D_I) R_I,  R_J <- R_J - A_JI U_I  for J > I   (R starts as the rhs)
+    // with both products on the matrix cores, so U_I = inv(D_I) (rhs_I - sum_{J<I} A_IJ U_J).
+    constexpr int DIP = 20;            // inverse row pitch: 16-byte reads of 16 rows, no conflict
+    constexpr int DIB = 16 * DIP + 16; // inverse block stride
+    static_assert(4 * DIB * 4 <= 2 * TM * BP * 2, "block inverses must fit the free key rows");
+    auto invert_diag = [&](float* sDi) {
+        if (gq < NB) {
+            const float* ab = sA + 16 * gq * AP + 16 * gq;  // diagonal block gq
+            float xc[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = r == li ? 1.f : 0.f;
+#pragma unroll
+                for (int q4 = 0; q4 < (r + 3) / 4; ++q4) {
+                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(ab + r * AP + 4 * q4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * q4 + e < r) acc -= a4[e] * xc[4 * q4 + e];
+                }
+                xc[r] = acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sDi[gq * DIB + r * DIP + li] = xc[r];
+        }
+    };
+    // Right-looking block substitution with every operand in registers (waves 0 and 1, one
+    // 16-column tile of U each): each block's right-hand side R_I (rows 4 gq + i, column li)
+    // and U_I stay in the accumulator layout, which is also the B-operand layout of a
+    // 16x16x4 product whose step i pairs reduction slot gq with row 4 gq + i; so U_I feeds
+    // the updates R_J -= A_JI U_I (J > I) directly.  All reads are issued first (blocks past
+    // the tree are read but never used).
+    auto substitute = [&](const float* sDi) {
+        const int N = wave;
+        f32x4 R[4], di[4], aJI[6];  // aJI: (J, I) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) R[I][i] = sU[(16 * I + 4 * gq + i) * UP + 16 * N + li];
+            di[I] = *reinterpret_cast<const f32x4*>(sDi + I * DIB + li * DIP + 4 * gq);
+        }
+#pragma unroll
+        for (int J = 1, n = 0; J < 4; ++J)
+#pragma unroll
+            for (int I = 0; I < J; ++I, ++n)
+                aJI[n] = *reinterpret_cast<const f32x4*>(sA + (16 * J + li) * AP + 16 * I + 4 * gq);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            if (I < NB) {
+                f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) u = mfma4(di[I][i], R[I][i], u);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sU[(16 * I + 4 * gq + i) * UP + 16 * N + li] = u[i];
+#pragma unroll
+                for (int J = I + 1; J < 4; ++J) {
+                    if (J < NB) {
+                        const f32x4 a = aJI[J * (J - 1) / 2 + I];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) R[J] = mfma4(-a[i], u[i], R[J]);
+                    }
+                }
+            }
+        }
+    };
+
+    // ---- 5. O = Qt h0 + P U ----------------------------------------------------------------
+    auto outputs = [&](const f32x4 (&qh)[2], int colb) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tile = wave + 4 * u;
+            if (tile < 2 * NB) {
+                const int I = tile >> 1, N = tile & 1;
+                // P's row tile I is zero right of its diagonal tile: reduce over s < 16 (I + 1),
+                // lane group gq taking 4 (I + 1) of them
+                f32x4 acc = qh[u];
+                const float* rp = sP + (16 * I + li) * AP + gq * 4 * (I + 1);
+                const float* ub = sU + gq * 4 * (I + 1) * UP + 16 * N + li;
+                if (I == 0) acc = tile_rows_cols<4>(rp, ub, UP, acc);
+                else if (I == 1) acc = tile_rows_cols<8>(rp, ub, UP, acc);
+                else if (I == 2) acc = tile_rows_cols<12>(rp, ub, UP, acc);
+                else acc = tile_rows_cols<16>(rp, ub, UP, acc);
+                const int col = colb + 16 * N + li;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * I + 4 * gq + i;
+                    if (r < T) o[(((size_t)b * T + r) * HV + h) * DV + col] = acc[i];
+                }
+            }
+        }
+    };
+
+    // Several column blocks per workgroup only where the diagonal inverses and one staged
+    // block fit the key rows freed once A and P are formed (dk = 128); the host asks for
+    // one otherwise.
+    constexpr int DIP0 = 20, DIB0 = 16 * DIP0 + 16;
+    constexpr bool kMulti = 4 * DIB0 * 4 + 2 * CB * BP * 2 + CB * (TM + 4) * 4 <= 2 * TM * BP * 2;
+    const int nblk_w = kMulti ? ncbw : 1;
+
+    // The first column block: its h0 columns in sA's memory and its v tile in sP's, both
+    // dead once A and P are formed; the next block's reads are issued as soon as the
+    // registers are free, so they are in flight through this block.
+    stage(hv, vraw, reinterpret_cast<__bf16*>(sA), sP);
+    if (nblk_w > 1) load_block(col0 + CB, hv, vraw);
+    lds_barrier();  // decayed rows, h0 columns and v tile (read across threads below)
+    f32x4 qh[2];
+    rhs(reinterpret_cast<const __bf16*>(sA), sP, qh);
+    lds_barrier();
 
     // ---- 3. A and P tiles, masked by ancestry (upper tiles are zero) -----------------------
     // Only the NB(NB+1)/2 lower tiles of each hold products; they are dealt evenly to the
@@ -441,110 +575,64 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
             dst[r * AP + s] = val;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- 4. (I + A) U = rhs by 16-row blocks ----------------------------------------------
-    // A_rs is nonzero only for s an ancestor of r, so s < r: I + A is unit lower triangular
-    // and so is each diagonal block D_I.  Waves 0 and 1 (column tiles 0 and 1 of U) each
-    // invert every diagonal block into a private LDS copy (sKt or sKh, both free now), so
-    // no barrier separates the inversion from its use; lane (block gq, column li) runs
-    // forward substitution down column li of inv(D_gq) in registers.  Then block by block
-    //   U_I = inv(D_I) R_I,  R_J <- R_J - A_JI U_I  for J > I   (R starts as the rhs)
-    // with both products on the matrix cores, so U_I = inv(D_I) (rhs_I - sum_{J<I} A_IJ U_J).
-    constexpr int DIP = 20;            // inverse row pitch: 16-byte reads of 16 rows, no conflict
-    constexpr int DIB = 16 * DIP + 16; // inverse block stride
-    static_assert(4 * DIB * 4 <= 2 * TM * BP * 2, "block inverses must fit the free key rows");
-    if (wave < 2) {
-        float* sDi = reinterpret_cast<float*>(wave == 0 ? sKt : sKh);
-        if (gq < NB) {
-            const float* ab = sA + 16 * gq * AP + 16 * gq;  // diagonal block gq
-            float xc[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = r == li ? 1.f : 0.f;
-#pragma unroll
-                for (int q4 = 0; q4 < (r + 3) / 4; ++q4) {
-                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(ab + r * AP + 4 * q4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (4 * q4 + e < r) acc -= a4[e] * xc[4 * q4 + e];
-                }
-                xc[r] = acc;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sDi[gq * DIB + r * DIP + li] = xc[r];
+    // The diagonal inverses.  With one column block, waves 0 and 1 each invert every
+    // diagonal block into a private copy (sKt or sKh, both free now), so no barrier separates
+    // the inversion from its use.  With several, the decayed keys and queries stay live for
+    // the later blocks: wave 0 writes the one copy at the start of sKh, followed by the
+    // later blocks' staged h0 columns and v tiles.
+    float* sInv = reinterpret_cast<float*>(sKh);
+    __bf16* sHn = reinterpret_cast<__bf16*>(sInv + 4 * DIB);
+    float* sVn = reinterpret_cast<float*>(sHn + 2 * CB * BP);
+    static_assert(DIB == DIB0, "one inverse layout");
+    if (nblk_w == 1) {
+        if (wave < 2) {
+            float* sDi = reinterpret_cast<float*>(wave == 0 ? sKt : sKh);
+            invert_diag(sDi);
+            substitute(sDi);
         }
-        // Right-looking block substitution with every operand in registers: each block's
-        // right-hand side R_I (rows 4 gq + i, column li of this wave's column tile) and U_I
-        // stay in the accumulator layout, which is also the B-operand layout of a 16x16x4
-        // product whose step i pairs reduction slot gq with row 4 gq + i; so U_I feeds the
-        // updates R_J -= A_JI U_I (J > I) directly.  All reads are issued first (blocks past
-        // the tree are read but never used).
-        const int N = wave;
-        f32x4 R[4], di[4], aJI[6];  // aJI: (J, I) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) R[I][i] = sU[(16 * I + 4 * gq + i) * UP + 16 * N + li];
-            di[I] = *reinterpret_cast<const f32x4*>(sDi + I * DIB + li * DIP + 4 * gq);
-        }
-#pragma unroll
-        for (int J = 1, n = 0; J < 4; ++J)
-#pragma unroll
-            for (int I = 0; I < J; ++I, ++n)
-                aJI[n] = *reinterpret_cast<const f32x4*>(sA + (16 * J + li) * AP + 16 * I + 4 * gq);
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            if (I < NB) {
-                f32x4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) u = mfma4(di[I][i], R[I][i], u);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sU[(16 * I + 4 * gq + i) * UP + 16 * N + li] = u[i];
-#pragma unroll
-                for (int J = I + 1; J < 4; ++J) {
-                    if (J < NB) {
-                        const f32x4 a = aJI[J * (J - 1) / 2 + I];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) R[J] = mfma4(-a[i], u[i], R[J]);
-                    }
-                }
-            }
-        }
+    } else {
+        if (wave == 0) invert_diag(sInv);
+        lds_barrier();
+        if (wave < 2) substitute(sInv);
     }
-    __syncthreads();
+    lds_barrier();
+    outputs(qh, col0);
 
-    // ---- 5. O = Qt h0 + P U ----------------------------------------------------------------
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int tile = wave + 4 * u;
-        if (tile < 2 * NB) {
-            const int I = tile >> 1, N = tile & 1;
-            // P's row tile I is zero right of its diagonal tile: reduce over s < 16 (I + 1),
-            // lane group gq taking 4 (I + 1) of them
-            f32x4 acc = qh[u];
-            const float* rp = sP + (16 * I + li) * AP + gq * 4 * (I + 1);
-            const float* ub = sU + gq * 4 * (I + 1) * UP + 16 * N + li;
-            if (I == 0) acc = tile_rows_cols<4>(rp, ub, UP, acc);
-            else if (I == 1) acc = tile_rows_cols<8>(rp, ub, UP, acc);
-            else if (I == 2) acc = tile_rows_cols<12>(rp, ub, UP, acc);
-            else acc = tile_rows_cols<16>(rp, ub, UP, acc);
-            const int col = col0 + 16 * N + li;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * I + 4 * gq + i;
-                if (r < T) o[(((size_t)b * T + r) * HV + h) * DV + col] = acc[i];
-            }
-        }
+    // Later column blocks (several per workgroup when there are enough heads to fill the
+    // chip): the decayed rows, A, P and the inverses are reused.
+    for (int j = 1; j < nblk_w; ++j) {
+        stage(hv, vraw, sHn, sVn);
+        if (j + 1 < nblk_w) load_block(col0 + (j + 1) * CB, hv, vraw);
+        lds_barrier();  // staged block; the previous block's outputs have read sU
+        rhs(sHn, sVn, qh);
+        lds_barrier();
+        if (wave < 2) substitute(sInv);
+        lds_barrier();
+        outputs(qh, col0 + j * CB);
     }
+}
+
+// Column blocks per workgroup: with enough (batch, value head, column block) triples for
+// several rounds of workgroups, a workgroup takes 2 or 4 blocks of one head and forms the
+// decayed rows, A, P and the diagonal inverses once for all of them, as long as the
+// workgroups still fill the 256 CUs (dk = 128 only; see the kernel).
+inline int tree_blocks_per_group(long long B, int HV, int ncb, int dk) {
+    if (dk != 128) return 1;
+    for (int w : {4, 2})
+        if (ncb % w == 0 && B * HV * (ncb / w) >= 256) return w;
+    return 1;
 }
 
 template <typename TIn, typename TG, int DK, bool KN, bool GS>
 hipError_t launch_tree_t(const LaunchArgs& a, const int32_t* parent) {
-    const long long nblk = (long long)a.B * a.HV * (a.dv / CB);
+    const int ncb = a.dv / CB;
+    const int ncbw = tree_blocks_per_group(a.B, a.HV, ncb, DK);
+    const long long nblk = (long long)a.B * a.HV * (ncb / ncbw);
     hipLaunchKernelGGL((tree_verify_kernel<TIn, TG, DK, KN, GS>), dim3((unsigned)nblk), dim3(256), 0,
                        (hipStream_t)a.stream, parent, (const TIn*)a.q, (const TIn*)a.k,
-                       (const TIn*)a.v, (const TG*)a.g, a.beta, a.h0, a.o, a.T, a.HK, a.HV, a.HG, a.dv);
+                       (const TIn*)a.v, (const TG*)a.g, a.beta, a.h0, a.o, a.T, a.HK, a.HV, a.HG, a.dv, ncbw);
     return hipGetLastError();
 }
 

@@ -82,3 +82,18 @@ def test_tree_batched_and_deterministic():
     sub = {n: (x[n][:2] if x[n] is not None else None) for n in x}
     ref = oracle.tree(**sub, parent=par[:2].numpy())
     assert err(o1[:2], ref) < TOL
+
+
+@pytest.mark.parametrize("B,dtype,h0", [(4, torch.bfloat16, True), (8, torch.float32, False)],
+                         ids=["two_blocks_per_group", "four_blocks_per_group"])
+def test_tree_column_block_groups(B, dtype, h0):
+    """With enough heads (B * HV * dv/32 >= 512 at dk = 128) a workgroup takes 2 or 4
+    32-column blocks of one head and forms the decayed rows, A, P and the diagonal inverses
+    once for them: every batch element and head against the oracle."""
+    x, par = _case(B, 64, 16, 32, 128, 128, "random", seed=311 + B, dtype=dtype, h0=h0)
+    d = dev(x)
+    note(f"tree column-block groups B={B} {dtype} h0={h0}")
+    o = gdr.tree_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], par.cuda(), h0=d["h0"])
+    torch.cuda.synchronize()
+    ref = oracle.tree(**x, parent=par.numpy())
+    assert err(o, ref) < TOL
