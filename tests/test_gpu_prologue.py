@@ -111,3 +111,18 @@ def test_noalloc_prologue():
     o, ht = gdr.chunk_prefill_noalloc(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], chunk=64, **kw("kg"))
     torch.cuda.synchronize()
     assert err(o, o_ref) < TOL and err(ht, ht_ref) < TOL
+
+
+def test_tree_verify_prologue_grouped_blocks():
+    """Raw keys and gate logits on the tree path where a workgroup serves four column blocks
+    of a head (B=8, HV=32, 128x128)."""
+    B, T, HK, HV, dk, dv = 8, 64, 16, 32, 128, 128
+    x = raw_inputs(B, T, HK, HV, dk, dv, seed=83)
+    par = make_tree(B, T, "random", seed=5)
+    ref = oracle.tree(x["q"], oracle.l2_normalize_keys(x["k"]), x["v"], oracle.neg_softplus(x["g"]), x["beta"],
+                      x["h0"], parent=par.numpy())
+    d = dev(x)
+    note("prologue tree verify, grouped column blocks")
+    o = gdr.tree_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], par.cuda(), h0=d["h0"], **kw("kg"))
+    torch.cuda.synchronize()
+    assert err(o, ref) < TOL
