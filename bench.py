@@ -650,19 +650,19 @@ def bench_prefill(w, steps, warmup, g_bf16=False, graph=False, pre_warm_ms=0.0):
     prep_ms = _mean([e[0].elapsed_time(e[1]) for e in ev])
     carry_ms = _mean([e[1].elapsed_time(e[2]) for e in ev])
     graph_ms = None
-    if graph:  # the same call captured once and replayed `steps` times (no host launch cost)
+    if graph:  # `steps` calls captured into one graph and replayed (no host launch cost per call)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             gs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-            st = L.gdr_chunk_prefill(*args[:-1], gs)
-            if st != 0:
-                raise RuntimeError(f"gdr status {st} under capture")
+            for _ in range(steps):
+                st = L.gdr_chunk_prefill(*args[:-1], gs)
+                if st != 0:
+                    raise RuntimeError(f"gdr status {st} under capture")
         g.replay()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        for _ in range(steps):
-            g.replay()
+        g.replay()
         b.record()
         torch.cuda.synchronize()
         graph_ms = a.elapsed_time(b) / steps
@@ -1043,7 +1043,7 @@ def main():
         "ceiling_ms": round(ceil_ms, 5), "path_frac_of_ceiling": round(ceil_ms / kern_ms, 4),
         "tokens_per_s_kernel_time": round(ntok / (kern_ms * 1e-3), 1),
         "carry": carry_plan(w.B, w.T, w.HV, w.dk, w.dv, w.chunk),
-        # the same step replayed from a HIP graph: no host launch cost between the kernels
+        # the timed steps captured into one HIP graph and replayed: no host launch cost
         "graph_replay": None if graph_ms is None else {
             "ms_per_step": round(graph_ms, 5), "tokens_per_s": round(ntok / (graph_ms * 1e-3), 1)},
         "counters": {"chunk_prep": read_util("chunk_prep"), "chunk_carry": read_util("chunk_carry")},
