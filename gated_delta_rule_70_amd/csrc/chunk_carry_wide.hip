@@ -449,19 +449,20 @@ void carry_wide_kernel(
 }
 
 // Start states of the segments: slot 0 = h0 (or zeros), slot s + 1 = M_s slot s + S_loc_s.
-// Two workgroups per head, each owning CTC = D/32 16-column tiles (half the columns): every
-// workgroup needs all of M_s, so fewer, wider workgroups move fewer bytes per step.  Wave w
-// owns state row tiles 2w and 2w + 1, i.e. exactly the rows of one 32-wide reduction step,
-// which it publishes to the other waves as hi/lo fp16 B fragments.  M and S_loc of the
+// A workgroup per head and group of CTC 16-column tiles: every workgroup needs all of M_s,
+// so with many heads fewer, wider workgroups move fewer bytes per step, and with few heads
+// narrow ones spread the sequential walk over more CUs (combine_tiles below).  Wave w owns
+// state row tiles 2w and 2w + 1, i.e. exactly the rows of one 32-wide reduction step, which
+// it publishes to the other waves as hi/lo fp16 B fragments.  M and S_loc of the
 // next segment are requested while the current one is combined.  Range: the start state
 // enters the products as S 2^-E (E from its largest magnitude over the workgroup, one extra
 // exchange per step), so its hi/lo halves stay inside fp16's range; the transition M is a
 // product of non-expansive maps (|M_ij| <= 1 for stable updates) and needs no scale.
-template <int D>
+template <int D, int CTC>
 __global__ __launch_bounds__(2 * D) void carry_combine_kernel(const float* h0, const float* xsum,
                                                            float* sstart, int NH, int NSEG) {
     constexpr int KC = D / 32;
-    constexpr int CTC = D / 32;  // column tiles per workgroup
+    static_assert((D / 16) % CTC == 0, "column tiles per workgroup");
     __shared__ half8 sB[2][KC][CTC][2][64];
     __shared__ float sMx[2][KC];  // each wave's largest |S|
     const int bh = blockIdx.x % NH;
@@ -592,6 +593,16 @@ __global__ __launch_bounds__(2 * D) void carry_combine_kernel(const float* h0, c
     }
 }
 
+// Column tiles per combine workgroup: the fewest that keep the grid at or below 256
+// workgroups (one tile each for up to 32 heads at 128x128; B=1 HV=32 T=32768: 26.5 against
+// 38.7 us with two workgroups per head).
+inline int combine_tiles(int NH, int D) {
+    const int tiles = D / 16;
+    int ctc = 1;
+    while (ctc < tiles && (long long)NH * (tiles / ctc) > 256) ctc *= 2;
+    return ctc;
+}
+
 template <typename TIn, int D, int C>
 hipError_t launch_wide_t(const LaunchArgs& a, int NC, int NSEG) {
     const int NH = a.B * a.HV;
@@ -604,8 +615,16 @@ hipError_t launch_wide_t(const LaunchArgs& a, int NC, int NSEG) {
         hipLaunchKernelGGL((carry_wide_kernel<TIn, D, C, true>), dim3((unsigned)(NH * (NSEG - 1))), dim3(512),
                            0, st, (const TIn*)a.v, nullptr, nullptr, nullptr, ws, xsum, nullptr, a.B,
                            a.T, a.HV, NC, NSEG, a.plan);
-        hipLaunchKernelGGL((carry_combine_kernel<D>), dim3((unsigned)(NH * 2)), dim3(2 * D), 0, st,
-                           a.h0, (const float*)xsum, sstart, NH, NSEG);
+        const int ctc = combine_tiles(NH, D);
+        const unsigned nblk = (unsigned)(NH * (D / 16 / ctc));
+#define GDR_COMBINE(T_)                                                                        \
+    if constexpr ((D / 16) % T_ == 0) {                                                        \
+        if (ctc == T_)                                                                         \
+            hipLaunchKernelGGL((carry_combine_kernel<D, T_>), dim3(nblk), dim3(2 * D), 0, st,    \
+                               a.h0, (const float*)xsum, sstart, NH, NSEG);                    \
+    }
+        GDR_COMBINE(1) GDR_COMBINE(2) GDR_COMBINE(4) GDR_COMBINE(8)
+#undef GDR_COMBINE
     }
     hipLaunchKernelGGL((carry_wide_kernel<TIn, D, C, false>), dim3((unsigned)(NH * NSEG)), dim3(256), 0,
                        st, (const TIn*)a.v, a.h0, a.o, a.ht, ws, nullptr, (const float*)sstart, a.B,
