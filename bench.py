@@ -485,6 +485,43 @@ def varlen_lengths(n=32, seed=9, lo=1, hi=4097):
     return [int(round(float(x))) for x in np.exp(rng.uniform(np.log(lo), np.log(hi), n))]
 
 
+def bench_long(T=262144, reps=3):
+    """One sequence longer than a single launch addresses (HK=16 HV=32 128/128 C=64, bf16,
+    h0, the long-prefill recipe): gdr_chunk_prefill runs it as a chain of windows.  Wall time
+    per call, CUDA events on the launch stream."""
+    import torch
+
+    import gated_delta_rule_70_amd as gdr
+    from gdr_synth import make_inputs
+
+    HK, HV, dk, dv, C = 16, 32, 128, 128, 64
+    x = make_inputs(1, T, HK, HV, dk, dv, seed=23, h0=True, beta_mode="uniform_half", g_scale=0.1)
+    d = {n: (None if t is None else t.cuda()) for n, t in x.items()}
+    del x
+    print(f"long prefill: inputs of {T} tokens on the device", file=sys.stderr, flush=True)
+    need = gdr.workspace_bytes(1, T, HK, HV, dk, dv, C)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o = torch.empty(1, T, HV, dv, device="cuda")
+    ht = torch.empty(1, HV, dk, dv, device="cuda")
+
+    def call():
+        gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], chunk=C, o=o, ht=ht, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    W = 130944  # rows per window at HV=32, 128x128, C=64 (include/gdr.h)
+    return {"workload": f"B=1 T={T} HK={HK} HV={HV} {dk}x{dv} C={C} bf16, h0, g_scale 0.1, beta in [0.5, 1)",
+            "windows": -(-T // W), "workspace_bytes": need, "ms_per_call": round(ms, 4),
+            "tokens_per_s": round(T / (ms * 1e-3), 1), "finite": bool(torch.isfinite(o).all() and torch.isfinite(ht).all())}
+
+
 def bench_varlen(reps=10, warmup=2):
     """A packed batch of 32 sequences with a log-uniform length mix (1 .. 4097 rows) at
     HK=16 HV=32 128/128 C=64, bf16: one gdr_chunk_prefill_varlen call, against one
@@ -959,7 +996,7 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-util", metavar="UTIL_DIR")
     ap.add_argument("--summarize-stats", nargs=3, metavar=("DIR", "NAME", "COMMAND"))
-    ap.add_argument("--section", choices=("tree", "short_calls", "prologue", "gate_heads", "varlen"),
+    ap.add_argument("--section", choices=("tree", "short_calls", "prologue", "gate_heads", "varlen", "long"),
                     help="run only this part of the benchmark (tree-verify cases or short calls) "
                          "and print its JSON; for kernel traces of those kernels")
     ap.add_argument("--profile-name", default=HEADLINE_PROFILE,
@@ -1002,6 +1039,8 @@ def main():
             res = bench_gate_heads()
         elif args.section == "varlen":
             res = bench_varlen()
+        elif args.section == "long":
+            res = bench_long()
         else:
             res = bench_tree(DECODE) if args.section == "tree" else bench_short_calls(DECODE)
         print(json.dumps({"section": args.section, **res}), flush=True)
