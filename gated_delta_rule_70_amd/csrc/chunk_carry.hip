@@ -513,11 +513,16 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
 // S' = diag(exp(gam_last)) S + Kb^T U, then take the next step's state exponent.  Output
 // waves (row tile w) load, scale and publish the chunk's v rows with their exponent before
 // the first barrier, and form the outputs from the two exchanges: O_w^T = S^T Qt_w^T after
-// the first barrier and + U^T P_w^T after the second, then store them.  The v stream, the
-// output operands, products and stores thus stay out of the chain waves' instruction stream
-// and vector-memory counter (B=1 T=4097, HV=32, 128x128, the carry right after the prep
-// kernel: 80 against 82 us for the one-role kernel, bitwise the same results).  Each role
-// keeps its own ring of three operand sets, loaded two chunks ahead as above.
+// the first barrier and + U^T P_w^T after the second.  The v stream, the output operands,
+// products and stores thus stay out of the chain waves' instruction stream and vector-memory
+// counter.  Each role keeps its own ring of three operand sets, loaded two chunks ahead as
+// above, and spreads the loads of one set over the step: the chain waves issue Tb after the
+// first barrier (not ahead of the state publish), the output waves issue P after it, and a
+// chunk's outputs are stored one step late, after the next chunk's first barrier, so no
+// store sits in the queue ahead of the loads a step waits for.  B=1 T=4097, HV=32, 128x128,
+// the carry right after the prep kernel: 70.5 us against 80 with every load of a set issued
+// at the top of the step and the stores at its end, and 82 for the one-role kernel, all
+// bitwise the same results.
 template <typename TIn, int DK, int DV, int C>
 __global__ __launch_bounds__(128 * (C / 16)) void chunk_carry_roles_kernel(
     const TIn* __restrict__ v, const float* h0, float* __restrict__ o, float* ht,
@@ -653,7 +658,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void chunk_carry_roles_kernel(
     // Both roles pass the same barriers: B0, then B1(n) and B2(n) for every chunk n.
     if (outw) {
         // ---- output waves: v rows, Qt and P fragments of row tile w and the row multipliers,
-        // two chunks ahead; outputs stored as soon as they are formed ----
+        // two chunks ahead; each chunk's outputs stored during the next chunk's step ----
         const int rowo = HV * DV * 4;
         const rsrc_t rs_o = make_rsrc(o + (size_t)sp.row0 * HV * DV, (uint32_t)sp.T * rowo);
         struct OFr {
@@ -661,20 +666,34 @@ __global__ __launch_bounds__(128 * (C / 16)) void chunk_carry_roles_kernel(
             float qs, ps;
             uint32_t v[ELT];
         };
-        auto load_o = [&](OFr& F, int n) {
-            const int vrec = n * R.bytes + lane * 16;
+        auto load_ov = [&](OFr& F, int n) {
             load_v(n, F.v);
             asm volatile("" ::: "memory");
-#pragma unroll
-            for (int qs = 0; qs < NQS; ++qs) ld(F.p[qs], 2 * qs > w ? kBeyond : vrec, R.off_p + w * NQS + qs);
+        };
+        auto load_oq = [&](OFr& F, int n) {
+            const int vrec = n * R.bytes + lane * 16;
 #pragma unroll
             for (int p = 0; p < KC; ++p) ld(F.q[p], vrec, R.off_qt + w * KC + p);
             const int rs = n * R.bytes + (16 * w + li) * 4;
             F.qs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_rec, rs, R.nfrag * 1024 + R.qsc * 4, 0));
+        };
+        auto load_op = [&](OFr& F, int n) {
+            const int vrec = n * R.bytes + lane * 16;
+#pragma unroll
+            for (int qs = 0; qs < NQS; ++qs) ld(F.p[qs], 2 * qs > w ? kBeyond : vrec, R.off_p + w * NQS + qs);
+            const int rs = n * R.bytes + (16 * w + li) * 4;
             F.ps = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_rec, rs, R.nfrag * 1024 + R.psc * 4, 0));
         };
+        auto load_o = [&](OFr& F, int n) {
+            load_ov(F, n);
+            load_op(F, n);
+            load_oq(F, n);
+        };
+        f32x4 Opend = {0.f, 0.f, 0.f, 0.f};  // the previous chunk's outputs and their offset
+        int opend = -1;
         auto ostep = [&](OFr& F, OFr& Fn, int n, int nn, int par) {
-            load_o(Fn, nn);
+            load_ov(Fn, nn);
+            load_oq(Fn, nn);
 #pragma unroll
             for (int e = 0; e < ELT; ++e) asm volatile("" : "+v"(F.v[e]));
             {  // this row tile's v rows of chunk n, times 2^-ev, and their exponent
@@ -686,6 +705,8 @@ __global__ __launch_bounds__(128 * (C / 16)) void chunk_carry_roles_kernel(
                 if (lane == 0) sE[par][4 + w] = evn;
             }
             lds_barrier();  // B1(n)
+            if (opend >= 0) buf_store_f32x4_stream(Opend, rs_o, opend, 0);
+            load_op(Fn, nn);
             const Exps x = read_exps(par);
             half8 SB[KC];
             read_sb(SB, par, x);
@@ -703,7 +724,8 @@ __global__ __launch_bounds__(128 * (C / 16)) void chunk_carry_roles_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) Ov[i] = fmaf(OP[i], fp, OQ[i] * fq);
             const int obase = ((n * C + 16 * w + li) * HV + h) * DV * 4 + (16 * cg + 4 * gq) * 4;
-            buf_store_f32x4_stream(Ov, rs_o, obase, 0);
+            Opend = Ov;
+            opend = obase;
         };
         lds_barrier();  // B0
         if (nc > 0) {
@@ -718,6 +740,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void chunk_carry_roles_kernel(
             }
             if (n < nc) ostep(FA, FC, n, min(n + 2, nc - 1), 0);
             if (n + 1 < nc) ostep(FB, FA, n + 1, min(n + 3, nc - 1), 1);
+            buf_store_f32x4_stream(Opend, rs_o, opend, 0);
         }
         return;
     }
@@ -782,7 +805,6 @@ __global__ __launch_bounds__(128 * (C / 16)) void chunk_carry_roles_kernel(
         return scale_exponent(wave_max(ms));
     };
     auto step = [&](Frags& F, Frags& Fn, Frags& Fx, int n, int nn, int par) {
-        ld_g1(Fn, nn);
 #pragma unroll
         for (int j = 0; j < OWN; ++j) {
             const int ct = w + NW * j;
@@ -791,6 +813,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void chunk_carry_roles_kernel(
         }
         if (lane == 0) sE[par][w] = es;
         lds_barrier();  // B1(n)
+        ld_g1(Fn, nn);
         const Exps x = read_exps(par);
         half8 SB[KC];
         read_sb(SB, par, x);
