@@ -347,20 +347,23 @@ def prefill_flops(B, T, HV, dk, dv, C):
 
 def carry_plan(B, T, HV, dk, dv, C):
     """Which carry the library runs for these dims (its shape rule, restated for reporting):
-    the whole-head carry with more than 128 (batch, head) pairs, or with 256 / heads
-    segments when every segment gets at least 16 chunks; the column-split carry otherwise."""
+    the whole-head carry with more than 128 (batch, head) pairs, or, when the heads' 16-column
+    tiles fit 256 workgroups, with 256 / heads segments once every segment gets at least 16
+    chunks; the column-split carry otherwise."""
     nh, nc = B * HV, -(-T // C)
     if dk != dv or dk not in (64, 128):
         return "column-split"
     if nh > 128:
         return "whole-head, 1 segment"
+    if nh * (dv // 16) > 256:
+        return "column-split"
     want = 256 // nh
     if nc >= 16 * want:
         return f"whole-head, {want} segments"
     return "column-split"
 
 
-OTHER_PREFILLS = ("prefill_b8_t512", "prefill_b8_t97", "prefill_b1_t32768")
+OTHER_PREFILLS = ("prefill_b8_t512", "prefill_b8_t97", "prefill_b1_t32768", "prefill_b2_t4097")
 
 
 def bench_io_lean(w, steps=10, warmup=2):

@@ -906,11 +906,14 @@ template <typename TIn, int DK, int DV, int C>
 static hipError_t dispatch_split(const LaunchArgs& a) {
     constexpr int CT = DV / 16;
     const long long tiles = (long long)a.B * a.HV * CT;
+    // the fewest tiles per workgroup that keep the grid within one round of 256 workgroups
+    // (B = 4 T = 1024, HV = 32, 128 x 128: 59 us with 4 tiles against 108 with one, which
+    // needs four rounds)
     if constexpr (CT >= 4 && C >= 32) {
-        if (tiles > 1024) return launch_carry_t<TIn, DK, DV, C, 4>(a);
+        if (tiles > 512) return launch_carry_t<TIn, DK, DV, C, 4>(a);
     }
     if constexpr (CT >= 2) {
-        if (tiles > 1024) return launch_carry_t<TIn, DK, DV, C, 2>(a);
+        if (tiles > 256) return launch_carry_t<TIn, DK, DV, C, 2>(a);
     }
     return launch_carry_roles<TIn, DK, DV, C>(a);
 }

@@ -129,11 +129,15 @@ struct ChunkRecord {
 // first.  The whole-head carry (dk == dv in {64, 128}) is used where it beats the
 // column-split one on an MI355X (256 compute units):
 //   * more than 128 heads: one segment, one workgroup per head;
-//   * fewer heads but enough chunks that the sequence can be cut into 256 / heads segments
-//     of at least 16 chunks each: that many segments, so ~256 workgroups carry at once.
-// (Measured at HV = 32, 128 x 128: B = 8 T = 512 carry 57 vs 64 us, B = 4 T = 4097 349 vs
-// 572 us, B = 1 T = 32768 704 vs 779 us; B = 1 T = 4097, 8 segments of 8 chunks, 127 vs
-// 88 us, so the column-split carry keeps that case.)  With more than one segment the
+//   * heads whose 16-column tiles fit one round of 256 workgroups (heads * dv / 16 <= 256),
+//     with enough chunks that the sequence can be cut into 256 / heads segments of at least
+//     16 chunks each: that many segments, so ~256 workgroups carry at once.
+// Between the two, the column split takes 2 or 4 tiles per workgroup and so still runs in
+// one round.  (Carry right after the prep kernel at HV = 32, 128 x 128, chunk 64, whole
+// head / column split: B = 8 T = 512 57 / 64 us; B = 1 T = 8192 215 / 221 us, T = 16384
+// 371 / 408 us, T = 32768 704 / 779 us; B = 1 T = 4097, 8 segments of 8 chunks, 127 / 88 us;
+// B = 2 T = 4097 (4 segments) 209 / 147 us, B = 4 T = 4097 (2 segments) 365 / 217 us,
+// B = 3 T = 3000 263 / 143 us, B = 2 T = 8192 360 / 264 us.)  With more than one segment the
 // workspace also holds each segment's summary [S_loc | M] (fp32, [heads][nseg - 1][2][dk]
 // [dk]) and start state (fp32, [heads][nseg][dk][dv]).  A pure function of the dims, so
 // the size query and the launch agree.
@@ -158,7 +162,7 @@ inline CarryLayout carry_layout(int B, int HV, int T, int dk, int dv, int chunk,
     if (dims_ok) {
         if (NH > 128) {
             L.wide = true;
-        } else if (!varlen) {
+        } else if (!varlen && NH * (dv / 16) <= 256) {
             const long long want = 256 / NH;  // >= 2
             if (NC >= 16 * want) {
                 L.wide = true;

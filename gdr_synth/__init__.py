@@ -65,8 +65,13 @@ PREFILL_1x32768 = Workload("prefill_b1_t32768", B=1, T=32768, HK=16, HV=32, dk=1
                            beta_mode="uniform_half", g_scale=0.1,
                            note="long prefill, slow decay (conditioning stress)")
 
+# Beside the five: two sequences of the single-sequence shape, with initial states.
+PREFILL_2x4097 = Workload("prefill_b2_t4097", B=2, T=4097, HK=16, HV=32, dk=128, dv=128,
+                          chunk=64, dtype=torch.bfloat16, seed=6, h0=True,
+                          note="two sequences of 4097 tokens with initial state")
+
 WORKLOADS = {w.name: w for w in (TINY, DECODE, PREFILL_1x4097, PREFILL_8x512, PREFILL_8x97,
-                                 PREFILL_1x32768)}
+                                 PREFILL_1x32768, PREFILL_2x4097)}
 
 
 def make_inputs(B: int, T: int, HK: int, HV: int, dk: int, dv: int, *,

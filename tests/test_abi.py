@@ -247,8 +247,9 @@ def _records(B, T, HV, dk, C):
 
 
 def test_workspace_carry_segments(L):
-    """The segmented carry's extra workspace: with at most 128 (batch, head) pairs and
-    enough chunks for 256 / heads segments of >= 16 chunks each, every segment but the last
+    """The segmented carry's extra workspace: with at most 128 (batch, head) pairs whose
+    16-column tiles fit 256 workgroups and enough chunks for 256 / heads segments of >= 16
+    chunks each, every segment but the last
     keeps an fp32 [S_loc | M] summary (2 dk x dk matrices) and every segment a start state
     (dk x dv); otherwise the workspace is the chunk records alone."""
     def ws(**kw):
@@ -263,6 +264,13 @@ def test_workspace_carry_segments(L):
     # 32 heads, 65 chunks: too few for 8 segments of 16 -> column-split carry, records only
     kw = dict(B=1, HK=16, HV=32, dk=128, dv=128, chunk=64, T=4097)
     assert ws(**kw) == _records(1, 4097, 32, 128, 64)
+    # 64 heads (512 tiles): column split with 2 tiles per workgroup, records only; the same
+    # heads at dv = 64 (256 tiles) take 4 segments
+    kw = dict(B=2, HK=16, HV=32, dk=128, dv=128, chunk=64, T=4097)
+    assert ws(**kw) == _records(2, 4097, 32, 128, 64)
+    kw = dict(B=2, HK=16, HV=32, dk=64, dv=64, chunk=64, T=4100)
+    m64 = 64 * 64 * 4
+    assert ws(**kw) == _records(2, 4100, 32, 64, 64) + 64 * 3 * 2 * m64 + 64 * 4 * m64
     # 256 heads: whole-head carry with a single segment, records only
     kw = dict(B=8, HK=16, HV=32, dk=128, dv=128, chunk=64, T=512)
     assert ws(**kw) == _records(8, 512, 32, 128, 64)
@@ -295,6 +303,7 @@ def test_bench_carry_plan_matches_library(L):
     mat = lambda dk: dk * dk * 4
     for B, HV, T, dk, C in [(1, 32, 4097, 128, 64), (1, 32, 32768, 128, 64), (8, 32, 512, 128, 64),
                             (2, 32, 4097, 128, 64), (4, 32, 4097, 64, 32), (2, 32, 512, 128, 64),
+                            (2, 32, 4100, 64, 64), (3, 32, 3000, 128, 64), (1, 16, 20000, 128, 64),
                             (1, 2, 32768, 64, 16), (1, 2, 600, 64, 16), (1, 4, 9000, 32, 16)]:
         d = dims(B=B, HK=HV // 2 if HV > 1 else 1, HV=HV, dk=dk, dv=dk, chunk=C, T=T)
         got = L.gdr_chunk_prefill_workspace_bytes(ctypes.byref(d))

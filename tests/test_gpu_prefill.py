@@ -7,8 +7,10 @@ import torch
 
 import gated_delta_rule_70_amd as gdr
 import oracle
-from gdr_synth import PREFILL_1x4097, PREFILL_1x32768, PREFILL_8x97, PREFILL_8x512, TINY, workload_inputs
-from gpu_util import TOL, bf16_exact_unit_keys, dev, err, note, oracle_on_groups, small_inputs, token_err
+from gdr_synth import (PREFILL_1x4097, PREFILL_1x32768, PREFILL_2x4097, PREFILL_8x97, PREFILL_8x512, TINY,
+                       workload_inputs)
+from gpu_util import (TOL, bf16_exact_unit_keys, dev, err, note, oracle_on_groups, sampled_groups, small_inputs,
+                      token_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -56,7 +58,7 @@ def test_tiny_workload_full():
     assert err(o, o_ref) < TOL and err(ht, ht_ref) < TOL
 
 
-@pytest.mark.parametrize("w", [PREFILL_1x4097, PREFILL_8x512, PREFILL_8x97, PREFILL_1x32768],
+@pytest.mark.parametrize("w", [PREFILL_1x4097, PREFILL_8x512, PREFILL_8x97, PREFILL_1x32768, PREFILL_2x4097],
                          ids=lambda w: w.name)
 def test_measured_workloads_all_heads(w):
     """Full-size runs in the benchmark's launch configuration, every (batch, value head)
@@ -153,6 +155,38 @@ def test_chunk_size_invariance():
     o_ref, ht_ref = oracle.sequential(**x)
     for o, ht in res:
         assert err(o, o_ref) < TOL and err(ht, ht_ref) < TOL
+
+
+# (B, T, HK, HV, dk, dv, chunk, dtype): column tiles per carry workgroup in the comment
+MULTI_TILE = [(2, 300, 16, 32, 128, 128, 64, torch.bfloat16),   # 512 tiles: 2 per workgroup
+              (3, 200, 16, 32, 128, 128, 32, torch.bfloat16),   # 768 tiles: 4
+              (4, 150, 8, 32, 64, 64, 16, torch.float32),       # 512 tiles, chunk 16: 2
+              (4, 130, 16, 32, 128, 64, 64, torch.bfloat16),    # dk != dv, 512 tiles: 2
+              (2, 4097, 16, 32, 128, 128, 64, torch.bfloat16)]  # the B=2 T=4097 shape: 2
+
+
+@pytest.mark.parametrize("case", MULTI_TILE, ids=lambda c: "B{}T{}HV{}_{}x{}C{}".format(*c[:2], *c[3:7]))
+def test_column_split_multi_tile(case):
+    """Between 32 and 128 (batch, head) pairs at dv = 128 (or more tiles than 256 at other
+    shapes) the column-split carry takes 2 or 4 column tiles per workgroup so the grid stays
+    within 256 workgroups; sampled key-head groups (the first and last among them) against
+    the oracle, outputs and final state."""
+    B, T, HK, HV, dk, dv, C, dt = case
+    x = small_inputs(B, T, HK, HV, dk, dv, dtype=dt, seed=T + HV + C)
+    need = gdr.workspace_bytes(B, T, HK, HV, dk, dv, C)
+    assert need == B * HV * (-(-T // C)) * gdr.workspace_bytes(1, C, 1, 1, dk, dv, C)  # records only
+    note(f"multi-tile column split {case}")
+    d = dev(x)
+    o, ht = run_prefill(d, C)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(ht).all()
+    G = HV // HK
+    groups = sampled_groups(B, HK, 3, seed=T)
+    ref = oracle_on_groups(x, groups, G)
+    for (b, kh), (o_r, ht_r) in ref.items():
+        hv = slice(kh * G, (kh + 1) * G)
+        eo, es = err(o[b, :, hv].cpu(), o_r), err(ht[b, hv].cpu(), ht_r)
+        assert eo < TOL and es < TOL, f"group {(b, kh)}: o {eo:.2e} state {es:.2e}"
 
 
 @pytest.mark.parametrize("dk", [64, 128])

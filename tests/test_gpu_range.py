@@ -2,8 +2,9 @@
 and o is linear in q, so a copy of a passing case scaled by a power of two is an equally
 valid input and must pass the same bar against the fp64 oracle (run on the scaled
 inputs, which bf16 and fp32 represent exactly).  Every carry form is exercised: the
-column split with 4, 2 and 1 waves per workgroup (chunk 64, 32, 16), one workgroup per
-head (more than 128 heads) and the time-segmented carry (few heads, many chunks)."""
+column split with 4, 2 and 1 waves per workgroup (chunk 64, 32, 16) and with four column
+tiles per workgroup (96 heads), one workgroup per head (more than 128 heads) and the
+time-segmented carry (few heads, many chunks)."""
 import zlib
 
 import pytest
@@ -20,8 +21,9 @@ CASES = {
     "split_c64": (2, 200, 2, 4, 128, 128, 64),
     "split_c32": (2, 200, 2, 4, 128, 128, 32),
     "split_c16": (2, 120, 2, 4, 64, 64, 16),
+    "split_4_tiles": (3, 130, 16, 32, 128, 128, 64),
     "whole_head": (2, 150, 40, 80, 128, 128, 64),
-    "segmented": (4, 2100, 16, 32, 64, 64, 64),
+    "segmented": (2, 4100, 16, 32, 64, 64, 64),
 }
 SCALES = {
     "vh_up": {"v": 2.0 ** 14, "h0": 2.0 ** 14},
