@@ -70,11 +70,13 @@ KERNEL_SOURCES = {  # kernel -> the sources its machine code is built from
 }
 # kernel -> substrings that all appear in its (demangled) name in profiler output; the
 # column-split carry is chunk_carry_roles_kernel (one column tile per workgroup) or
-# chunk_carry_kernel (several), the whole-head carry's full and summary passes
-# are carry_wide_kernel<..., false> and <..., true>; the decode step is decode_kernel and a
-# multi-token fused recurrence token_kernel
+# chunk_carry_kernel (several), the whole-head carry's full and summary passes (fp32 o,
+# as the benchmark runs them) are carry_wide_kernel<..., false, false> and
+# <..., true, false>; the decode step is decode_kernel and a multi-token fused recurrence
+# token_kernel
 KERNEL_SYMBOL = {"chunk_prep": ("chunk_prep_kernel",), "chunk_carry": ("chunk_carry_",),
-                 "carry_full": ("carry_wide_kernel", "false>"), "carry_sum": ("carry_wide_kernel", "true>"),
+                 "carry_full": ("carry_wide_kernel", "false, false>"),
+                 "carry_sum": ("carry_wide_kernel", "true, false>"),
                  "carry_combine": ("carry_combine_kernel",),
                  "decode": ("decode_kernel",), "fused_recurrent": ("token_kernel",),
                  "tree_verify": ("tree_verify_kernel",)}
@@ -320,14 +322,14 @@ def summarize_stats(d, out_name, command):
     print(f"wrote {path}")
 
 
-def prefill_bytes(B, T, HK, HV, dk, dv, elt, h0, g_elt=4):
+def prefill_bytes(B, T, HK, HV, dk, dv, elt, h0, g_elt=4, o_elt=4):
     """Algorithmic HBM bytes of one prefill, split by the kernel that must move them.
 
     prep  : q, k (once per key head), g (g_elt bytes per value), beta
-    carry : v, o, the initial state (if any) and the final state
+    carry : v, o (o_elt bytes per value), the initial state (if any) and the final state
     """
     prep = B * T * (2 * HK * dk * elt + HV * (dk * g_elt + 4))
-    carry = B * T * HV * (dv * elt + dv * 4) + B * HV * dk * dv * 4 * (2 if h0 else 1)
+    carry = B * T * HV * (dv * elt + dv * o_elt) + B * HV * dk * dv * 4 * (2 if h0 else 1)
     return prep, carry
 
 
@@ -367,18 +369,35 @@ OTHER_PREFILLS = ("prefill_b8_t512", "prefill_b8_t97", "prefill_b1_t32768", "pre
 
 
 def bench_io_lean(w, steps=10, warmup=2):
-    """The same prefill with g stored as bf16 (GDR_G_BF16): per-stage kernel times and
-    throughput, and the path's algorithmic bytes at that input format."""
+    """The same prefill with g stored as bf16 (GDR_G_BF16), then also with o stored as bf16
+    (GDR_O_BF16): per-stage kernel times and throughput, and the path's algorithmic bytes at
+    each format."""
     import torch
 
-    x, o, ht, wall, prep_ms, carry_ms, _ = bench_prefill(w, steps, warmup, g_bf16=True, pre_warm_ms=100.0)
     elt = 2 if w.dtype == torch.bfloat16 else 4
-    b_prep, b_carry = prefill_bytes(w.B, w.T, w.HK, w.HV, w.dk, w.dv, elt, w.h0, g_elt=2)
-    kern = prep_ms + carry_ms
-    return {"workload": f"{w.name} with bf16 g", "prep_ms": round(prep_ms, 5), "carry_ms": round(carry_ms, 5),
-            "ms_per_step": round(wall / steps * 1e3, 5), "tokens_per_s": round(w.B * w.T / (wall / steps), 1),
-            "path_alg_bytes": b_prep + b_carry,
-            "path_hbm_frac": round((b_prep + b_carry) / (kern * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    out = {}
+    for key, o_bf16 in (("bf16 g", False), ("bf16 g and o", True)):
+        x, o, ht, wall, prep_ms, carry_ms, _ = bench_prefill(w, steps, warmup, g_bf16=True, o_bf16=o_bf16,
+                                                            pre_warm_ms=100.0)
+        b_prep, b_carry = prefill_bytes(w.B, w.T, w.HK, w.HV, w.dk, w.dv, elt, w.h0, g_elt=2,
+                                        o_elt=2 if o_bf16 else 4)
+        kern = prep_ms + carry_ms
+        r = {"workload": f"{w.name} with {key}", "prep_ms": round(prep_ms, 5), "carry_ms": round(carry_ms, 5),
+             "ms_per_step": round(wall / steps * 1e3, 5), "tokens_per_s": round(w.B * w.T / (wall / steps), 1),
+             "path_alg_bytes": b_prep + b_carry,
+             "path_hbm_frac": round((b_prep + b_carry) / (kern * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if not o_bf16:
+            out = r
+        else:
+            out["with_bf16_o"] = r
+    # where the carry is bound by HBM (the whole-head carry at many heads), o's bytes count most
+    from gdr_synth import WORKLOADS
+    w8 = WORKLOADS["prefill_b8_t512"]
+    x, o, ht, wall, prep_ms, carry_ms, _ = bench_prefill(w8, steps, warmup, o_bf16=True, pre_warm_ms=100.0)
+    out["prefill_b8_t512_bf16_o"] = {"prep_ms": round(prep_ms, 5), "carry_ms": round(carry_ms, 5),
+                                     "ms_per_step": round(wall / steps * 1e3, 5),
+                                     "tokens_per_s": round(w8.B * w8.T / (wall / steps), 1)}
+    return out
 
 
 def bench_prologue(w, steps=10, warmup=2):
@@ -627,7 +646,7 @@ def _mean(xs):
     return sum(xs) / len(xs)
 
 
-def bench_prefill(w, steps, warmup, g_bf16=False, graph=False, pre_warm_ms=0.0):
+def bench_prefill(w, steps, warmup, g_bf16=False, graph=False, pre_warm_ms=0.0, o_bf16=False):
     """Wall time of `steps` back-to-back prefills (gdr_chunk_prefill through the C ABI, its
     arguments marshalled once, so the host enqueues far faster than the GPU runs), then the
     per-stage kernel times from a second pass of the same calls with HIP events on the launch
@@ -644,13 +663,13 @@ def bench_prefill(w, steps, warmup, g_bf16=False, graph=False, pre_warm_ms=0.0):
         d["g"] = d["g"].to(torch.bfloat16)
     B, T, HK, HV, dk, dv, C = w.B, w.T, w.HK, w.HV, w.dk, w.dv, w.chunk
     ws = torch.empty(gdr.workspace_bytes(B, T, HK, HV, dk, dv, C), dtype=torch.uint8, device="cuda")
-    o = torch.empty(B, T, HV, dv, device="cuda")
+    o = torch.empty(B, T, HV, dv, device="cuda", dtype=torch.bfloat16 if o_bf16 else torch.float32)
     ht = torch.empty(B, HV, dk, dv, device="cuda")
     # one binding call validates the shapes; the timed calls reuse its marshalled arguments
     gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], chunk=C, o=o, ht=ht, workspace=ws)
     L = gdr.lib()
     dims = gdr.Dims(B, T, HK, HV, dk, dv, C, gdr.BF16 if w.dtype == torch.bfloat16 else gdr.F32,
-                    gdr.G_BF16 if g_bf16 else 0)
+                    (gdr.G_BF16 if g_bf16 else 0) | (gdr.O_BF16 if o_bf16 else 0))
     ptr = lambda t: ctypes.c_void_p(0 if t is None else t.data_ptr())
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     args = (ctypes.byref(dims), ptr(d["q"]), ptr(d["k"]), ptr(d["v"]), ptr(d["g"]), ptr(d["beta"]), ptr(d["h0"]),

@@ -12,7 +12,8 @@ if the library is missing, the calls raise.
 
 Layouts (dense, row-major, on the GPU): q, k ``[B,T,HK,dk]`` and v ``[B,T,HV,dv]`` in
 bf16 or fp32; g ``[B,T,HV,dk]`` and beta ``[B,T,HV]`` in fp32; states ``[B,HV,dk,dv]``
-fp32; o ``[B,T,HV,dv]`` fp32.
+fp32; o ``[B,T,HV,dv]`` fp32, or bf16 with ``out_dtype=torch.bfloat16`` (or a bf16 ``o``
+passed in): every entry point then stores each fp32 output rounded to nearest even.
 """
 from __future__ import annotations
 
@@ -25,10 +26,10 @@ __all__ = ["decode_step", "fused_recurrent", "chunk_prefill", "chunk_prefill_noa
            "tree_verify", "chunk_prefill_varlen", "fused_recurrent_varlen", "workspace_bytes_varlen",
            "NOALLOC_SCRATCH_BYTES", "VARLEN_MAX_SEQS",
            "workspace_bytes", "GdrError", "lib", "Dims", "LIB_PATH", "ABI_VERSION",
-           "RECURRENT_MAX_T", "TREE_MAX_T"]
+           "RECURRENT_MAX_T", "TREE_MAX_T", "O_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so")
-ABI_VERSION = 7
+ABI_VERSION = 8
 NOALLOC_SCRATCH_BYTES = 64 << 20  # gdr_chunk_prefill_noalloc: the library's per-device scratch
 RECURRENT_MAX_T = 8  # gdr_forward: calls of at most this many tokens take the fused recurrence
 TREE_MAX_T = 64      # gdr_tree_verify: most nodes per tree
@@ -39,6 +40,7 @@ G_SOFTPLUS = 0x4  # g given as gate logits a; the kernels use -softplus(a)
 G_PER_KEY_HEAD = 0x8  # g is [B,T,HK,dk]: one gate per key head, shared by its value heads
 PREP_SPLIT = 0x10  # prefill prep: one workgroup per key head (gram once per GQA group)
 PREP_FUSED = 0x20  # prefill prep: one workgroup per value head
+O_BF16 = 0x40  # o stored as bf16 (each fp32 output rounded to nearest even)
 PREP_SPLIT_MAX_GROUP = 8  # largest HV / HK the split prep serves
 VARLEN_MAX_SEQS = 4096  # most sequences in one packed variable-length call
 
@@ -127,6 +129,17 @@ def _need(t: torch.Tensor, name: str, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _out(o, shape, device, out_dtype):
+    """The output tensor: ``o`` if given, else a new one of ``out_dtype``.  Either way fp32
+    or bf16 (bf16: every entry point stores each fp32 output rounded to nearest even)."""
+    if o is None:
+        o = torch.empty(shape, device=device, dtype=out_dtype)
+    if o.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"o must be float32 or bfloat16, got {o.dtype}")
+    _need(o, "o")
+    return o
+
+
 def _dims(q, v, chunk, g=None, k_l2norm=False, g_softplus=False, prep="auto") -> Dims:
     """gdr_dims for the call.  The gate layout follows g's shape: [B,T,HK,dk] with HK != HV
     is a gate per key head (so is HK == HV with the split prep forced, where the two layouts
@@ -194,23 +207,22 @@ def workspace_bytes(B, T, HK, HV, dk, dv, chunk=64, dtype=torch.bfloat16) -> int
 
 
 def decode_step(q, k, v, g, beta, state, o=None, out_state=None, stream=None, k_l2norm=False,
-                g_softplus=False):
+                g_softplus=False, out_dtype=torch.float32):
     """One decode step (T == 1).  Updates ``state`` in place unless ``out_state`` is given.
 
     ``state`` may be None (zero initial state; then ``out_state`` receives the new state if
-    given).  Returns ``o`` ``[B,1,HV,dv]`` fp32.
+    given).  Returns ``o`` ``[B,1,HV,dv]`` (fp32, or ``out_dtype``).
     """
     ht = state if out_state is None else out_state
     B, T, HK, HV, dk, dv = _check_shapes(q, k, v, g, beta, h0=state, o=o, ht=ht)
     _check_inputs(q, k, v, g, beta)
     if state is not None:
         _need(state, "state", torch.float32)
-    if o is None:
-        o = torch.empty(B, T, HV, dv, device=q.device, dtype=torch.float32)
-    _need(o, "o", torch.float32)
+    o = _out(o, (B, T, HV, dv), q.device, out_dtype)
     if ht is not None:
         _need(ht, "out_state", torch.float32)
     d = _dims(q, v, 0, g, k_l2norm, g_softplus)
+    d.flags |= O_BF16 if o.dtype == torch.bfloat16 else 0
     _check(lib().gdr_decode_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                  _ptr(state), _ptr(o), _ptr(ht), _stream(stream)))
     return o
@@ -218,7 +230,7 @@ def decode_step(q, k, v, g, beta, state, o=None, out_state=None, stream=None, k_
 
 def chunk_prefill(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
                   workspace=None, want_state: bool = True, stream=None, stage: str = "both",
-                  k_l2norm=False, g_softplus=False, prep: str = "auto"):
+                  k_l2norm=False, g_softplus=False, prep: str = "auto", out_dtype=torch.float32):
     """Chunkwise WY/UT prefill over all T tokens.  Returns ``(o, ht)`` (``ht`` None if not wanted).
 
     ``workspace`` (optional) is a uint8 GPU tensor of at least ``workspace_bytes(...)``
@@ -233,14 +245,13 @@ def chunk_prefill(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
     _check_inputs(q, k, v, g, beta)
     if h0 is not None:
         _need(h0, "h0", torch.float32)
-    if o is None:
-        o = torch.empty(B, T, HV, dv, device=q.device, dtype=torch.float32)
-    _need(o, "o", torch.float32)
+    o = _out(o, (B, T, HV, dv), q.device, out_dtype)
     if ht is None and want_state:
         ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
     if ht is not None:
         _need(ht, "ht", torch.float32)
     d = _dims(q, v, chunk, g, k_l2norm, g_softplus, prep)
+    d.flags |= O_BF16 if o.dtype == torch.bfloat16 else 0
     need = int(lib().gdr_chunk_prefill_workspace_bytes(ctypes.byref(d)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
@@ -253,7 +264,7 @@ def chunk_prefill(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
 
 def chunk_prefill_noalloc(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None,
                           want_state: bool = True, stream=None, k_l2norm=False, g_softplus=False,
-                          prep: str = "auto"):
+                          prep: str = "auto", out_dtype=torch.float32):
     """gdr_chunk_prefill_noalloc: the chunked prefill with the library's own per-device
     scratch as workspace (no device allocation inside the call; pass ``o`` and ``ht`` to
     allocate nothing here either).  Returns ``(o, ht)``.  Calls needing more than
@@ -262,21 +273,20 @@ def chunk_prefill_noalloc(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht
     _check_inputs(q, k, v, g, beta)
     if h0 is not None:
         _need(h0, "h0", torch.float32)
-    if o is None:
-        o = torch.empty(B, T, HV, dv, device=q.device, dtype=torch.float32)
-    _need(o, "o", torch.float32)
+    o = _out(o, (B, T, HV, dv), q.device, out_dtype)
     if ht is None and want_state:
         ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
     if ht is not None:
         _need(ht, "ht", torch.float32)
     d = _dims(q, v, chunk, g, k_l2norm, g_softplus, prep)
+    d.flags |= O_BF16 if o.dtype == torch.bfloat16 else 0
     _check(lib().gdr_chunk_prefill_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                            _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht), _stream(stream)))
     return o, ht
 
 
 def fused_recurrent(q, k, v, g, beta, h0=None, o=None, ht=None, want_state: bool = True,
-                    stream=None, k_l2norm=False, g_softplus=False):
+                    stream=None, k_l2norm=False, g_softplus=False, out_dtype=torch.float32):
     """The token recurrence over all T tokens in one launch (gdr_fused_recurrent): the state
     stays on chip for the whole call.  Returns ``(o, ht)``; ``ht`` may be ``h0`` itself
     (in-place), and is None if not wanted."""
@@ -284,35 +294,34 @@ def fused_recurrent(q, k, v, g, beta, h0=None, o=None, ht=None, want_state: bool
     _check_inputs(q, k, v, g, beta)
     if h0 is not None:
         _need(h0, "h0", torch.float32)
-    if o is None:
-        o = torch.empty(B, T, HV, dv, device=q.device, dtype=torch.float32)
-    _need(o, "o", torch.float32)
+    o = _out(o, (B, T, HV, dv), q.device, out_dtype)
     if ht is None and want_state:
         ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
     if ht is not None:
         _need(ht, "ht", torch.float32)
     d = _dims(q, v, 0, g, k_l2norm, g_softplus)
+    d.flags |= O_BF16 if o.dtype == torch.bfloat16 else 0
     _check(lib().gdr_fused_recurrent(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                      _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht), _stream(stream)))
     return o, ht
 
 
 def forward(q, k, v, g, beta, h0=None, chunk: int = 64, o=None, ht=None, workspace=None,
-            want_state: bool = True, stream=None, k_l2norm=False, g_softplus=False, prep: str = "auto"):
+            want_state: bool = True, stream=None, k_l2norm=False, g_softplus=False, prep: str = "auto",
+            out_dtype=torch.float32):
     """Routed call (gdr_forward): the fused recurrence for T <= RECURRENT_MAX_T, the chunked
     prefill otherwise.  Returns ``(o, ht)``."""
     B, T, HK, HV, dk, dv = _check_shapes(q, k, v, g, beta, h0=h0, o=o, ht=ht)
     _check_inputs(q, k, v, g, beta)
     if h0 is not None:
         _need(h0, "h0", torch.float32)
-    if o is None:
-        o = torch.empty(B, T, HV, dv, device=q.device, dtype=torch.float32)
-    _need(o, "o", torch.float32)
+    o = _out(o, (B, T, HV, dv), q.device, out_dtype)
     if ht is None and want_state:
         ht = torch.empty(B, HV, dk, dv, device=q.device, dtype=torch.float32)
     if ht is not None:
         _need(ht, "ht", torch.float32)
     d = _dims(q, v, chunk, g, k_l2norm, g_softplus, prep)
+    d.flags |= O_BF16 if o.dtype == torch.bfloat16 else 0
     if T > RECURRENT_MAX_T and workspace is None:
         need = int(lib().gdr_chunk_prefill_workspace_bytes(ctypes.byref(d)))
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
@@ -363,7 +372,7 @@ def _packed(q, k, v, g, beta, cu_seqlens, h0, o, ht):
 
 def chunk_prefill_varlen(q, k, v, g, beta, cu_seqlens, h0=None, chunk: int = 64, o=None, ht=None,
                          workspace=None, want_state: bool = True, stream=None, k_l2norm=False,
-                         g_softplus=False, prep: str = "auto"):
+                         g_softplus=False, prep: str = "auto", out_dtype=torch.float32):
     """Chunked prefill of a packed batch (gdr_chunk_prefill_varlen): N sequences laid end
     to end in T rows, sequence i on rows ``[cu_seqlens[i], cu_seqlens[i+1])`` (an int32 GPU
     tensor), each run from its own ``h0[i]``.  Token tensors are ``[T, H, d]`` (or with a
@@ -373,14 +382,13 @@ def chunk_prefill_varlen(q, k, v, g, beta, cu_seqlens, h0=None, chunk: int = 64,
     _need(cu_seqlens, "cu_seqlens", torch.int32)
     if h0 is not None:
         _need(h0, "h0", torch.float32)
-    if o is None:
-        o = torch.empty(o_shape, device=q.device, dtype=torch.float32)
-    _need(o, "o", torch.float32)
+    o = _out(o, o_shape, q.device, out_dtype)
     if ht is None and want_state:
         ht = torch.empty(N, HV, dk, dv, device=q.device, dtype=torch.float32)
     if ht is not None:
         _need(ht, "ht", torch.float32)
     d = _dims(q4, v4, chunk, g4, k_l2norm, g_softplus, prep)
+    d.flags |= O_BF16 if o.dtype == torch.bfloat16 else 0
     d.B = N
     need = int(lib().gdr_chunk_prefill_varlen_workspace_bytes(ctypes.byref(d)))
     if workspace is None:
@@ -393,7 +401,7 @@ def chunk_prefill_varlen(q, k, v, g, beta, cu_seqlens, h0=None, chunk: int = 64,
 
 
 def fused_recurrent_varlen(q, k, v, g, beta, cu_seqlens, h0=None, o=None, ht=None, want_state: bool = True,
-                           stream=None, k_l2norm=False, g_softplus=False):
+                           stream=None, k_l2norm=False, g_softplus=False, out_dtype=torch.float32):
     """The fused token recurrence over a packed batch (gdr_fused_recurrent_varlen); layouts
     as for :func:`chunk_prefill_varlen`.  Returns ``(o, ht)``."""
     q4, k4, v4, g4, b4, o_shape, (N, T, HK, HV, dk, dv) = _packed(q, k, v, g, beta, cu_seqlens, h0, o, ht)
@@ -401,14 +409,13 @@ def fused_recurrent_varlen(q, k, v, g, beta, cu_seqlens, h0=None, o=None, ht=Non
     _need(cu_seqlens, "cu_seqlens", torch.int32)
     if h0 is not None:
         _need(h0, "h0", torch.float32)
-    if o is None:
-        o = torch.empty(o_shape, device=q.device, dtype=torch.float32)
-    _need(o, "o", torch.float32)
+    o = _out(o, o_shape, q.device, out_dtype)
     if ht is None and want_state:
         ht = torch.empty(N, HV, dk, dv, device=q.device, dtype=torch.float32)
     if ht is not None:
         _need(ht, "ht", torch.float32)
     d = _dims(q4, v4, 0, g4, k_l2norm, g_softplus)
+    d.flags |= O_BF16 if o.dtype == torch.bfloat16 else 0
     d.B = N
     _check(lib().gdr_fused_recurrent_varlen(ctypes.byref(d), _ptr(cu_seqlens), _ptr(q4), _ptr(k4), _ptr(v4),
                                             _ptr(g4), _ptr(b4), _ptr(h0), _ptr(o), _ptr(ht), _stream(stream)))
@@ -416,7 +423,7 @@ def fused_recurrent_varlen(q, k, v, g, beta, cu_seqlens, h0=None, o=None, ht=Non
 
 
 def tree_verify(q, k, v, g, beta, parent, h0=None, o=None, stream=None, k_l2norm=False,
-                g_softplus=False):
+                g_softplus=False, out_dtype=torch.float32):
     """Tree-verify solve (gdr_tree_verify): ``parent`` is an int32 GPU tensor ``[B,T]`` of
     parent node indices (-1: continues from ``h0``).  Returns ``o`` ``[B,T,HV,dv]``, each
     node's output along its root path."""
@@ -425,10 +432,9 @@ def tree_verify(q, k, v, g, beta, parent, h0=None, o=None, stream=None, k_l2norm
     _need(parent, "parent", torch.int32)
     if h0 is not None:
         _need(h0, "h0", torch.float32)
-    if o is None:
-        o = torch.empty(B, T, HV, dv, device=q.device, dtype=torch.float32)
-    _need(o, "o", torch.float32)
+    o = _out(o, (B, T, HV, dv), q.device, out_dtype)
     d = _dims(q, v, 0, g, k_l2norm, g_softplus)
+    d.flags |= O_BF16 if o.dtype == torch.bfloat16 else 0
     _check(lib().gdr_tree_verify(ctypes.byref(d), _ptr(parent), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                  _ptr(beta), _ptr(h0), _ptr(o), _stream(stream)))
     return o

@@ -91,10 +91,11 @@ __device__ __forceinline__ float raw_absmax(uint32_t x) {
     }
 }
 
-template <typename TIn, int DK, int DV, int C, int NT>
+template <typename TIn, int DK, int DV, int C, int NT, bool OBF>
 __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
-    const TIn* __restrict__ v, const float* h0, float* __restrict__ o, float* ht,
+    const TIn* __restrict__ v, const float* h0, void* __restrict__ o, float* ht,
     const unsigned char* __restrict__ ws, int B, int T, int HV, int NC, const int32_t* __restrict__ plan) {
+    constexpr int obf = OBF;  // o stored as bf16 (a compile-time choice: no branch per store)
     constexpr int NB = C / 16;
     constexpr int NW = NB;                    // one wave per 16-row tile of the chunk
     constexpr int NQS = (C + 31) / 32;
@@ -154,10 +155,11 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
     // index, row within a chunk) go to SGPRs; one per-lane offset is built per chunk.
     const unsigned char* rec0 = ws + ((size_t)sp.c0 * HV + (size_t)h * sp.nc) * R.bytes;
     const int rowv = HV * DV * ELT;  // bytes between consecutive tokens of v
-    const int rowo = HV * DV * 4;    // ... of o
+    const int rowo = HV * DV * o_elt(obf);  // ... of o
     const rsrc_t rs_rec = make_rsrc(rec0, (uint32_t)sp.nc * R.bytes);
     const rsrc_t rs_v = make_rsrc(v + (size_t)sp.row0 * HV * DV, (uint32_t)sp.T * rowv);
-    const rsrc_t rs_o = make_rsrc(o + (size_t)sp.row0 * HV * DV, (uint32_t)sp.T * rowo);
+    const rsrc_t rs_o =
+        make_rsrc(static_cast<unsigned char*>(o) + (size_t)sp.row0 * rowo, (uint32_t)sp.T * rowo);
 
     // v rows of a chunk.  Wave w loads rows 16w .. 16w+15 of its workgroup's 16*NT columns
     // with one vector load per 16-column tile (lane l: row l/4, four columns 4(l%4)..),
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
     auto store_o = [&](int n, const f32x4 (&O)[NT]) {
         const int obase = ((n * C + 16 * w + li) * HV + h) * DV * 4 + (16 * cg * NT + 4 * gq) * 4;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) buf_store_f32x4_stream(O[nt], rs_o, obase, nt * 64);
+        for (int nt = 0; nt < NT; ++nt) store_o4_stream(O[nt], rs_o, obase, nt * 64, obf);
     };
 
     // This wave's operand fragments, in registers, in a ring of three sets (the empty asm
@@ -523,10 +525,11 @@ __global__ __launch_bounds__(64 * (C / 16)) void chunk_carry_kernel(
 // the carry right after the prep kernel: 70.5 us against 80 with every load of a set issued
 // at the top of the step and the stores at its end, and 82 for the one-role kernel, all
 // bitwise the same results.
-template <typename TIn, int DK, int DV, int C>
+template <typename TIn, int DK, int DV, int C, bool OBF>
 __global__ __launch_bounds__(128 * (C / 16)) void chunk_carry_roles_kernel(
-    const TIn* __restrict__ v, const float* h0, float* __restrict__ o, float* ht,
+    const TIn* __restrict__ v, const float* h0, void* __restrict__ o, float* ht,
     const unsigned char* __restrict__ ws, int B, int T, int HV, int NC, const int32_t* __restrict__ plan) {
+    constexpr int obf = OBF;  // o stored as bf16 (a compile-time choice: no branch per store)
     constexpr int NT = 1;
     constexpr int NB = C / 16;
     constexpr int NW = NB;
@@ -659,8 +662,9 @@ __global__ __launch_bounds__(128 * (C / 16)) void chunk_carry_roles_kernel(
     if (outw) {
         // ---- output waves: v rows, Qt and P fragments of row tile w and the row multipliers,
         // two chunks ahead; each chunk's outputs stored during the next chunk's step ----
-        const int rowo = HV * DV * 4;
-        const rsrc_t rs_o = make_rsrc(o + (size_t)sp.row0 * HV * DV, (uint32_t)sp.T * rowo);
+        const int rowo = HV * DV * o_elt(obf);
+        const rsrc_t rs_o =
+            make_rsrc(static_cast<unsigned char*>(o) + (size_t)sp.row0 * rowo, (uint32_t)sp.T * rowo);
         struct OFr {
             half8 q[KC], p[NQS];
             float qs, ps;
@@ -705,7 +709,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void chunk_carry_roles_kernel(
                 if (lane == 0) sE[par][4 + w] = evn;
             }
             lds_barrier();  // B1(n)
-            if (opend >= 0) buf_store_f32x4_stream(Opend, rs_o, opend, 0);
+            if (opend >= 0) store_o4_stream(Opend, rs_o, opend, 0, obf);
             load_op(Fn, nn);
             const Exps x = read_exps(par);
             half8 SB[KC];
@@ -740,7 +744,7 @@ __global__ __launch_bounds__(128 * (C / 16)) void chunk_carry_roles_kernel(
             }
             if (n < nc) ostep(FA, FC, n, min(n + 2, nc - 1), 0);
             if (n + 1 < nc) ostep(FB, FA, n + 1, min(n + 3, nc - 1), 1);
-            buf_store_f32x4_stream(Opend, rs_o, opend, 0);
+            store_o4_stream(Opend, rs_o, opend, 0, obf);
         }
         return;
     }
@@ -878,24 +882,32 @@ __global__ __launch_bounds__(128 * (C / 16)) void chunk_carry_roles_kernel(
     }
 }
 
-template <typename TIn, int DK, int DV, int C>
-static hipError_t launch_carry_roles(const LaunchArgs& a) {
+template <typename TIn, int DK, int DV, int C, bool OBF>
+static hipError_t launch_carry_roles_o(const LaunchArgs& a) {
     const int NC = a.plan ? 0 : (a.T + C - 1) / C;
     const long long nblk = (long long)a.B * a.HV * (DV / 16);
-    hipLaunchKernelGGL((chunk_carry_roles_kernel<TIn, DK, DV, C>), dim3((unsigned)nblk), dim3(128 * (C / 16)), 0,
-                       (hipStream_t)a.stream, (const TIn*)a.v, a.h0, a.o, a.ht, (const unsigned char*)a.workspace, a.B,
-                       a.T, a.HV, NC, a.plan);
+    hipLaunchKernelGGL((chunk_carry_roles_kernel<TIn, DK, DV, C, OBF>), dim3((unsigned)nblk), dim3(128 * (C / 16)),
+                       0, (hipStream_t)a.stream, (const TIn*)a.v, a.h0, a.o, a.ht, (const unsigned char*)a.workspace,
+                       a.B, a.T, a.HV, NC, a.plan);
     return hipGetLastError();
 }
+template <typename TIn, int DK, int DV, int C>
+static hipError_t launch_carry_roles(const LaunchArgs& a) {
+    return a.o_bf16 ? launch_carry_roles_o<TIn, DK, DV, C, true>(a) : launch_carry_roles_o<TIn, DK, DV, C, false>(a);
+}
 
-template <typename TIn, int DK, int DV, int C, int NT>
-static hipError_t launch_carry_t(const LaunchArgs& a) {
+template <typename TIn, int DK, int DV, int C, int NT, bool OBF>
+static hipError_t launch_carry_o(const LaunchArgs& a) {
     const int NC = a.plan ? 0 : (a.T + C - 1) / C;  // packed batches: per sequence, from the plan
     const long long nblk = (long long)a.B * a.HV * (DV / (16 * NT));
-    hipLaunchKernelGGL((chunk_carry_kernel<TIn, DK, DV, C, NT>), dim3((unsigned)nblk),
+    hipLaunchKernelGGL((chunk_carry_kernel<TIn, DK, DV, C, NT, OBF>), dim3((unsigned)nblk),
                        dim3(64 * (C / 16)), 0, (hipStream_t)a.stream, (const TIn*)a.v, a.h0, a.o,
                        a.ht, (const unsigned char*)a.workspace, a.B, a.T, a.HV, NC, a.plan);
     return hipGetLastError();
+}
+template <typename TIn, int DK, int DV, int C, int NT>
+static hipError_t launch_carry_t(const LaunchArgs& a) {
+    return a.o_bf16 ? launch_carry_o<TIn, DK, DV, C, NT, true>(a) : launch_carry_o<TIn, DK, DV, C, NT, false>(a);
 }
 
 // Column split: with few heads every 16-column tile gets its own workgroup (the most

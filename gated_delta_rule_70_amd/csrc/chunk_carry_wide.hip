@@ -98,12 +98,13 @@ __device__ __forceinline__ int seg_begin(int s, int NC, int NSEG) {
 //              identity, without v); both are written to `xsum` at the segment's end.
 // The staged records fill most of the LDS, so one workgroup runs per CU (full pass: one wave
 // per SIMD; summary pass: two); the attribute states that occupancy to the compiler.
-template <typename TIn, int D, int C, bool SUM>
+template <typename TIn, int D, int C, bool SUM, bool OBF = false>
 __global__ __launch_bounds__(SUM ? 512 : 256) __attribute__((amdgpu_waves_per_eu(SUM ? 2 : 1, SUM ? 2 : 1)))
 void carry_wide_kernel(
-    const TIn* __restrict__ v, const float* h0, float* __restrict__ o, float* ht,
+    const TIn* __restrict__ v, const float* h0, void* __restrict__ o, float* ht,
     const unsigned char* __restrict__ ws, float* xsum, const float* sstart, int B, int T,
     int HV, int NCD, int NSEG, const int32_t* __restrict__ plan) {
+    constexpr int obf = OBF;  // o stored as bf16 (a compile-time choice: no branch per store)
     using ST = Stage<C, D, SUM>;
     constexpr ChunkRecord R = ST::R;
     constexpr int NB = ST::NB, NQS = ST::NQS, KC = ST::KC, DKT = ST::DKT;
@@ -191,9 +192,10 @@ void carry_wide_kernel(
     const unsigned char* rec0 = ws + ((size_t)sp.c0 * HV + (size_t)h * NC) * R.bytes;
     const rsrc_t rs_rec = make_rsrc(rec0, (uint32_t)NC * R.bytes);
     const int rowv = HV * D * ELT;
-    const int rowo = HV * D * 4;
+    const int rowo = HV * D * o_elt(obf);
     const rsrc_t rs_v = make_rsrc(v + (size_t)sp.row0 * HV * D, (uint32_t)sp.T * rowv);
-    const rsrc_t rs_o = make_rsrc(o + (size_t)sp.row0 * HV * D, (uint32_t)sp.T * rowo);
+    const rsrc_t rs_o =
+        make_rsrc(static_cast<unsigned char*>(o) + (size_t)sp.row0 * rowo, (uint32_t)sp.T * rowo);
 
     // Record staging: each wave copies its share of the copy list straight from memory into
     // the LDS buffer with LDS-DMA loads (16 bytes per lane, no registers); the copy of chunk
@@ -263,7 +265,7 @@ void carry_wide_kernel(
                 const int obase = on ? ((n * C + 16 * r + li) * HV + h) * D * 4 + (col0 + 4 * gq) * 4
                                      : (int)0xFFFFFF00u;
 #pragma unroll
-                for (int ct = 0; ct < CTW; ++ct) buf_store_f32x4_stream(Oq[r][ct], rs_o, obase, ct * 64);
+                for (int ct = 0; ct < CTW; ++ct) store_o4_stream(Oq[r][ct], rs_o, obase, ct * 64, obf);
             }
         }
     };
@@ -626,9 +628,14 @@ hipError_t launch_wide_t(const LaunchArgs& a, int NC, int NSEG) {
         GDR_COMBINE(1) GDR_COMBINE(2) GDR_COMBINE(4) GDR_COMBINE(8)
 #undef GDR_COMBINE
     }
-    hipLaunchKernelGGL((carry_wide_kernel<TIn, D, C, false>), dim3((unsigned)(NH * NSEG)), dim3(256), 0,
-                       st, (const TIn*)a.v, a.h0, a.o, a.ht, ws, nullptr, (const float*)sstart, a.B,
-                       a.T, a.HV, NC, NSEG, a.plan);
+    if (a.o_bf16)
+        hipLaunchKernelGGL((carry_wide_kernel<TIn, D, C, false, true>), dim3((unsigned)(NH * NSEG)), dim3(256), 0,
+                           st, (const TIn*)a.v, a.h0, a.o, a.ht, ws, nullptr, (const float*)sstart, a.B,
+                           a.T, a.HV, NC, NSEG, a.plan);
+    else
+        hipLaunchKernelGGL((carry_wide_kernel<TIn, D, C, false, false>), dim3((unsigned)(NH * NSEG)), dim3(256), 0,
+                           st, (const TIn*)a.v, a.h0, a.o, a.ht, ws, nullptr, (const float*)sstart, a.B,
+                           a.T, a.HV, NC, NSEG, a.plan);
     return hipGetLastError();
 }
 

@@ -43,9 +43,9 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
                                                     const TIn* __restrict__ v,
                                                     const TG* __restrict__ g,
                                                     const float* __restrict__ beta,
-                                                    const float* h0, float* __restrict__ o,
+                                                    const float* h0, void* __restrict__ o,
                                                     float* ht, int T, int HK, int HV, int HG,
-                                                    const int32_t* __restrict__ cu) {
+                                                    const int32_t* __restrict__ cu, int obf) {
     constexpr int BVD = DV < 64 ? DV : 64;   // columns per workgroup
     constexpr int NQ = BVD / 4;              // column quads per row
     constexpr int NRL = 256 / NQ;            // row lanes
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256) void token_kernel(const TIn* __restrict__ q,
         __syncthreads();
         if (tid < NQ) {
             const f32x4 out = red_o[0][cq] + red_o[1][cq] + red_o[2][cq] + red_o[3][cq];
-            *reinterpret_cast<f32x4*>(o + vb0 + tok * vb_t) = out;
+            store_o4(o, vb0 + tok * vb_t, out, obf);
         }
     }
     if (ht != nullptr) {
@@ -199,7 +199,7 @@ template <typename TIn, typename TG, int DK, int DV, bool KN, bool GS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
                    const TG* __restrict__ g, const float* __restrict__ beta, const float* h0,
-                   float* __restrict__ o, float* ht, int HK, int HV, int HG) {
+                   void* __restrict__ o, float* ht, int HK, int HV, int HG, int obf) {
     constexpr int BVD = DV < 64 ? DV : 64;
     constexpr int NQ = BVD / 4;
     constexpr int NRL = 256 / NQ;
@@ -301,7 +301,7 @@ void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const T
     __syncthreads();
     if (tid < NQ) {
         const f32x4 out = red_o[0][cq] + red_o[1][cq] + red_o[2][cq] + red_o[3][cq];
-        *reinterpret_cast<f32x4*>(o + vb) = out;
+        store_o4(o, vb, out, obf);
     }
     if (ht != nullptr) {
 #pragma unroll
@@ -317,11 +317,12 @@ static hipError_t launch_tokens_t(const LaunchArgs& a) {
     if (a.T == 1 && a.cu_seqlens == nullptr) {
         hipLaunchKernelGGL((decode_kernel<TIn, TG, DK, DV, KN, GS>), dim3((unsigned)nblk), dim3(256), 0,
                            (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
-                           (const TG*)a.g, a.beta, a.h0, a.o, a.ht, a.HK, a.HV, a.HG);
+                           (const TG*)a.g, a.beta, a.h0, a.o, a.ht, a.HK, a.HV, a.HG, (int)a.o_bf16);
     } else {
         hipLaunchKernelGGL((token_kernel<TIn, TG, DK, DV, KN, GS>), dim3((unsigned)nblk), dim3(256), 0,
                            (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
-                           (const TG*)a.g, a.beta, a.h0, a.o, a.ht, a.T, a.HK, a.HV, a.HG, a.cu_seqlens);
+                           (const TG*)a.g, a.beta, a.h0, a.o, a.ht, a.T, a.HK, a.HV, a.HG, a.cu_seqlens,
+                           (int)a.o_bf16);
     }
     return hipGetLastError();
 }

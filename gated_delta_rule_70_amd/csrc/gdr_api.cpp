@@ -78,7 +78,8 @@ bool tensor_sizes(const gdr_dims& d, size_t elt, Sizes* s, bool varlen) {
     const size_t btg = (d.flags & GDR_G_PER_KEY_HEAD) ? bth : btv;  // g rows: key or value heads
     if (!mul_ok(btg, (size_t)d.dk, &x) || !mul_ok(x, gelt, &s->g)) return false;
     if (!mul_ok(btv, 4, &s->beta)) return false;
-    if (!mul_ok(btv, (size_t)d.dv, &x) || !mul_ok(x, 4, &s->o)) return false;
+    const size_t oelt = (d.flags & GDR_O_BF16) ? 2 : 4;
+    if (!mul_ok(btv, (size_t)d.dv, &x) || !mul_ok(x, oelt, &s->o)) return false;
     size_t bh;
     if (!mul_ok((size_t)d.B, (size_t)d.HV, &bh) || !mul_ok(bh, (size_t)d.dk, &x) ||
         !mul_ok(x, (size_t)d.dv, &x) || !mul_ok(x, 4, &s->state))
@@ -93,7 +94,7 @@ enum class Path { decode, tokens, chunked };
 // Shared validation of dims, pointers, alignment and aliasing.  `cu` is the sequence
 // boundary array of a packed variable-length call (nullptr otherwise).
 int validate(const gdr_dims* d, Path path, const void* q, const void* k, const void* v,
-             const void* g, const float* beta, const float* h0, const float* o,
+             const void* g, const float* beta, const float* h0, const void* o,
              const float* ht, Sizes* sizes, const int32_t* cu = nullptr, bool varlen = false) {
     if (!d || !q || !k || !v || !g || !beta || !o || (varlen && !cu)) return GDR_ERR_NULL;
     if (d->B < 1 || d->T < 1 || d->HK < 1 || d->HV < 1 || d->HV % d->HK != 0) return GDR_ERR_SHAPE;
@@ -102,7 +103,7 @@ int validate(const gdr_dims* d, Path path, const void* q, const void* k, const v
     if (!supported_head_dim(d->dk) || !supported_head_dim(d->dv)) return GDR_ERR_UNSUPPORTED;
     if (d->qkv_dtype != GDR_BF16 && d->qkv_dtype != GDR_F32) return GDR_ERR_UNSUPPORTED;
     constexpr int32_t known = GDR_G_BF16 | GDR_K_L2NORM | GDR_G_SOFTPLUS | GDR_G_PER_KEY_HEAD |
-                              GDR_PREP_SPLIT | GDR_PREP_FUSED;
+                              GDR_PREP_SPLIT | GDR_PREP_FUSED | GDR_O_BF16;
     if ((d->flags & ~known) != 0) return GDR_ERR_UNSUPPORTED;
     if ((d->flags & GDR_G_BF16) && d->qkv_dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
     if ((d->flags & GDR_PREP_SPLIT) &&
@@ -143,7 +144,7 @@ int validate(const gdr_dims* d, Path path, const void* q, const void* k, const v
 }
 
 gdr::LaunchArgs make_args(const gdr_dims* d, const void* q, const void* k, const void* v,
-                          const void* g, const float* beta, const float* h0, float* o, float* ht,
+                          const void* g, const float* beta, const float* h0, void* o, float* ht,
                           void* workspace, void* stream, const int32_t* cu = nullptr) {
     gdr::LaunchArgs a{};
     a.B = d->B;
@@ -157,6 +158,7 @@ gdr::LaunchArgs make_args(const gdr_dims* d, const void* q, const void* k, const
     a.g_bf16 = (d->flags & GDR_G_BF16) != 0;
     a.k_l2norm = (d->flags & GDR_K_L2NORM) != 0;
     a.g_softplus = (d->flags & GDR_G_SOFTPLUS) != 0;
+    a.o_bf16 = (d->flags & GDR_O_BF16) != 0;
     const bool gk = (d->flags & GDR_G_PER_KEY_HEAD) != 0;
     a.HG = gk ? d->HK : d->HV;
     const int G = d->HV / d->HK;
@@ -262,7 +264,7 @@ const char* gdr_status_str(int status) {
 }
 
 int gdr_decode_step(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                    const void* g, const float* beta, const float* h0, float* o, float* ht,
+                    const void* g, const float* beta, const float* h0, void* o, float* ht,
                     void* stream) {
     Sizes s;
     const int st = validate(dims, Path::decode, q, k, v, g, beta, h0, o, ht, &s);
@@ -272,7 +274,7 @@ int gdr_decode_step(const gdr_dims* dims, const void* q, const void* k, const vo
 }
 
 int gdr_fused_recurrent(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                        const void* g, const float* beta, const float* h0, float* o, float* ht,
+                        const void* g, const float* beta, const float* h0, void* o, float* ht,
                         void* stream) {
     Sizes s;
     const int st = validate(dims, Path::tokens, q, k, v, g, beta, h0, o, ht, &s);
@@ -297,10 +299,11 @@ size_t gdr_chunk_prefill_varlen_workspace_bytes(const gdr_dims* dims) {
 // or, without ht, through a state slot after the window's records in the workspace.
 static int prefill_windows(const gdr_dims* dims, long long W, const void* q, const void* k,
                            const void* v, const void* g, const float* beta, const float* h0,
-                           float* o, float* ht, void* workspace, void* stream) {
+                           void* o, float* ht, void* workspace, void* stream) {
     const size_t elt = dims->qkv_dtype == GDR_F32 ? 4 : 2;
     const size_t gelt = (dims->flags & GDR_G_BF16) ? 2 : 4;
     const size_t HG = (dims->flags & GDR_G_PER_KEY_HEAD) ? dims->HK : dims->HV;
+    const size_t oelt = (dims->flags & GDR_O_BF16) ? 2 : 4;
     const size_t HK = dims->HK, HV = dims->HV, dk = dims->dk, dv = dims->dv;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     const size_t win = (gdr::carry_layout(1, dims->HV, (int)W, dims->dk, dims->dv, dims->chunk).total + 255) / 256 * 256;
@@ -319,7 +322,8 @@ static int prefill_windows(const gdr_dims* dims, long long W, const void* q, con
                                           static_cast<const unsigned char*>(k) + row * HK * dk * elt,
                                           static_cast<const unsigned char*>(v) + row * HV * dv * elt,
                                           static_cast<const unsigned char*>(g) + row * HG * dk * gelt,
-                                          beta + row * HV, hin, o + row * HV * dv, hout, ws, stream);
+                                          beta + row * HV, hin, static_cast<unsigned char*>(o) + row * HV * dv * oelt,
+                                          hout, ws, stream);
             if (gdr::launch_chunk_prep(a) != hipSuccess || gdr::launch_chunk_carry(a) != hipSuccess)
                 return GDR_ERR_HIP;
         }
@@ -328,7 +332,7 @@ static int prefill_windows(const gdr_dims* dims, long long W, const void* q, con
 }
 
 static int prefill_stages(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                          const void* g, const float* beta, const float* h0, float* o, float* ht,
+                          const void* g, const float* beta, const float* h0, void* o, float* ht,
                           void* workspace, size_t workspace_bytes, void* stream, bool prep,
                           bool carry, const int32_t* cu = nullptr) {
     Sizes s;
@@ -365,14 +369,14 @@ static int prefill_stages(const gdr_dims* dims, const void* q, const void* k, co
 }
 
 int gdr_chunk_prefill(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                      const void* g, const float* beta, const float* h0, float* o, float* ht,
+                      const void* g, const float* beta, const float* h0, void* o, float* ht,
                       void* workspace, size_t workspace_bytes, void* stream) {
     return prefill_stages(dims, q, k, v, g, beta, h0, o, ht, workspace, workspace_bytes, stream,
                           true, true);
 }
 
 int gdr_chunk_prefill_noalloc(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                              const void* g, const float* beta, const float* h0, float* o,
+                              const void* g, const float* beta, const float* h0, void* o,
                               float* ht, void* stream) {
     Sizes s;
     const int st = validate(dims, Path::chunked, q, k, v, g, beta, h0, o, ht, &s);
@@ -387,14 +391,14 @@ int gdr_chunk_prefill_noalloc(const gdr_dims* dims, const void* q, const void* k
 }
 
 int gdr_chunk_prep(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                   const void* g, const float* beta, const float* h0, float* o, float* ht,
+                   const void* g, const float* beta, const float* h0, void* o, float* ht,
                    void* workspace, size_t workspace_bytes, void* stream) {
     return prefill_stages(dims, q, k, v, g, beta, h0, o, ht, workspace, workspace_bytes, stream,
                           true, false);
 }
 
 int gdr_chunk_carry(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                    const void* g, const float* beta, const float* h0, float* o, float* ht,
+                    const void* g, const float* beta, const float* h0, void* o, float* ht,
                     void* workspace, size_t workspace_bytes, void* stream) {
     return prefill_stages(dims, q, k, v, g, beta, h0, o, ht, workspace, workspace_bytes, stream,
                           false, true);
@@ -402,7 +406,7 @@ int gdr_chunk_carry(const gdr_dims* dims, const void* q, const void* k, const vo
 
 int gdr_chunk_prefill_varlen(const gdr_dims* dims, const int32_t* cu_seqlens, const void* q,
                              const void* k, const void* v, const void* g, const float* beta,
-                             const float* h0, float* o, float* ht, void* workspace,
+                             const float* h0, void* o, float* ht, void* workspace,
                              size_t workspace_bytes, void* stream) {
     if (!cu_seqlens) return GDR_ERR_NULL;
     return prefill_stages(dims, q, k, v, g, beta, h0, o, ht, workspace, workspace_bytes, stream,
@@ -411,7 +415,7 @@ int gdr_chunk_prefill_varlen(const gdr_dims* dims, const int32_t* cu_seqlens, co
 
 int gdr_fused_recurrent_varlen(const gdr_dims* dims, const int32_t* cu_seqlens, const void* q,
                                const void* k, const void* v, const void* g, const float* beta,
-                               const float* h0, float* o, float* ht, void* stream) {
+                               const float* h0, void* o, float* ht, void* stream) {
     Sizes s;
     const int st = validate(dims, Path::tokens, q, k, v, g, beta, h0, o, ht, &s, cu_seqlens, true);
     if (st != GDR_OK) return st;
@@ -420,7 +424,7 @@ int gdr_fused_recurrent_varlen(const gdr_dims* dims, const int32_t* cu_seqlens, 
 }
 
 int gdr_tree_verify(const gdr_dims* dims, const int32_t* parent, const void* q, const void* k,
-                    const void* v, const void* g, const float* beta, const float* h0, float* o,
+                    const void* v, const void* g, const float* beta, const float* h0, void* o,
                     void* stream) {
     if (!parent) return GDR_ERR_NULL;
     Sizes s;
@@ -434,7 +438,7 @@ int gdr_tree_verify(const gdr_dims* dims, const int32_t* parent, const void* q, 
 }
 
 int gdr_forward(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                const void* g, const float* beta, const float* h0, float* o, float* ht,
+                const void* g, const float* beta, const float* h0, void* o, float* ht,
                 void* workspace, size_t workspace_bytes, void* stream) {
     if (dims && dims->T >= 1 && dims->T <= GDR_RECURRENT_MAX_T)
         return gdr_fused_recurrent(dims, q, k, v, g, beta, h0, o, ht, stream);

@@ -95,6 +95,42 @@ __device__ __forceinline__ void buf_store_f32x4_stream(f32x4 x, rsrc_t r, int vo
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, voff, soff, kStream);
 }
 
+// ---- outputs o: fp32, or bf16 when the caller asks for it (obf) ----------------------------
+// A bf16 output is the fp32 result rounded to the nearest bf16, ties to even (the hardware
+// conversion in the default rounding mode), as it is stored.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 bf16x4_bits(f32x4 x) {
+    const bf16x4v b = {static_cast<__bf16>(x[0]), static_cast<__bf16>(x[1]), static_cast<__bf16>(x[2]),
+                       static_cast<__bf16>(x[3])};
+    return __builtin_bit_cast(u32x2, b);
+}
+// Bytes per output element.
+__device__ __forceinline__ int o_elt(int obf) { return obf ? 2 : 4; }
+// Four consecutive outputs, given the byte offsets (voff, soff) they have in fp32 storage;
+// in bf16 storage they sit at half those offsets.  An offset beyond the buffer range drops
+// the store either way.
+__device__ __forceinline__ void store_o4_stream(f32x4 x, rsrc_t r, int voff, int soff, int obf) {
+    if (obf)
+        __builtin_amdgcn_raw_buffer_store_b64(bf16x4_bits(x), r, voff >> 1, soff >> 1, kStream);
+    else
+        buf_store_f32x4_stream(x, r, voff, soff);
+}
+// Four consecutive outputs at element index i of o (i a multiple of 4, o 16-byte aligned).
+__device__ __forceinline__ void store_o4(void* o, size_t i, f32x4 x, int obf) {
+    if (obf)
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + i) = bf16x4_bits(x);
+    else
+        *reinterpret_cast<f32x4*>(static_cast<float*>(o) + i) = x;
+}
+// One output at element index i of o.
+__device__ __forceinline__ void store_o1(void* o, size_t i, float x, int obf) {
+    if (obf)
+        static_cast<__bf16*>(o)[i] = static_cast<__bf16>(x);
+    else
+        static_cast<float*>(o)[i] = x;
+}
+
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
 // (lgkmcnt(0)), then s_barrier.  Unlike __syncthreads() it does not wait for outstanding
 // global/buffer loads (vmcnt), so prefetches stay in flight across it.  The empty asm

@@ -19,13 +19,14 @@ struct LaunchArgs {
     bool g_bf16;      // g stored as bf16 (only with bf16 q/k/v)
     bool k_l2norm;    // keys given raw: every kernel uses k / |k|_2 (fused prologue)
     bool g_softplus;  // g given as gate logits a: every kernel uses -softplus(a)
+    bool o_bf16;      // o stored as bf16 (each fp32 output rounded to nearest even)
     const void* q;
     const void* k;
     const void* v;
     const void* g;
     const float* beta;
     const float* h0;
-    float* o;
+    void* o;          // fp32, or bf16 with o_bf16
     float* ht;
     void* workspace;
     void* stream;

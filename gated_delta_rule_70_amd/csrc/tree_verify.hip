@@ -139,7 +139,8 @@ template <typename TIn, typename TG, int DK, bool KN, bool GS>
 __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int32_t* __restrict__ parent, const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* __restrict__ v, const TG* __restrict__ g, const float* __restrict__ beta,
-    const float* __restrict__ h0, float* __restrict__ o, int T, int HK, int HV, int HG, int DV, int ncbw) {
+    const float* __restrict__ h0, void* __restrict__ o, int T, int HK, int HV, int HG, int DV, int ncbw,
+    int obf) {
     constexpr int KP = DK + 4;   // row pitch (floats) of the fp32 g rows and decay prefixes
     constexpr int AP = TM + 4;
     constexpr int UP = CB + 4;
@@ -516,7 +517,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * I + 4 * gq + i;
-                    if (r < T) o[(((size_t)b * T + r) * HV + h) * DV + col] = acc[i];
+                    if (r < T) store_o1(o, (((size_t)b * T + r) * HV + h) * DV + col, acc[i], obf);
                 }
             }
         }
@@ -632,7 +633,8 @@ hipError_t launch_tree_t(const LaunchArgs& a, const int32_t* parent) {
     const long long nblk = (long long)a.B * a.HV * (ncb / ncbw);
     hipLaunchKernelGGL((tree_verify_kernel<TIn, TG, DK, KN, GS>), dim3((unsigned)nblk), dim3(256), 0,
                        (hipStream_t)a.stream, parent, (const TIn*)a.q, (const TIn*)a.k,
-                       (const TIn*)a.v, (const TG*)a.g, a.beta, a.h0, a.o, a.T, a.HK, a.HV, a.HG, a.dv, ncbw);
+                       (const TIn*)a.v, (const TG*)a.g, a.beta, a.h0, a.o, a.T, a.HK, a.HV, a.HG, a.dv, ncbw,
+                       (int)a.o_bf16);
     return hipGetLastError();
 }
 

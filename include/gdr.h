@@ -18,7 +18,8 @@
  *       g     [B][T][HV][dk]   log-decay, fp32 (bf16 with GDR_G_BF16; [B][T][HK][dk] with
  *                              GDR_G_PER_KEY_HEAD)
  *       beta  [B][T][HV]       fp32
- *       h0,ht [B][HV][dk][dv]  fp32 state       o     [B][T][HV][dv]  fp32
+ *       h0,ht [B][HV][dk][dv]  fp32 state       o     [B][T][HV][dv]  fp32 (bf16 with
+ *                                                                        GDR_O_BF16)
  *     value head h reads key head h / (HV/HK) (contiguous GQA groups).
  *   - h0 == NULL means a zero initial state; ht == NULL means the final state is not
  *     written.  ht may equal h0 exactly (in-place carry) but must not partially overlap
@@ -68,7 +69,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 7
+#define GDR_ABI_VERSION 8
 
 typedef enum {
     GDR_OK = 0,
@@ -135,13 +136,26 @@ typedef enum { GDR_BF16 = 0, GDR_F32 = 1 } gdr_dtype;
 #define GDR_PREP_SPLIT 0x10
 #define GDR_PREP_FUSED 0x20
 #define GDR_PREP_SPLIT_MAX_GROUP 8
+/*
+ * Output format (gdr_dims.flags).
+ *   GDR_O_BF16  o is stored as bf16: every output is computed in fp32 exactly as without the
+ *               flag and rounded to the nearest bf16 (ties to even) as it is stored, so the
+ *               call's o is bitwise the bf16 rounding of the same call's fp32 o; states
+ *               stay fp32.  The I/O-lean output of the follow-up work on the prefill's HBM
+ *               bytes: o (dv values per token and value head) is the prefill's largest
+ *               output.  Every entry point takes it, with either q/k/v dtype.  The rounding
+ *               alone moves each value by up to 2^-8 of it (about 1.7e-3 relative over a
+ *               tensor of normally distributed values), so the fp32 path's agreement with
+ *               the fp64 recurrence does not carry over to o below that level.
+ */
+#define GDR_O_BF16 0x40
 
 typedef struct {
     int32_t B, T, HK, HV, dk, dv;
     int32_t chunk;      /* prefill chunk length C (ignored by the token-recurrence calls)  */
     int32_t qkv_dtype;  /* gdr_dtype of q, k and v                                         */
-    int32_t flags;      /* GDR_G_BF16 | GDR_K_L2NORM | GDR_G_SOFTPLUS | GDR_G_PER_KEY_HEAD,
-                           GDR_PREP_SPLIT or GDR_PREP_FUSED                                  */
+    int32_t flags;      /* GDR_G_BF16 | GDR_K_L2NORM | GDR_G_SOFTPLUS | GDR_G_PER_KEY_HEAD |
+                           GDR_O_BF16, GDR_PREP_SPLIT or GDR_PREP_FUSED                      */
 } gdr_dims;
 
 /*
@@ -152,7 +166,7 @@ typedef struct {
  * Normally called in place (ht == h0).  Uses no workspace.
  */
 int gdr_decode_step(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                    const void* g, const float* beta, const float* h0, float* o, float* ht,
+                    const void* g, const float* beta, const float* h0, void* o, float* ht,
                     void* stream);
 
 /*
@@ -167,7 +181,7 @@ int gdr_decode_step(const gdr_dims* dims, const void* q, const void* k, const vo
  * gdr_decode_step.  Uses no workspace.
  */
 int gdr_fused_recurrent(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                        const void* g, const float* beta, const float* h0, float* o, float* ht,
+                        const void* g, const float* beta, const float* h0, void* o, float* ht,
                         void* stream);
 
 /*
@@ -192,7 +206,7 @@ size_t gdr_chunk_prefill_workspace_bytes(const gdr_dims* dims);
  * gdr_chunk_prefill_workspace_bytes(dims) bytes; its contents on entry are ignored.
  */
 int gdr_chunk_prefill(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                      const void* g, const float* beta, const float* h0, float* o, float* ht,
+                      const void* g, const float* beta, const float* h0, void* o, float* ht,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -214,10 +228,10 @@ int gdr_chunk_prefill(const gdr_dims* dims, const void* q, const void* k, const 
  * Splitting them lets a caller time or overlap the stages.
  */
 int gdr_chunk_prep(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                   const void* g, const float* beta, const float* h0, float* o, float* ht,
+                   const void* g, const float* beta, const float* h0, void* o, float* ht,
                    void* workspace, size_t workspace_bytes, void* stream);
 int gdr_chunk_carry(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                    const void* g, const float* beta, const float* h0, float* o, float* ht,
+                    const void* g, const float* beta, const float* h0, void* o, float* ht,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -230,7 +244,7 @@ int gdr_chunk_carry(const gdr_dims* dims, const void* q, const void* k, const vo
  */
 #define GDR_RECURRENT_MAX_T 8
 int gdr_forward(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                const void* g, const float* beta, const float* h0, float* o, float* ht,
+                const void* g, const float* beta, const float* h0, void* o, float* ht,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -267,7 +281,7 @@ int gdr_forward(const gdr_dims* dims, const void* q, const void* k, const void* 
 size_t gdr_chunk_prefill_varlen_workspace_bytes(const gdr_dims* dims);
 int gdr_chunk_prefill_varlen(const gdr_dims* dims, const int32_t* cu_seqlens, const void* q,
                              const void* k, const void* v, const void* g, const float* beta,
-                             const float* h0, float* o, float* ht, void* workspace,
+                             const float* h0, void* o, float* ht, void* workspace,
                              size_t workspace_bytes, void* stream);
 
 /*
@@ -276,7 +290,7 @@ int gdr_chunk_prefill_varlen(const gdr_dims* dims, const int32_t* cu_seqlens, co
  */
 int gdr_fused_recurrent_varlen(const gdr_dims* dims, const int32_t* cu_seqlens, const void* q,
                                const void* k, const void* v, const void* g, const float* beta,
-                               const float* h0, float* o, float* ht, void* stream);
+                               const float* h0, void* o, float* ht, void* stream);
 
 /*
  * Tree-verify solve (uzu PR #576, "Support TreeUpdateSolve kernel": a gram over a
@@ -293,7 +307,7 @@ int gdr_fused_recurrent_varlen(const gdr_dims* dims, const int32_t* cu_seqlens, 
  */
 #define GDR_TREE_MAX_T 64
 int gdr_tree_verify(const gdr_dims* dims, const int32_t* parent, const void* q, const void* k,
-                    const void* v, const void* g, const float* beta, const float* h0, float* o,
+                    const void* v, const void* g, const float* beta, const float* h0, void* o,
                     void* stream);
 
 /*
@@ -311,7 +325,7 @@ int gdr_tree_verify(const gdr_dims* dims, const int32_t* parent, const void* q, 
  */
 #define GDR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 int gdr_chunk_prefill_noalloc(const gdr_dims* dims, const void* q, const void* k, const void* v,
-                              const void* g, const float* beta, const float* h0, float* o,
+                              const void* g, const float* beta, const float* h0, void* o,
                               float* ht, void* stream);
 
 /* Static English text for a status code (never NULL). */

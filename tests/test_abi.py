@@ -315,10 +315,10 @@ def test_bench_carry_plan_matches_library(L):
 
 def test_input_format_flags(L):
     """gdr_dims.flags: GDR_G_BF16 (bf16 q/k/v only), GDR_K_L2NORM, GDR_G_SOFTPLUS,
-    GDR_G_PER_KEY_HEAD and one of GDR_PREP_SPLIT (needs a per-key-head gate and HV/HK <= 8)
-    or GDR_PREP_FUSED are defined; anything else is refused before any HIP call on every
-    entry point."""
-    for bad in (dict(flags=0x40), dict(flags=1 << 30), dict(flags=-1), dict(flags=1, qkv_dtype=1),
+    GDR_G_PER_KEY_HEAD, GDR_O_BF16 and one of GDR_PREP_SPLIT (needs a per-key-head gate and
+    HV/HK <= 8) or GDR_PREP_FUSED are defined; anything else is refused before any HIP call
+    on every entry point."""
+    for bad in (dict(flags=0x80), dict(flags=1 << 30), dict(flags=-1), dict(flags=1, qkv_dtype=1),
                 dict(flags=7, qkv_dtype=1),
                 dict(flags=0x10),                  # split prep without a per-key-head gate
                 dict(flags=0x38),                  # split and fused both forced
@@ -334,6 +334,25 @@ def test_bf16_g_extent_in_alias_checks(L):
     gbytes = 2 * 5 * 4 * 64 * 2
     assert prefill(L, dims(flags=1), o=addr(3, gbytes - 16)) == EALIAS
     assert prefill(L, dims(flags=0), o=addr(3, 2 * gbytes - 16)) == EALIAS  # fp32 g: twice the bytes
+
+
+def test_bf16_o_extent_in_alias_checks(L):
+    """With GDR_O_BF16, o spans B*T*HV*dv*2 bytes: ht over its last 16 bytes overlaps it, ht
+    right after it does not (which only an fp32 o would reach)."""
+    obytes = 2 * 5 * 4 * 32 * 2
+    assert prefill(L, dims(flags=0x40), ht=addr(6, obytes - 16)) == EALIAS
+    assert prefill(L, dims(flags=0), ht=addr(6, obytes)) == EALIAS
+    for entry in ("gdr_decode_step", "gdr_fused_recurrent"):
+        assert decode(L, dims(T=1, flags=0x40), entry=entry, ht=addr(6, 2 * 4 * 32 * 2 - 16)) == EALIAS
+
+
+@pytest.mark.skipif("_gpu_visible()", reason="valid fake pointers would reach a real GPU")
+def test_bf16_o_valid_arguments_reach_the_runtime_without_a_gpu(L):
+    obytes = 2 * 5 * 4 * 32 * 2
+    assert prefill(L, dims(flags=0x40), ht=addr(6, obytes)) == EHIP
+    assert prefill(L, dims(flags=0x41), ht=addr(6, obytes)) == EHIP  # with bf16 g
+    assert decode(L, dims(T=1, flags=0x40, qkv_dtype=1), ht=addr(6, 2 * 4 * 32 * 2)) == EHIP
+    assert tree(L, dims(T=8, dv=64, flags=0x40)) == EHIP
 
 
 @pytest.mark.skipif("_gpu_visible()", reason="valid fake pointers would reach a real GPU")
