@@ -74,6 +74,19 @@ def test_prefill_varlen_column_split(dims, C, dtype):
     check(o, ht, x, cu, lengths)
 
 
+@pytest.mark.parametrize("lengths,HV", [([1, 97, 300], 32), ([200, 0, 65, 1], 16)],
+                         ids=["3x32_heads_4_tiles", "4x16_heads_2_tiles"])
+def test_prefill_varlen_column_split_multi_tile(lengths, HV):
+    """Between 32 and 128 (sequence, head) pairs at dv = 128: the column-split carry with
+    4 (96 pairs) or 2 (64 pairs) column tiles per workgroup, sequences read from the plan."""
+    x, cu = packed_inputs(lengths, HV // 2, HV, 128, 128, seed=sum(lengths) + HV)
+    d = gpu(x)
+    note(f"varlen prefill multi-tile column split {lengths} HV={HV}")
+    o, ht = gdr.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], cu.cuda(), h0=d["h0"], chunk=64)
+    torch.cuda.synchronize()
+    check(o, ht, x, cu, lengths)
+
+
 def test_prefill_varlen_zero_h0_and_no_state():
     lengths = [33, 1, 70]
     x, cu = packed_inputs(lengths, 2, 4, 128, 128, seed=5, h0=False)
