@@ -302,9 +302,10 @@ __device__ __forceinline__ void prep_wave(const PrepCtx& s, const TIn* __restric
         for (int hh = 0; hh < 2; ++hh) {
             const int cb = 32 * p + 16 * hh + 4 * gq;
             f32x4 gv;
-            if constexpr (GE == 4) {
-                gv = buf_load_f32x4(rs_g, ((tr * HG + hg) * DK + cb) * 4, 0);
-            } else {  // four bf16 values, widened exactly
+            if constexpr (GE == 4) {  // g is read once: streamed, so it does not displace the records
+                gv = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rs_g, ((tr * HG + hg) * DK + cb) * 4, 0, kStream));
+            } else {  // four bf16 values, widened exactly (half the bytes; the default policy is faster)
                 const auto u = __builtin_amdgcn_raw_buffer_load_b64(rs_g, ((tr * HG + hg) * DK + cb) * 2, 0, 0);
                 gv = f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xFFFF0000u),
                            __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xFFFF0000u)};

@@ -82,14 +82,19 @@ __device__ __forceinline__ void buf_store_f32(float x, rsrc_t r, int voff, int s
 __device__ __forceinline__ void buf_store_f32x4(f32x4 x, rsrc_t r, int voff, int soff) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, voff, soff, 0);
 }
-// Cache-policy operand of stores whose data is not read again by the kernels that follow
-// (the gfx950 non-temporal bit): the prefill's outputs o.  Written that way they do not
-// displace the chunk records, which the carry reads right after the prep wrote them.
-// Measured at HV = 32, 128 x 128, C = 64: the carry takes 84.5 instead of 94 us at B = 1,
-// T = 4097, 57.6 instead of 64 us at B = 8, T = 512, 702 us either way at B = 1, T = 32768.
-// Streaming loads as well was measured and dropped: the log-decays in the prep (the prep
-// 4-16 us slower) and v in the whole-head carry (up to 30 % slower) lose by it, v in the
-// column-split carry gains nothing.
+// Cache-policy operand (the gfx950 non-temporal bit) of the accesses whose data no later
+// kernel of the prefill reads: the outputs o, stored by the carry, and the log-decays g
+// (fp32), loaded once by the prep.  That way neither displaces the chunk records from the
+// last-level cache, which the prep writes and the carry reads right after.  Measured at
+// HV = 32, 128 x 128, C = 64: o streamed, the carry takes 84.5 instead of 94 us at B = 1,
+// T = 4097 and 57.6 instead of 64 us at B = 8, T = 512; g streamed as well, 62.6 instead of
+// 72.1 us at B = 1, T = 4097 (the whole prefill 122 instead of 132 us) and 55.6 instead of
+// 61.0 us at B = 8, T = 512, the prep unchanged.  Where the records outgrow the cache
+// (B = 2, T = 4097; B = 1, T = 32768) neither changes anything.  Streaming q and k as well
+// slows the prep by 10-17 % (each key head's rows serve the G value heads of its group
+// through L2), v in the column-split carry by 13 % (its 8 column groups share each v
+// line), v in the whole-head carry by up to 30 %; a bf16 g streamed slows the prep by 9 %
+// (59.9 against 65.1 us at B = 1, T = 4097) and is read with the default policy.
 constexpr int kStream = 2;
 __device__ __forceinline__ void buf_store_f32x4_stream(f32x4 x, rsrc_t r, int voff, int soff) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, voff, soff, kStream);
