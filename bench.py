@@ -1095,8 +1095,16 @@ def main():
     path_tflops = (f_prep + f_carry) / (kern_ms * 1e-3) / 1e12
     # the path's ceiling: its algorithmic bytes at HBM peak or its flops at MFMA peak
     ceil_ms = max((b_prep + b_carry) / (HBM_PEAK_GBS * 1e9), (f_prep + f_carry) / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+    # both stages against the HBM peak by their own algorithmic bytes (the roofline line above
+    # is the longer one's)
+    per_kernel = {}
+    for k, ms, nb in (("chunk_prep", prep_ms, b_prep), ("chunk_carry", carry_ms, b_carry)):
+        gbs = nb / (ms * 1e-3) / 1e9
+        per_kernel[k] = {"achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "alg_bytes_per_launch": nb, "traffic": read_traffic(k)}
     prefill = {
         "kernels_ms": {"chunk_prep": round(prep_ms, 5), "chunk_carry": round(carry_ms, 5)},
+        "kernels_hbm": per_kernel,
         "path_alg_bytes": b_prep + b_carry, "path_alg_flops": f_prep + f_carry,
         "path_hbm_GBps": round(path_gbs, 1), "path_hbm_frac": round(path_gbs / HBM_PEAK_GBS, 4),
         "path_mfma_TFLOPs": round(path_tflops, 2),
