@@ -176,3 +176,36 @@ def test_windowed_prefill_bf16_o():
         a = o16[:, t0:t0 + 16384].view(torch.int16)
         b = o32[:, t0:t0 + 16384].to(torch.bfloat16).view(torch.int16)
         assert torch.equal(a, b), t0
+
+
+@pytest.mark.parametrize("gate_heads", ["value", "key"])
+def test_bf16_o_with_prologue_and_gate_heads(gate_heads):
+    """bf16 o combined with raw keys and gate logits (the fused prologue) and with a gate per
+    key head or per value head: the prefill (both prep forms where the gate is per key head)
+    and the decode step, each bitwise the rounded fp32 o of the same call."""
+    B, T, HK, HV, dk = 2, 150, 2, 8, 128
+    x = make_inputs(B, T, HK, HV, dk, dk, seed=78, h0=True, gate_heads=gate_heads)
+    gen = torch.Generator("cpu").manual_seed(79)
+    scale = torch.exp(torch.empty(B, T, HK, 1).uniform_(-2.3, 2.3, generator=gen))
+    x["k"] = (x["k"].float() * scale).to(torch.bfloat16)
+    x["g"] = torch.randn(x["g"].shape, generator=gen)
+    d = dev(x)
+    flags = dict(k_l2norm=True, g_softplus=True)
+    preps = ["fused", "split"] if gate_heads == "key" else ["auto"]
+    for prep in preps:
+        note(f"bf16 o with prologue, gate per {gate_heads} head, prep {prep}")
+        o32, h32 = gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], chunk=64, prep=prep,
+                                     **flags)
+        o16, h16 = gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], chunk=64, prep=prep,
+                                     out_dtype=torch.bfloat16, **flags)
+        torch.cuda.synchronize()
+        same(o16, o32)
+        assert torch.equal(h16, h32)
+    t1 = {n: (None if t is None else (t[:, :1].contiguous() if t.dim() >= 3 and n != "h0" else t))
+          for n, t in d.items()}
+    s32, s16 = d["h0"].clone(), d["h0"].clone()
+    o32 = gdr.decode_step(t1["q"], t1["k"], t1["v"], t1["g"], t1["beta"], s32, **flags)
+    o16 = gdr.decode_step(t1["q"], t1["k"], t1["v"], t1["g"], t1["beta"], s16, out_dtype=torch.bfloat16, **flags)
+    torch.cuda.synchronize()
+    same(o16, o32)
+    assert torch.equal(s16, s32)
